@@ -1,0 +1,227 @@
+"""Throughput of the tiled ViT tower on one MI355X.
+
+A step is one forward pass of the whole path -- patchify + patch embed, the
+32 blocks (LayerNorm, QKV, tiled RoPE attention, O, LayerNorm, MLP), the
+raster-order tower output, the 2x2 merge and the projector -- over one batch
+of synthetic input that is already resident in device memory.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload tower_448]
+
+Prints one JSON line.  Beside the headline workload it times, with HIP events
+on the stream the kernels run on, the dominant kernel (the bf16 GEMM at the
+FC1 shape) and the attention kernel through their own entry points, and the
+2016x2016 single image as a secondary workload.  The CPU oracle is timed on a
+bounded sample (one 448x448 image through the full tower) on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA, 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0
+
+
+def gemm_flops_per_token(d=1280, mlp=5120, P=6144):
+    """Algorithmic GEMM FLOPs per token for one block and for the projector."""
+    block = 2 * (3 * d * d + d * d + 2 * d * mlp)
+    proj = 2 * (d * P + P * P) + 2 * (4 * P * P + P * P) / 4
+    return block, proj
+
+
+def workload_flops(wl):
+    N = wl.tokens
+    block, proj = gemm_flops_per_token()
+    gemm = N * (2 * 1176 * 1280 + wl.layers * block + (proj if wl.projector else 0))
+    attn = wl.layers * sum(4 * (h * w) ** 2 * 1280 for _, h, w in wl.grids)
+    return gemm, attn
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="tower_448", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--secondary", default="tower_2016", help="second workload ('' to skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-iters", type=int, default=20)
+    return ap.parse_args()
+
+
+class Runner:
+    def __init__(self, vt, torch, tw, wl):
+        self.vt, self.torch, self.tw, self.wl = vt, torch, tw, wl
+        self.grids = list(wl.grids)
+        self.cfg = vt.config(layers=wl.layers)
+        N = wl.tokens
+        self.px = torch.from_numpy(synth.make_batch_pixels(wl).view(np.int16)).cuda()
+        self.ws = vt.workspace(vt.vt_tower_workspace_size(self.cfg, self.grids))
+        self.tower = torch.empty((N, 1280), dtype=torch.int16, device="cuda")
+        self.out = (torch.empty((N // 4, 6144), dtype=torch.int16, device="cuda")
+                    if wl.projector else None)
+
+    def step(self):
+        self.vt.vt_tower_forward(self.cfg, self.px, self.grids, self.tw, self.tower, None,
+                                 self.out, self.ws)
+
+    def time(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        s.record()
+        for _ in range(steps):
+            self.step()
+        e.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return s.elapsed_time(e) / 1e3, wall
+
+
+def time_kernel(torch, fn, iters):
+    """Average duration of one launch sequence of ``fn`` with HIP events
+    recorded on the current stream, the stream the library launches on."""
+    fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / 1e3 / iters
+
+
+def gemm_roofline(vt, torch, M, iters):
+    """The FC1 GEMM (M x 5120 x 1280, bias + GELU epilogue) on its own."""
+    N, K = 5120, 1280
+    g = np.random.Generator(np.random.PCG64(0))
+    x = torch.from_numpy(synth.bf16_bits(g.standard_normal((M, K), dtype=np.float32)).view(np.int16)).cuda()
+    w = torch.from_numpy(synth.bf16_bits(g.standard_normal((N, K), dtype=np.float32) * 0.02).view(np.int16)).cuda()
+    b = torch.zeros(N, dtype=torch.int16, device="cuda")
+    out = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    ws = vt.workspace(vt.vt_linear_workspace_size(M, N, K))
+    t = time_kernel(torch, lambda: vt.vt_linear(x, M, K, w, N, b, vt.VT_EPI_GELU_TANH_BF16, out, ws), iters)
+    flops = 2.0 * M * N * K
+    return {"kernel": "gemm_kernel (FC1: %d x %d x %d, bias+GELU epilogue)" % (M, N, K),
+            "bound": "mfma", "achieved": flops / t / 1e12, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": flops / t / 1e12 / PEAK_BF16_TFLOPS, "traffic": None,
+            "flops_per_launch": flops, "avg_launch_us": t * 1e6}
+
+
+def attention_roofline(vt, torch, grids, iters):
+    """vt_attention_varlen on the workload's token layout (random bf16 q, k, v)."""
+    N = sum(h * w for _, h, w in grids)
+    g = np.random.Generator(np.random.PCG64(1))
+    qkv = torch.from_numpy(synth.bf16_bits(g.standard_normal((N, 3840), dtype=np.float32) * 0.7).view(np.int16)).cuda()
+    cfg = vt.config()
+    cu = torch.empty(len(grids) + 1, dtype=torch.int32, device="cuda")
+    pos = torch.empty((N, 3), dtype=torch.int32, device="cuda")
+    vt.vt_build_metadata(grids, cu, pos)
+    max_seq = max(h * w for _, h, w in grids)
+    ws = vt.workspace(vt.vt_block_workspace_size(cfg, N, len(grids), max_seq))
+    out = torch.empty((N, 1280), dtype=torch.int16, device="cuda")
+    t = time_kernel(torch, lambda: vt.vt_attention_varlen(cfg, qkv, cu, pos, len(grids), N, max_seq,
+                                                          out, vt.VT_BF16, ws), iters)
+    flops = float(sum(4 * (h * w) ** 2 * 1280 for _, h, w in grids))
+    return {"kernel": "attention_kernel (%d tokens, %d images)" % (N, len(grids)), "bound": "mfma",
+            "achieved": flops / t / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": flops / t / 1e12 / PEAK_BF16_TFLOPS, "flops_per_launch": flops,
+            "avg_launch_us": t * 1e6, "note": "average includes the schedule and RoPE-table prologue kernels"}
+
+
+def cpu_baseline(weights):
+    """The oracle, untuned, on one 448x448 image through the full tower."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    wl = synth.WORKLOADS["tower_448"]
+    px = synth.make_batch_pixels(wl)
+    t0 = time.perf_counter()
+    oracle.tower_forward(px, list(wl.grids), weights)
+    dt = time.perf_counter() - t0
+    return {"value": wl.tokens / dt, "unit": "patches/s", "cores": int(threads), "kind": "oracle",
+            "sample": "one 448x448 image (1024 patches) through the 32-layer tower, merge and "
+                      "projector, numpy fp32 on the host, %.1f s" % dt,
+            "host_cpus": os.cpu_count(),
+            "usable_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus %d is not supported "
+                                   "(the multi-GPU sharding is a design note, not code)" % a.gpus}))
+        sys.exit(2)
+    import torch
+    import vision_transformer_encoder_tiled_amd as vt
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    wl = synth.WORKLOADS[a.workload]
+    weights = synth.make_weights(32, projector=True)
+    dev = {k: torch.from_numpy(v.view(np.int16)).cuda() for k, v in weights.items()}
+    tw = vt.TowerWeights(dev, 32)
+
+    run = Runner(vt, torch, tw, wl)
+    secs, wall = run.time(a.steps, a.warmup)
+    ms = secs / a.steps * 1e3
+    gemm_f, attn_f = workload_flops(wl)
+    value = wl.tokens * a.steps / secs
+
+    res = {
+        "metric": "ViT-tower patches/s (MiniMax-M3 tower: 32 layers + 2x2 merge + projector)",
+        "value": value, "unit": "patches/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded U[0,1) pixels, random-init N(0,0.02) bf16 weights)",
+        "config": {"workload": wl.name, "images": wl.n_img, "patches": wl.tokens,
+                   "grid_hw": [list(g[1:]) for g in wl.grids][:16], "layers": wl.layers,
+                   "projector": wl.projector, "attention_operands": "fp16", "gemm_operands": "bf16",
+                   "accumulate": "fp32", "residual": "fp32"},
+        "images_per_s": wl.n_img * a.steps / secs,
+        "wall_s_timed_region": wall,
+        "tflops_total": (gemm_f + attn_f) / (secs / a.steps) / 1e12,
+    }
+    M = wl.tokens
+    res["roofline"] = gemm_roofline(vt, torch, M, a.kernel_iters)
+    res["attention_roofline"] = attention_roofline(vt, torch, list(wl.grids), a.kernel_iters)
+
+    if a.secondary:
+        wl2 = synth.WORKLOADS[a.secondary]
+        del run
+        run2 = Runner(vt, torch, tw, wl2)
+        k2 = max(3, a.steps // 4)
+        s2, _ = run2.time(k2, 1)
+        g2, at2 = workload_flops(wl2)
+        res["secondary"] = {
+            "workload": wl2.name, "patches": wl2.tokens, "images": wl2.n_img,
+            "patches_per_s": wl2.tokens * k2 / s2, "images_per_s": wl2.n_img * k2 / s2,
+            "ms_per_step": s2 / k2 * 1e3, "steps": k2,
+            "tflops_total": (g2 + at2) / (s2 / k2) / 1e12,
+            "attention_roofline": attention_roofline(vt, torch, list(wl2.grids), max(3, a.kernel_iters // 4)),
+            "gemm_roofline": gemm_roofline(vt, torch, wl2.tokens, max(3, a.kernel_iters // 4)),
+        }
+        del run2
+
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(weights)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,235 @@
+/*
+ * vt.h -- C ABI of the tiled ViT vision tower for AMD MI355X (gfx950).
+ *
+ * The library computes the forward pass of a CLIP-style ViT vision tower of
+ * the MiniMax-M3 shape (MiniMax-M3-Vision README, "Architecture" table:
+ * 32 layers, hidden 1280, 16 heads, MLP 5120, patch 14, Conv3d patch embed,
+ * 3D RoPE, GELU; 2x2 spatial merge, temporal patch 2; projector
+ * Linear(1280,6144) GELU Linear(6144,6144), flatten four 6144-wide patches,
+ * Linear(24576,6144) GELU Linear(6144,6144)).  Attention is computed tiled
+ * with an online softmax: no [seq, seq] buffer exists at any point, so memory
+ * is linear in the number of patches (the quadratic score buffer is what caps
+ * image size in "init.rs (VisionEncoder::new)", doc comment of
+ * CEILING_MAX_PATCHES).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.    Every device pointer is owned by the caller.  The library never
+ *            allocates or frees device memory; scratch comes from the caller's
+ *            workspace (`ws`, `ws_bytes`), sized by the *_workspace_size
+ *            functions.  Host arrays (the grid list) are read during the call
+ *            and not kept.
+ * Dtypes.    "bf16" tensors are uint16 bit patterns of bfloat16.  Weights are
+ *            bf16 in PyTorch Linear layout [out, in] (row-major, the input
+ *            dimension contiguous).  The residual stream is fp32.
+ * Alignment. Every device pointer must be 16-byte aligned; the workspace
+ *            256-byte aligned.
+ * Tokens.    Inside the library, and at every boundary that says "token
+ *            order", the tokens of one image are stored in 2x2-window order:
+ *            with w2 = w/2, token 4*(R*w2 + C) + 2*dr + dc is the patch at
+ *            row 2R+dr, column 2C+dc.  The four patches of merged token
+ *            m = R*w2 + C are therefore adjacent and the 2x2 merge is a
+ *            reshape.  Images follow each other in grid-list order.  Outputs
+ *            documented as "raster" use row-major patch order instead.
+ * Streams.   `stream` is a hipStream_t (NULL = the default stream).  Calls
+ *            only enqueue work; they return before it finishes.  Inputs must
+ *            stay valid until the stream reaches that point.
+ * Errors.    Arguments are validated on the host before any launch, in every
+ *            build; a failing call launches nothing and returns a status
+ *            code, with details in vt_last_error() (thread-local).  Launch
+ *            failures return VT_ERR_HIP.  Nothing is clamped silently.
+ * Threads.   Calls are reentrant; there is no global mutable state other
+ *            than the thread-local error string.
+ */
+#ifndef VT_H
+#define VT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum vt_status {
+  VT_OK = 0,
+  VT_ERR_INVALID_ARG = 1,   /* NULL, negative/zero size, odd grid, misaligned pointer */
+  VT_ERR_UNSUPPORTED = 2,   /* valid request outside what the kernels implement */
+  VT_ERR_WORKSPACE = 3,     /* ws_bytes below the *_workspace_size() value */
+  VT_ERR_HIP = 4            /* a HIP launch or runtime call failed */
+} vt_status;
+
+typedef enum vt_dtype { VT_BF16 = 0, VT_FP32 = 1 } vt_dtype;
+
+/* Row order of a [tokens, width] tensor at the boundary. */
+typedef enum vt_order { VT_ORDER_WINDOW = 0, VT_ORDER_RASTER = 1 } vt_order;
+
+/* Epilogue of vt_linear (y = x W^T + b, fp32 accumulation). */
+typedef enum vt_epilogue {
+  VT_EPI_BF16 = 0,          /* out bf16 = y                                   */
+  VT_EPI_GELU_TANH_BF16 = 1,/* out bf16 = gelu_tanh(y)                        */
+  VT_EPI_GELU_ERF_BF16 = 2, /* out bf16 = gelu_erf(y)                         */
+  VT_EPI_RESID_F32 = 3,     /* out fp32 += y   (residual update, in place)    */
+  VT_EPI_F32 = 4            /* out fp32 = y                                   */
+} vt_epilogue;
+
+/* One image: t frames x h x w patches.  The temporal patch is 2 and a single
+ * frame is repeated to fill it ("v2_loaders FINDINGS", section 3), so t == 1
+ * for still images; h and w must be even (2x2 merge). */
+typedef struct vt_grid_thw { int32_t t, h, w; } vt_grid_thw;
+
+/* Tower shape.  vt_config_default() fills the MiniMax-M3 shape; the kernels
+ * implement head_dim 80, patch 14, temporal patch 2, merge 2; other widths
+ * must be multiples of 64 (hidden, mlp, proj_*) and hidden = heads*head_dim. */
+typedef struct vt_config {
+  int32_t layers;           /* 32 */
+  int32_t hidden;           /* 1280 */
+  int32_t heads;            /* 16 */
+  int32_t head_dim;         /* 80 */
+  int32_t mlp;              /* 5120 */
+  int32_t patch;            /* 14 */
+  int32_t t_patch;          /* 2 */
+  int32_t merge;            /* 2 */
+  int32_t proj_hidden;      /* 6144 */
+  int32_t proj_out;         /* 6144 */
+  float ln_eps;             /* 1e-6 */
+  float rope_theta;         /* 10000 */
+  int32_t rope_pairs[3];    /* rotation pairs on the t, h, w axes: 8, 16, 16 */
+  int32_t rope_shared_ladder; /* 0: per-axis ladder theta^(-k/n_axis); 1: theta^(-2j/head_dim) */
+  int32_t gelu_erf_projector; /* 0: GELU(tanh) in the projector (default); 1: exact erf GELU */
+} vt_config;
+
+/* Weights of one pre-LN block.  W_qkv rows are [Q | K | V], each head-major
+ * (heads x head_dim).  Biases may be NULL (read as zero); LN gamma/beta may not. */
+typedef struct vt_block_weights {
+  const uint16_t *ln1_g, *ln1_b;
+  const uint16_t *w_qkv, *b_qkv;   /* [3*hidden, hidden], [3*hidden] */
+  const uint16_t *w_o, *b_o;       /* [hidden, hidden], [hidden]     */
+  const uint16_t *ln2_g, *ln2_b;
+  const uint16_t *w_fc1, *b_fc1;   /* [mlp, hidden], [mlp]           */
+  const uint16_t *w_fc2, *b_fc2;   /* [hidden, mlp], [hidden]        */
+} vt_block_weights;
+
+/* Projector (MiniMax-M3-Vision README, Architecture table, Projector row). */
+typedef struct vt_projector_weights {
+  const uint16_t *w1, *b1;   /* [proj_hidden, hidden]                       */
+  const uint16_t *w2, *b2;   /* [proj_hidden, proj_hidden]                  */
+  const uint16_t *w3, *b3;   /* [proj_out, 4*proj_hidden]  (24576 wide)     */
+  const uint16_t *w4, *b4;   /* [proj_out, proj_out]                        */
+} vt_projector_weights;
+
+typedef struct vt_tower_weights {
+  const uint16_t *w_patch;   /* [hidden, 3*2*14*14] = Conv3d [hidden,3,2,14,14] flattened */
+  const uint16_t *b_patch;   /* [hidden] or NULL */
+  const vt_block_weights *blocks; /* host array of cfg->layers blocks */
+  vt_projector_weights proj;
+} vt_tower_weights;
+
+/* ---------------------------------------------------------------- basics */
+void vt_config_default(vt_config* cfg);
+const char* vt_status_string(vt_status s);
+/* Detail of the last failed call on this thread ("" if none).  Never NULL. */
+const char* vt_last_error(void);
+/* Library version string. */
+const char* vt_version(void);
+
+/* Workspace bytes for vt_tower_forward / vt_patch_embed / vt_merge_project on
+ * this grid list.  Affine in the token count (no term grows with seq^2).
+ * Returns 0 and sets vt_last_error() if the arguments are invalid. */
+size_t vt_tower_workspace_size(const vt_config* cfg, const vt_grid_thw* grid, int32_t n_img);
+
+/* Workspace bytes for vt_block_forward and vt_attention_varlen.
+ * Returns 0 and sets vt_last_error() if the arguments are invalid. */
+size_t vt_block_workspace_size(const vt_config* cfg, int32_t total_tokens, int32_t n_img,
+                               int32_t max_seqlen);
+
+/* ---------------------------------------------------------------- metadata
+ * Integer maps of a grid list, written on the device ("v2_loaders FINDINGS",
+ * section 3: grid_thw; section 1: per-image native-resolution grids).
+ *   cu_seqlens   [n_img+1] int32: cu[0] = 0, cu[i+1] = cu[i] + t*h*w.
+ *   pos_thw      [N, 3] int32 in token order: (t, row, col) patch coordinates,
+ *                restarting at 0 for each image.
+ *   raster_index [N] int32 in token order, or NULL: global raster index
+ *                (cu[i] + row*w + col) of each token. */
+vt_status vt_build_metadata(const vt_grid_thw* grid, int32_t n_img, int32_t* cu_seqlens,
+                            int32_t* pos_thw, int32_t* raster_index, void* stream);
+
+/* ---------------------------------------------------------------- steps */
+/* Patchify + patch embed (README Architecture: patch 14, Conv3d patch embed;
+ * FINDINGS s.3: the frame is repeated to fill the temporal patch of 2).
+ *   pixels    bf16, the images one after another, each [3, 14h, 14w] row-major.
+ *   resid_out fp32 [N, hidden] in token order: X W_patch^T + b_patch, where
+ *             row X[j] = (channel, tau, py, px) of token j's 3x2x14x14 block. */
+vt_status vt_patch_embed(const vt_config* cfg, const uint16_t* pixels, const vt_grid_thw* grid,
+                         int32_t n_img, const uint16_t* w_patch, const uint16_t* b_patch,
+                         float* resid_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Tiled varlen non-causal attention with 3D RoPE on Q and K.
+ *   qkv        bf16 [N, 3, heads, head_dim] (the QKV Linear output).
+ *   cu_seqlens [n_img+1] int32 on the device; image i attends only to its own
+ *              tokens cu[i] .. cu[i+1]-1 (block-diagonal, no padding tokens).
+ *   pos_thw    [N, 3] int32 on the device: the RoPE positions of each token.
+ *              Every coordinate must lie in [0, max_seqlen).
+ *   out        [N, heads*head_dim], bf16 or fp32 by out_dtype:
+ *              softmax(RoPE(q) RoPE(k)^T / sqrt(head_dim)) v per image and head.
+ *   max_seqlen must be >= every image's token count; total_tokens = cu[n_img].
+ * No [n, n] buffer is formed: memory is O(total_tokens). */
+vt_status vt_attention_varlen(const vt_config* cfg, const uint16_t* qkv, const int32_t* cu_seqlens,
+                              const int32_t* pos_thw, int32_t n_img, int32_t total_tokens,
+                              int32_t max_seqlen, void* out, vt_dtype out_dtype, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* One pre-LN block on the fp32 residual, in place:
+ *   R += O(attention(RoPE(LN1(R) W_qkv^T + b_qkv)))  with O(a) = a W_o^T + b_o
+ *   R += GELU_tanh(LN2(R) W_fc1^T + b_fc1) W_fc2^T + b_fc2
+ * LayerNorm: biased variance over hidden, eps inside the square root.
+ * Arguments as in vt_attention_varlen; resid is [total_tokens, hidden]. */
+vt_status vt_block_forward(const vt_config* cfg, float* resid, const vt_block_weights* w,
+                           const int32_t* cu_seqlens, const int32_t* pos_thw, int32_t n_img,
+                           int32_t total_tokens, int32_t max_seqlen, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* 2x2 merge + projector (README Architecture, Projector row).
+ *   tower      bf16 [N, hidden] tower tokens, rows in `order`.
+ *   merged_raw bf16 [N/4, 4*hidden] or NULL: the 2x2 gather of the tower
+ *              tokens (the "5120-wide merged tokens"), merged raster order.
+ *   out        bf16 [N/4, proj_out], merged raster order per image:
+ *              Y = GELU(T W1^T + b1) W2^T + b2 per token; Z[m] = the four Y
+ *              rows of merged token m in slot order 2*dr+dc (24576 wide);
+ *              out = GELU(Z W3^T + b3) W4^T + b4. */
+vt_status vt_merge_project(const vt_config* cfg, const uint16_t* tower, vt_order order,
+                           const vt_grid_thw* grid, int32_t n_img, const vt_projector_weights* w,
+                           uint16_t* merged_raw, uint16_t* out, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* The whole forward pass: patch embed, cfg->layers blocks, then (if `out` is
+ * not NULL) merge + projector.
+ *   tower_out  bf16 [N, hidden] raster order, or NULL (last_hidden_state).
+ *   merged_raw bf16 [N/4, 4*hidden] or NULL.
+ *   out        bf16 [N/4, proj_out] or NULL.  At least one output is needed. */
+vt_status vt_tower_forward(const vt_config* cfg, const uint16_t* pixels, const vt_grid_thw* grid,
+                           int32_t n_img, const vt_tower_weights* w, uint16_t* tower_out,
+                           uint16_t* merged_raw, uint16_t* out, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* ---------------------------------------------------------------- kernels
+ * The two non-attention kernels of the path, exposed on their own.
+ * vt_linear: y = x W^T + b with x bf16 [M, K], W bf16 [N, K], b bf16 [N] or
+ * NULL, fp32 accumulation, then the epilogue (see vt_epilogue); out is bf16
+ * or fp32 [M, N].  K must be a multiple of 8; N a multiple of 64.
+ * ws: at least vt_linear_workspace_size(M, N, K) bytes (may be 0). */
+size_t vt_linear_workspace_size(int32_t M, int32_t N, int32_t K);
+vt_status vt_linear(const uint16_t* x, int32_t M, int32_t K, const uint16_t* w, int32_t N,
+                    const uint16_t* bias, vt_epilogue epi, void* out, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* vt_layer_norm: out bf16 [rows, width] = LN(x) * g + b over fp32 x [rows, width];
+ * width must be a multiple of 256 and at most 4096. */
+vt_status vt_layer_norm(const float* x, int32_t rows, int32_t width, const uint16_t* g,
+                        const uint16_t* b, float eps, uint16_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VT_H */

@@ -1,0 +1,163 @@
+"""Host-side checks of the C-ABI library: it loads, exports every declared
+symbol, sizes its workspace linearly in the token count, and rejects invalid
+arguments before launching anything.  No GPU needed: every call here fails
+validation (or only computes sizes), so no HIP work is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import vision_transformer_encoder_tiled_amd as vt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vt.h")
+
+# Fake but aligned device addresses: validation must reject the call before
+# any of them is dereferenced.  Used only where no GPU is present, so that a
+# validation bug cannot turn into a device access.
+needs_no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
+                                  reason="fake-pointer validation tests run on hosts without a GPU")
+FAKE = 0x100000
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(vt_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    declared = header_functions()
+    assert len(declared) == 15
+    assert sorted(vt.EXPORTED) == declared
+    lib = ctypes.CDLL(vt.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert vt.vt_version().startswith("vt ")
+
+
+def test_default_config_is_the_minimax_m3_shape():
+    c = vt.vt_config_default()
+    assert (c.layers, c.hidden, c.heads, c.head_dim, c.mlp) == (32, 1280, 16, 80, 5120)
+    assert (c.patch, c.t_patch, c.merge, c.proj_hidden, c.proj_out) == (14, 2, 2, 6144, 6144)
+    assert list(c.rope_pairs) == [8, 16, 16]
+    assert c.ln_eps == pytest.approx(1e-6) and c.rope_theta == 10000.0
+
+
+def test_workspace_is_affine_in_tokens():
+    cfg = vt.config()
+    # large square images: no split-K partial buffers, so the size is exactly affine
+    sizes = [vt.vt_tower_workspace_size(cfg, [(1, 64, 64)] * k) for k in (8, 16, 24, 32)]
+    d1 = sizes[1] - sizes[0]
+    assert abs((sizes[2] - sizes[1]) - d1) <= 4096 and abs((sizes[3] - sizes[2]) - d1) <= 4096
+    per_token = d1 / (8 * 64 * 64)
+    assert per_token < 64 * 1024          # tens of KB per token ...
+    # ... so a 2016x2016 image (20,736 patches) needs well under a GB of scratch,
+    # against ~13.8 GB for one layer's untiled fp16 [16, n, n] score tensor.
+    ws2016 = vt.vt_tower_workspace_size(cfg, [(1, 144, 144)])
+    assert ws2016 < 1.5e9
+    assert 16 * 20736 ** 2 * 2 > 13.7e9
+    blk = [vt.vt_block_workspace_size(cfg, n, 1, n) for n in (4096, 8192, 16384)]
+    assert abs((blk[2] - blk[1]) - 2 * (blk[1] - blk[0])) <= 4096
+
+
+def test_workspace_size_reports_invalid_grids():
+    cfg = vt.config()
+    assert vt.vt_tower_workspace_size(cfg, [(1, 3, 4)]) == 0
+    assert "even" in vt.last_error()
+    assert vt.vt_tower_workspace_size(cfg, [(2, 4, 4)]) == 0
+    assert "t = 2" in vt.last_error()
+    bad = vt.config(head_dim=64, hidden=1024, rope_pairs=(0, 16, 16))
+    assert vt.vt_tower_workspace_size(bad, [(1, 4, 4)]) == 0
+    assert "head_dim 80" in vt.last_error()
+
+
+def _call_metadata(grids):
+    g, n = vt._lib._grid(grids)
+    return vt.LIB.vt_build_metadata(g, n, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None, None)
+
+
+@needs_no_gpu
+def test_metadata_rejects_bad_grids_before_launch():
+    assert _call_metadata([(1, 3, 4)]) == vt.VT_ERR_INVALID_ARG
+    assert _call_metadata([(1, 4, 0)]) == vt.VT_ERR_INVALID_ARG
+    assert _call_metadata([(3, 4, 4)]) == vt.VT_ERR_UNSUPPORTED
+    g, _ = vt._lib._grid([(1, 4, 4)])
+    assert vt.LIB.vt_build_metadata(g, 0, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None,
+                                    None) == vt.VT_ERR_INVALID_ARG
+    assert vt.LIB.vt_build_metadata(g, 1, None, ctypes.c_void_p(FAKE), None,
+                                    None) == vt.VT_ERR_INVALID_ARG
+
+
+def _attn(cfg, qkv=FAKE, out=FAKE, n_img=1, total=64, max_seq=64, ws=FAKE, ws_bytes=None,
+          dtype=vt.VT_BF16):
+    if ws_bytes is None:
+        ws_bytes = vt.vt_block_workspace_size(cfg, total, n_img, max_seq)
+    P = lambda v: None if v is None else ctypes.c_void_p(v)
+    return vt.LIB.vt_attention_varlen(ctypes.byref(cfg), P(qkv), P(FAKE), P(FAKE), n_img, total,
+                                      max_seq, P(out), dtype, P(ws), ws_bytes, None)
+
+
+@needs_no_gpu
+def test_attention_validation():
+    cfg = vt.config()
+    need = vt.vt_block_workspace_size(cfg, 64, 1, 64)
+    assert need > 0
+    assert _attn(cfg, ws_bytes=need - 1) == vt.VT_ERR_WORKSPACE
+    assert "too small" in vt.last_error()
+    assert _attn(cfg, qkv=None) == vt.VT_ERR_INVALID_ARG
+    assert _attn(cfg, qkv=FAKE + 8) == vt.VT_ERR_INVALID_ARG          # misaligned
+    assert "aligned" in vt.last_error()
+    assert _attn(cfg, ws=FAKE + 64) == vt.VT_ERR_INVALID_ARG          # workspace not 256-B aligned
+    assert _attn(cfg, max_seq=65) == vt.VT_ERR_INVALID_ARG            # max_seqlen > total
+    assert _attn(cfg, n_img=0) == vt.VT_ERR_INVALID_ARG
+    assert _attn(cfg, dtype=7) == vt.VT_ERR_INVALID_ARG
+    assert _attn(vt.config(head_dim=64, hidden=1024, rope_pairs=(0, 16, 16))) == vt.VT_ERR_UNSUPPORTED
+    assert _attn(vt.config(rope_pairs=(8, 12, 20))) == vt.VT_ERR_UNSUPPORTED
+    assert _attn(vt.config(rope_pairs=(8, 16, 8))) == vt.VT_ERR_INVALID_ARG
+
+
+@needs_no_gpu
+def test_linear_and_layer_norm_validation():
+    P = ctypes.c_void_p
+    L = vt.LIB
+    assert L.vt_linear(P(FAKE), 16, 100, P(FAKE), 64, None, 0, P(FAKE), None, 0, None) == vt.VT_ERR_UNSUPPORTED
+    assert L.vt_linear(P(FAKE), 16, 64, P(FAKE), 96, None, 0, P(FAKE), None, 0, None) == vt.VT_ERR_UNSUPPORTED
+    assert L.vt_linear(P(FAKE), 0, 64, P(FAKE), 64, None, 0, P(FAKE), None, 0, None) == vt.VT_ERR_INVALID_ARG
+    assert L.vt_linear(P(FAKE), 16, 64, P(FAKE), 64, P(FAKE + 2), 0, P(FAKE), None, 0, None) == vt.VT_ERR_INVALID_ARG
+    assert L.vt_linear(P(FAKE), 16, 64, P(FAKE), 64, None, 9, P(FAKE), None, 0, None) == vt.VT_ERR_INVALID_ARG
+    # small M with a long K plans a split-K: the partial buffer must be supplied
+    need = vt.vt_linear_workspace_size(256, 6144, 24576)
+    assert need > 0
+    assert L.vt_linear(P(FAKE), 256, 24576, P(FAKE), 6144, None, 0, P(FAKE), None, 0, None) == vt.VT_ERR_WORKSPACE
+    assert L.vt_layer_norm(P(FAKE), 4, 1000, P(FAKE), P(FAKE), 1e-6, P(FAKE), None) == vt.VT_ERR_UNSUPPORTED
+    assert L.vt_layer_norm(P(FAKE), 4, 1280, P(FAKE), P(FAKE), 0.0, P(FAKE), None) == vt.VT_ERR_INVALID_ARG
+    assert L.vt_layer_norm(None, 4, 1280, P(FAKE), P(FAKE), 1e-6, P(FAKE), None) == vt.VT_ERR_INVALID_ARG
+
+
+@needs_no_gpu
+def test_tower_validation():
+    cfg = vt.config(layers=0)
+    g, n = vt._lib._grid([(1, 4, 4)])
+    tw = vt.vt_tower_weights()
+    tw.w_patch = FAKE
+    P = ctypes.c_void_p
+    need = vt.vt_tower_workspace_size(cfg, [(1, 4, 4)])
+    L = vt.LIB
+    # no output requested
+    assert L.vt_tower_forward(ctypes.byref(cfg), P(FAKE), g, n, ctypes.byref(tw), None, None, None,
+                              P(FAKE), need, None) == vt.VT_ERR_INVALID_ARG
+    # projector requested without projector weights
+    assert L.vt_tower_forward(ctypes.byref(cfg), P(FAKE), g, n, ctypes.byref(tw), None, None,
+                              P(FAKE), P(FAKE), need, None) == vt.VT_ERR_INVALID_ARG
+    assert "projector" in vt.last_error()
+    # workspace one byte short
+    assert L.vt_tower_forward(ctypes.byref(cfg), P(FAKE), g, n, ctypes.byref(tw), P(FAKE), None,
+                              None, P(FAKE), need - 1, None) == vt.VT_ERR_WORKSPACE
+    # layers > 0 with no block array
+    cfg1 = vt.config(layers=1)
+    assert L.vt_tower_forward(ctypes.byref(cfg1), P(FAKE), g, n, ctypes.byref(tw), P(FAKE), None,
+                              None, P(FAKE), need, None) == vt.VT_ERR_INVALID_ARG
+    assert vt.LIB.vt_status_string(3) == b"VT_ERR_WORKSPACE"

@@ -1,0 +1,320 @@
+"""GPU parity of the individual steps against the oracle, through the C ABI.
+
+Integer work (metadata, patchify, merge) is compared bit for bit; floating
+point against the fp32 oracle fed the same bf16 bits, with the tolerances
+stated in each test.  Full-size shapes are checked on sampled rows that the
+oracle computes one by one."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import (bf16_f32, cosine_rows, dev_bits, host_bits, log, random_bf16, rel_l2,
+                      rng, window_to_raster)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def vt():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import vision_transformer_encoder_tiled_amd as m
+    return m
+
+
+# ---------------------------------------------------------------- metadata
+@pytest.mark.parametrize("grids", [
+    [(1, 16, 16)],
+    [(1, 2, 2), (1, 6, 10), (1, 16, 18)],
+    list(synth.WORKLOADS["tower_mixed8"].grids),
+    [(1, 144, 144)],
+])
+def test_metadata_bit_exact(vt, grids):
+    log(f"metadata {grids[:3]}")
+    N = sum(h * w for _, h, w in grids)
+    cu = torch.full((len(grids) + 1,), -1, dtype=torch.int32, device="cuda")
+    pos = torch.full((N, 3), -1, dtype=torch.int32, device="cuda")
+    ridx = torch.full((N,), -1, dtype=torch.int32, device="cuda")
+    vt.vt_build_metadata(grids, cu, pos, ridx)
+    torch.cuda.synchronize()
+    assert np.array_equal(cu.cpu().numpy(), oracle.cu_seqlens(grids))
+    perm = window_to_raster(grids)
+    assert np.array_equal(ridx.cpu().numpy(), perm)
+    assert np.array_equal(pos.cpu().numpy(), oracle.positions(grids)[perm])
+
+
+# ---------------------------------------------------------------- patch embed
+@pytest.mark.parametrize("grids", [[(1, 16, 16)], [(1, 2, 2), (1, 6, 10), (1, 4, 2)]])
+def test_patch_embed(vt, grids):
+    log(f"patch_embed {grids}")
+    cfg = vt.config(layers=0)
+    px = np.concatenate([synth.make_pixels(h, w, 10 + i).reshape(-1) for i, (_, h, w) in enumerate(grids)])
+    w = synth.make_weights(0, projector=False, affine="random")
+    N = sum(h * ww for _, h, ww in grids)
+    ws = vt.workspace(vt.vt_tower_workspace_size(cfg, grids))
+    R = torch.empty((N, 1280), dtype=torch.float32, device="cuda")
+    vt.vt_patch_embed(cfg, dev_bits(px, torch), grids, dev_bits(w["patch_w"], torch),
+                      dev_bits(w["patch_b"], torch), R, ws)
+    torch.cuda.synchronize()
+    W = oracle.weights_f32(w)
+    want = oracle.patch_embed(oracle.split_pixels(bf16_f32(px), grids), W, grids)
+    got = R.cpu().numpy()[np.argsort(window_to_raster(grids))]
+    assert rel_l2(got, want) < 1e-5
+    assert np.max(np.abs(got - want)) < 1e-4 * np.max(np.abs(want)) + 1e-5
+
+
+# ---------------------------------------------------------------- LayerNorm
+@pytest.mark.parametrize("rows,width", [(1, 1280), (77, 1280), (300, 256), (33, 4096)])
+def test_layer_norm(vt, rows, width):
+    log(f"layer_norm {rows}x{width}")
+    x = rng(1).standard_normal((rows, width), dtype=np.float32) * 3 + 0.5
+    g = random_bf16(width, 2, 0.2)
+    g = synth.bf16_bits(bf16_f32(g) + 1)
+    b = random_bf16(width, 3, 0.1)
+    out = torch.empty((rows, width), dtype=torch.int16, device="cuda")
+    vt.vt_layer_norm(torch.from_numpy(x).cuda(), rows, width, dev_bits(g, torch), dev_bits(b, torch),
+                     1e-6, out)
+    torch.cuda.synchronize()
+    got = bf16_f32(host_bits(out))
+    want = oracle.layer_norm(x, bf16_f32(g), bf16_f32(b), 1e-6)
+    # bf16 output: within one rounding (2^-8 relative) plus fp32 reduction noise
+    assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -8 + 1e-5)
+
+
+# ---------------------------------------------------------------- GEMM
+GEMM_SHAPES = [  # (M, N, K, what)
+    (256, 1280, 1176, "patch embed, 224x224"),
+    (1024, 3840, 1280, "QKV, 448x448"),
+    (1024, 1280, 1280, "O, 448x448 (split-K)"),
+    (1024, 5120, 1280, "FC1, 448x448"),
+    (1024, 1280, 5120, "FC2, 448x448 (split-K)"),
+    (1024, 6144, 1280, "projector 1, 448x448"),
+    (1024, 6144, 6144, "projector 2, 448x448"),
+    (256, 6144, 24576, "merged MLP 1, 448x448 (split-K)"),
+    (256, 6144, 6144, "merged MLP 2, 448x448 (split-K)"),
+    (77, 192, 72, "ragged M, K tail"),
+    (20736, 5120, 1280, "FC1, 2016x2016 (256 tile)"),
+    (20736, 1280, 5120, "FC2, 2016x2016"),
+    (5184, 6144, 24576, "merged MLP 1, 2016x2016"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,what", GEMM_SHAPES)
+def test_linear_shapes(vt, M, N, K, what):
+    log(f"linear {M}x{N}x{K} ({what})")
+    x = random_bf16((M, K), 100 + M % 97)
+    w = random_bf16((N, K), 200 + N % 89, 0.02)
+    b = random_bf16(N, 300, 0.1)
+    ws = vt.workspace(vt.vt_linear_workspace_size(M, N, K))
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    xd, wd, bd = dev_bits(x, torch), dev_bits(w, torch), dev_bits(b, torch)
+    vt.vt_linear(xd, M, K, wd, N, bd, vt.VT_EPI_F32, out, ws)
+    torch.cuda.synchronize()
+    rows = np.arange(M) if M <= 1024 else np.unique(np.r_[0:64, M - 64:M, rng(5).integers(0, M, 128)])
+    want = oracle.linear(bf16_f32(x)[rows], bf16_f32(w), bf16_f32(b))
+    got = out.cpu().numpy()[rows]
+    scale = np.sqrt(K) * 0.02
+    assert np.max(np.abs(got - want)) < 2e-5 * scale * 8 + 1e-6, what
+    assert rel_l2(got, want) < 1e-5
+
+
+@pytest.mark.parametrize("epi", ["bf16", "gelu_tanh", "gelu_erf", "resid"])
+@pytest.mark.parametrize("M,N,K", [(200, 512, 320), (1024, 1280, 5120)])
+def test_linear_epilogues(vt, epi, M, N, K):
+    log(f"linear epilogue {epi} {M}x{N}x{K}")
+    x = random_bf16((M, K), 7)
+    w = random_bf16((N, K), 8, 0.05)
+    b = random_bf16(N, 9, 0.5)
+    ws = vt.workspace(vt.vt_linear_workspace_size(M, N, K))
+    xd, wd, bd = dev_bits(x, torch), dev_bits(w, torch), dev_bits(b, torch)
+    y = oracle.linear(bf16_f32(x), bf16_f32(w), bf16_f32(b))
+    if epi == "resid":
+        r0 = rng(10).standard_normal((M, N), dtype=np.float32)
+        out = torch.from_numpy(r0.copy()).cuda()
+        vt.vt_linear(xd, M, K, wd, N, bd, vt.VT_EPI_RESID_F32, out, ws)
+        torch.cuda.synchronize()
+        got, want = out.cpu().numpy(), r0 + y
+        assert np.max(np.abs(got - want)) < 1e-4
+        return
+    code = {"bf16": vt.VT_EPI_BF16, "gelu_tanh": vt.VT_EPI_GELU_TANH_BF16,
+            "gelu_erf": vt.VT_EPI_GELU_ERF_BF16}[epi]
+    want = {"bf16": y, "gelu_tanh": oracle.gelu_tanh(y), "gelu_erf": oracle.gelu_erf(y)}[epi]
+    out = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    vt.vt_linear(xd, M, K, wd, N, bd, code, out, ws)
+    torch.cuda.synchronize()
+    got = bf16_f32(host_bits(out))
+    assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -8 + 2e-5)
+
+
+# ---------------------------------------------------------------- attention
+def attention_case(vt, grids, seed, rows=None, qk_scale=1.0):
+    """Run vt_attention_varlen (fp32 output) on seeded bf16 qkv; return
+    (gpu [N,1280] in raster order restricted to rows, oracle same)."""
+    N = sum(h * w for _, h, w in grids)
+    H, hd = 16, 80
+    g = rng(seed)
+    qkv = g.standard_normal((N, 3, H, hd), dtype=np.float32)
+    qkv[:, :2] *= np.float32(qk_scale)
+    qkv_bits = synth.bf16_bits(qkv)                      # window (library) order
+    perm = window_to_raster(grids)                       # library token j -> raster perm[j]
+    cfg = vt.config()
+    cu = torch.empty(len(grids) + 1, dtype=torch.int32, device="cuda")
+    pos = torch.empty((N, 3), dtype=torch.int32, device="cuda")
+    vt.vt_build_metadata(grids, cu, pos)
+    max_seq = max(h * w for _, h, w in grids)
+    ws = vt.workspace(vt.vt_block_workspace_size(cfg, N, len(grids), max_seq))
+    out = torch.empty((N, H * hd), dtype=torch.float32, device="cuda")
+    vt.vt_attention_varlen(cfg, dev_bits(qkv_bits, torch), cu, pos, len(grids), N, max_seq, out,
+                           vt.VT_FP32, ws)
+    torch.cuda.synchronize()
+    got_w = out.cpu().numpy()
+    # oracle in raster order
+    q_r = np.empty((N, 3, H, hd), np.float32)
+    q_r[perm] = bf16_f32(qkv_bits)
+    pos_r = oracle.positions(grids)
+    axis, inv = oracle.rope_tables()
+    cu_r = oracle.cu_seqlens(grids)
+    got_r = np.empty_like(got_w)
+    got_r[perm] = got_w
+    q = oracle.apply_rope(q_r[:, 0], pos_r, axis, inv)
+    k = oracle.apply_rope(q_r[:, 1], pos_r, axis, inv)
+    v = q_r[:, 2]
+    if rows is None:
+        want = oracle.attention_varlen(q, k, v, cu_r).reshape(N, H * hd)
+        return got_r, want
+    wants = []
+    for i in range(len(grids)):
+        a, b = cu_r[i], cu_r[i + 1]
+        rr = [r - a for r in rows if a <= r < b]
+        if rr:
+            wants.append((np.array(rr) + a,
+                          oracle.attention_image(q[a:b], k[a:b], v[a:b], rows=rr).reshape(len(rr), -1)))
+    idx = np.concatenate([x[0] for x in wants])
+    return got_r[idx], np.concatenate([x[1] for x in wants])
+
+
+@pytest.mark.parametrize("grids,seed", [
+    ([(1, 16, 16)], 1),                                   # 224x224: 256 tokens
+    ([(1, 32, 32)], 2),                                   # 448x448: 1024 tokens
+    ([(1, 2, 2), (1, 6, 10), (1, 16, 18), (1, 2, 40)], 3),  # ragged tiles, tiny images
+    ([(1, 32, 32)] * 3, 4),                               # packed 448x448 images
+])
+def test_attention_parity(vt, grids, seed):
+    log(f"attention {grids}")
+    got, want = attention_case(vt, grids, seed)
+    err = np.max(np.abs(got - want))
+    log(f"  max abs err {err:.3e}")
+    assert err <= 2e-3
+
+
+def layer0_qkv_bits(grids, seeds):
+    """The QKV activations of block 0 on seeded images (oracle, fp32, rounded
+    to bf16 as the QKV Linear's bf16 output): realistic attention inputs."""
+    W = synth.make_weights(1, projector=False)
+    Wf = oracle.weights_f32(W)
+    px = np.concatenate([synth.make_pixels(h, w, s).reshape(-1) for (_, h, w), s in zip(grids, seeds)])
+    R = oracle.patch_embed(oracle.split_pixels(bf16_f32(px), grids), Wf, grids).astype(np.float32)
+    x = oracle.layer_norm(R, Wf["l0.ln1_g"], Wf["l0.ln1_b"], 1e-6)
+    return synth.bf16_bits(oracle.linear(x, Wf["l0.w_qkv"], Wf["l0.b_qkv"]))
+
+
+@pytest.mark.parametrize("grids,seeds", [([(1, 16, 16)], [1]), ([(1, 32, 32)], [2])])
+@pytest.mark.parametrize("out_dtype", ["fp32", "bf16"])
+def test_attention_on_block0_activations(vt, grids, seeds, out_dtype):
+    """Attention on the block-0 QKV activations of the 224x224 and 448x448
+    images: max abs error <= 2e-3 (fp32 output); the bf16 output adds at most
+    half a bf16 ulp of the value (2^-8 relative)."""
+    log(f"attention block0 {grids} {out_dtype}")
+    qkv_r = layer0_qkv_bits(grids, seeds)
+    N = qkv_r.shape[0]
+    perm = window_to_raster(grids)
+    cfg = vt.config()
+    cu = torch.empty(len(grids) + 1, dtype=torch.int32, device="cuda")
+    pos = torch.empty((N, 3), dtype=torch.int32, device="cuda")
+    vt.vt_build_metadata(grids, cu, pos)
+    ws = vt.workspace(vt.vt_block_workspace_size(cfg, N, len(grids), N))
+    f32 = out_dtype == "fp32"
+    out = torch.empty((N, 1280), dtype=torch.float32 if f32 else torch.int16, device="cuda")
+    vt.vt_attention_varlen(cfg, dev_bits(qkv_r[perm], torch), cu, pos, len(grids), N, N, out,
+                           vt.VT_FP32 if f32 else vt.VT_BF16, ws)
+    torch.cuda.synchronize()
+    got_w = out.cpu().numpy() if f32 else bf16_f32(host_bits(out))
+    got = np.empty_like(got_w)
+    got[perm] = got_w
+    x = bf16_f32(qkv_r).reshape(N, 3, 16, 80)
+    axis, inv = oracle.rope_tables()
+    pos_r = oracle.positions(grids)
+    want = oracle.attention_varlen(oracle.apply_rope(x[:, 0], pos_r, axis, inv),
+                                   oracle.apply_rope(x[:, 1], pos_r, axis, inv), x[:, 2],
+                                   oracle.cu_seqlens(grids)).reshape(N, 1280)
+    err = np.abs(got - want)
+    log(f"  max abs err {err.max():.3e}")
+    bound = 2e-3 if f32 else 2e-3 + np.abs(want) * 2.0 ** -8
+    assert np.all(err <= bound)
+
+
+def test_attention_sharp_scores(vt):
+    """Stress case: q, k ~ N(0, 9) make scores of std ~9 and peaked rows, so
+    the online-max rescaling is exercised.  The error is then set by the
+    16-bit MFMA operands: a score q.k/sqrt(80) built from fp16-rounded q and k
+    carries an error of about 9 * 2^-11 (std), and an output moves by about
+    that much times |v| ~ 1; the bound is 8 such standard deviations."""
+    got, want = attention_case(vt, [(1, 20, 24)], 11, qk_scale=3.0)
+    err = np.max(np.abs(got - want))
+    log(f"attention sharp: max abs err {err:.3e}")
+    assert err <= 8 * 9 * 2.0 ** -11
+
+
+def test_attention_mixed_grids_sampled(vt):
+    grids = list(synth.WORKLOADS["tower_mixed8"].grids)
+    N = sum(h * w for _, h, w in grids)
+    rows = np.unique(rng(6).integers(0, N, 300))
+    got, want = attention_case(vt, grids, 5, rows=rows)
+    err = np.max(np.abs(got - want))
+    log(f"attention mixed8 ({N} tokens): max abs err {err:.3e}")
+    assert err <= 2e-3
+
+
+def test_attention_2016_sampled(vt):
+    grids = [(1, 144, 144)]
+    rows = np.unique(np.r_[0:32, 20736 - 32:20736, rng(7).integers(0, 20736, 200)])
+    got, want = attention_case(vt, grids, 6, rows=rows)
+    err = np.max(np.abs(got - want))
+    log(f"attention 2016 (20736 tokens): max abs err {err:.3e}")
+    assert err <= 2e-3
+
+
+# ---------------------------------------------------------------- one block
+@pytest.mark.parametrize("affine", ["canonical", "random"])
+def test_block_224(vt, affine):
+    """One block on a 224x224 image (16x16 patches), against the oracle fed the
+    same bf16 weights; the GPU residual enters as the oracle's fp32 patch embed."""
+    log(f"block 224 {affine}")
+    wl = synth.WORKLOADS["block_224"]
+    W = synth.make_weights(1, projector=False, affine=affine)
+    px = synth.make_batch_pixels(wl)
+    ref = oracle.tower_forward(px, wl.grids, W, n_layers=1, projector_on=False, keep_layers=True)
+    Wf = oracle.weights_f32(W)
+    R0 = oracle.patch_embed(oracle.split_pixels(bf16_f32(px), wl.grids), Wf, wl.grids).astype(np.float32)
+    perm = window_to_raster(wl.grids)
+    cfg = vt.config(layers=1)
+    N = 256
+    dw = {k: dev_bits(v, torch) for k, v in W.items()}
+    cu = torch.empty(2, dtype=torch.int32, device="cuda")
+    pos = torch.empty((N, 3), dtype=torch.int32, device="cuda")
+    vt.vt_build_metadata(wl.grids, cu, pos)
+    R = torch.from_numpy(R0[perm].copy()).cuda()
+    bw = vt.block_weights(dw, "l0.")
+    ws = vt.workspace(vt.vt_block_workspace_size(cfg, N, 1, N))
+    vt.vt_block_forward(cfg, R, bw, cu, pos, 1, N, N, ws)
+    torch.cuda.synchronize()
+    got = np.empty((N, 1280), np.float32)
+    got[perm] = R.cpu().numpy()
+    e = rel_l2(got, ref["tower"])
+    log(f"  block rel-L2 {e:.3e}, min cos {cosine_rows(got, ref['tower']).min():.6f}")
+    assert e <= 1e-2
+    assert cosine_rows(got, ref["tower"]).min() >= 0.999

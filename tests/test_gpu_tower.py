@@ -1,0 +1,220 @@
+"""GPU parity of the whole tower (patch embed, 32 blocks, 2x2 merge,
+projector) against the fp32 oracle fed the same bf16 weights and pixels.
+
+Bounds: per-layer relative L2 of the residual <= 1e-2; projected tokens:
+minimum cosine over tokens >= 0.999.  Batched workloads are compared on
+images the oracle runs alone (attention is block-diagonal, every other step
+is per token or per image, so an image's outputs do not depend on the rest
+of the batch)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import (bf16_f32, cosine_rows, dev_bits, host_bits, log, rel_l2, rng,
+                      window_to_raster)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def vt():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import vision_transformer_encoder_tiled_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def weights():
+    log("generating the seeded tower + projector weights")
+    return synth.make_weights(32, projector=True)
+
+
+@pytest.fixture(scope="module")
+def dev(vt, weights):
+    d = {k: dev_bits(v, torch) for k, v in weights.items()}
+    return d, vt.TowerWeights(d, 32)
+
+
+def gpu_tower(vt, tw, grids, px, layers=32, merged=True):
+    cfg = vt.config(layers=layers)
+    N = sum(h * w for _, h, w in grids)
+    ws = vt.workspace(vt.vt_tower_workspace_size(cfg, grids))
+    tower = torch.empty((N, 1280), dtype=torch.int16, device="cuda")
+    mraw = torch.empty((N // 4, 5120), dtype=torch.int16, device="cuda") if merged else None
+    out = torch.empty((N // 4, 6144), dtype=torch.int16, device="cuda")
+    vt.vt_tower_forward(cfg, dev_bits(px, torch), grids, tw, tower, mraw, out, ws)
+    torch.cuda.synchronize()
+    return {"tower": host_bits(tower), "merged_raw": host_bits(mraw) if merged else None,
+            "out": host_bits(out)}
+
+
+def image_pixels(wl, idx):
+    (t, h, w), s = wl.grids[idx], wl.seeds[idx]
+    return synth.make_pixels(h, w, s).reshape(-1)
+
+
+# ---------------------------------------------------------------- 448x448
+def test_tower_448_layer_by_layer(vt, weights, dev):
+    """One 448x448 image: the residual after every block (rel-L2 <= 1e-2),
+    the tower output and the projected tokens (min cosine >= 0.999)."""
+    wl = synth.WORKLOADS["tower_448"]
+    px = synth.make_batch_pixels(wl)
+    grids = list(wl.grids)
+    log("oracle 448x448, 32 layers")
+    ref = oracle.tower_forward(px, grids, weights, keep_layers=True)
+    d, tw = dev
+    N = 1024
+    perm = window_to_raster(grids)
+    cfg = vt.config()
+    ws = vt.workspace(vt.vt_tower_workspace_size(cfg, grids))
+    R = torch.empty((N, 1280), dtype=torch.float32, device="cuda")
+    vt.vt_patch_embed(cfg, dev_bits(px, torch), grids, d["patch_w"], d["patch_b"], R, ws)
+    cu = torch.empty(2, dtype=torch.int32, device="cuda")
+    pos = torch.empty((N, 3), dtype=torch.int32, device="cuda")
+    vt.vt_build_metadata(grids, cu, pos)
+    bws = vt.workspace(vt.vt_block_workspace_size(cfg, N, 1, N))
+    errs = []
+    for l in range(32):
+        bw = vt.block_weights(d, f"l{l}.")
+        vt.vt_block_forward(cfg, R, bw, cu, pos, 1, N, N, bws)
+        got = np.empty((N, 1280), np.float32)
+        got[perm] = R.cpu().numpy()
+        errs.append(rel_l2(got, ref["layers"][l]))
+    log("per-layer rel-L2: " + " ".join(f"{e:.1e}" for e in errs))
+    assert max(errs) <= 1e-2
+    # merge + projector on the layer-by-layer residual (window order input) ...
+    T = synth.bf16_bits(R.cpu().numpy())
+    out_lbl = torch.empty((N // 4, 6144), dtype=torch.int16, device="cuda")
+    pw = vt.projector_weights(d)
+    vt.vt_merge_project(cfg, dev_bits(T, torch), vt.VT_ORDER_WINDOW, grids, pw, None, out_lbl, ws)
+    # ... equals the fused tower entry point bit for bit (same kernels, same order)
+    res = gpu_tower(vt, tw, grids, px)
+    assert np.array_equal(host_bits(out_lbl), res["out"])
+    t_r = bf16_f32(res["tower"])
+    e_t = rel_l2(t_r, ref["tower"])
+    cos = cosine_rows(bf16_f32(res["out"]), ref["out"])
+    log(f"tower rel-L2 {e_t:.2e}; projected cosine min {cos.min():.6f} mean {cos.mean():.6f}; "
+        f"whole-tensor rel-L2 {rel_l2(bf16_f32(res['out']), ref['out']):.2e}")
+    assert e_t <= 1e-2
+    assert cos.min() >= 0.999
+    # merged_raw is the 2x2 gather of the tower tokens, bit for bit
+    assert np.array_equal(res["merged_raw"], res["tower"][oracle.merge_map(grids)].reshape(-1, 5120))
+    # raster-order input to vt_merge_project gives the same projection
+    out_r = torch.empty((N // 4, 6144), dtype=torch.int16, device="cuda")
+    vt.vt_merge_project(cfg, dev_bits(res["tower"], torch), vt.VT_ORDER_RASTER, grids, pw, None, out_r, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out_r), res["out"])
+
+
+def test_tower_deterministic(vt, dev):
+    wl = synth.WORKLOADS["tower_448"]
+    px = synth.make_batch_pixels(wl)
+    a = gpu_tower(vt, dev[1], list(wl.grids), px)
+    b = gpu_tower(vt, dev[1], list(wl.grids), px)
+    assert all(np.array_equal(a[k], b[k]) for k in ("tower", "merged_raw", "out"))
+
+
+# ---------------------------------------------------------------- batches
+@pytest.mark.parametrize("name,sample", [("tower_448x16", [0, 11]), ("tower_mixed8", None)])
+def test_tower_batched_sampled_images(vt, weights, dev, name, sample):
+    wl = synth.WORKLOADS[name]
+    grids = list(wl.grids)
+    if sample is None:  # the two smallest images of the mixed batch
+        sample = list(np.argsort([h * w for _, h, w in grids])[:2])
+    log(f"{name}: {len(grids)} images, {wl.tokens} tokens; oracle on images {sample}")
+    res = gpu_tower(vt, dev[1], grids, synth.make_batch_pixels(wl), merged=False)
+    cu = oracle.cu_seqlens(grids)
+    for i in sample:
+        g1 = [grids[i]]
+        ref = oracle.tower_forward(image_pixels(wl, i), g1, weights)
+        a, b = cu[i], cu[i + 1]
+        t = bf16_f32(res["tower"][a:b])
+        o = bf16_f32(res["out"][a // 4:b // 4])
+        cos = cosine_rows(o, ref["out"])
+        log(f"  image {i} {g1}: tower rel-L2 {rel_l2(t, ref['tower']):.2e}, cosine min {cos.min():.6f}")
+        assert rel_l2(t, ref["tower"]) <= 1e-2
+        assert cos.min() >= 0.999
+
+
+# ---------------------------------------------------------------- 2016x2016
+def oracle_block_rows(R, W, grids, rows, cfg=None):
+    """The oracle's block 0 for the query rows ``rows`` only: K and V of every
+    token, attention and the MLP for the sampled rows (one image)."""
+    cfg = cfg or oracle.Config()
+    N = R.shape[0]
+    pos = oracle.positions(grids)
+    x = oracle.layer_norm(R, W["l0.ln1_g"], W["l0.ln1_b"], cfg.ln_eps)
+    qkv = oracle.linear(x, W["l0.w_qkv"], W["l0.b_qkv"]).reshape(N, 3, 16, 80)
+    axis, inv = oracle.rope_tables()
+    q = oracle.apply_rope(qkv[rows, 0], pos[rows], axis, inv)
+    k = oracle.apply_rope(qkv[:, 1], pos, axis, inv)
+    v = qkv[:, 2]
+    qfull = np.zeros_like(k)
+    qfull[rows] = q
+    a = oracle.attention_image(qfull, k, v, rows=rows).reshape(len(rows), 1280)
+    r = R[rows] + oracle.linear(a, W["l0.w_o"], W["l0.b_o"])
+    y = oracle.layer_norm(r, W["l0.ln2_g"], W["l0.ln2_b"], cfg.ln_eps)
+    return r + oracle.linear(oracle.gelu_tanh(oracle.linear(y, W["l0.w_fc1"], W["l0.b_fc1"])),
+                             W["l0.w_fc2"], W["l0.b_fc2"])
+
+
+def test_2016_block0_sampled_rows(vt, weights, dev):
+    """Block 0 at 20,736 tokens (the launch configuration of the 2016x2016
+    workload), with the oracle's patch embedding as input, on sampled rows."""
+    wl = synth.WORKLOADS["tower_2016"]
+    grids = list(wl.grids)
+    px = synth.make_batch_pixels(wl)
+    W = oracle.weights_f32({k: v for k, v in weights.items() if k.startswith(("patch", "l0."))})
+    R0 = oracle.patch_embed(oracle.split_pixels(bf16_f32(px), grids), W, grids).astype(np.float32)
+    rows = np.unique(np.r_[0:16, 20736 - 16:20736, rng(8).integers(0, 20736, 96)])
+    log("oracle block 0 on sampled rows at 20736 tokens")
+    want = oracle_block_rows(R0, W, grids, rows)
+    d, _ = dev
+    N = 20736
+    perm = window_to_raster(grids)
+    cfg = vt.config()
+    cu = torch.empty(2, dtype=torch.int32, device="cuda")
+    pos = torch.empty((N, 3), dtype=torch.int32, device="cuda")
+    vt.vt_build_metadata(grids, cu, pos)
+    R = torch.from_numpy(R0[perm].copy()).cuda()
+    ws = vt.workspace(vt.vt_block_workspace_size(cfg, N, 1, N))
+    vt.vt_block_forward(cfg, R, vt.block_weights(d, "l0."), cu, pos, 1, N, N, ws)
+    torch.cuda.synchronize()
+    got = np.empty((N, 1280), np.float32)
+    got[perm] = R.cpu().numpy()
+    e = rel_l2(got[rows], want)
+    log(f"  block0 @20736 sampled rel-L2 {e:.2e}")
+    assert e <= 1e-2
+
+
+def test_2016_tower_memory_and_invariance(vt, dev):
+    """The full 2016x2016 tower: scratch is linear in tokens (no [n, n]
+    buffer), results are finite, deterministic, and unchanged when another
+    image is packed into the same call."""
+    wl = synth.WORKLOADS["tower_2016"]
+    grids = list(wl.grids)
+    px = synth.make_batch_pixels(wl)
+    cfg = vt.config()
+    ws_bytes = vt.vt_tower_workspace_size(cfg, grids)
+    untiled = 16 * 20736 ** 2 * 2
+    log(f"2016x2016 workspace {ws_bytes / 1e9:.3f} GB vs one layer's untiled fp16 scores {untiled / 1e9:.1f} GB")
+    assert ws_bytes < untiled / 10
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    a = gpu_tower(vt, dev[1], grids, px, merged=False)
+    peak = torch.cuda.max_memory_allocated() - base
+    log(f"  peak device memory above the weights: {peak / 1e9:.3f} GB")
+    assert peak < ws_bytes + 0.5e9
+    o = bf16_f32(a["out"])
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(bf16_f32(a["tower"])))
+    b = gpu_tower(vt, dev[1], grids, px, merged=False)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["tower"], b["tower"])
+    # pack a 448x448 image after it: the 2016x2016 rows do not change
+    px2 = np.concatenate([px, synth.make_pixels(32, 32, 2).reshape(-1)])
+    c = gpu_tower(vt, dev[1], grids + [(1, 32, 32)], px2, merged=False)
+    assert np.array_equal(c["tower"][:20736], a["tower"])
+    assert np.array_equal(c["out"][:5184], a["out"])

@@ -1,0 +1,280 @@
+"""ctypes binding of libvt.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls and passes
+torch tensors as raw device pointers, the current HIP stream as the stream.
+All computation happens in the HIP kernels of the library; there is no
+fallback: if ``libvt.so`` is missing the import raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libvt.so")
+
+VT_OK, VT_ERR_INVALID_ARG, VT_ERR_UNSUPPORTED, VT_ERR_WORKSPACE, VT_ERR_HIP = range(5)
+VT_BF16, VT_FP32 = 0, 1
+VT_ORDER_WINDOW, VT_ORDER_RASTER = 0, 1
+VT_EPI_BF16, VT_EPI_GELU_TANH_BF16, VT_EPI_GELU_ERF_BF16, VT_EPI_RESID_F32, VT_EPI_F32 = range(5)
+
+EXPORTED = ("vt_config_default", "vt_status_string", "vt_last_error", "vt_version",
+            "vt_tower_workspace_size", "vt_block_workspace_size", "vt_build_metadata",
+            "vt_patch_embed", "vt_attention_varlen", "vt_block_forward", "vt_merge_project",
+            "vt_tower_forward", "vt_linear_workspace_size", "vt_linear", "vt_layer_norm")
+
+
+class VtError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{_status_name(status)}: {msg}")
+        self.status = status
+
+
+class vt_grid_thw(ctypes.Structure):
+    _fields_ = [("t", ctypes.c_int32), ("h", ctypes.c_int32), ("w", ctypes.c_int32)]
+
+
+class vt_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("layers", "hidden", "heads", "head_dim", "mlp",
+                                              "patch", "t_patch", "merge", "proj_hidden",
+                                              "proj_out")] + [
+        ("ln_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+        ("rope_pairs", ctypes.c_int32 * 3), ("rope_shared_ladder", ctypes.c_int32),
+        ("gelu_erf_projector", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+
+
+class vt_block_weights(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_g",
+                                  "ln2_b", "w_fc1", "b_fc1", "w_fc2", "b_fc2")]
+
+
+class vt_projector_weights(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("w1", "b1", "w2", "b2", "w3", "b3", "w4", "b4")]
+
+
+class vt_tower_weights(ctypes.Structure):
+    _fields_ = [("w_patch", _P), ("b_patch", _P), ("blocks", ctypes.POINTER(vt_block_weights)),
+                ("proj", vt_projector_weights)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m vision_transformer_encoder_tiled_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    C, I32, SZ = ctypes.c_char_p, ctypes.c_int32, ctypes.c_size_t
+    cfgp, gridp = ctypes.POINTER(vt_config), ctypes.POINTER(vt_grid_thw)
+    sig = {
+        "vt_config_default": (None, [cfgp]),
+        "vt_status_string": (C, [ctypes.c_int]),
+        "vt_last_error": (C, []),
+        "vt_version": (C, []),
+        "vt_tower_workspace_size": (SZ, [cfgp, gridp, I32]),
+        "vt_block_workspace_size": (SZ, [cfgp, I32, I32, I32]),
+        "vt_build_metadata": (ctypes.c_int, [gridp, I32, _P, _P, _P, _P]),
+        "vt_patch_embed": (ctypes.c_int, [cfgp, _P, gridp, I32, _P, _P, _P, _P, SZ, _P]),
+        "vt_attention_varlen": (ctypes.c_int, [cfgp, _P, _P, _P, I32, I32, I32, _P, ctypes.c_int,
+                                               _P, SZ, _P]),
+        "vt_block_forward": (ctypes.c_int, [cfgp, _P, ctypes.POINTER(vt_block_weights), _P, _P,
+                                            I32, I32, I32, _P, SZ, _P]),
+        "vt_merge_project": (ctypes.c_int, [cfgp, _P, ctypes.c_int, gridp, I32,
+                                            ctypes.POINTER(vt_projector_weights), _P, _P, _P, SZ,
+                                            _P]),
+        "vt_tower_forward": (ctypes.c_int, [cfgp, _P, gridp, I32, ctypes.POINTER(vt_tower_weights),
+                                            _P, _P, _P, _P, SZ, _P]),
+        "vt_linear_workspace_size": (SZ, [I32, I32, I32]),
+        "vt_linear": (ctypes.c_int, [_P, I32, I32, _P, I32, _P, ctypes.c_int, _P, _P, SZ, _P]),
+        "vt_layer_norm": (ctypes.c_int, [_P, I32, I32, _P, _P, ctypes.c_float, _P, _P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+LIB = _load()
+
+
+def _status_name(s):
+    return LIB.vt_status_string(int(s)).decode()
+
+
+def last_error() -> str:
+    return LIB.vt_last_error().decode()
+
+
+def _check(status):
+    if status != VT_OK:
+        raise VtError(status, last_error())
+
+
+# ------------------------------------------------------------------ marshalling helpers
+def _ptr(t):
+    """Device pointer of a tensor (None -> NULL)."""
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _grid(grids):
+    arr = (vt_grid_thw * len(grids))()
+    for i, (t, h, w) in enumerate(grids):
+        arr[i].t, arr[i].h, arr[i].w = int(t), int(h), int(w)
+    return arr, len(grids)
+
+
+def config(**overrides) -> vt_config:
+    c = vt_config()
+    LIB.vt_config_default(ctypes.byref(c))
+    for k, v in overrides.items():
+        if k == "rope_pairs":
+            for i in range(3):
+                c.rope_pairs[i] = int(v[i])
+        else:
+            setattr(c, k, v)
+    return c
+
+
+def vt_config_default() -> vt_config:
+    return config()
+
+
+def vt_version() -> str:
+    return LIB.vt_version().decode()
+
+
+def vt_tower_workspace_size(cfg, grids) -> int:
+    g, n = _grid(grids)
+    return int(LIB.vt_tower_workspace_size(ctypes.byref(cfg), g, n))
+
+
+def vt_block_workspace_size(cfg, total_tokens, n_img, max_seqlen) -> int:
+    return int(LIB.vt_block_workspace_size(ctypes.byref(cfg), total_tokens, n_img, max_seqlen))
+
+
+def vt_linear_workspace_size(M, N, K) -> int:
+    return int(LIB.vt_linear_workspace_size(M, N, K))
+
+
+def vt_build_metadata(grids, cu_seqlens, pos_thw, raster_index=None, stream=None):
+    g, n = _grid(grids)
+    _check(LIB.vt_build_metadata(g, n, _ptr(cu_seqlens), _ptr(pos_thw), _ptr(raster_index),
+                                 _stream(stream)))
+
+
+def vt_patch_embed(cfg, pixels, grids, w_patch, b_patch, resid_out, ws, stream=None):
+    g, n = _grid(grids)
+    _check(LIB.vt_patch_embed(ctypes.byref(cfg), _ptr(pixels), g, n, _ptr(w_patch), _ptr(b_patch),
+                              _ptr(resid_out), _ptr(ws), ws.numel() if ws is not None else 0,
+                              _stream(stream)))
+
+
+def vt_attention_varlen(cfg, qkv, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen, out,
+                        out_dtype, ws, stream=None):
+    _check(LIB.vt_attention_varlen(ctypes.byref(cfg), _ptr(qkv), _ptr(cu_seqlens), _ptr(pos_thw),
+                                   n_img, total_tokens, max_seqlen, _ptr(out), out_dtype, _ptr(ws),
+                                   ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def block_weights(w: dict, prefix: str = "") -> vt_block_weights:
+    """vt_block_weights from a dict of device tensors (missing biases -> NULL)."""
+    b = vt_block_weights()
+    for name, _ in vt_block_weights._fields_:
+        t = w.get(prefix + name)
+        setattr(b, name, None if t is None else t.data_ptr())
+    return b
+
+
+def projector_weights(w: dict) -> vt_projector_weights:
+    p = vt_projector_weights()
+    for name, _ in vt_projector_weights._fields_:
+        t = w.get("p_" + name)
+        setattr(p, name, None if t is None else t.data_ptr())
+    return p
+
+
+def vt_block_forward(cfg, resid, bw: vt_block_weights, cu_seqlens, pos_thw, n_img, total_tokens,
+                     max_seqlen, ws, stream=None):
+    _check(LIB.vt_block_forward(ctypes.byref(cfg), _ptr(resid), ctypes.byref(bw), _ptr(cu_seqlens),
+                                _ptr(pos_thw), n_img, total_tokens, max_seqlen, _ptr(ws),
+                                ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def vt_merge_project(cfg, tower, order, grids, pw: vt_projector_weights, merged_raw, out, ws,
+                     stream=None):
+    g, n = _grid(grids)
+    _check(LIB.vt_merge_project(ctypes.byref(cfg), _ptr(tower), order, g, n,
+                                ctypes.byref(pw) if pw is not None else None, _ptr(merged_raw),
+                                _ptr(out), _ptr(ws), ws.numel() if ws is not None else 0,
+                                _stream(stream)))
+
+
+class TowerWeights:
+    """Keeps the ctypes structs of a tower weight set alive (device tensors in ``w``)."""
+
+    def __init__(self, w: dict, n_layers: int):
+        self.w = w
+        self.blocks = (vt_block_weights * max(1, n_layers))()
+        for i in range(n_layers):
+            self.blocks[i] = block_weights(w, f"l{i}.")
+        self.struct = vt_tower_weights()
+        self.struct.w_patch = w["patch_w"].data_ptr()
+        bp = w.get("patch_b")
+        self.struct.b_patch = None if bp is None else bp.data_ptr()
+        self.struct.blocks = ctypes.cast(self.blocks, ctypes.POINTER(vt_block_weights))
+        if "p_w1" in w:
+            self.struct.proj = projector_weights(w)
+
+
+def vt_tower_forward(cfg, pixels, grids, tw: TowerWeights, tower_out, merged_raw, out, ws,
+                     stream=None):
+    g, n = _grid(grids)
+    _check(LIB.vt_tower_forward(ctypes.byref(cfg), _ptr(pixels), g, n, ctypes.byref(tw.struct),
+                                _ptr(tower_out), _ptr(merged_raw), _ptr(out), _ptr(ws),
+                                ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def vt_linear(x, M, K, w, N, bias, epi, out, ws=None, stream=None):
+    _check(LIB.vt_linear(_ptr(x), M, K, _ptr(w), N, _ptr(bias), epi, _ptr(out), _ptr(ws),
+                         ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def vt_layer_norm(x, rows, width, g, b, eps, out, stream=None):
+    _check(LIB.vt_layer_norm(_ptr(x), rows, width, _ptr(g), _ptr(b), float(eps), _ptr(out),
+                             _stream(stream)))
+
+
+# ------------------------------------------------------------------ device helpers
+def to_device_bits(a: np.ndarray, device="cuda"):
+    """Upload uint16 bf16 bits as an int16 tensor (same bytes)."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
+
+
+def bits_to_numpy(t) -> np.ndarray:
+    """Download an int16/bf16 tensor holding bf16 bits as uint16."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
+    return t.cpu().numpy().view(np.uint16)
+
+
+def workspace(nbytes: int, device="cuda"):
+    """A 256-byte aligned uint8 workspace tensor (torch's allocator aligns to 512 B)."""
+    import torch
+    t = torch.empty(max(1, int(nbytes)), dtype=torch.uint8, device=device)
+    assert t.data_ptr() % 256 == 0
+    return t

@@ -1,0 +1,141 @@
+// Integer metadata of a packed image batch, on the device.
+//
+// For each image i with grid (t=1, h, w) (grid_thw of "v2_loaders FINDINGS"
+// section 3; one native-resolution grid per image as in its section 1):
+//   cu_seqlens[i]  first token of the image (prefix sum of h*w),
+//   pos_thw[j]     (t, row, col) of token j, restarting at 0 per image,
+//   raster_index[j] cu[i] + row*w + col,
+//   tok_img[j]     i.
+// Tokens are stored in 2x2-window order: token 4*(R*(w/2) + C) + 2*dr + dc of
+// an image is the patch at (2R+dr, 2C+dc), so the 2x2 merge of the
+// MiniMax-M3-Vision README ("Token compression" row) is a reshape.
+#include "vt_device.h"
+#include "vt_kernels.h"
+
+namespace vt {
+
+__global__ void __launch_bounds__(256) metadata_kernel(MetaChunk c, int32_t* __restrict__ cu_seqlens,
+                                                       ImgInfo* __restrict__ info,
+                                                       int32_t* __restrict__ pos_thw,
+                                                       int32_t* __restrict__ raster_index,
+                                                       int32_t* __restrict__ tok_img) {
+  const int li = blockIdx.y;  // image within the chunk
+  if (li >= c.count) return;
+  const int img = c.first + li;
+  const int h = c.h[li], w = c.w[li], base = c.cu[li];
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (cu_seqlens) cu_seqlens[img] = base;
+    if (info) info[img] = ImgInfo{h, w, c.pix_off[li]};
+  }
+  const int n = h * w, w2 = w >> 1;
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x) {
+    const int m = j >> 2, k = j & 3;
+    const int row = 2 * (m / w2) + (k >> 1);
+    const int col = 2 * (m % w2) + (k & 1);
+    const int t = base + j;
+    if (pos_thw) {
+      pos_thw[3 * t + 0] = 0;
+      pos_thw[3 * t + 1] = row;
+      pos_thw[3 * t + 2] = col;
+    }
+    if (raster_index) raster_index[t] = base + row * w + col;
+    if (tok_img) tok_img[t] = img;
+  }
+}
+
+hipError_t launch_metadata(const MetaChunk& c, int32_t max_tokens_in_chunk, int32_t* cu_seqlens,
+                           ImgInfo* info, int32_t* pos_thw, int32_t* raster_index,
+                           int32_t* tok_img, hipStream_t s) {
+  int bx = (max_tokens_in_chunk + 255) / 256;
+  if (bx > 64) bx = 64;
+  if (bx < 1) bx = 1;
+  hipLaunchKernelGGL(metadata_kernel, dim3(bx, c.count), dim3(256), 0, s, c, cu_seqlens, info,
+                     pos_thw, raster_index, tok_img);
+  return hipGetLastError();
+}
+
+__global__ void cu_last_kernel(int32_t* cu_seqlens, int32_t n_img, int32_t total) {
+  if (threadIdx.x == 0) cu_seqlens[n_img] = total;
+}
+
+hipError_t launch_cu_last(int32_t* cu_seqlens, int32_t n_img, int32_t total, hipStream_t s) {
+  hipLaunchKernelGGL(cu_last_kernel, dim3(1), dim3(64), 0, s, cu_seqlens, n_img, total);
+  return hipGetLastError();
+}
+
+// One workgroup.  rank(i) = #{j : n_j > n_i, or n_j == n_i and j < i} orders
+// the images largest first (longest-processing-time first: the expensive
+// q-tiles are dispatched before the cheap ones).  tile_start is the
+// exclusive prefix sum of ceil(n/q_tile) in rank order, with
+// tile_start[n_img] = the total number of q-tiles.
+__global__ void __launch_bounds__(1024) attn_schedule_kernel(const int32_t* __restrict__ cu,
+                                                             int32_t n_img, int32_t q_tile,
+                                                             int32_t* __restrict__ order,
+                                                             int32_t* __restrict__ tile_start) {
+  __shared__ int32_t part[1024];
+  const int tid = threadIdx.x, nt = blockDim.x;
+  for (int i = tid; i < n_img; i += nt) {
+    const int ni = cu[i + 1] - cu[i];
+    int r = 0;
+    for (int j = 0; j < n_img; ++j) {
+      const int nj = cu[j + 1] - cu[j];
+      r += (nj > ni) || (nj == ni && j < i);
+    }
+    order[r] = i;
+  }
+  __syncthreads();
+  // chunked exclusive scan over ranks
+  const int per = (n_img + nt - 1) / nt;
+  const int lo = tid * per, hi = min(n_img, lo + per);
+  int sum = 0;
+  for (int r = lo; r < hi; ++r) {
+    const int i = order[r];
+    sum += (cu[i + 1] - cu[i] + q_tile - 1) / q_tile;
+  }
+  part[tid] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int t = 0; t < nt; ++t) {
+      const int v = part[t];
+      part[t] = run;
+      run += v;
+    }
+    tile_start[n_img] = run;
+  }
+  __syncthreads();
+  int run = part[tid];
+  for (int r = lo; r < hi; ++r) {
+    tile_start[r] = run;
+    const int i = order[r];
+    run += (cu[i + 1] - cu[i] + q_tile - 1) / q_tile;
+  }
+}
+
+hipError_t launch_attn_schedule(const int32_t* cu_seqlens, int32_t n_img, int32_t q_tile,
+                                int32_t* order, int32_t* tile_start, hipStream_t s) {
+  hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, s, cu_seqlens, n_img, q_tile,
+                     order, tile_start);
+  return hipGetLastError();
+}
+
+// cs[pos * pairs + j] = (cos, sin)(pos * inv_freq[j]), formed in double and
+// rounded to fp32 (the table is small: pairs x n_pos entries).
+__global__ void __launch_bounds__(256) rope_table_kernel(RopeFreq f, int32_t n_pos,
+                                                         float2* __restrict__ cs) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_pos * f.pairs) return;
+  const int pos = i / f.pairs, j = i - pos * f.pairs;
+  const double ang = double(pos) * f.inv_freq[j];
+  double sn, cn;
+  sincos(ang, &sn, &cn);
+  cs[i] = make_float2(float(cn), float(sn));
+}
+
+hipError_t launch_rope_table(const RopeFreq& f, int32_t n_pos, float2* cs, hipStream_t s) {
+  const int n = n_pos * f.pairs;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s, f, n_pos, cs);
+  return hipGetLastError();
+}
+
+}  // namespace vt

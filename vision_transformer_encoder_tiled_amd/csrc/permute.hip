@@ -1,0 +1,95 @@
+// Memory-bound permutations: patchify (pixels -> patch rows in token order),
+// row permutation between token order and raster order, fp32 -> bf16 cast.
+#include "vt_device.h"
+#include "vt_kernels.h"
+
+namespace vt {
+
+// One thread per (token, channel, py): reads the 14 pixels of that patch row
+// and writes them twice (tau = 0 and tau = 1: the single frame is repeated to
+// fill the temporal patch of 2, "v2_loaders FINDINGS" section 3).  Row layout
+// of X is (channel, tau, py, px), the flattened Conv3d weight order.
+// Pixel rows start at even offsets (14 * col bf16), so the 14 values are read
+// as 7 aligned 32-bit words.
+__global__ void __launch_bounds__(256) patchify_kernel(const uint16_t* __restrict__ pix,
+                                                       const ImgInfo* __restrict__ info,
+                                                       const int32_t* __restrict__ cu,
+                                                       const int32_t* __restrict__ tok_img,
+                                                       int32_t total, uint16_t* __restrict__ X) {
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= int64_t(total) * 42) return;
+  const int tok = int(gid / 42);
+  const int rem = int(gid - int64_t(tok) * 42);
+  const int ch = rem / 14, py = rem - ch * 14;
+  const int img = tok_img[tok];
+  const ImgInfo in = info[img];
+  const int j = tok - cu[img];
+  const int w2 = in.w >> 1;
+  const int m = j >> 2, k = j & 3;
+  const int row = 2 * (m / w2) + (k >> 1);
+  const int col = 2 * (m % w2) + (k & 1);
+  const int64_t W = int64_t(in.w) * 14, H = int64_t(in.h) * 14;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(
+      pix + in.pix_off + int64_t(ch) * H * W + (int64_t(row) * 14 + py) * W + int64_t(col) * 14);
+  uint32_t v[7];
+#pragma unroll
+  for (int i = 0; i < 7; ++i) v[i] = src[i];
+  uint32_t* dst0 = reinterpret_cast<uint32_t*>(X + int64_t(tok) * 1176 + (ch * 2 + 0) * 196 + py * 14);
+  uint32_t* dst1 = reinterpret_cast<uint32_t*>(X + int64_t(tok) * 1176 + (ch * 2 + 1) * 196 + py * 14);
+#pragma unroll
+  for (int i = 0; i < 7; ++i) {
+    dst0[i] = v[i];
+    dst1[i] = v[i];
+  }
+}
+
+hipError_t launch_patchify(const uint16_t* pixels, const ImgInfo* info, const int32_t* cu_seqlens,
+                           const int32_t* tok_img, int32_t total_tokens, uint16_t* X,
+                           hipStream_t s) {
+  const int64_t n = int64_t(total_tokens) * 42;
+  hipLaunchKernelGGL(patchify_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, pixels,
+                     info, cu_seqlens, tok_img, total_tokens, X);
+  return hipGetLastError();
+}
+
+// One workgroup per row; rows are moved as 16-byte vectors (width % 8 == 0).
+__global__ void __launch_bounds__(256) row_permute_kernel(const uint16_t* __restrict__ src,
+                                                          uint16_t* __restrict__ dst,
+                                                          const int32_t* __restrict__ ridx,
+                                                          int32_t width, int scatter) {
+  const int r = blockIdx.x;
+  const int other = ridx[r];
+  const int64_t so = int64_t(scatter ? r : other) * width;
+  const int64_t dof = int64_t(scatter ? other : r) * width;
+  const uint4* s4 = reinterpret_cast<const uint4*>(src + so);
+  uint4* d4 = reinterpret_cast<uint4*>(dst + dof);
+  for (int i = threadIdx.x; i < width / 8; i += blockDim.x) d4[i] = s4[i];
+}
+
+hipError_t launch_row_permute(const uint16_t* src, uint16_t* dst, const int32_t* raster_index,
+                              int32_t rows, int32_t width, bool scatter, hipStream_t s) {
+  hipLaunchKernelGGL(row_permute_kernel, dim3(rows), dim3(256), 0, s, src, dst, raster_index,
+                     width, scatter ? 1 : 0);
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256) f32_to_bf16_kernel(const float4* __restrict__ src,
+                                                          uint2* __restrict__ dst, size_t n4) {
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n4;
+       i += size_t(gridDim.x) * blockDim.x) {
+    const float4 v = src[i];
+    dst[i] = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+  }
+}
+
+hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t s) {
+  const size_t n4 = n / 4;  // n % 4 == 0 (widths are multiples of 64)
+  size_t blocks = (n4 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(unsigned(blocks)), dim3(256), 0, s,
+                     reinterpret_cast<const float4*>(src), reinterpret_cast<uint2*>(dst), n4);
+  return hipGetLastError();
+}
+
+}  // namespace vt

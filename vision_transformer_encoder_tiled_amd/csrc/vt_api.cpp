@@ -1,0 +1,627 @@
+// C ABI of the tiled ViT vision tower: argument validation, workspace
+// planning (linear in the token count), and launch sequencing on the
+// caller's stream.  Every check runs before the first launch, in every
+// build; a failing call launches nothing and records the reason in a
+// thread-local string.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/vt.h"
+#include "vt_kernels.h"
+
+#define VT_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_err;
+
+vt_status fail(vt_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+#define VT_TRY_HIP(expr)                                                                   \
+  do {                                                                                     \
+    hipError_t _e = (expr);                                                                \
+    if (_e != hipSuccess) return fail(VT_ERR_HIP, "%s: %s", #expr, hipGetErrorString(_e)); \
+  } while (0)
+
+constexpr int64_t kMaxTokens = int64_t(1) << 26;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+vt_status check_config(const vt_config* c) {
+  if (!c) return fail(VT_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->hidden <= 0 || c->heads <= 0 || c->head_dim <= 0 || c->mlp <= 0 || c->layers < 0 ||
+      c->proj_hidden <= 0 || c->proj_out <= 0)
+    return fail(VT_ERR_INVALID_ARG, "config sizes must be positive (layers >= 0)");
+  if (c->hidden != c->heads * c->head_dim)
+    return fail(VT_ERR_INVALID_ARG, "hidden %d != heads %d * head_dim %d", c->hidden, c->heads,
+                c->head_dim);
+  if (!(c->ln_eps > 0.f) || !(c->rope_theta > 0.f))
+    return fail(VT_ERR_INVALID_ARG, "ln_eps and rope_theta must be > 0");
+  if (c->rope_pairs[0] < 0 || c->rope_pairs[1] < 0 || c->rope_pairs[2] < 0 ||
+      c->rope_pairs[0] + c->rope_pairs[1] + c->rope_pairs[2] != c->head_dim / 2)
+    return fail(VT_ERR_INVALID_ARG, "rope_pairs must be >= 0 and sum to head_dim/2");
+  if (c->head_dim != 80)
+    return fail(VT_ERR_UNSUPPORTED, "attention kernel implements head_dim 80 (got %d)", c->head_dim);
+  if (c->patch != 14 || c->t_patch != 2 || c->merge != 2)
+    return fail(VT_ERR_UNSUPPORTED, "kernels implement patch 14, temporal patch 2, merge 2");
+  if (c->rope_pairs[0] % 8 || c->rope_pairs[1] % 8 || c->rope_pairs[2] % 8)
+    return fail(VT_ERR_UNSUPPORTED, "rope_pairs must be multiples of 8");
+  if (c->hidden % 256 || c->hidden > 4096)
+    return fail(VT_ERR_UNSUPPORTED, "hidden must be a multiple of 256, at most 4096");
+  if (c->mlp % 64 || c->proj_hidden % 64 || c->proj_out % 64)
+    return fail(VT_ERR_UNSUPPORTED, "mlp, proj_hidden and proj_out must be multiples of 64");
+  if (c->heads > 1024) return fail(VT_ERR_UNSUPPORTED, "at most 1024 heads");
+  return VT_OK;
+}
+
+struct GridInfo {
+  int64_t tokens = 0;
+  int32_t max_hw = 0;     // largest h or w: RoPE positions lie in [0, max_hw)
+  int32_t max_seq = 0;    // largest image token count
+  int64_t pixels = 0;
+};
+
+vt_status check_grid(const vt_grid_thw* grid, int32_t n_img, GridInfo* gi) {
+  if (!grid) return fail(VT_ERR_INVALID_ARG, "grid is NULL");
+  if (n_img <= 0) return fail(VT_ERR_INVALID_ARG, "n_img must be >= 1 (got %d)", n_img);
+  GridInfo g;
+  for (int i = 0; i < n_img; ++i) {
+    const vt_grid_thw& x = grid[i];
+    if (x.t <= 0 || x.h <= 0 || x.w <= 0)
+      return fail(VT_ERR_INVALID_ARG, "image %d: t, h, w must be positive (got %d, %d, %d)", i,
+                  x.t, x.h, x.w);
+    if (x.h % 2 || x.w % 2)
+      return fail(VT_ERR_INVALID_ARG, "image %d: h and w must be even for the 2x2 merge (got %d x %d)",
+                  i, x.h, x.w);
+    if (x.t != 1)
+      return fail(VT_ERR_UNSUPPORTED, "image %d: t = %d; only still images (t = 1) are implemented",
+                  i, x.t);
+    const int64_t n = int64_t(x.h) * x.w;
+    g.tokens += n;
+    if (g.tokens > kMaxTokens)
+      return fail(VT_ERR_UNSUPPORTED, "more than %lld tokens in one call", (long long)kMaxTokens);
+    g.max_hw = std::max(g.max_hw, std::max(x.h, x.w));
+    g.max_seq = std::max<int32_t>(g.max_seq, int32_t(n));
+    g.pixels += n * 3 * 196;
+  }
+  *gi = g;
+  return VT_OK;
+}
+
+// ---- workspace carving
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+struct Dims {
+  int32_t N, n_img, d, mlp, heads, P, Pout;
+};
+
+// Buffers of one block, used by vt_block_forward and vt_tower_forward.
+struct BlockBufs {
+  int32_t* order;
+  int32_t* tile_start;
+  float2* rope;
+  uint16_t* xn;    // [N, d] LayerNorm output
+  uint16_t* act;   // [N, max(4d, mlp)]: qkv [N,3d] then attn [N,d]; later the MLP hidden [N, mlp]
+  void* gemm_ws;   // split-K partials
+};
+
+size_t block_gemm_ws(int N, int d, int mlp) {
+  size_t w = vt::gemm_workspace_bytes(N, d, 1176);  // patch embed shares this buffer
+  w = std::max(w, vt::gemm_workspace_bytes(N, 3 * d, d));
+  w = std::max(w, vt::gemm_workspace_bytes(N, d, d));
+  w = std::max(w, vt::gemm_workspace_bytes(N, mlp, d));
+  w = std::max(w, vt::gemm_workspace_bytes(N, d, mlp));
+  return w;
+}
+
+void carve_block(Carver& c, const Dims& D, int32_t n_pos, BlockBufs* b) {
+  b->order = c.take<int32_t>(D.n_img);
+  b->tile_start = c.take<int32_t>(D.n_img + 1);
+  b->rope = c.take<float2>(size_t(n_pos) * 40);
+  b->xn = c.take<uint16_t>(size_t(D.N) * D.d);
+  b->act = c.take<uint16_t>(size_t(D.N) * std::max(4 * D.d, D.mlp));
+  b->gemm_ws = c.take<char>(block_gemm_ws(D.N, D.d, D.mlp));
+}
+
+struct TowerBufs {
+  int32_t *cu, *pos, *ridx, *tok_img;
+  vt::ImgInfo* info;
+  float* R;        // [N, d] fp32 residual
+  uint16_t* X;     // [N, 1176] patches (aliases the block's act region)
+  uint16_t* T;     // [N, d] bf16 tower tokens, token order
+  uint16_t *Y1, *Y2, *U;
+  void* proj_ws;
+  BlockBufs blk;
+};
+
+size_t proj_gemm_ws(int N, int d, int P, int Pout) {
+  size_t w = 0;
+  w = std::max(w, vt::gemm_workspace_bytes(N, P, d));
+  w = std::max(w, vt::gemm_workspace_bytes(N, P, P));
+  w = std::max(w, vt::gemm_workspace_bytes(N / 4, Pout, 4 * P));
+  w = std::max(w, vt::gemm_workspace_bytes(N / 4, Pout, Pout));
+  return w;
+}
+
+void carve_tower(Carver& c, const Dims& D, int32_t n_pos, TowerBufs* t) {
+  t->cu = c.take<int32_t>(D.n_img + 1);
+  t->info = c.take<vt::ImgInfo>(D.n_img);
+  t->pos = c.take<int32_t>(size_t(D.N) * 3);
+  t->ridx = c.take<int32_t>(D.N);
+  t->tok_img = c.take<int32_t>(D.N);
+  t->R = c.take<float>(size_t(D.N) * D.d);
+  t->T = c.take<uint16_t>(size_t(D.N) * D.d);
+  carve_block(c, D, n_pos, &t->blk);
+  // Patches are only live before the first block: they share the act region
+  // when it is large enough, else get their own buffer.
+  if (size_t(std::max(4 * D.d, D.mlp)) >= 1176)
+    t->X = t->blk.act;
+  else
+    t->X = c.take<uint16_t>(size_t(D.N) * 1176);
+  t->Y1 = c.take<uint16_t>(size_t(D.N) * D.P);
+  t->Y2 = c.take<uint16_t>(size_t(D.N) * D.P);
+  t->U = c.take<uint16_t>(size_t(D.N / 4) * D.Pout);
+  t->proj_ws = c.take<char>(proj_gemm_ws(D.N, D.d, D.P, D.Pout));
+}
+
+Dims dims_of(const vt_config* cfg, int64_t N, int32_t n_img) {
+  return Dims{int32_t(N), n_img, cfg->hidden, cfg->mlp, cfg->heads, cfg->proj_hidden,
+              cfg->proj_out};
+}
+
+vt::RopeFreq rope_freq(const vt_config* cfg, int32_t* axis_code) {
+  vt::RopeFreq f{};
+  const int half = cfg->head_dim / 2;
+  f.pairs = half;
+  int j = 0, code = 0;
+  for (int a = 0; a < 3; ++a) {
+    const int n = cfg->rope_pairs[a];
+    for (int k = 0; k < n; ++k, ++j) {
+      // per-axis ladder theta^(-2k / (2n)); shared ladder theta^(-2j / head_dim)
+      f.inv_freq[j] = cfg->rope_shared_ladder
+                          ? std::pow(double(cfg->rope_theta), -2.0 * j / cfg->head_dim)
+                          : std::pow(double(cfg->rope_theta), -2.0 * k / (2.0 * n));
+      if (j % 8 == 0) code |= a << (2 * (j / 8));
+    }
+  }
+  *axis_code = code;
+  return f;
+}
+
+vt_status launch_meta(const vt_grid_thw* grid, int32_t n_img, int64_t total, int32_t* cu,
+                      vt::ImgInfo* info, int32_t* pos, int32_t* ridx, int32_t* tok_img,
+                      hipStream_t s) {
+  int64_t tok = 0, pix = 0;
+  for (int first = 0; first < n_img; first += vt::kMetaChunk) {
+    vt::MetaChunk c{};
+    c.first = first;
+    c.count = std::min(vt::kMetaChunk, n_img - first);
+    int32_t maxn = 0;
+    for (int i = 0; i < c.count; ++i) {
+      const vt_grid_thw& g = grid[first + i];
+      c.h[i] = g.h;
+      c.w[i] = g.w;
+      c.cu[i] = int32_t(tok);
+      c.pix_off[i] = pix;
+      const int64_t n = int64_t(g.h) * g.w;
+      maxn = std::max<int32_t>(maxn, int32_t(n));
+      tok += n;
+      pix += n * 3 * 196;
+    }
+    VT_TRY_HIP(vt::launch_metadata(c, maxn, cu, info, pos, ridx, tok_img, s));
+  }
+  if (cu) VT_TRY_HIP(vt::launch_cu_last(cu, n_img, int32_t(total), s));
+  return VT_OK;
+}
+
+// The per-call attention prologue: LPT schedule and RoPE cos/sin table.
+vt_status attn_prologue(const vt_config* cfg, const int32_t* cu, int32_t n_img, int32_t n_pos,
+                        const BlockBufs& b, int32_t* axis_code, hipStream_t s) {
+  VT_TRY_HIP(vt::launch_attn_schedule(cu, n_img, vt::kAttnQTile, b.order, b.tile_start, s));
+  const vt::RopeFreq f = rope_freq(cfg, axis_code);
+  VT_TRY_HIP(vt::launch_rope_table(f, n_pos, b.rope, s));
+  return VT_OK;
+}
+
+int32_t max_q_tiles(int64_t N, int32_t n_img) {
+  return int32_t((N + vt::kAttnQTile - 1) / vt::kAttnQTile + n_img);
+}
+
+float q_scale_log2(const vt_config* cfg) {
+  return float(1.4426950408889634 / std::sqrt(double(cfg->head_dim)));
+}
+
+vt_status run_attention(const vt_config* cfg, const uint16_t* qkv, const int32_t* cu,
+                        const int32_t* pos, int32_t n_img, int64_t N, int32_t n_pos,
+                        int32_t axis_code, const BlockBufs& b, void* out, bool f32,
+                        hipStream_t s) {
+  VT_TRY_HIP(vt::launch_attention(qkv, cu, pos, b.order, b.tile_start, n_img, max_q_tiles(N, n_img),
+                                  cfg->heads, n_pos, axis_code, b.rope, q_scale_log2(cfg), out, f32,
+                                  s));
+  return VT_OK;
+}
+
+vt_status run_block(const vt_config* cfg, float* R, const vt_block_weights* w, const int32_t* cu,
+                    const int32_t* pos, int32_t n_img, int64_t N, int32_t n_pos, int32_t axis_code,
+                    const BlockBufs& b, hipStream_t s) {
+  const int d = cfg->hidden, mlp = cfg->mlp, M = int(N);
+  uint16_t* qkv = b.act;
+  uint16_t* att = b.act + size_t(N) * 3 * d;
+  VT_TRY_HIP(vt::launch_layer_norm(R, M, d, w->ln1_g, w->ln1_b, cfg->ln_eps, b.xn, s));
+  VT_TRY_HIP(vt::launch_gemm(b.xn, M, d, w->w_qkv, 3 * d, w->b_qkv, vt::kEpiBf16, qkv, b.gemm_ws, s));
+  vt_status st = run_attention(cfg, qkv, cu, pos, n_img, N, n_pos, axis_code, b, att, false, s);
+  if (st != VT_OK) return st;
+  VT_TRY_HIP(vt::launch_gemm(att, M, d, w->w_o, d, w->b_o, vt::kEpiResid, R, b.gemm_ws, s));
+  VT_TRY_HIP(vt::launch_layer_norm(R, M, d, w->ln2_g, w->ln2_b, cfg->ln_eps, b.xn, s));
+  VT_TRY_HIP(vt::launch_gemm(b.xn, M, d, w->w_fc1, mlp, w->b_fc1, vt::kEpiGeluTanh, b.act, b.gemm_ws, s));
+  VT_TRY_HIP(vt::launch_gemm(b.act, M, mlp, w->w_fc2, d, w->b_fc2, vt::kEpiResid, R, b.gemm_ws, s));
+  return VT_OK;
+}
+
+vt_status check_block_weights(const vt_block_weights* w, int layer) {
+  if (!w) return fail(VT_ERR_INVALID_ARG, "block weights %d are NULL", layer);
+  const void* req[] = {w->ln1_g, w->ln1_b, w->w_qkv, w->w_o, w->ln2_g, w->ln2_b, w->w_fc1, w->w_fc2};
+  const char* names[] = {"ln1_g", "ln1_b", "w_qkv", "w_o", "ln2_g", "ln2_b", "w_fc1", "w_fc2"};
+  for (int i = 0; i < 8; ++i) {
+    if (!req[i]) return fail(VT_ERR_INVALID_ARG, "block %d: %s is NULL", layer, names[i]);
+    if (!aligned16(req[i]))
+      return fail(VT_ERR_INVALID_ARG, "block %d: %s is not 16-byte aligned", layer, names[i]);
+  }
+  const void* opt[] = {w->b_qkv, w->b_o, w->b_fc1, w->b_fc2};
+  for (const void* p : opt)
+    if (p && !aligned16(p)) return fail(VT_ERR_INVALID_ARG, "block %d: a bias is not 16-byte aligned", layer);
+  return VT_OK;
+}
+
+vt_status check_proj_weights(const vt_projector_weights* w) {
+  if (!w) return fail(VT_ERR_INVALID_ARG, "projector weights are NULL");
+  const void* req[] = {w->w1, w->w2, w->w3, w->w4};
+  for (int i = 0; i < 4; ++i) {
+    if (!req[i]) return fail(VT_ERR_INVALID_ARG, "projector w%d is NULL", i + 1);
+    if (!aligned16(req[i])) return fail(VT_ERR_INVALID_ARG, "projector w%d is not 16-byte aligned", i + 1);
+  }
+  const void* opt[] = {w->b1, w->b2, w->b3, w->b4};
+  for (const void* p : opt)
+    if (p && !aligned16(p)) return fail(VT_ERR_INVALID_ARG, "a projector bias is not 16-byte aligned");
+  return VT_OK;
+}
+
+vt_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need && !ws) return fail(VT_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (ws && (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)))
+    return fail(VT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(VT_ERR_WORKSPACE, "workspace of %zu bytes is too small: %zu needed", ws_bytes, need);
+  return VT_OK;
+}
+
+vt_status check_ptr(const void* p, const char* name) {
+  if (!p) return fail(VT_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(VT_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return VT_OK;
+}
+
+size_t block_ws_bytes(const vt_config* cfg, int64_t N, int32_t n_img, int32_t n_pos) {
+  Carver c(nullptr);
+  BlockBufs b;
+  carve_block(c, dims_of(cfg, N, n_img), n_pos, &b);
+  return c.off;
+}
+
+size_t tower_ws_bytes(const vt_config* cfg, const GridInfo& gi, int32_t n_img) {
+  Carver c(nullptr);
+  TowerBufs t;
+  carve_tower(c, dims_of(cfg, gi.tokens, n_img), gi.max_hw, &t);
+  return c.off;
+}
+
+// Everything after the last block: bf16 cast, optional outputs, projector.
+vt_status run_tail(const vt_config* cfg, const TowerBufs& t, const uint16_t* T, int64_t N,
+                   const vt_projector_weights* pw, uint16_t* merged_raw, uint16_t* out,
+                   hipStream_t s) {
+  const int d = cfg->hidden, P = cfg->proj_hidden, Po = cfg->proj_out, M = int(N);
+  if (merged_raw)
+    VT_TRY_HIP(hipMemcpyAsync(merged_raw, T, size_t(N) * d * sizeof(uint16_t),
+                              hipMemcpyDeviceToDevice, s));
+  if (out) {
+    const int e1 = cfg->gelu_erf_projector ? vt::kEpiGeluErf : vt::kEpiGeluTanh;
+    VT_TRY_HIP(vt::launch_gemm(T, M, d, pw->w1, P, pw->b1, e1, t.Y1, t.proj_ws, s));
+    VT_TRY_HIP(vt::launch_gemm(t.Y1, M, P, pw->w2, P, pw->b2, vt::kEpiBf16, t.Y2, t.proj_ws, s));
+    // token order keeps the four patches of a merged token adjacent: Y2 viewed
+    // as [N/4, 4P] is the flattened 2x2 group, slot k = 2*dr + dc.
+    VT_TRY_HIP(vt::launch_gemm(t.Y2, M / 4, 4 * P, pw->w3, Po, pw->b3, e1, t.U, t.proj_ws, s));
+    VT_TRY_HIP(vt::launch_gemm(t.U, M / 4, Po, pw->w4, Po, pw->b4, vt::kEpiBf16, out, t.proj_ws, s));
+  }
+  return VT_OK;
+}
+
+}  // namespace
+
+// =================================================================== ABI
+VT_API void vt_config_default(vt_config* c) {
+  if (!c) return;
+  c->layers = 32;
+  c->hidden = 1280;
+  c->heads = 16;
+  c->head_dim = 80;
+  c->mlp = 5120;
+  c->patch = 14;
+  c->t_patch = 2;
+  c->merge = 2;
+  c->proj_hidden = 6144;
+  c->proj_out = 6144;
+  c->ln_eps = 1e-6f;
+  c->rope_theta = 10000.f;
+  c->rope_pairs[0] = 8;
+  c->rope_pairs[1] = 16;
+  c->rope_pairs[2] = 16;
+  c->rope_shared_ladder = 0;
+  c->gelu_erf_projector = 0;
+}
+
+VT_API const char* vt_status_string(vt_status s) {
+  switch (s) {
+    case VT_OK: return "VT_OK";
+    case VT_ERR_INVALID_ARG: return "VT_ERR_INVALID_ARG";
+    case VT_ERR_UNSUPPORTED: return "VT_ERR_UNSUPPORTED";
+    case VT_ERR_WORKSPACE: return "VT_ERR_WORKSPACE";
+    case VT_ERR_HIP: return "VT_ERR_HIP";
+  }
+  return "VT_ERR_UNKNOWN";
+}
+
+VT_API const char* vt_last_error(void) { return g_err.c_str(); }
+
+VT_API const char* vt_version(void) { return "vt 0.1 gfx950"; }
+
+VT_API size_t vt_tower_workspace_size(const vt_config* cfg, const vt_grid_thw* grid, int32_t n_img) {
+  if (check_config(cfg) != VT_OK) return 0;
+  GridInfo gi;
+  if (check_grid(grid, n_img, &gi) != VT_OK) return 0;
+  return tower_ws_bytes(cfg, gi, n_img);
+}
+
+VT_API size_t vt_block_workspace_size(const vt_config* cfg, int32_t total_tokens, int32_t n_img,
+                                      int32_t max_seqlen) {
+  if (check_config(cfg) != VT_OK) return 0;
+  if (total_tokens <= 0 || n_img <= 0 || max_seqlen <= 0) {
+    fail(VT_ERR_INVALID_ARG, "total_tokens, n_img and max_seqlen must be positive");
+    return 0;
+  }
+  return block_ws_bytes(cfg, total_tokens, n_img, max_seqlen);
+}
+
+VT_API vt_status vt_build_metadata(const vt_grid_thw* grid, int32_t n_img, int32_t* cu_seqlens,
+                                   int32_t* pos_thw, int32_t* raster_index, void* stream) {
+  GridInfo gi;
+  vt_status st = check_grid(grid, n_img, &gi);
+  if (st != VT_OK) return st;
+  if (!cu_seqlens || !pos_thw) return fail(VT_ERR_INVALID_ARG, "cu_seqlens and pos_thw are required");
+  return launch_meta(grid, n_img, gi.tokens, cu_seqlens, nullptr, pos_thw, raster_index, nullptr,
+                     static_cast<hipStream_t>(stream));
+}
+
+VT_API vt_status vt_patch_embed(const vt_config* cfg, const uint16_t* pixels, const vt_grid_thw* grid,
+                                int32_t n_img, const uint16_t* w_patch, const uint16_t* b_patch,
+                                float* resid_out, void* ws, size_t ws_bytes, void* stream) {
+  vt_status st = check_config(cfg);
+  if (st != VT_OK) return st;
+  GridInfo gi;
+  if ((st = check_grid(grid, n_img, &gi)) != VT_OK) return st;
+  if ((st = check_ptr(pixels, "pixels")) != VT_OK) return st;
+  if ((st = check_ptr(w_patch, "w_patch")) != VT_OK) return st;
+  if (b_patch && !aligned16(b_patch)) return fail(VT_ERR_INVALID_ARG, "b_patch is not 16-byte aligned");
+  if ((st = check_ptr(resid_out, "resid_out")) != VT_OK) return st;
+  const size_t need = tower_ws_bytes(cfg, gi, n_img);
+  if ((st = check_ws(ws, ws_bytes, need)) != VT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver c(ws);
+  TowerBufs t;
+  carve_tower(c, dims_of(cfg, gi.tokens, n_img), gi.max_hw, &t);
+  st = launch_meta(grid, n_img, gi.tokens, t.cu, t.info, t.pos, t.ridx, t.tok_img, s);
+  if (st != VT_OK) return st;
+  VT_TRY_HIP(vt::launch_patchify(pixels, t.info, t.cu, t.tok_img, int32_t(gi.tokens), t.X, s));
+  VT_TRY_HIP(vt::launch_gemm(t.X, int(gi.tokens), 1176, w_patch, cfg->hidden, b_patch, vt::kEpiF32,
+                             resid_out, t.blk.gemm_ws, s));
+  return VT_OK;
+}
+
+static vt_status check_varlen(const vt_config* cfg, const int32_t* cu_seqlens, const int32_t* pos_thw,
+                              int32_t n_img, int32_t total_tokens, int32_t max_seqlen) {
+  vt_status st = check_config(cfg);
+  if (st != VT_OK) return st;
+  if (!cu_seqlens || !pos_thw) return fail(VT_ERR_INVALID_ARG, "cu_seqlens and pos_thw are required");
+  if (n_img <= 0 || total_tokens <= 0 || max_seqlen <= 0)
+    return fail(VT_ERR_INVALID_ARG, "n_img, total_tokens and max_seqlen must be positive");
+  if (max_seqlen > total_tokens)
+    return fail(VT_ERR_INVALID_ARG, "max_seqlen %d exceeds total_tokens %d", max_seqlen, total_tokens);
+  if (total_tokens > kMaxTokens)
+    return fail(VT_ERR_UNSUPPORTED, "more than %lld tokens in one call", (long long)kMaxTokens);
+  return VT_OK;
+}
+
+VT_API vt_status vt_attention_varlen(const vt_config* cfg, const uint16_t* qkv,
+                                     const int32_t* cu_seqlens, const int32_t* pos_thw,
+                                     int32_t n_img, int32_t total_tokens, int32_t max_seqlen,
+                                     void* out, vt_dtype out_dtype, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  vt_status st = check_varlen(cfg, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen);
+  if (st != VT_OK) return st;
+  if ((st = check_ptr(qkv, "qkv")) != VT_OK) return st;
+  if ((st = check_ptr(out, "out")) != VT_OK) return st;
+  if (out_dtype != VT_BF16 && out_dtype != VT_FP32) return fail(VT_ERR_INVALID_ARG, "bad out_dtype");
+  const size_t need = block_ws_bytes(cfg, total_tokens, n_img, max_seqlen);
+  if ((st = check_ws(ws, ws_bytes, need)) != VT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver c(ws);
+  BlockBufs b;
+  carve_block(c, dims_of(cfg, total_tokens, n_img), max_seqlen, &b);
+  int32_t axis_code = 0;
+  if ((st = attn_prologue(cfg, cu_seqlens, n_img, max_seqlen, b, &axis_code, s)) != VT_OK) return st;
+  return run_attention(cfg, qkv, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen, axis_code, b,
+                       out, out_dtype == VT_FP32, s);
+}
+
+VT_API vt_status vt_block_forward(const vt_config* cfg, float* resid, const vt_block_weights* w,
+                                  const int32_t* cu_seqlens, const int32_t* pos_thw, int32_t n_img,
+                                  int32_t total_tokens, int32_t max_seqlen, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  vt_status st = check_varlen(cfg, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen);
+  if (st != VT_OK) return st;
+  if ((st = check_ptr(resid, "resid")) != VT_OK) return st;
+  if ((st = check_block_weights(w, 0)) != VT_OK) return st;
+  const size_t need = block_ws_bytes(cfg, total_tokens, n_img, max_seqlen);
+  if ((st = check_ws(ws, ws_bytes, need)) != VT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver c(ws);
+  BlockBufs b;
+  carve_block(c, dims_of(cfg, total_tokens, n_img), max_seqlen, &b);
+  int32_t axis_code = 0;
+  if ((st = attn_prologue(cfg, cu_seqlens, n_img, max_seqlen, b, &axis_code, s)) != VT_OK) return st;
+  return run_block(cfg, resid, w, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen, axis_code, b, s);
+}
+
+VT_API vt_status vt_merge_project(const vt_config* cfg, const uint16_t* tower, vt_order order,
+                                  const vt_grid_thw* grid, int32_t n_img,
+                                  const vt_projector_weights* w, uint16_t* merged_raw, uint16_t* out,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  vt_status st = check_config(cfg);
+  if (st != VT_OK) return st;
+  GridInfo gi;
+  if ((st = check_grid(grid, n_img, &gi)) != VT_OK) return st;
+  if ((st = check_ptr(tower, "tower")) != VT_OK) return st;
+  if (order != VT_ORDER_WINDOW && order != VT_ORDER_RASTER)
+    return fail(VT_ERR_INVALID_ARG, "order must be VT_ORDER_WINDOW or VT_ORDER_RASTER");
+  if (!out && !merged_raw) return fail(VT_ERR_INVALID_ARG, "out and merged_raw are both NULL");
+  if (out) {
+    if ((st = check_ptr(out, "out")) != VT_OK) return st;
+    if ((st = check_proj_weights(w)) != VT_OK) return st;
+  }
+  if (merged_raw && (st = check_ptr(merged_raw, "merged_raw")) != VT_OK) return st;
+  const size_t need = tower_ws_bytes(cfg, gi, n_img);
+  if ((st = check_ws(ws, ws_bytes, need)) != VT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver c(ws);
+  TowerBufs t;
+  carve_tower(c, dims_of(cfg, gi.tokens, n_img), gi.max_hw, &t);
+  const uint16_t* T = tower;
+  if (order == VT_ORDER_RASTER) {
+    st = launch_meta(grid, n_img, gi.tokens, nullptr, nullptr, nullptr, t.ridx, nullptr, s);
+    if (st != VT_OK) return st;
+    VT_TRY_HIP(vt::launch_row_permute(tower, t.T, t.ridx, int32_t(gi.tokens), cfg->hidden, false, s));
+    T = t.T;
+  }
+  return run_tail(cfg, t, T, gi.tokens, w, merged_raw, out, s);
+}
+
+VT_API vt_status vt_tower_forward(const vt_config* cfg, const uint16_t* pixels,
+                                  const vt_grid_thw* grid, int32_t n_img, const vt_tower_weights* w,
+                                  uint16_t* tower_out, uint16_t* merged_raw, uint16_t* out, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  vt_status st = check_config(cfg);
+  if (st != VT_OK) return st;
+  GridInfo gi;
+  if ((st = check_grid(grid, n_img, &gi)) != VT_OK) return st;
+  if ((st = check_ptr(pixels, "pixels")) != VT_OK) return st;
+  if (!w) return fail(VT_ERR_INVALID_ARG, "weights are NULL");
+  if ((st = check_ptr(w->w_patch, "w_patch")) != VT_OK) return st;
+  if (w->b_patch && !aligned16(w->b_patch)) return fail(VT_ERR_INVALID_ARG, "b_patch is not 16-byte aligned");
+  if (cfg->layers > 0 && !w->blocks) return fail(VT_ERR_INVALID_ARG, "blocks is NULL");
+  for (int l = 0; l < cfg->layers; ++l)
+    if ((st = check_block_weights(&w->blocks[l], l)) != VT_OK) return st;
+  if (!tower_out && !merged_raw && !out) return fail(VT_ERR_INVALID_ARG, "no output requested");
+  if (out) {
+    if ((st = check_ptr(out, "out")) != VT_OK) return st;
+    if ((st = check_proj_weights(&w->proj)) != VT_OK) return st;
+  }
+  if (tower_out && (st = check_ptr(tower_out, "tower_out")) != VT_OK) return st;
+  if (merged_raw && (st = check_ptr(merged_raw, "merged_raw")) != VT_OK) return st;
+  const size_t need = tower_ws_bytes(cfg, gi, n_img);
+  if ((st = check_ws(ws, ws_bytes, need)) != VT_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver c(ws);
+  TowerBufs t;
+  const int64_t N = gi.tokens;
+  carve_tower(c, dims_of(cfg, N, n_img), gi.max_hw, &t);
+  if ((st = launch_meta(grid, n_img, N, t.cu, t.info, t.pos, t.ridx, t.tok_img, s)) != VT_OK) return st;
+  int32_t axis_code = 0;
+  if ((st = attn_prologue(cfg, t.cu, n_img, gi.max_hw, t.blk, &axis_code, s)) != VT_OK) return st;
+  VT_TRY_HIP(vt::launch_patchify(pixels, t.info, t.cu, t.tok_img, int32_t(N), t.X, s));
+  VT_TRY_HIP(vt::launch_gemm(t.X, int(N), 1176, w->w_patch, cfg->hidden, w->b_patch, vt::kEpiF32, t.R,
+                             t.blk.gemm_ws, s));
+  for (int l = 0; l < cfg->layers; ++l) {
+    st = run_block(cfg, t.R, &w->blocks[l], t.cu, t.pos, n_img, N, gi.max_hw, axis_code, t.blk, s);
+    if (st != VT_OK) return st;
+  }
+  VT_TRY_HIP(vt::launch_f32_to_bf16(t.R, t.T, size_t(N) * cfg->hidden, s));
+  if (tower_out)
+    VT_TRY_HIP(vt::launch_row_permute(t.T, tower_out, t.ridx, int32_t(N), cfg->hidden, true, s));
+  return run_tail(cfg, t, t.T, N, &w->proj, merged_raw, out, s);
+}
+
+VT_API size_t vt_linear_workspace_size(int32_t M, int32_t N, int32_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return vt::gemm_workspace_bytes(M, N, K);
+}
+
+VT_API vt_status vt_linear(const uint16_t* x, int32_t M, int32_t K, const uint16_t* w, int32_t N,
+                           const uint16_t* bias, vt_epilogue epi, void* out, void* ws,
+                           size_t ws_bytes, void* stream) {
+  vt_status st;
+  if ((st = check_ptr(x, "x")) != VT_OK) return st;
+  if ((st = check_ptr(w, "w")) != VT_OK) return st;
+  if ((st = check_ptr(out, "out")) != VT_OK) return st;
+  if (bias && !aligned16(bias)) return fail(VT_ERR_INVALID_ARG, "bias is not 16-byte aligned");
+  if (M <= 0 || N <= 0 || K <= 0) return fail(VT_ERR_INVALID_ARG, "M, N, K must be positive");
+  if (K % 8) return fail(VT_ERR_UNSUPPORTED, "K must be a multiple of 8 (got %d)", K);
+  if (N % 64) return fail(VT_ERR_UNSUPPORTED, "N must be a multiple of 64 (got %d)", N);
+  if (int64_t(M) * N > (int64_t(1) << 34) || int64_t(M) > kMaxTokens)
+    return fail(VT_ERR_UNSUPPORTED, "M x N too large");
+  if (epi < VT_EPI_BF16 || epi > VT_EPI_F32) return fail(VT_ERR_INVALID_ARG, "bad epilogue %d", int(epi));
+  if ((st = check_ws(ws, ws_bytes, vt::gemm_workspace_bytes(M, N, K))) != VT_OK) return st;
+  VT_TRY_HIP(vt::launch_gemm(x, M, K, w, N, bias, int(epi), out, ws, static_cast<hipStream_t>(stream)));
+  return VT_OK;
+}
+
+VT_API vt_status vt_layer_norm(const float* x, int32_t rows, int32_t width, const uint16_t* g,
+                               const uint16_t* b, float eps, uint16_t* out, void* stream) {
+  vt_status st;
+  if ((st = check_ptr(x, "x")) != VT_OK) return st;
+  if ((st = check_ptr(g, "g")) != VT_OK) return st;
+  if ((st = check_ptr(b, "b")) != VT_OK) return st;
+  if ((st = check_ptr(out, "out")) != VT_OK) return st;
+  if (rows <= 0 || width <= 0) return fail(VT_ERR_INVALID_ARG, "rows and width must be positive");
+  if (width % 256 || width > 4096)
+    return fail(VT_ERR_UNSUPPORTED, "width must be a multiple of 256, at most 4096 (got %d)", width);
+  if (!(eps > 0.f)) return fail(VT_ERR_INVALID_ARG, "eps must be > 0");
+  VT_TRY_HIP(vt::launch_layer_norm(x, rows, width, g, b, eps, out, static_cast<hipStream_t>(stream)));
+  return VT_OK;
+}

@@ -1,0 +1,68 @@
+// Host-side launchers of the gfx950 kernels.  Each returns hipSuccess or the
+// launch error; shapes are validated by the caller (vt_api.cpp) before any
+// launcher runs.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vt {
+
+// ---- metadata (meta.hip)
+constexpr int kMetaChunk = 128;  // images per metadata launch (kernel-argument table)
+struct ImgInfo {                 // one image as the device kernels see it
+  int32_t h, w;
+  int64_t pix_off;               // first pixel of the image in the packed pixel array
+};
+struct MetaChunk {
+  int32_t first, count;          // images [first, first+count)
+  int32_t h[kMetaChunk], w[kMetaChunk], cu[kMetaChunk];
+  int64_t pix_off[kMetaChunk];
+};
+hipError_t launch_metadata(const MetaChunk& c, int32_t max_tokens_in_chunk, int32_t* cu_seqlens,
+                           ImgInfo* info, int32_t* pos_thw, int32_t* raster_index,
+                           int32_t* tok_img, hipStream_t s);
+hipError_t launch_cu_last(int32_t* cu_seqlens, int32_t n_img, int32_t total, hipStream_t s);
+
+// Attention work schedule: images ordered by token count (largest first),
+// tile_start[r] = first q-tile of the image of rank r.
+hipError_t launch_attn_schedule(const int32_t* cu_seqlens, int32_t n_img, int32_t q_tile,
+                                int32_t* order, int32_t* tile_start, hipStream_t s);
+// RoPE table cs[pos][j] = (cos, sin)(pos * inv_freq[j]), pos < n_pos, j < 40.
+struct RopeFreq { double inv_freq[64]; int32_t pairs; };
+hipError_t launch_rope_table(const RopeFreq& f, int32_t n_pos, float2* cs, hipStream_t s);
+
+// ---- permutations (permute.hip)
+hipError_t launch_patchify(const uint16_t* pixels, const ImgInfo* info, const int32_t* cu_seqlens,
+                           const int32_t* tok_img, int32_t total_tokens, uint16_t* X,
+                           hipStream_t s);
+// dst[raster_index[j]] = src[j] (scatter == true) or dst[j] = src[raster_index[j]].
+hipError_t launch_row_permute(const uint16_t* src, uint16_t* dst, const int32_t* raster_index,
+                              int32_t rows, int32_t width, bool scatter, hipStream_t s);
+hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t s);
+
+// ---- LayerNorm (layernorm.hip)
+hipError_t launch_layer_norm(const float* x, int32_t rows, int32_t width, const uint16_t* g,
+                             const uint16_t* b, float eps, uint16_t* out, hipStream_t s);
+
+// ---- GEMM (gemm.hip)
+enum Epi : int { kEpiBf16 = 0, kEpiGeluTanh = 1, kEpiGeluErf = 2, kEpiResid = 3, kEpiF32 = 4 };
+struct GemmPlan {
+  int bm, bn;        // tile
+  int splits;        // split-K factor (1 = none)
+  int kper;          // K elements per split (multiple of 64)
+};
+GemmPlan plan_gemm(int M, int N, int K);
+size_t gemm_workspace_bytes(int M, int N, int K);
+hipError_t launch_gemm(const uint16_t* A, int M, int K, const uint16_t* B, int N,
+                       const uint16_t* bias, int epi, void* out, void* ws, hipStream_t s);
+
+// ---- attention (attention.hip)
+constexpr int kAttnQTile = 128;
+hipError_t launch_attention(const uint16_t* qkv, const int32_t* cu_seqlens, const int32_t* pos_thw,
+                            const int32_t* order, const int32_t* tile_start, int32_t n_img,
+                            int32_t max_tiles, int32_t heads, int32_t n_pos, int32_t axis_code,
+                            const float2* rope_cs, float q_scale_log2, void* out, bool out_f32,
+                            hipStream_t s);
+
+}  // namespace vt
