@@ -1,67 +1,168 @@
-// Tiled varlen non-causal multi-head attention with 3D RoPE fused into the
-// Q and K loads, for head_dim 80 on the gfx950 matrix cores.
+// Tiled varlen non-causal multi-head attention with 3D RoPE, head_dim 80,
+// on the gfx950 matrix cores.
 //
 // The pages describe the untiled form -- a per-head [seq, seq] fp32 score
 // matrix, a row softmax into a bf16 [seq, seq] probability matrix, then P V
 // ("init.rs (VisionEncoder::new)": build_scratch and the GEMM-based ViT SDPA
 // kernel list) -- and name that quadratic buffer as the limit on image size
 // (doc comment of CEILING_MAX_PATCHES).  Here the scores never leave the MFMA
-// accumulators: each workgroup owns 128 queries of one head of one image and
+// accumulators: a workgroup owns 128 queries of one head of one image and
 // streams that image's keys in tiles of 64 through LDS with an online
-// softmax (running max m, running sum l, rescaled output), so memory is
-// O(tokens).
+// softmax, so memory is O(tokens).
 //
-// Operand precision: the inputs are bf16, the MFMA operands fp16 (rotated
-// and scaled Q, rotated K, V, and the probabilities P), accumulation fp32.
-// fp16 runs at the bf16 rate on gfx950 and carries 3 more mantissa bits:
-// rounding P to bf16 alone would cost up to ~2^-9 |v| per output.  bf16 V
-// converts to fp16 exactly inside the fp16 range; |RoPE(q)| log2(e)/sqrt(80),
-// |k| and |v| must stay below 65504 (larger values become infinite, they
-// are not clamped).
+// Two kernels:
 //
-// Work split (4 wavefronts, 32 queries each):
+// attn_pack_kernel (the Q/K/V load stage, once per token and head):
+//   rotate q and k with 3D RoPE (rotate-half pairs (j, j+40), angle
+//   pos[axis(j)] * inv_freq[j] from a (cos, sin) table built in double),
+//   scale q by log2(e)/sqrt(80), convert q, k, v to fp16, and lay K and V
+//   out as "tile images": for each (head, 64-key tile of an image) the exact
+//   bytes the attention kernel wants in LDS -- K as [64 keys][88] (16-byte
+//   padded rows: conflict-free 16-byte fragment reads) followed by V^T as
+//   [80 dims][68] (conflict-free 8-byte reads).  Each image's keys start on
+//   a fresh tile; the padding keys are zero.  Rotating here instead of per
+//   (query tile, key tile) removes all RoPE and conversion work from the
+//   inner loop, which is VALU-bound at head_dim 80.
+//
+// attention_kernel: 4 wavefronts x 32 queries.
 //   S^T = K Q^T   v_mfma_f32_32x32x16_f16, 2 key blocks x 5 dim slices of
-//                 16 (head_dim 80 = 5 x 16 exactly).  The accumulator layout
-//                 gives each lane one query and 16 keys of each 32-key block.
+//                 16 (head_dim 80 = 5 x 16 exactly).  Each lane holds one
+//                 query and 16 keys of each 32-key block.
 //   O^T = V^T P^T v_mfma_f32_32x32x16_f16, 4 key slices x 3 dim blocks of
-//                 32 (80 padded to 96: rows 80..95 read zeros).  The P
-//                 operand comes straight from the score registers: the keys
-//                 of a 16-key MFMA slice are permuted (k positions 0..7 of a
-//                 lane half hold keys +0..3 and +8..11), and V^T is read in
-//                 the same permuted order, which leaves the sum unchanged.
-// K tiles are rotated (rotate-half RoPE, pairs (j, j+40), angle
-// pos[axis(j)] * inv_freq[j] from a cos/sin table) on their way from global
-// memory to LDS; V tiles are written to LDS transposed ([dim][key]) so the
-// V^T operand is two 8-byte reads.  Q is rotated once, scaled by
-// log2(e)/sqrt(80) and kept in registers; the softmax uses exp2.
+//                 32.  P comes straight from the score registers: the keys
+//                 of a 16-key slice are permuted (k positions 0..7 of a lane
+//                 half hold keys +0..3 and +8..11) and V^T is read in the
+//                 same order.  Dims 80..95 of the third block are padding;
+//                 LDS row 80 of V^T holds ones, so that MFMA row produces
+//                 the softmax denominator l = sum(P) for free, from the same
+//                 fp16 P as the numerator.
+//   Online softmax in the log2 domain with lazy rescaling: the running max
+//   used for exp2 is only raised (and O, l rescaled) when some row's max
+//   grows by more than 8, decided once per wavefront; P is then at most
+//   2^8, well inside fp16.
+//   Tile images are copied global -> registers -> LDS (double buffered, one
+//   barrier per tile) as 16-byte vectors, with no arithmetic.
+//
+// Operand precision: fp16 operands, fp32 accumulation.  fp16 runs at the
+// bf16 rate on gfx950 with 3 more mantissa bits; rounding P to bf16 would
+// cost up to ~2^-9 |v| per output.  |RoPE(q)| log2(e)/sqrt(80), |k| and |v|
+// must stay below 65504 (not clamped: larger values become infinite).
 //
 // Grid: one workgroup per (q-tile, head), head fastest, q-tiles of the
 // largest images first (longest-processing-time order).  With 16 heads and
 // round-robin dispatch over the 8 XCDs, every q-tile of one (image, head)
-// lands on the same XCD, so its K/V stream is shared through that XCD's L2.
+// lands on the same XCD, so its K/V stream is shared through one L2.
 #include "vt_device.h"
 #include "vt_kernels.h"
 
 namespace vt {
 
 namespace {
-constexpr int HD = 80;      // head_dim
-constexpr int BQ = kAttnQTile;  // queries per workgroup
-constexpr int BKV = 64;     // keys per tile
-constexpr int KROW = 88;    // LDS row stride of the K tile (fp16): 176 B, conflict-free 16-B reads
-constexpr int VROW = 68;    // LDS row stride of the V^T tile (fp16): 136 B, conflict-free 8-B reads
-constexpr int K_ITEMS = BKV * 5;   // (key, 8-pair chunk) items per K tile
-constexpr int V_ITEMS = BKV / 2 * 10;  // (key pair, 8-dim chunk) items per V tile
+constexpr int HD = 80;              // head_dim
+constexpr int BQ = kAttnQTile;      // queries per workgroup
+constexpr int BKV = kAttnKTile;     // keys per tile
+constexpr int KROW = 88;            // fp16 per K row in a tile image (176 B)
+constexpr int VROW = 68;            // fp16 per V^T row in a tile image (136 B)
+constexpr int K_IMG = BKV * KROW;   // fp16 elements of the K part
+constexpr int V_IMG = HD * VROW;    // fp16 elements of the V^T part (rows 0..79)
+constexpr int TILE_IMG = K_IMG + V_IMG;          // 11072 fp16 = 22144 B
+constexpr int TILE_VEC = TILE_IMG * 2 / 16;      // 1384 16-byte vectors
+constexpr int LDS_BUF = TILE_IMG + 16 * VROW;    // + V^T rows 80..95 (ones, zeros)
+constexpr int COPY_IT = (TILE_VEC + 255) / 256;  // 6 copy rounds of 256 threads
+constexpr float kLazy = 8.0f;       // log2 growth of the row max tolerated before rescaling
+static_assert(TILE_IMG * 2 == kAttnTileBytes, "tile image size");
 }  // namespace
 
-__global__ void __launch_bounds__(256) attention_kernel(
+// ---------------------------------------------------------------- pack
+// Block (64 keys x 5 chunks) per (key tile, head): thread = (key k = tid%64,
+// chunk c = tid/64) handles rotation pairs 8c..8c+7, i.e. dims 8c..8c+7 and
+// 40+8c..40+8c+7 of q, k and v for that key's token.
+__global__ void __launch_bounds__(320) attn_pack_kernel(
     const uint16_t* __restrict__ qkv, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ pos, const int32_t* __restrict__ order,
-    const int32_t* __restrict__ tile_start, int32_t n_img, int32_t heads, int32_t n_pos,
-    const float2* __restrict__ rope_cs, int32_t axis_code, float q_scale_log2,
-    void* __restrict__ out, int32_t out_f32) {
-  __shared__ __align__(16) uint16_t sK[2][BKV * KROW];
-  __shared__ __align__(16) uint16_t sV[2][HD * VROW];
+    const int32_t* __restrict__ pos, const int32_t* __restrict__ ktile_start, int32_t n_img,
+    int32_t heads, int32_t n_pos, const float2* __restrict__ rope_cs, int32_t axis_code,
+    float q_scale_log2, uint16_t* __restrict__ qpk, uint16_t* __restrict__ kv) {
+  const int T = blockIdx.x, head = blockIdx.y;
+  if (T >= ktile_start[n_img]) return;
+  int lo = 0, hi = n_img - 1;  // image of tile T: largest i with ktile_start[i] <= T
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (ktile_start[mid] <= T) lo = mid; else hi = mid - 1;
+  }
+  const int k = threadIdx.x & 63, c = threadIdx.x >> 6;
+  const int tok = cu[lo] + (T - ktile_start[lo]) * BKV + k;
+  const bool valid = tok < cu[lo + 1];
+  uint16_t* img = kv + (int64_t(head) * ktile_start[n_img] + T) * TILE_IMG;
+  uint32_t kr[8], vt[8];  // rotated k (fp16 pairs) and v (fp16 pairs)
+  if (valid) {
+    const int64_t ld = int64_t(3) * heads * HD;
+    const uint16_t* row = qkv + int64_t(tok) * ld + head * HD;
+    const int ax = (axis_code >> (2 * c)) & 3;
+    const int p = min(max(pos[3 * tok + ax], 0), n_pos - 1);
+    const float4* cs4 = reinterpret_cast<const float4*>(rope_cs + int64_t(p) * 40 + 8 * c);
+    float cs[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = cs4[j];
+      cs[4 * j] = v.x; cs[4 * j + 1] = v.y; cs[4 * j + 2] = v.z; cs[4 * j + 3] = v.w;
+    }
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {  // 0: q, 1: k
+      const uint4 a = reinterpret_cast<const uint4*>(row + which * heads * HD)[c];
+      const uint4 b = reinterpret_cast<const uint4*>(row + which * heads * HD)[c + 5];
+      const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+      const float sc = which == 0 ? q_scale_log2 : 1.0f;
+      uint32_t r1[4], r2[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x1l = bflo(aw[j]), x1h = bfhi(aw[j]), x2l = bflo(bw[j]), x2h = bfhi(bw[j]);
+        const float cl = cs[4 * j], sl = cs[4 * j + 1], ch = cs[4 * j + 2], sh = cs[4 * j + 3];
+        r1[j] = pack_f16x2((x1l * cl - x2l * sl) * sc, (x1h * ch - x2h * sh) * sc);
+        r2[j] = pack_f16x2((x2l * cl + x1l * sl) * sc, (x2h * ch + x1h * sh) * sc);
+      }
+      if (which == 0) {
+        uint16_t* q = qpk + (int64_t(tok) * heads + head) * HD;
+        reinterpret_cast<uint4*>(q)[c] = make_uint4(r1[0], r1[1], r1[2], r1[3]);
+        reinterpret_cast<uint4*>(q)[c + 5] = make_uint4(r2[0], r2[1], r2[2], r2[3]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { kr[j] = r1[j]; kr[4 + j] = r2[j]; }
+      }
+    }
+    const uint4 a = reinterpret_cast<const uint4*>(row + 2 * heads * HD)[c];
+    const uint4 b = reinterpret_cast<const uint4*>(row + 2 * heads * HD)[c + 5];
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      vt[j] = pack_f16x2(bflo(aw[j]), bfhi(aw[j]));
+      vt[4 + j] = pack_f16x2(bflo(bw[j]), bfhi(bw[j]));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kr[j] = vt[j] = 0u;
+  }
+  // K rows: dims 8c..8c+7 and 40+8c..40+8c+7 of key k.
+  *reinterpret_cast<uint4*>(img + k * KROW + 8 * c) = make_uint4(kr[0], kr[1], kr[2], kr[3]);
+  *reinterpret_cast<uint4*>(img + k * KROW + 40 + 8 * c) = make_uint4(kr[4], kr[5], kr[6], kr[7]);
+  // V^T: element (dim, key k).  A wavefront (fixed c) writes 64 consecutive keys per dim.
+  uint16_t* vtimg = img + K_IMG;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    vtimg[(8 * c + 2 * j) * VROW + k] = uint16_t(vt[j] & 0xffffu);
+    vtimg[(8 * c + 2 * j + 1) * VROW + k] = uint16_t(vt[j] >> 16);
+    vtimg[(40 + 8 * c + 2 * j) * VROW + k] = uint16_t(vt[4 + j] & 0xffffu);
+    vtimg[(40 + 8 * c + 2 * j + 1) * VROW + k] = uint16_t(vt[4 + j] >> 16);
+  }
+  // The row padding (K dims 80..87, V^T keys 64..67) is never read.
+}
+
+// ---------------------------------------------------------------- attention
+__global__ void __launch_bounds__(256) attention_kernel(
+    const uint16_t* __restrict__ qpk, const uint16_t* __restrict__ kv,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ order,
+    const int32_t* __restrict__ tile_start, const int32_t* __restrict__ ktile_start,
+    int32_t n_img, int32_t heads, void* __restrict__ out, int32_t out_f32) {
+  __shared__ __align__(16) uint16_t lds[2][LDS_BUF];
 
   const int head = blockIdx.x % heads;
   const int tile = blockIdx.x / heads;
@@ -75,145 +176,62 @@ __global__ void __launch_bounds__(256) attention_kernel(
   const int kbeg = cu[img], kend = cu[img + 1];
   const int q0 = kbeg + (tile - tile_start[lo]) * BQ;
   const int qend = min(q0 + BQ, kend);
+  const int ntiles = (kend - kbeg + BKV - 1) / BKV;
+  const uint4* src = reinterpret_cast<const uint4*>(
+      kv + (int64_t(head) * ktile_start[n_img] + ktile_start[img]) * TILE_IMG);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, ln = lane & 31;
-  const int64_t ld = int64_t(3) * heads * HD;  // qkv row stride (elements)
-  const uint16_t* Qg = qkv + head * HD;
-  const uint16_t* Kg = qkv + (heads + head) * HD;
-  const uint16_t* Vg = qkv + (2 * heads + head) * HD;
-  const int pmax = n_pos - 1;
 
-  // ---- Q: load the full row, rotate, scale, keep this lane's 5 MFMA B-operand fragments.
+  // V^T rows 80..95 of both buffers: row 80 = ones (the row-sum row), rest zero.
+  for (int i = tid; i < 2 * 16 * VROW; i += 256) {
+    const int b = i / (16 * VROW), r = i % (16 * VROW);
+    lds[b][TILE_IMG + r] = (r < VROW) ? uint16_t(0x3C00) : uint16_t(0);
+  }
+
+  // Q fragments (B operand of S^T = K Q^T): dims 16s + 8hf .. +7 of this lane's query.
   const int qrow = q0 + wave * 32 + ln;
   const bool qvalid = qrow < qend;
   const int qr = qvalid ? qrow : qend - 1;
   f16x8_t qfrag[5];
   {
-    float qf[HD];
-    const uint4* src = reinterpret_cast<const uint4*>(Qg + int64_t(qr) * ld);
+    const uint4* q = reinterpret_cast<const uint4*>(qpk + (int64_t(qr) * heads + head) * HD);
 #pragma unroll
-    for (int c = 0; c < 10; ++c) {
-      const uint4 u = src[c];
-      qf[8 * c + 0] = bflo(u.x); qf[8 * c + 1] = bfhi(u.x);
-      qf[8 * c + 2] = bflo(u.y); qf[8 * c + 3] = bfhi(u.y);
-      qf[8 * c + 4] = bflo(u.z); qf[8 * c + 5] = bfhi(u.z);
-      qf[8 * c + 6] = bflo(u.w); qf[8 * c + 7] = bfhi(u.w);
-    }
-    int p3[3];
-#pragma unroll
-    for (int a = 0; a < 3; ++a) p3[a] = min(max(pos[3 * qr + a], 0), pmax);
-#pragma unroll
-    for (int c = 0; c < 5; ++c) {
-      const int ax = (axis_code >> (2 * c)) & 3;
-      const float2* cs = rope_cs + int64_t(p3[ax]) * 40 + 8 * c;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float2 r = cs[i];
-        const float x1 = qf[8 * c + i], x2 = qf[40 + 8 * c + i];
-        qf[8 * c + i] = (x1 * r.x - x2 * r.y) * q_scale_log2;
-        qf[40 + 8 * c + i] = (x2 * r.x + x1 * r.y) * q_scale_log2;
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < 5; ++s) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        qfrag[s][i] = (_Float16)(hf ? qf[16 * s + 8 + i] : qf[16 * s + i]);
-    }
+    for (int s = 0; s < 5; ++s) qfrag[s] = __builtin_bit_cast(f16x8_t, q[2 * s + hf]);
   }
 
-  // ---- K/V tile staging (global -> registers -> LDS).
-  uint4 kreg[2][2];
-  float2 kcs[2][8];
-  uint4 vreg[2][2];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int i = tid + 256 * it;
-      if (i < K_ITEMS) {
-        const int key = i / 5, c = i - key * 5;
-        const int kk = kt + key;
-        if (kk < kend) {
-          const uint4* src = reinterpret_cast<const uint4*>(Kg + int64_t(kk) * ld);
-          kreg[it][0] = src[c];
-          kreg[it][1] = src[c + 5];
-          const int ax = (axis_code >> (2 * c)) & 3;
-          const int p = min(max(pos[3 * kk + ax], 0), pmax);
-          const float4* cs = reinterpret_cast<const float4*>(rope_cs + int64_t(p) * 40 + 8 * c);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float4 v = cs[j];
-            kcs[it][2 * j] = make_float2(v.x, v.y);
-            kcs[it][2 * j + 1] = make_float2(v.z, v.w);
-          }
-        } else {
-          kreg[it][0] = kreg[it][1] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) kcs[it][j] = make_float2(1.f, 0.f);
-        }
-      }
-      if (i < V_ITEMS) {
-        const int kp = i & 31, c = i >> 5;
-        const int kk = kt + 2 * kp;
-        vreg[it][0] = kk < kend ? reinterpret_cast<const uint4*>(Vg + int64_t(kk) * ld)[c]
-                                : make_uint4(0, 0, 0, 0);
-        vreg[it][1] = kk + 1 < kend ? reinterpret_cast<const uint4*>(Vg + int64_t(kk + 1) * ld)[c]
-                                    : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int i = tid + 256 * it;
-      if (i < K_ITEMS) {
-        const int key = i / 5, c = i - key * 5;
-        const uint32_t a[4] = {kreg[it][0].x, kreg[it][0].y, kreg[it][0].z, kreg[it][0].w};
-        const uint32_t b[4] = {kreg[it][1].x, kreg[it][1].y, kreg[it][1].z, kreg[it][1].w};
-        uint32_t ra[4], rb[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float x1l = bflo(a[j]), x1h = bfhi(a[j]);
-          const float x2l = bflo(b[j]), x2h = bfhi(b[j]);
-          const float2 cl = kcs[it][2 * j], ch = kcs[it][2 * j + 1];
-          ra[j] = pack_f16x2(x1l * cl.x - x2l * cl.y, x1h * ch.x - x2h * ch.y);
-          rb[j] = pack_f16x2(x2l * cl.x + x1l * cl.y, x2h * ch.x + x1h * ch.y);
-        }
-        uint16_t* dst = sK[buf] + key * KROW;
-        *reinterpret_cast<uint4*>(dst + 8 * c) = make_uint4(ra[0], ra[1], ra[2], ra[3]);
-        *reinterpret_cast<uint4*>(dst + 40 + 8 * c) = make_uint4(rb[0], rb[1], rb[2], rb[3]);
-      }
-      if (i < V_ITEMS) {
-        const int kp = i & 31, c = i >> 5;
-        const uint32_t a[4] = {vreg[it][0].x, vreg[it][0].y, vreg[it][0].z, vreg[it][0].w};
-        const uint32_t b[4] = {vreg[it][1].x, vreg[it][1].y, vreg[it][1].z, vreg[it][1].w};
-        uint16_t* dst = sV[buf] + (8 * c) * VROW + 2 * kp;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // dims 8c+2j (low halves) and 8c+2j+1 (high halves) of keys 2kp, 2kp+1, as fp16
-          *reinterpret_cast<uint32_t*>(dst + (2 * j) * VROW) = pack_f16x2(bflo(a[j]), bflo(b[j]));
-          *reinterpret_cast<uint32_t*>(dst + (2 * j + 1) * VROW) = pack_f16x2(bfhi(a[j]), bfhi(b[j]));
-        }
-      }
-    }
-  };
+  // Tile copy: 1384 16-byte vectors = 5 per thread + 104 threads with a sixth.
+  static_assert(COPY_IT == 6 && TILE_VEC - 5 * 256 > 0, "copy split");
+  const bool has6 = tid < TILE_VEC - 5 * 256;
+  uint4 st0, st1, st2, st3, st4, st5 = make_uint4(0, 0, 0, 0);
+#define VT_ATT_GLOAD(t)                                              \
+  do {                                                               \
+    const uint4* g_ = src + int64_t(t) * TILE_VEC + tid;             \
+    st0 = g_[0]; st1 = g_[256]; st2 = g_[512]; st3 = g_[768];        \
+    st4 = g_[1024];                                                  \
+    if (has6) st5 = g_[1280];                                        \
+  } while (0)
+#define VT_ATT_LSTORE(b)                                             \
+  do {                                                               \
+    uint4* d_ = reinterpret_cast<uint4*>(lds[b]) + tid;              \
+    d_[0] = st0; d_[256] = st1; d_[512] = st2; d_[768] = st3;        \
+    d_[1024] = st4;                                                  \
+    if (has6) d_[1280] = st5;                                        \
+  } while (0)
 
   f32x16_t acc[3];
 #pragma unroll
   for (int d = 0; d < 3; ++d)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[d][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_use = -INFINITY;
 
-  gload(kbeg);
-  lstore(0);
+  VT_ATT_GLOAD(0);
+  VT_ATT_LSTORE(0);
   __syncthreads();
-  const int ntiles = (kend - kbeg + BKV - 1) / BKV;
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    const int kt = kbeg + t * BKV;
-    if (t + 1 < ntiles) gload(kt + BKV);
+    if (t + 1 < ntiles) VT_ATT_GLOAD(t + 1);
 
     // S^T = K Q^T for 64 keys: two 32-key blocks.
     f32x16_t s[2];
@@ -221,7 +239,7 @@ __global__ void __launch_bounds__(256) attention_kernel(
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[b][e] = 0.f;
-    const uint16_t* kb = sK[buf] + ln * KROW + 8 * hf;
+    const uint16_t* kb = lds[buf] + ln * KROW + 8 * hf;
 #pragma unroll
     for (int sl = 0; sl < 5; ++sl) {
 #pragma unroll
@@ -230,7 +248,8 @@ __global__ void __launch_bounds__(256) attention_kernel(
         s[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qfrag[sl], s[b], 0, 0, 0);
       }
     }
-    // s[b][4g + r] is key kt + 32b + 8g + 4hf + r of query ln.
+    // s[b][4g + r] is key kbeg + 64t + 32b + 8g + 4hf + r of query ln.
+    const int kt = kbeg + t * BKV;
     if (kt + BKV > kend) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
@@ -238,59 +257,55 @@ __global__ void __launch_bounds__(256) attention_kernel(
         for (int e = 0; e < 16; ++e)
           if (kt + 32 * b + 8 * (e >> 2) + 4 * hf + (e & 3) >= kend) s[b][e] = -INFINITY;
     }
-    float mx = s[0][0];
+    float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int e = 2; e < 16; ++e) mx = fmaxf(mx, s[0][e]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[1][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // Lazy rescale: raise the running max only when it grows by more than kLazy.
+    if (__any(mx > m_use + kLazy)) {
+      const float m_new = fmaxf(m_use, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);  // 0 on the first tile
+      m_use = m_new;
+#pragma unroll
+      for (int d = 0; d < 3; ++d)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[d][e] *= alpha;
+    }
+    f16x8_t pf[4];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[b][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float lsum = 0.f;
-    f16x8_t pf[4];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(s[b][e] - m_new);
-        lsum += p;
-        pf[2 * b + (e >> 3)][e & 7] = (_Float16)p;
-      }
-    }
-    l_run = l_run * alpha + lsum;
-#pragma unroll
-    for (int d = 0; d < 3; ++d)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[d][e] *= alpha;
+      for (int e = 0; e < 16; ++e)
+        pf[2 * b + (e >> 3)][e & 7] = (_Float16)__builtin_amdgcn_exp2f(s[b][e] - m_use);
 
-    // O^T += V^T P^T over 4 slices of 16 keys.
-    const uint16_t* vb = sV[buf];
+    // O^T += V^T P^T over 4 slices of 16 keys; dims 80..95 are the padding
+    // rows (row 80 = ones -> the row sum l).
+    const uint16_t* vb = lds[buf] + K_IMG;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int kb0 = 16 * ks + 4 * hf;
 #pragma unroll
       for (int d = 0; d < 3; ++d) {
-        const int dim = 32 * d + ln;
-        f16x8_t a;
-        if (d < 2 || dim < HD) {
-          const uint2 lo4 = *reinterpret_cast<const uint2*>(vb + dim * VROW + kb0);
-          const uint2 hi4 = *reinterpret_cast<const uint2*>(vb + dim * VROW + kb0 + 8);
-          a = __builtin_bit_cast(f16x8_t, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
-        } else {
-          a = __builtin_bit_cast(f16x8_t, make_uint4(0, 0, 0, 0));
-        }
+        const uint16_t* vr = vb + (32 * d + ln) * VROW + kb0;
+        const uint2 lo4 = *reinterpret_cast<const uint2*>(vr);
+        const uint2 hi4 = *reinterpret_cast<const uint2*>(vr + 8);
+        const f16x8_t a = __builtin_bit_cast(f16x8_t, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
         acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ks], acc[d], 0, 0, 0);
       }
     }
 
-    if (t + 1 < ntiles) lstore(buf ^ 1);
+    if (t + 1 < ntiles) VT_ATT_LSTORE(buf ^ 1);
     __syncthreads();
   }
+#undef VT_ATT_GLOAD
+#undef VT_ATT_LSTORE
 
-  // ---- normalise and store: acc[d][4g + r] is dim 32d + 8g + 4hf + r of query ln.
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.0f / l_tot;
+  // ---- normalise and store: acc[d][4g + r] is dim 32d + 8g + 4hf + r of query ln;
+  // the row sum l (dim 80) is acc[2][8] in the lanes with hf == 0.
+  const float l_half0 = __shfl(acc[2][8], ln, 64);
+  const float inv = 1.0f / l_half0;
   if (!qvalid) return;
   const int64_t orow = int64_t(qrow) * heads * HD + head * HD;
 #pragma unroll
@@ -313,14 +328,19 @@ __global__ void __launch_bounds__(256) attention_kernel(
 }
 
 hipError_t launch_attention(const uint16_t* qkv, const int32_t* cu_seqlens, const int32_t* pos_thw,
-                            const int32_t* order, const int32_t* tile_start, int32_t n_img,
-                            int32_t max_tiles, int32_t heads, int32_t n_pos, int32_t axis_code,
-                            const float2* rope_cs, float q_scale_log2, void* out, bool out_f32,
-                            hipStream_t s) {
-  const int64_t blocks = int64_t(max_tiles) * heads;
-  hipLaunchKernelGGL(attention_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, qkv, cu_seqlens,
-                     pos_thw, order, tile_start, n_img, heads, n_pos, rope_cs, axis_code,
-                     q_scale_log2, out, out_f32 ? 1 : 0);
+                            const int32_t* order, const int32_t* tile_start,
+                            const int32_t* ktile_start, int32_t n_img, int32_t max_qtiles,
+                            int32_t max_ktiles, int32_t heads, int32_t n_pos, int32_t axis_code,
+                            const float2* rope_cs, float q_scale_log2, uint16_t* qpk, uint16_t* kv,
+                            void* out, bool out_f32, hipStream_t s) {
+  hipLaunchKernelGGL(attn_pack_kernel, dim3(max_ktiles, heads), dim3(320), 0, s, qkv, cu_seqlens,
+                     pos_thw, ktile_start, n_img, heads, n_pos, rope_cs, axis_code, q_scale_log2,
+                     qpk, kv);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t blocks = int64_t(max_qtiles) * heads;
+  hipLaunchKernelGGL(attention_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, qpk, kv,
+                     cu_seqlens, order, tile_start, ktile_start, n_img, heads, out, out_f32 ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -63,15 +63,47 @@ hipError_t launch_cu_last(int32_t* cu_seqlens, int32_t n_img, int32_t total, hip
   return hipGetLastError();
 }
 
+// Exclusive prefix sum over r < n of f(r) by one workgroup (chunked: each
+// thread sums a contiguous run, thread 0 scans the run totals).
+template <class F>
+__device__ void block_scan(int n, F f, int32_t* out, int32_t* part) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int per = (n + nt - 1) / nt;
+  const int lo = tid * per, hi = min(n, lo + per);
+  int sum = 0;
+  for (int r = lo; r < hi; ++r) sum += f(r);
+  part[tid] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int t = 0; t < nt; ++t) {
+      const int v = part[t];
+      part[t] = run;
+      run += v;
+    }
+    out[n] = run;
+  }
+  __syncthreads();
+  int run = part[tid];
+  for (int r = lo; r < hi; ++r) {
+    out[r] = run;
+    run += f(r);
+  }
+  __syncthreads();
+}
+
 // One workgroup.  rank(i) = #{j : n_j > n_i, or n_j == n_i and j < i} orders
 // the images largest first (longest-processing-time first: the expensive
 // q-tiles are dispatched before the cheap ones).  tile_start is the
 // exclusive prefix sum of ceil(n/q_tile) in rank order, with
-// tile_start[n_img] = the total number of q-tiles.
+// tile_start[n_img] = the total number of q-tiles; ktile_start the prefix
+// sum of ceil(n/k_tile) in image order.
 __global__ void __launch_bounds__(1024) attn_schedule_kernel(const int32_t* __restrict__ cu,
                                                              int32_t n_img, int32_t q_tile,
+                                                             int32_t k_tile,
                                                              int32_t* __restrict__ order,
-                                                             int32_t* __restrict__ tile_start) {
+                                                             int32_t* __restrict__ tile_start,
+                                                             int32_t* __restrict__ ktile_start) {
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x, nt = blockDim.x;
   for (int i = tid; i < n_img; i += nt) {
@@ -84,38 +116,18 @@ __global__ void __launch_bounds__(1024) attn_schedule_kernel(const int32_t* __re
     order[r] = i;
   }
   __syncthreads();
-  // chunked exclusive scan over ranks
-  const int per = (n_img + nt - 1) / nt;
-  const int lo = tid * per, hi = min(n_img, lo + per);
-  int sum = 0;
-  for (int r = lo; r < hi; ++r) {
-    const int i = order[r];
-    sum += (cu[i + 1] - cu[i] + q_tile - 1) / q_tile;
-  }
-  part[tid] = sum;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int t = 0; t < nt; ++t) {
-      const int v = part[t];
-      part[t] = run;
-      run += v;
-    }
-    tile_start[n_img] = run;
-  }
-  __syncthreads();
-  int run = part[tid];
-  for (int r = lo; r < hi; ++r) {
-    tile_start[r] = run;
-    const int i = order[r];
-    run += (cu[i + 1] - cu[i] + q_tile - 1) / q_tile;
-  }
+  block_scan(n_img, [&](int r) { const int i = order[r]; return (cu[i + 1] - cu[i] + q_tile - 1) / q_tile; },
+             tile_start, part);
+  block_scan(n_img, [&](int i) { return (cu[i + 1] - cu[i] + k_tile - 1) / k_tile; },
+             ktile_start, part);
 }
 
 hipError_t launch_attn_schedule(const int32_t* cu_seqlens, int32_t n_img, int32_t q_tile,
-                                int32_t* order, int32_t* tile_start, hipStream_t s) {
-  hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, s, cu_seqlens, n_img, q_tile,
-                     order, tile_start);
+                                int32_t k_tile, int32_t* order, int32_t* tile_start,
+                                int32_t* ktile_start, hipStream_t s) {
+  const int threads = n_img >= 1024 ? 1024 : (n_img >= 256 ? 256 : 64);
+  hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(threads), 0, s, cu_seqlens, n_img, q_tile,
+                     k_tile, order, tile_start, ktile_start);
   return hipGetLastError();
 }
 

@@ -126,6 +126,9 @@ struct Dims {
 struct BlockBufs {
   int32_t* order;
   int32_t* tile_start;
+  int32_t* ktile_start;
+  uint16_t* qpk;   // [N, heads, 80] fp16 rotated, scaled Q
+  uint16_t* kv;    // heads x max_ktiles K/V tile images (fp16)
   float2* rope;
   uint16_t* xn;    // [N, d] LayerNorm output
   uint16_t* act;   // [N, max(4d, mlp)]: qkv [N,3d] then attn [N,d]; later the MLP hidden [N, mlp]
@@ -141,9 +144,17 @@ size_t block_gemm_ws(int N, int d, int mlp) {
   return w;
 }
 
+int32_t max_k_tiles(int64_t N, int32_t n_img) {
+  return int32_t((N + vt::kAttnKTile - 1) / vt::kAttnKTile + n_img);
+}
+
 void carve_block(Carver& c, const Dims& D, int32_t n_pos, BlockBufs* b) {
   b->order = c.take<int32_t>(D.n_img);
   b->tile_start = c.take<int32_t>(D.n_img + 1);
+  b->ktile_start = c.take<int32_t>(D.n_img + 1);
+  b->qpk = c.take<uint16_t>(size_t(D.N) * D.d);
+  b->kv = reinterpret_cast<uint16_t*>(
+      c.take<char>(size_t(D.heads) * max_k_tiles(D.N, D.n_img) * vt::kAttnTileBytes));
   b->rope = c.take<float2>(size_t(n_pos) * 40);
   b->xn = c.take<uint16_t>(size_t(D.N) * D.d);
   b->act = c.take<uint16_t>(size_t(D.N) * std::max(4 * D.d, D.mlp));
@@ -244,7 +255,8 @@ vt_status launch_meta(const vt_grid_thw* grid, int32_t n_img, int64_t total, int
 // The per-call attention prologue: LPT schedule and RoPE cos/sin table.
 vt_status attn_prologue(const vt_config* cfg, const int32_t* cu, int32_t n_img, int32_t n_pos,
                         const BlockBufs& b, int32_t* axis_code, hipStream_t s) {
-  VT_TRY_HIP(vt::launch_attn_schedule(cu, n_img, vt::kAttnQTile, b.order, b.tile_start, s));
+  VT_TRY_HIP(vt::launch_attn_schedule(cu, n_img, vt::kAttnQTile, vt::kAttnKTile, b.order,
+                                      b.tile_start, b.ktile_start, s));
   const vt::RopeFreq f = rope_freq(cfg, axis_code);
   VT_TRY_HIP(vt::launch_rope_table(f, n_pos, b.rope, s));
   return VT_OK;
@@ -262,9 +274,9 @@ vt_status run_attention(const vt_config* cfg, const uint16_t* qkv, const int32_t
                         const int32_t* pos, int32_t n_img, int64_t N, int32_t n_pos,
                         int32_t axis_code, const BlockBufs& b, void* out, bool f32,
                         hipStream_t s) {
-  VT_TRY_HIP(vt::launch_attention(qkv, cu, pos, b.order, b.tile_start, n_img, max_q_tiles(N, n_img),
-                                  cfg->heads, n_pos, axis_code, b.rope, q_scale_log2(cfg), out, f32,
-                                  s));
+  VT_TRY_HIP(vt::launch_attention(qkv, cu, pos, b.order, b.tile_start, b.ktile_start, n_img,
+                                  max_q_tiles(N, n_img), max_k_tiles(N, n_img), cfg->heads, n_pos,
+                                  axis_code, b.rope, q_scale_log2(cfg), b.qpk, b.kv, out, f32, s));
   return VT_OK;
 }
 

@@ -25,9 +25,11 @@ hipError_t launch_metadata(const MetaChunk& c, int32_t max_tokens_in_chunk, int3
 hipError_t launch_cu_last(int32_t* cu_seqlens, int32_t n_img, int32_t total, hipStream_t s);
 
 // Attention work schedule: images ordered by token count (largest first),
-// tile_start[r] = first q-tile of the image of rank r.
+// tile_start[r] = first q-tile of the image of rank r; ktile_start[i] = first
+// 64-key tile of image i (image order) in the packed K/V tile images.
 hipError_t launch_attn_schedule(const int32_t* cu_seqlens, int32_t n_img, int32_t q_tile,
-                                int32_t* order, int32_t* tile_start, hipStream_t s);
+                                int32_t k_tile, int32_t* order, int32_t* tile_start,
+                                int32_t* ktile_start, hipStream_t s);
 // RoPE table cs[pos][j] = (cos, sin)(pos * inv_freq[j]), pos < n_pos, j < 40.
 struct RopeFreq { double inv_freq[64]; int32_t pairs; };
 hipError_t launch_rope_table(const RopeFreq& f, int32_t n_pos, float2* cs, hipStream_t s);
@@ -58,11 +60,15 @@ hipError_t launch_gemm(const uint16_t* A, int M, int K, const uint16_t* B, int N
                        const uint16_t* bias, int epi, void* out, void* ws, hipStream_t s);
 
 // ---- attention (attention.hip)
-constexpr int kAttnQTile = 128;
+constexpr int kAttnQTile = 128;        // queries per workgroup
+constexpr int kAttnKTile = 64;         // keys per tile
+constexpr int kAttnTileBytes = 22144;  // one (head, key tile) image: K [64][88] + V^T [80][68] fp16
+// qpk: [N, heads, 80] fp16 rotated+scaled Q; kv: heads x max_ktiles tile images.
 hipError_t launch_attention(const uint16_t* qkv, const int32_t* cu_seqlens, const int32_t* pos_thw,
-                            const int32_t* order, const int32_t* tile_start, int32_t n_img,
-                            int32_t max_tiles, int32_t heads, int32_t n_pos, int32_t axis_code,
-                            const float2* rope_cs, float q_scale_log2, void* out, bool out_f32,
-                            hipStream_t s);
+                            const int32_t* order, const int32_t* tile_start,
+                            const int32_t* ktile_start, int32_t n_img, int32_t max_qtiles,
+                            int32_t max_ktiles, int32_t heads, int32_t n_pos, int32_t axis_code,
+                            const float2* rope_cs, float q_scale_log2, uint16_t* qpk, uint16_t* kv,
+                            void* out, bool out_f32, hipStream_t s);
 
 }  // namespace vt
