@@ -49,15 +49,16 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// GELU, tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))).
-// tanh(u) = sign(u) (1 - e) / (1 + e) with e = exp(-2|u|).
+// GELU, tanh form: 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3),
+// evaluated as x * sigmoid(2u) = x / (1 + 2^(-2u log2 e)) with the hardware
+// exp2 and reciprocal (about 1 ulp each; the result is rounded to bf16).
+// Large negative x: the exponential overflows to +inf and the result is -0.
 __device__ __forceinline__ float gelu_tanh(float x) {
-  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
-  float u = k0 * (x + 0.044715f * x * x * x);
-  float e = __expf(-2.0f * fabsf(u));
-  float t = (1.0f - e) / (1.0f + e);
-  t = copysignf(t, u);
-  return 0.5f * x * (1.0f + t);
+  const float c1 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+  const float c3 = c1 * 0.044715f;
+  const float x2 = x * x;
+  const float e = __builtin_amdgcn_exp2f(x * fmaf(c3, x2, c1));
+  return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 // GELU, exact form with the device erf.
 __device__ __forceinline__ float gelu_erf(float x) {
