@@ -170,25 +170,17 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Direct-load variant (K a multiple of 64): tiles go from global memory
+// Direct-load variant (K a multiple of 32): tiles go from global memory
 // straight into LDS with global_load_lds_dwordx4 (gfx950), so no VGPRs stage
-// them and the next K tile's loads stay in flight while the current one is
-// multiplied.  Lane i of a load instruction lands at LDS base + 16 i, so the
-// layout is chosen by which global chunk each lane fetches: rows of 64 bf16
-// (128 B, 8 chunks of 16 B) with logical chunk c of row r stored at
-// physical chunk c ^ swz(r), swz(r) = (r' ^ r' >> 3) & 7 with r' = r mod 16.
-// Sixteen aligned consecutive rows read at one logical chunk then hit 16
-// distinct 16-byte bank groups (and any 8 aligned rows 8 distinct ones), so
-// the MFMA fragment reads are conflict-free without padding.
+// them and three K steps stay in flight while one is multiplied.  Lane i of
+// a load instruction lands at LDS base + 16 i, so the layout is chosen by
+// which global chunk each lane fetches: XOR-swizzled rows (swz4 below) keep
+// the MFMA fragment reads free of bank conflicts without padding.
 //
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs; block
 // b is remapped so that each XCD runs a contiguous range of tiles, walked in
 // groups of 4 tile rows (GROUP_M): the ~32 tiles an XCD runs at once share
 // 4 activation panels and 8 weight panels through its L2.
-// Swizzle of row r: a function of r mod 16 only, so it is unchanged by the
-// 32- and 64-row steps between a lane's copies and between fragment blocks.
-__device__ __forceinline__ int swz(int r) { return ((r & 15) ^ ((r & 15) >> 3)) & 7; }
-
 // s_waitcnt immediate: vmcnt <= n, expcnt and lgkmcnt unconstrained (gfx9 encoding).
 template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -236,7 +228,15 @@ __device__ __forceinline__ void xcd_group_tile(int tiles_m, int tiles_n, int* tm
   *tn = in_g / gsz;
 }
 
+// 64-byte rows (K step 32 = 4 chunks of 16 B): logical chunk c of row r
+// lives in physical chunk c ^ swz4(r), a function of r mod 16 chosen so that
+// 16 aligned consecutive rows read at one logical chunk fall in 16 distinct
+// 16-byte bank groups (64 banks) and any 8 aligned rows in 8 (32 banks).
+__device__ __forceinline__ int swz4(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+
 // GWM x GWN wavefronts; each owns a (BM/GWM) x (BN/GWN) block of C.
+// K is consumed in steps of 32 through a ring of 4 LDS stages: three steps
+// are in flight while one is multiplied, one workgroup barrier per step.
 template <int BM, int BN, int GWM, int GWN, int EPI, bool SPLIT>
 __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
     const uint16_t* __restrict__ A, int M, int K, const uint16_t* __restrict__ B, int N,
@@ -244,9 +244,12 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
   constexpr int NW = GWM * GWN;
   constexpr int WM = BM / GWM, WN = BN / GWN;
   constexpr int TB = WM / 32, FB = WN / 32;
-  constexpr int LA = BM / (8 * NW), LB = BN / (8 * NW);  // copies per lane per K tile
-  constexpr int A_BYTES = BM * 128, STAGE = (BM + BN) * 128;
-  static_assert(WM % 32 == 0 && WN % 32 == 0 && LA * 8 * NW == BM && LB * 8 * NW == BN, "tiling");
+  constexpr int BK = 32, NST = 4;
+  constexpr int LA = BM / (16 * NW), LB = BN / (16 * NW);  // copies per lane per K step
+  constexpr int CP = LA + LB;
+  constexpr int A_BYTES = BM * 64, STAGE = (BM + BN) * 64;
+  static_assert(WM % 32 == 0 && WN % 32 == 0 && LA * 16 * NW == BM && LB * 16 * NW == BN, "tiling");
+  static_assert(NST * STAGE <= 160 * 1024, "LDS");
   extern __shared__ __align__(16) uint16_t lds[];
   const char* smem = reinterpret_cast<const char*>(lds);
 
@@ -257,31 +260,30 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
   const int m0 = tm * BM, n0 = tn * BN;
   const int kbeg = SPLIT ? blockIdx.y * kper : 0;
   const int kend = SPLIT ? min(K, kbeg + kper) : K;
-  const int nk = (kend - kbeg) / 64;
+  const int nk = (kend - kbeg) / BK;
 
-  // Copy j of this lane: row 8 (wave + NW j) + lane / 8 of the tile, logical
-  // chunk (lane % 8) ^ swz(row) -- it lands in physical chunk lane % 8 (row
-  // steps of 8 NW keep swz(row) fixed).  Rows past M (N) read the last valid
-  // row; their results are never stored.
-  const int lrow = 8 * wave + (lane >> 3);
-  const int lchunk = (lane & 7) ^ swz(lrow);
+  // Copy j of this lane: tile row 16 (wave + NW j) + lane / 4, logical chunk
+  // (lane % 4) ^ swz4(row), landing in physical chunk lane % 4.  Rows past M
+  // (N) read the last valid row; their results are never stored.
+  const int lrow = 16 * wave + (lane >> 2);
+  const int lchunk = (lane & 3) ^ swz4(lrow);
   const uint16_t* ga = A + int64_t(min(m0 + lrow, M - 1)) * K + kbeg + 8 * lchunk;
   const uint16_t* gb = B + int64_t(min(n0 + lrow, N - 1)) * K + kbeg + 8 * lchunk;
   int64_t oa[LA], ob[LB];
 #pragma unroll
   for (int j = 0; j < LA; ++j)
-    oa[j] = int64_t(min(m0 + lrow + 8 * NW * j, M - 1) - min(m0 + lrow, M - 1)) * K;
+    oa[j] = int64_t(min(m0 + lrow + 16 * NW * j, M - 1) - min(m0 + lrow, M - 1)) * K;
 #pragma unroll
   for (int j = 0; j < LB; ++j)
-    ob[j] = int64_t(min(n0 + lrow + 8 * NW * j, N - 1) - min(n0 + lrow, N - 1)) * K;
+    ob[j] = int64_t(min(n0 + lrow + 16 * NW * j, N - 1) - min(n0 + lrow, N - 1)) * K;
   const uint32_t lds0 = lds_offset(lds) + 1024 * wave;
 
-  auto issue = [&](int it, int stage) {
-    const uint32_t sa = __builtin_amdgcn_readfirstlane(lds0 + stage * STAGE);
+  auto issue = [&](int it) {
+    const uint32_t sa = __builtin_amdgcn_readfirstlane(lds0 + (it % NST) * STAGE);
 #pragma unroll
-    for (int j = 0; j < LA; ++j) dma16(ga + oa[j] + it * 64, sa + 1024 * NW * j);
+    for (int j = 0; j < LA; ++j) dma16(ga + oa[j] + it * BK, sa + 1024 * NW * j);
 #pragma unroll
-    for (int j = 0; j < LB; ++j) dma16(gb + ob[j] + it * 64, sa + A_BYTES + 1024 * NW * j);
+    for (int j = 0; j < LB; ++j) dma16(gb + ob[j] + it * BK, sa + A_BYTES + 1024 * NW * j);
   };
 
   f32x16_t acc[FB][TB];
@@ -293,56 +295,75 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
       for (int e = 0; e < 16; ++e) acc[f][t][e] = 0.f;
 
   const int fr = lane & 31, h = lane >> 5;
-  const int sw = swz(fr);
-  int choff[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) choff[kk] = 16 * ((2 * kk + h) ^ sw);
+  const int sw = swz4(fr);
+  const int choff0 = 16 * ((0 + h) ^ sw), choff1 = 16 * ((2 + h) ^ sw);
 
-  if (nk > 0) issue(0, 0);
-  for (int it = 0; it < nk; ++it) {
-    const int stage = it & 1;
-    if (it + 1 < nk) {
-      issue(it + 1, stage ^ 1);
-      wait_vmcnt<LA + LB>();  // this lane's copies of tile `it` have landed
-    } else {
-      wait_vmcnt<0>();
+  // Fragments of one K step (two MFMA k slices of 16).
+  struct Frags {
+    bf16x8_t w0[FB], t0[TB], w1[FB], t1[TB];
+  };
+  auto load_frags = [&](Frags& F, int step) {
+    const char* st = smem + (step % NST) * STAGE;
+    const char* a_base = st + (wm * WM + fr) * 64;
+    const char* b_base = st + A_BYTES + (wn * WN + fr) * 64;
+#pragma unroll
+    for (int f = 0; f < FB; ++f) F.w0[f] = *reinterpret_cast<const bf16x8_t*>(b_base + f * 2048 + choff0);
+#pragma unroll
+    for (int t = 0; t < TB; ++t) F.t0[t] = *reinterpret_cast<const bf16x8_t*>(a_base + t * 2048 + choff0);
+#pragma unroll
+    for (int f = 0; f < FB; ++f) F.w1[f] = *reinterpret_cast<const bf16x8_t*>(b_base + f * 2048 + choff1);
+#pragma unroll
+    for (int t = 0; t < TB; ++t) F.t1[t] = *reinterpret_cast<const bf16x8_t*>(a_base + t * 2048 + choff1);
+  };
+  auto mma = [&](const Frags& F) {
+#pragma unroll
+    for (int f = 0; f < FB; ++f)
+#pragma unroll
+      for (int t = 0; t < TB; ++t)
+        acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.w0[f], F.t0[t], acc[f][t], 0, 0, 0);
+#pragma unroll
+    for (int f = 0; f < FB; ++f)
+#pragma unroll
+      for (int t = 0; t < TB; ++t)
+        acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.w1[f], F.t1[t], acc[f][t], 0, 0, 0);
+  };
+  // One K step: copies for step it+3 go out, step it+1's fragments are read
+  // while step it's are multiplied; then step it+2's copies must have landed
+  // (by every wave) before the next step reads them.
+  // The fragment reads are unconditional (on the last step they read a
+  // stale, never used stage): a branch around them makes the compiler wait
+  // for every outstanding LDS read before the first MFMA of the step.
+  auto step = [&](int it, const Frags& cur, Frags& nxt) {
+    if (it + NST - 1 < nk) issue(it + NST - 1);  // into the stage step it-1 used
+    load_frags(nxt, it + 1);
+    mma(cur);
+#pragma unroll
+    for (int i = 0; i < 2 * (FB + TB); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
-    __builtin_amdgcn_s_barrier();  // ... and every other lane's
-    const char* a_base = smem + stage * STAGE + (wm * WM + fr) * 128;
-    const char* b_base = smem + stage * STAGE + A_BYTES + (wn * WN + fr) * 128;
-    bf16x8_t bw[2][FB], at[2][TB];
-#pragma unroll
-    for (int f = 0; f < FB; ++f) bw[0][f] = *reinterpret_cast<const bf16x8_t*>(b_base + f * 4096 + choff[0]);
-#pragma unroll
-    for (int t = 0; t < TB; ++t) at[0][t] = *reinterpret_cast<const bf16x8_t*>(a_base + t * 4096 + choff[0]);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int cur = kk & 1, nxt = cur ^ 1;
-      if (kk < 3) {
-#pragma unroll
-        for (int f = 0; f < FB; ++f)
-          bw[nxt][f] = *reinterpret_cast<const bf16x8_t*>(b_base + f * 4096 + choff[kk + 1]);
-#pragma unroll
-        for (int t = 0; t < TB; ++t)
-          at[nxt][t] = *reinterpret_cast<const bf16x8_t*>(a_base + t * 4096 + choff[kk + 1]);
-      }
-#pragma unroll
-      for (int f = 0; f < FB; ++f)
-#pragma unroll
-        for (int t = 0; t < TB; ++t)
-          acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw[cur][f], at[cur][t], acc[f][t], 0, 0, 0);
-      if (kk < 3) {
-        // interleave the next step's fragment reads with this step's MFMAs
-#pragma unroll
-        for (int i = 0; i < FB + TB; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, FB * TB - FB - TB, 0);
-      }
-    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * FB * TB - 2 * (FB + TB), 0);
+    if (it + NST - 1 < nk) wait_vmcnt<CP>();
+    else wait_vmcnt<0>();
     wait_lds_reads();
-    __builtin_amdgcn_s_barrier();  // stage `it` may now be overwritten
+    __builtin_amdgcn_s_barrier();
+  };
+
+#pragma unroll
+  for (int i = 0; i < NST - 1; ++i)
+    if (i < nk) issue(i);
+  if (nk > 0) {
+    if (NST - 1 < nk) wait_vmcnt<CP>();  // steps 0 and 1 landed, step 2 may be in flight
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    Frags F0, F1;
+    load_frags(F0, 0);
+    int it = 0;
+    for (; it + 1 < nk; it += 2) {
+      step(it, F0, F1);
+      step(it + 1, F1, F0);
+    }
+    if (it < nk) step(it, F0, F1);
   }
 
 #pragma unroll
@@ -426,10 +447,10 @@ template <int BM, int BN, int EPI, bool SPLIT>
 static hipError_t launch_tile(const uint16_t* A, int M, int K, const uint16_t* B, int N,
                               const uint16_t* bias, void* out, float* part, const GemmPlan& p,
                               hipStream_t s) {
-  if (K % 64 == 0) {
+  if (K % 32 == 0 && (!SPLIT || p.kper % 32 == 0)) {
     // 256 x 256 tiles: 8 wavefronts (2 per SIMD, 128 x 64 each); 128 x 128: 4 (64 x 64 each)
     constexpr int GWM = 2, GWN = (BM == 256) ? 4 : 2;
-    const size_t lds = size_t(2) * (BM + BN) * 128;
+    const size_t lds = size_t(4) * (BM + BN) * 64;
     auto kern = gemm_dl_kernel<BM, BN, GWM, GWN, EPI, SPLIT>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
