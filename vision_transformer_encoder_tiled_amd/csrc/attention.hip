@@ -15,33 +15,41 @@
 // attn_pack_kernel (the Q/K/V load stage, once per token and head):
 //   rotate q and k with 3D RoPE (rotate-half pairs (j, j+40), angle
 //   pos[axis(j)] * inv_freq[j] from a (cos, sin) table built in double),
-//   scale q by log2(e)/sqrt(80), convert q, k, v to fp16, and lay K and V
-//   out as "tile images": for each (head, 64-key tile of an image) the exact
-//   bytes the attention kernel wants in LDS -- K as [64 keys][88] (16-byte
-//   padded rows: conflict-free 16-byte fragment reads) followed by V^T as
-//   [80 dims][68] (conflict-free 8-byte reads).  Each image's keys start on
-//   a fresh tile; the padding keys are zero.  Rotating here instead of per
-//   (query tile, key tile) removes all RoPE and conversion work from the
-//   inner loop, which is VALU-bound at head_dim 80.
+//   scale q by log2(e)/sqrt(80), convert q, k, v to fp16, and write K and V
+//   as 24 KB "tile images", one per (head, 64-key tile of an image): the
+//   exact bytes the attention kernel wants in LDS.
+//     K   [64 keys][88]  fp16, 16-byte padded rows (conflict-free 16-byte
+//                        fragment reads of 32 consecutive keys);
+//     V^T [81 dims][72]  fp16, dims as rows; inside each group of 16 keys
+//                        the key slots are ordered 0-3, 8-11, 4-7, 12-15 so
+//                        that the 8 keys one lane feeds to an MFMA k slice
+//                        are adjacent (one 16-byte read); row 80 is all ones.
+//   Each image's keys start on a fresh tile; the padding keys are zero.
+//   Rotating here, once, rather than per (query tile, key tile) keeps all
+//   RoPE and conversion work out of the inner loop, which is VALU-bound at
+//   head_dim 80.
 //
 // attention_kernel: 4 wavefronts x 32 queries.
 //   S^T = K Q^T   v_mfma_f32_32x32x16_f16, 2 key blocks x 5 dim slices of
 //                 16 (head_dim 80 = 5 x 16 exactly).  Each lane holds one
 //                 query and 16 keys of each 32-key block.
 //   O^T = V^T P^T v_mfma_f32_32x32x16_f16, 4 key slices x 3 dim blocks of
-//                 32.  P comes straight from the score registers: the keys
-//                 of a 16-key slice are permuted (k positions 0..7 of a lane
-//                 half hold keys +0..3 and +8..11) and V^T is read in the
-//                 same order.  Dims 80..95 of the third block are padding;
-//                 LDS row 80 of V^T holds ones, so that MFMA row produces
-//                 the softmax denominator l = sum(P) for free, from the same
-//                 fp16 P as the numerator.
+//                 32.  P comes straight from the score registers (the key
+//                 order inside a slice matches the V^T slot order).  Dims
+//                 80..95 of the third block are padding: the all-ones row
+//                 80 makes that MFMA row the softmax denominator l = sum(P),
+//                 from the same fp16 P as the numerator; rows 81..95 are
+//                 never stored.
 //   Online softmax in the log2 domain with lazy rescaling: the running max
 //   used for exp2 is only raised (and O, l rescaled) when some row's max
 //   grows by more than 8, decided once per wavefront; P is then at most
-//   2^8, well inside fp16.
-//   Tile images are copied global -> registers -> LDS (double buffered, one
-//   barrier per tile) as 16-byte vectors, with no arithmetic.
+//   2^8, well inside fp16.  The two lane halves of a query combine their
+//   maxima with v_permlane32_swap.
+//   Tile images stream global -> LDS by direct DMA (global_load_lds) into a
+//   ring of 3 stages: the copy of tile t+2 is in flight while tile t is
+//   processed.  Scores are software-pipelined one tile ahead: the MFMAs of
+//   tile t+1's S^T are issued between tile t's row max and its
+//   exponentials.  One workgroup barrier per tile.
 //
 // Operand precision: fp16 operands, fp32 accumulation.  fp16 runs at the
 // bf16 rate on gfx950 with 3 more mantissa bits; rounding P to bf16 would
@@ -61,16 +69,22 @@ namespace {
 constexpr int HD = 80;              // head_dim
 constexpr int BQ = kAttnQTile;      // queries per workgroup
 constexpr int BKV = kAttnKTile;     // keys per tile
-constexpr int KROW = 88;            // fp16 per K row in a tile image (176 B)
-constexpr int VROW = 68;            // fp16 per V^T row in a tile image (136 B)
-constexpr int K_IMG = BKV * KROW;   // fp16 elements of the K part
-constexpr int V_IMG = HD * VROW;    // fp16 elements of the V^T part (rows 0..79)
-constexpr int TILE_IMG = K_IMG + V_IMG;          // 11072 fp16 = 22144 B
-constexpr int TILE_VEC = TILE_IMG * 2 / 16;      // 1384 16-byte vectors
-constexpr int LDS_BUF = TILE_IMG + 16 * VROW;    // + V^T rows 80..95 (ones, zeros)
-constexpr int COPY_IT = (TILE_VEC + 255) / 256;  // 6 copy rounds of 256 threads
+constexpr int KROW = 88;            // fp16 per K row (176 B)
+constexpr int VROW = 72;            // fp16 per V^T row (144 B)
+constexpr int K_BYTES = BKV * KROW * 2;          // 11264
+constexpr int V_ROWS = HD + 1;                   // dims 0..79 and the ones row
+constexpr int IMG_BYTES = kAttnTileBytes;        // 24576: K + V^T rows 0..80 + pad
+constexpr int STAGE_BYTES = K_BYTES + 96 * VROW * 2;  // 25088: the MFMA reads V^T rows up to 95
+constexpr int NST = 3;
+constexpr int COPIES = IMG_BYTES / (1024 * 4);   // DMA instructions per wave per tile
 constexpr float kLazy = 8.0f;       // log2 growth of the row max tolerated before rescaling
-static_assert(TILE_IMG * 2 == kAttnTileBytes, "tile image size");
+static_assert(K_BYTES + V_ROWS * VROW * 2 <= IMG_BYTES, "tile image size");
+static_assert(COPIES * 4 * 1024 == IMG_BYTES, "tile image must be whole 4 KB rounds");
+
+// V^T slot of key k inside its group of 16: swap bits 2 and 3.
+__device__ __forceinline__ int vslot(int k) {
+  return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
 }  // namespace
 
 // ---------------------------------------------------------------- pack
@@ -92,7 +106,7 @@ __global__ void __launch_bounds__(320) attn_pack_kernel(
   const int k = threadIdx.x & 63, c = threadIdx.x >> 6;
   const int tok = cu[lo] + (T - ktile_start[lo]) * BKV + k;
   const bool valid = tok < cu[lo + 1];
-  uint16_t* img = kv + (int64_t(head) * ktile_start[n_img] + T) * TILE_IMG;
+  char* img = reinterpret_cast<char*>(kv) + (int64_t(head) * ktile_start[n_img] + T) * IMG_BYTES;
   uint32_t kr[8], vt[8];  // rotated k (fp16 pairs) and v (fp16 pairs)
   if (valid) {
     const int64_t ld = int64_t(3) * heads * HD;
@@ -142,18 +156,22 @@ __global__ void __launch_bounds__(320) attn_pack_kernel(
     for (int j = 0; j < 8; ++j) kr[j] = vt[j] = 0u;
   }
   // K rows: dims 8c..8c+7 and 40+8c..40+8c+7 of key k.
-  *reinterpret_cast<uint4*>(img + k * KROW + 8 * c) = make_uint4(kr[0], kr[1], kr[2], kr[3]);
-  *reinterpret_cast<uint4*>(img + k * KROW + 40 + 8 * c) = make_uint4(kr[4], kr[5], kr[6], kr[7]);
-  // V^T: element (dim, key k).  A wavefront (fixed c) writes 64 consecutive keys per dim.
-  uint16_t* vtimg = img + K_IMG;
+  uint16_t* kimg = reinterpret_cast<uint16_t*>(img);
+  *reinterpret_cast<uint4*>(kimg + k * KROW + 8 * c) = make_uint4(kr[0], kr[1], kr[2], kr[3]);
+  *reinterpret_cast<uint4*>(kimg + k * KROW + 40 + 8 * c) = make_uint4(kr[4], kr[5], kr[6], kr[7]);
+  // V^T: element (dim, slot of key k).  A wavefront (fixed c) writes 64 keys per dim.
+  uint16_t* vimg = reinterpret_cast<uint16_t*>(img + K_BYTES);
+  const int s = vslot(k);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    vtimg[(8 * c + 2 * j) * VROW + k] = uint16_t(vt[j] & 0xffffu);
-    vtimg[(8 * c + 2 * j + 1) * VROW + k] = uint16_t(vt[j] >> 16);
-    vtimg[(40 + 8 * c + 2 * j) * VROW + k] = uint16_t(vt[4 + j] & 0xffffu);
-    vtimg[(40 + 8 * c + 2 * j + 1) * VROW + k] = uint16_t(vt[4 + j] >> 16);
+    vimg[(8 * c + 2 * j) * VROW + s] = uint16_t(vt[j] & 0xffffu);
+    vimg[(8 * c + 2 * j + 1) * VROW + s] = uint16_t(vt[j] >> 16);
+    vimg[(40 + 8 * c + 2 * j) * VROW + s] = uint16_t(vt[4 + j] & 0xffffu);
+    vimg[(40 + 8 * c + 2 * j + 1) * VROW + s] = uint16_t(vt[4 + j] >> 16);
   }
-  // The row padding (K dims 80..87, V^T keys 64..67) is never read.
+  if (c == 0) vimg[HD * VROW + k] = uint16_t(0x3C00);  // the all-ones row (fp16 1.0)
+  // Row padding (K dims 80..87, V^T slots 64..71) and the tail of the image
+  // are never read for rows that reach the output.
 }
 
 // ---------------------------------------------------------------- attention
@@ -162,7 +180,7 @@ __global__ void __launch_bounds__(256) attention_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ order,
     const int32_t* __restrict__ tile_start, const int32_t* __restrict__ ktile_start,
     int32_t n_img, int32_t heads, void* __restrict__ out, int32_t out_f32) {
-  __shared__ __align__(16) uint16_t lds[2][LDS_BUF];
+  extern __shared__ __align__(16) char lds[];
 
   const int head = blockIdx.x % heads;
   const int tile = blockIdx.x / heads;
@@ -177,17 +195,20 @@ __global__ void __launch_bounds__(256) attention_kernel(
   const int q0 = kbeg + (tile - tile_start[lo]) * BQ;
   const int qend = min(q0 + BQ, kend);
   const int ntiles = (kend - kbeg + BKV - 1) / BKV;
-  const uint4* src = reinterpret_cast<const uint4*>(
-      kv + (int64_t(head) * ktile_start[n_img] + ktile_start[img]) * TILE_IMG);
+  const char* src = reinterpret_cast<const char*>(kv) +
+                    (int64_t(head) * ktile_start[n_img] + ktile_start[img]) * IMG_BYTES;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, ln = lane & 31;
+  const uint32_t lds_wave = lds_offset(lds) + 1024 * wave;
 
-  // V^T rows 80..95 of both buffers: row 80 = ones (the row-sum row), rest zero.
-  for (int i = tid; i < 2 * 16 * VROW; i += 256) {
-    const int b = i / (16 * VROW), r = i % (16 * VROW);
-    lds[b][TILE_IMG + r] = (r < VROW) ? uint16_t(0x3C00) : uint16_t(0);
-  }
+  // Tile t -> stage t % 3: each wave copies its COPIES 1 KB pieces.
+  auto issue = [&](int t) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_wave + (t % NST) * STAGE_BYTES);
+    const char* g = src + int64_t(t) * IMG_BYTES + 1024 * wave + 16 * lane;
+#pragma unroll
+    for (int j = 0; j < COPIES; ++j) dma16(g + 4096 * j, base + 4096 * j);
+  };
 
   // Q fragments (B operand of S^T = K Q^T): dims 16s + 8hf .. +7 of this lane's query.
   const int qrow = q0 + wave * 32 + ln;
@@ -200,24 +221,19 @@ __global__ void __launch_bounds__(256) attention_kernel(
     for (int s = 0; s < 5; ++s) qfrag[s] = __builtin_bit_cast(f16x8_t, q[2 * s + hf]);
   }
 
-  // Tile copy: 1384 16-byte vectors = 5 per thread + 104 threads with a sixth.
-  static_assert(COPY_IT == 6 && TILE_VEC - 5 * 256 > 0, "copy split");
-  const bool has6 = tid < TILE_VEC - 5 * 256;
-  uint4 st0, st1, st2, st3, st4, st5 = make_uint4(0, 0, 0, 0);
-#define VT_ATT_GLOAD(t)                                              \
-  do {                                                               \
-    const uint4* g_ = src + int64_t(t) * TILE_VEC + tid;             \
-    st0 = g_[0]; st1 = g_[256]; st2 = g_[512]; st3 = g_[768];        \
-    st4 = g_[1024];                                                  \
-    if (has6) st5 = g_[1280];                                        \
-  } while (0)
-#define VT_ATT_LSTORE(b)                                             \
-  do {                                                               \
-    uint4* d_ = reinterpret_cast<uint4*>(lds[b]) + tid;              \
-    d_[0] = st0; d_[256] = st1; d_[512] = st2; d_[768] = st3;        \
-    d_[1024] = st4;                                                  \
-    if (has6) d_[1280] = st5;                                        \
-  } while (0)
+  // Per-lane LDS offsets inside a stage.
+  const int koff = ln * KROW * 2 + 16 * hf;                  // + 32 b KROW*2 + 32 sl
+  const int voff = K_BYTES + ln * VROW * 2 + 16 * hf;        // + (32 d) VROW*2 + 32 ks
+
+  f16x8_t kf[10];
+  auto load_k = [&](int t) {
+    const char* st = lds + (t % NST) * STAGE_BYTES + koff;
+#pragma unroll
+    for (int sl = 0; sl < 5; ++sl)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        kf[2 * sl + b] = *reinterpret_cast<const f16x8_t*>(st + b * 32 * KROW * 2 + 32 * sl);
+  };
 
   f32x16_t acc[3];
 #pragma unroll
@@ -226,43 +242,69 @@ __global__ void __launch_bounds__(256) attention_kernel(
     for (int e = 0; e < 16; ++e) acc[d][e] = 0.f;
   float m_use = -INFINITY;
 
-  VT_ATT_GLOAD(0);
-  VT_ATT_LSTORE(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) VT_ATT_GLOAD(t + 1);
-
-    // S^T = K Q^T for 64 keys: two 32-key blocks.
-    f32x16_t s[2];
+  auto qk = [&](f32x16_t (&sc)[2]) {
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[b][e] = 0.f;
-    const uint16_t* kb = lds[buf] + ln * KROW + 8 * hf;
+      for (int e = 0; e < 16; ++e) sc[b][e] = 0.f;
 #pragma unroll
-    for (int sl = 0; sl < 5; ++sl) {
+    for (int sl = 0; sl < 5; ++sl)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const f16x8_t a = *reinterpret_cast<const f16x8_t*>(kb + b * 32 * KROW + 16 * sl);
-        s[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qfrag[sl], s[b], 0, 0, 0);
-      }
-    }
-    // s[b][4g + r] is key kbeg + 64t + 32b + 8g + 4hf + r of query ln.
+      for (int b = 0; b < 2; ++b)
+        sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[2 * sl + b], qfrag[sl], sc[b], 0, 0, 0);
+  };
+
+  issue(0);
+  if (ntiles > 1) issue(1);
+  if (ntiles > 1) wait_vmcnt<COPIES>();
+  else wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  load_k(0);
+  f32x16_t s_cur[2], s_nxt[2];
+  qk(s_cur);
+
+  // Iteration t: the scores of tile t (s_cur) were issued one iteration
+  // earlier.  The MFMAs for tile t+1's scores are issued between the row max
+  // and the exponentials of tile t, so they execute under that VALU work.
+  for (int t = 0; t < ntiles; ++t) {
+    // Every wave is done reading tile t-1 (V) and tile t (K); tile t+1 has landed.
+    wait_vmcnt<0>();
+    wait_lds_reads();
+    __builtin_amdgcn_s_barrier();
+    if (t + 2 < ntiles) issue(t + 2);  // into the stage tile t-1 used
+    if (t + 1 < ntiles) load_k(t + 1);
+
+    // s_cur[b][4g + r] is key kbeg + 64t + 32b + 8g + 4hf + r of query ln.
     const int kt = kbeg + t * BKV;
     if (kt + BKV > kend) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (kt + 32 * b + 8 * (e >> 2) + 4 * hf + (e & 3) >= kend) s[b][e] = -INFINITY;
+          if (kt + 32 * b + 8 * (e >> 2) + 4 * hf + (e & 3) >= kend) s_cur[b][e] = -INFINITY;
     }
-    float mx = fmaxf(s[0][0], s[0][1]);
+    float mx = fmaxf(s_cur[0][0], s_cur[0][1]);
 #pragma unroll
-    for (int e = 2; e < 16; ++e) mx = fmaxf(mx, s[0][e]);
+    for (int e = 2; e < 16; ++e) mx = fmaxf(mx, s_cur[0][e]);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[1][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s_cur[1][e]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+
+    if (t + 1 < ntiles) qk(s_nxt);  // tile t+1's scores, in flight during the exponentials
+
+    // V^T fragments of tile t: one 16-byte read per (key slice, dim block).
+    const char* vst = lds + (t % NST) * STAGE_BYTES + voff;
+    f16x8_t vf[12];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int d = 0; d < 3; ++d)
+        vf[3 * ks + d] = *reinterpret_cast<const f16x8_t*>(vst + 32 * d * VROW * 2 + 32 * ks);
+
     // Lazy rescale: raise the running max only when it grows by more than kLazy.
     if (__any(mx > m_use + kLazy)) {
       const float m_new = fmaxf(m_use, mx);
@@ -278,29 +320,18 @@ __global__ void __launch_bounds__(256) attention_kernel(
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        pf[2 * b + (e >> 3)][e & 7] = (_Float16)__builtin_amdgcn_exp2f(s[b][e] - m_use);
+        pf[2 * b + (e >> 3)][e & 7] = (_Float16)__builtin_amdgcn_exp2f(s_cur[b][e] - m_use);
 
-    // O^T += V^T P^T over 4 slices of 16 keys; dims 80..95 are the padding
-    // rows (row 80 = ones -> the row sum l).
-    const uint16_t* vb = lds[buf] + K_IMG;
+    // O^T += V^T P^T over 4 slices of 16 keys.
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int kb0 = 16 * ks + 4 * hf;
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int d = 0; d < 3; ++d) {
-        const uint16_t* vr = vb + (32 * d + ln) * VROW + kb0;
-        const uint2 lo4 = *reinterpret_cast<const uint2*>(vr);
-        const uint2 hi4 = *reinterpret_cast<const uint2*>(vr + 8);
-        const f16x8_t a = __builtin_bit_cast(f16x8_t, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
-        acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ks], acc[d], 0, 0, 0);
-      }
-    }
+      for (int d = 0; d < 3; ++d)
+        acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[3 * ks + d], pf[ks], acc[d], 0, 0, 0);
 
-    if (t + 1 < ntiles) VT_ATT_LSTORE(buf ^ 1);
-    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < 2; ++b) s_cur[b] = s_nxt[b];
   }
-#undef VT_ATT_GLOAD
-#undef VT_ATT_LSTORE
 
   // ---- normalise and store: acc[d][4g + r] is dim 32d + 8g + 4hf + r of query ln;
   // the row sum l (dim 80) is acc[2][8] in the lanes with hf == 0.
@@ -338,8 +369,13 @@ hipError_t launch_attention(const uint16_t* qkv, const int32_t* cu_seqlens, cons
                      qpk, kv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const size_t lds = size_t(NST) * STAGE_BYTES;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(attention_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+      int(lds));
+  if (attr != hipSuccess) return attr;
   const int64_t blocks = int64_t(max_qtiles) * heads;
-  hipLaunchKernelGGL(attention_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, qpk, kv,
+  hipLaunchKernelGGL(attention_kernel, dim3(unsigned(blocks)), dim3(256), lds, s, qpk, kv,
                      cu_seqlens, order, tile_start, ktile_start, n_img, heads, out, out_f32 ? 1 : 0);
   return hipGetLastError();
 }

@@ -65,4 +65,39 @@ __device__ __forceinline__ float gelu_erf(float x) {
   return 0.5f * x * (1.0f + erff(x * 0.7071067811865476f));
 }
 
+// ---- LDS DMA and explicit waits (gfx950)
+
+// s_waitcnt immediate: vmcnt <= n, expcnt and lgkmcnt unconstrained (gfx9 encoding).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until this wavefront's LDS reads have returned (lgkmcnt = 0; vmcnt and
+// expcnt unconstrained).  Needed before the barrier that releases a stage for
+// overwriting: the compiler may otherwise consume the last fragment reads
+// (and so wait for them) only after the barrier.
+__device__ __forceinline__ void wait_lds_reads() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4) | (0 << 8));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// LDS byte offset of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+
+// One 16-byte global -> LDS copy per lane: lane i writes LDS [lds + 16 i].
+// Issued as inline assembly so the compiler does not treat every later LDS
+// read as dependent on it (it cannot tell the two pipeline stages apart and
+// would wait for all outstanding copies); completion is awaited explicitly
+// with wait_vmcnt before the workgroup barrier that publishes a stage.  The
+// instruction has no register result; the address VGPRs are read at issue.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+
 }  // namespace vt

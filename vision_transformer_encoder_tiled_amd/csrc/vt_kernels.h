@@ -62,7 +62,7 @@ hipError_t launch_gemm(const uint16_t* A, int M, int K, const uint16_t* B, int N
 // ---- attention (attention.hip)
 constexpr int kAttnQTile = 128;        // queries per workgroup
 constexpr int kAttnKTile = 64;         // keys per tile
-constexpr int kAttnTileBytes = 22144;  // one (head, key tile) image: K [64][88] + V^T [80][68] fp16
+constexpr int kAttnTileBytes = 24576;  // one (head, key tile) image: K [64][88] + V^T [81][72] fp16 + pad
 // qpk: [N, heads, 80] fp16 rotated+scaled Q; kv: heads x max_ktiles tile images.
 hipError_t launch_attention(const uint16_t* qkv, const int32_t* cu_seqlens, const int32_t* pos_thw,
                             const int32_t* order, const int32_t* tile_start,
