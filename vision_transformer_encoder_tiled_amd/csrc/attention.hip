@@ -40,11 +40,12 @@
 //                 80 makes that MFMA row the softmax denominator l = sum(P),
 //                 from the same fp16 P as the numerator; rows 81..95 are
 //                 never stored.
-//   Online softmax in the log2 domain with lazy rescaling: the running max
-//   used for exp2 is only raised (and O, l rescaled) when some row's max
-//   grows by more than 8, decided once per wavefront; P is then at most
-//   2^8, well inside fp16.  The two lane halves of a query combine their
-//   maxima with v_permlane32_swap.
+//   Online softmax in the log2 domain with lazy rescaling: the reference max
+//   m of a query is set by the first key tile and only raised (O and l
+//   rescaled) when some row's max grows by more than 8, decided once per
+//   wavefront; P is then at most 2^8, well inside fp16.  The score MFMAs
+//   accumulate onto -m, so the exponentials need no subtraction.  The two
+//   lane halves of a query combine their maxima with v_permlane32_swap.
 //   Tile images stream global -> LDS by direct DMA (global_load_lds) into a
 //   ring of 3 stages: the copy of tile t+2 is in flight while tile t is
 //   processed.  Scores are software-pipelined one tile ahead: the MFMAs of
@@ -240,18 +241,40 @@ __global__ void __launch_bounds__(256) attention_kernel(
   for (int d = 0; d < 3; ++d)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[d][e] = 0.f;
-  float m_use = -INFINITY;
 
-  auto qk = [&](f32x16_t (&sc)[2]) {
+  // S^T for one tile; the accumulation starts from c0 (all entries -m for the
+  // lane's query), so the scores come out already relative to the running max.
+  auto qk = [&](f32x16_t (&sc)[2], const f32x16_t& c0) {
 #pragma unroll
     for (int b = 0; b < 2; ++b)
+      sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[b], qfrag[0], c0, 0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sc[b][e] = 0.f;
-#pragma unroll
-    for (int sl = 0; sl < 5; ++sl)
+    for (int sl = 1; sl < 5; ++sl)
 #pragma unroll
       for (int b = 0; b < 2; ++b)
         sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[2 * sl + b], qfrag[sl], sc[b], 0, 0, 0);
+  };
+  // Keys past the image end (last tile only) get -inf scores.
+  auto mask = [&](f32x16_t (&sc)[2], int t) {
+    const int kt = kbeg + t * BKV;
+    if (kt + BKV > kend) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (kt + 32 * b + 8 * (e >> 2) + 4 * hf + (e & 3) >= kend) sc[b][e] = -INFINITY;
+    }
+  };
+  // Row max over this lane's 32 scores, combined with the other lane half.
+  auto rowmax = [&](const f32x16_t (&sc)[2]) {
+    float mx = fmaxf(sc[0][0], sc[0][1]);
+#pragma unroll
+    for (int e = 2; e < 16; ++e) mx = fmaxf(mx, sc[0][e]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[1][e]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                     false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
   };
 
   issue(0);
@@ -260,13 +283,25 @@ __global__ void __launch_bounds__(256) attention_kernel(
   else wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
   load_k(0);
-  f32x16_t s_cur[2], s_nxt[2];
-  qk(s_cur);
 
-  // Iteration t: the scores of tile t (s_cur) were issued one iteration
-  // earlier.  The MFMAs for tile t+1's scores are issued between the row max
-  // and the exponentials of tile t, so they execute under that VALU work.
-  for (int t = 0; t < ntiles; ++t) {
+  // Tile 0 fixes the reference max m (per query): its scores are computed
+  // from zero and shifted once; later tiles start their accumulation at -m.
+  f32x16_t sa[2], sb[2], negm;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) negm[e] = 0.f;
+  qk(sa, negm);
+  mask(sa, 0);
+  float m_use = rowmax(sa);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) negm[e] = -m_use;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sa[b][e] -= m_use;
+
+  // One tile; `cur` holds tile t's scores relative to m.  Tile t+1's score
+  // MFMAs are issued before tile t's exponentials so they run underneath.
+  auto body = [&](int t, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
     // Every wave is done reading tile t-1 (V) and tile t (K); tile t+1 has landed.
     wait_vmcnt<0>();
     wait_lds_reads();
@@ -274,64 +309,69 @@ __global__ void __launch_bounds__(256) attention_kernel(
     if (t + 2 < ntiles) issue(t + 2);  // into the stage tile t-1 used
     if (t + 1 < ntiles) load_k(t + 1);
 
-    // s_cur[b][4g + r] is key kbeg + 64t + 32b + 8g + 4hf + r of query ln.
-    const int kt = kbeg + t * BKV;
-    if (kt + BKV > kend) {
+    if (t > 0) {
+      mask(cur, t);
+      const float mx = rowmax(cur);  // relative to m
+      // Lazy rescale: raise m only when some row's max grew by more than kLazy.
+      if (__any(mx > kLazy)) {
+        const float delta = fmaxf(mx, 0.f);
+        m_use += delta;
+        const float alpha = __builtin_amdgcn_exp2f(-delta);
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+        for (int d = 0; d < 3; ++d)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (kt + 32 * b + 8 * (e >> 2) + 4 * hf + (e & 3) >= kend) s_cur[b][e] = -INFINITY;
-    }
-    float mx = fmaxf(s_cur[0][0], s_cur[0][1]);
+          for (int e = 0; e < 16; ++e) acc[d][e] *= alpha;
 #pragma unroll
-    for (int e = 2; e < 16; ++e) mx = fmaxf(mx, s_cur[0][e]);
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s_cur[1][e]);
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                       false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+          for (int e = 0; e < 16; ++e) cur[b][e] -= delta;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) negm[e] = -m_use;
+      }
     }
 
-    if (t + 1 < ntiles) qk(s_nxt);  // tile t+1's scores, in flight during the exponentials
+    if (t + 1 < ntiles) qk(nxt, negm);  // tile t+1's scores, in flight during the exponentials
 
-    // V^T fragments of tile t: one 16-byte read per (key slice, dim block).
+    // V^T fragments of tile t: one 16-byte read per (key slice, dim block),
+    // in two halves to bound the live registers.
     const char* vst = lds + (t % NST) * STAGE_BYTES + voff;
-    f16x8_t vf[12];
+    f16x8_t vf[6];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int d = 0; d < 3; ++d)
         vf[3 * ks + d] = *reinterpret_cast<const f16x8_t*>(vst + 32 * d * VROW * 2 + 32 * ks);
 
-    // Lazy rescale: raise the running max only when it grows by more than kLazy.
-    if (__any(mx > m_use + kLazy)) {
-      const float m_new = fmaxf(m_use, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);  // 0 on the first tile
-      m_use = m_new;
-#pragma unroll
-      for (int d = 0; d < 3; ++d)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[d][e] *= alpha;
-    }
     f16x8_t pf[4];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        pf[2 * b + (e >> 3)][e & 7] = (_Float16)__builtin_amdgcn_exp2f(s_cur[b][e] - m_use);
+        pf[2 * b + (e >> 3)][e & 7] = (_Float16)__builtin_amdgcn_exp2f(cur[b][e]);
 
     // O^T += V^T P^T over 4 slices of 16 keys.
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int d = 0; d < 3; ++d)
         acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[3 * ks + d], pf[ks], acc[d], 0, 0, 0);
-
 #pragma unroll
-    for (int b = 0; b < 2; ++b) s_cur[b] = s_nxt[b];
+    for (int ks = 2; ks < 4; ++ks)
+#pragma unroll
+      for (int d = 0; d < 3; ++d)
+        vf[3 * (ks - 2) + d] = *reinterpret_cast<const f16x8_t*>(vst + 32 * d * VROW * 2 + 32 * ks);
+#pragma unroll
+    for (int ks = 2; ks < 4; ++ks)
+#pragma unroll
+      for (int d = 0; d < 3; ++d)
+        acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[3 * (ks - 2) + d], pf[ks], acc[d], 0, 0, 0);
+  };
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    body(t, sa, sb);
+    body(t + 1, sb, sa);
   }
+  if (t < ntiles) body(t, sa, sb);
 
   // ---- normalise and store: acc[d][4g + r] is dim 32d + 8g + 4hf + r of query ln;
   // the row sum l (dim 80) is acc[2][8] in the lanes with hf == 0.
