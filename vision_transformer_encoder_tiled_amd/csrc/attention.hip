@@ -29,7 +29,10 @@
 //   RoPE and conversion work out of the inner loop, which is VALU-bound at
 //   head_dim 80.
 //
-// attention_kernel: 4 wavefronts x 32 queries.
+// attention_kernel: 4 wavefronts, each with 32 queries.  KG = 1: one
+//   workgroup = 128 queries, every wavefront walks all key tiles.  KG = 2
+//   (small images, so that every CU gets a workgroup): 64 queries, two
+//   groups of 2 wavefronts take alternate key tiles and merge at the end.
 //   S^T = K Q^T   v_mfma_f32_32x32x16_f16, 2 key blocks x 5 dim slices of
 //                 16 (head_dim 80 = 5 x 16 exactly).  Each lane holds one
 //                 query and 16 keys of each 32-key block.
@@ -68,7 +71,6 @@ namespace vt {
 
 namespace {
 constexpr int HD = 80;              // head_dim
-constexpr int BQ = kAttnQTile;      // queries per workgroup
 constexpr int BKV = kAttnKTile;     // keys per tile
 constexpr int KROW = 88;            // fp16 per K row (176 B)
 constexpr int VROW = 72;            // fp16 per V^T row (144 B)
@@ -89,25 +91,25 @@ __device__ __forceinline__ int vslot(int k) {
 }  // namespace
 
 // ---------------------------------------------------------------- pack
-// Block (64 keys x 5 chunks) per (key tile, head): thread = (key k = tid%64,
-// chunk c = tid/64) handles rotation pairs 8c..8c+7, i.e. dims 8c..8c+7 and
-// 40+8c..40+8c+7 of q, k and v for that key's token.
+// Block per (key tile, head), 320 threads = 64 keys x 5 chunks with the
+// chunk fastest, so a wavefront reads runs of 80 contiguous bytes of each
+// token's q, k and v.  Thread (k, c) handles rotation pairs 8c..8c+7, i.e.
+// dims 8c..8c+7 and 40+8c..40+8c+7 of q, k and v of key k.  V is
+// transposed through LDS so that every V^T row leaves as 128 contiguous
+// bytes.
 __global__ void __launch_bounds__(320) attn_pack_kernel(
-    const uint16_t* __restrict__ qkv, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ pos, const int32_t* __restrict__ ktile_start, int32_t n_img,
-    int32_t heads, int32_t n_pos, const float2* __restrict__ rope_cs, int32_t axis_code,
-    float q_scale_log2, uint16_t* __restrict__ qpk, uint16_t* __restrict__ kv) {
+    const uint16_t* __restrict__ qkv, const int32_t* __restrict__ pos,
+    const int2* __restrict__ kdesc, int32_t heads, int32_t n_pos,
+    const float2* __restrict__ rope_cs, int32_t axis_code, float q_scale_log2,
+    uint16_t* __restrict__ qpk, uint16_t* __restrict__ kv) {
+  __shared__ __align__(16) uint16_t vs[HD * BKV];  // V^T [dim][slot], 128 B rows
   const int T = blockIdx.x, head = blockIdx.y;
-  if (T >= ktile_start[n_img]) return;
-  int lo = 0, hi = n_img - 1;  // image of tile T: largest i with ktile_start[i] <= T
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (ktile_start[mid] <= T) lo = mid; else hi = mid - 1;
-  }
-  const int k = threadIdx.x & 63, c = threadIdx.x >> 6;
-  const int tok = cu[lo] + (T - ktile_start[lo]) * BKV + k;
-  const bool valid = tok < cu[lo + 1];
-  char* img = reinterpret_cast<char*>(kv) + (int64_t(head) * ktile_start[n_img] + T) * IMG_BYTES;
+  const int2 desc = kdesc[T];
+  if (desc.x < 0) return;
+  const int k = threadIdx.x / 5, c = threadIdx.x % 5;
+  const int tok = desc.x + k;
+  const bool valid = tok < desc.y;
+  char* img = reinterpret_cast<char*>(kv) + (int64_t(T) * heads + head) * IMG_BYTES;
   uint32_t kr[8], vt[8];  // rotated k (fp16 pairs) and v (fp16 pairs)
   if (valid) {
     const int64_t ld = int64_t(3) * heads * HD;
@@ -156,63 +158,81 @@ __global__ void __launch_bounds__(320) attn_pack_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) kr[j] = vt[j] = 0u;
   }
-  // K rows: dims 8c..8c+7 and 40+8c..40+8c+7 of key k.
+  // K rows: dims 8c..8c+7 and 40+8c..40+8c+7 of key k (padding keys are zero).
   uint16_t* kimg = reinterpret_cast<uint16_t*>(img);
   *reinterpret_cast<uint4*>(kimg + k * KROW + 8 * c) = make_uint4(kr[0], kr[1], kr[2], kr[3]);
   *reinterpret_cast<uint4*>(kimg + k * KROW + 40 + 8 * c) = make_uint4(kr[4], kr[5], kr[6], kr[7]);
-  // V^T: element (dim, slot of key k).  A wavefront (fixed c) writes 64 keys per dim.
-  uint16_t* vimg = reinterpret_cast<uint16_t*>(img + K_BYTES);
+  // V^T through LDS: element (dim, slot of key k).
   const int s = vslot(k);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    vimg[(8 * c + 2 * j) * VROW + s] = uint16_t(vt[j] & 0xffffu);
-    vimg[(8 * c + 2 * j + 1) * VROW + s] = uint16_t(vt[j] >> 16);
-    vimg[(40 + 8 * c + 2 * j) * VROW + s] = uint16_t(vt[4 + j] & 0xffffu);
-    vimg[(40 + 8 * c + 2 * j + 1) * VROW + s] = uint16_t(vt[4 + j] >> 16);
+    vs[(8 * c + 2 * j) * BKV + s] = uint16_t(vt[j] & 0xffffu);
+    vs[(8 * c + 2 * j + 1) * BKV + s] = uint16_t(vt[j] >> 16);
+    vs[(40 + 8 * c + 2 * j) * BKV + s] = uint16_t(vt[4 + j] & 0xffffu);
+    vs[(40 + 8 * c + 2 * j + 1) * BKV + s] = uint16_t(vt[4 + j] >> 16);
   }
-  if (c == 0) vimg[HD * VROW + k] = uint16_t(0x3C00);  // the all-ones row (fp16 1.0)
+  __syncthreads();
+  // Rows 0..79 from LDS and row 80 = fp16 1.0, 16 bytes (8 slots) per thread.
   // Row padding (K dims 80..87, V^T slots 64..71) and the tail of the image
   // are never read for rows that reach the output.
+  uint16_t* vimg = reinterpret_cast<uint16_t*>(img + K_BYTES);
+  for (int i = threadIdx.x; i < V_ROWS * (BKV / 8); i += 320) {
+    const int d = i >> 3, sg = i & 7;
+    const uint4 v = d < HD ? *reinterpret_cast<const uint4*>(vs + d * BKV + 8 * sg)
+                           : make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+    *reinterpret_cast<uint4*>(vimg + d * VROW + 8 * sg) = v;
+  }
 }
 
 // ---------------------------------------------------------------- attention
+// KG = key groups.  The 4 wavefronts form KG groups of 4/KG; a group owns
+// all the workgroup's 32 * 4/KG queries and every KG-th key tile of the
+// image (tile r*KG + g in round r).  With KG = 2 a workgroup holds 64
+// queries, so small images give twice as many workgroups; the groups'
+// partial (max, O, l) are merged through LDS at the end.
+template <int KG>
 __global__ void __launch_bounds__(256) attention_kernel(
     const uint16_t* __restrict__ qpk, const uint16_t* __restrict__ kv,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ order,
-    const int32_t* __restrict__ tile_start, const int32_t* __restrict__ ktile_start,
-    int32_t n_img, int32_t heads, void* __restrict__ out, int32_t out_f32) {
+    const int4* __restrict__ qdesc, int32_t heads, void* __restrict__ out, int32_t out_f32) {
+  constexpr int QW = 4 / KG;              // query wavefronts per group
+  constexpr int WQ = 32 * QW;             // queries per workgroup
+  constexpr int STAGE = KG * STAGE_BYTES; // one round: KG tiles
   extern __shared__ __align__(16) char lds[];
 
   const int head = blockIdx.x % heads;
-  const int tile = blockIdx.x / heads;
-  if (tile >= tile_start[n_img]) return;
-  int lo = 0, hi = n_img - 1;  // largest rank r with tile_start[r] <= tile
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  const int img = order[lo];
-  const int kbeg = cu[img], kend = cu[img + 1];
-  const int q0 = kbeg + (tile - tile_start[lo]) * BQ;
-  const int qend = min(q0 + BQ, kend);
+  const int4 desc = qdesc[blockIdx.x / heads];  // (first query, image begin, image end, first key tile)
+  if (desc.x < 0) return;
+  const int q0 = desc.x, kbeg = desc.y, kend = desc.z;
+  const int qend = min(q0 + WQ, kend);
   const int ntiles = (kend - kbeg + BKV - 1) / BKV;
-  const char* src = reinterpret_cast<const char*>(kv) +
-                    (int64_t(head) * ktile_start[n_img] + ktile_start[img]) * IMG_BYTES;
+  const int rounds = (ntiles + KG - 1) / KG;
+  // Tile t of this (image, head) is image (desc.w + t) * heads + head.
+  const char* src = reinterpret_cast<const char*>(kv) + (int64_t(desc.w) * heads + head) * IMG_BYTES;
+  const int64_t tile_stride = int64_t(heads) * IMG_BYTES;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = wave / QW, qw = wave % QW;
   const int hf = lane >> 5, ln = lane & 31;
   const uint32_t lds_wave = lds_offset(lds) + 1024 * wave;
 
-  // Tile t -> stage t % 3: each wave copies its COPIES 1 KB pieces.
-  auto issue = [&](int t) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_wave + (t % NST) * STAGE_BYTES);
-    const char* g = src + int64_t(t) * IMG_BYTES + 1024 * wave + 16 * lane;
+  // Round r -> stage r % 3: tile r*KG + j at offset j * STAGE_BYTES; each
+  // wavefront copies COPIES 1 KB pieces of every tile that exists.
+  auto issue = [&](int r) {
 #pragma unroll
-    for (int j = 0; j < COPIES; ++j) dma16(g + 4096 * j, base + 4096 * j);
+    for (int j = 0; j < KG; ++j) {
+      const int t = r * KG + j;
+      if (t < ntiles) {
+        const uint32_t base =
+            __builtin_amdgcn_readfirstlane(lds_wave + (r % NST) * STAGE + j * STAGE_BYTES);
+        const char* g = src + t * tile_stride + 1024 * wave + 16 * lane;
+#pragma unroll
+        for (int c = 0; c < COPIES; ++c) dma16(g + 4096 * c, base + 4096 * c);
+      }
+    }
   };
 
   // Q fragments (B operand of S^T = K Q^T): dims 16s + 8hf .. +7 of this lane's query.
-  const int qrow = q0 + wave * 32 + ln;
+  const int qrow = q0 + qw * 32 + ln;
   const bool qvalid = qrow < qend;
   const int qr = qvalid ? qrow : qend - 1;
   f16x8_t qfrag[5];
@@ -222,13 +242,13 @@ __global__ void __launch_bounds__(256) attention_kernel(
     for (int s = 0; s < 5; ++s) qfrag[s] = __builtin_bit_cast(f16x8_t, q[2 * s + hf]);
   }
 
-  // Per-lane LDS offsets inside a stage.
-  const int koff = ln * KROW * 2 + 16 * hf;                  // + 32 b KROW*2 + 32 sl
-  const int voff = K_BYTES + ln * VROW * 2 + 16 * hf;        // + (32 d) VROW*2 + 32 ks
+  // Per-lane LDS offsets inside this group's tile of a stage.
+  const int koff = grp * STAGE_BYTES + ln * KROW * 2 + 16 * hf;            // + 32 b KROW*2 + 32 sl
+  const int voff = grp * STAGE_BYTES + K_BYTES + ln * VROW * 2 + 16 * hf;  // + (32 d) VROW*2 + 32 ks
 
   f16x8_t kf[10];
-  auto load_k = [&](int t) {
-    const char* st = lds + (t % NST) * STAGE_BYTES + koff;
+  auto load_k = [&](int r) {
+    const char* st = lds + (r % NST) * STAGE + koff;
 #pragma unroll
     for (int sl = 0; sl < 5; ++sl)
 #pragma unroll
@@ -278,39 +298,45 @@ __global__ void __launch_bounds__(256) attention_kernel(
   };
 
   issue(0);
-  if (ntiles > 1) issue(1);
-  if (ntiles > 1) wait_vmcnt<COPIES>();
-  else wait_vmcnt<0>();
-  __builtin_amdgcn_s_barrier();
-  load_k(0);
+  if (rounds > 1) issue(1);
+  wait_vmcnt<0>();
+  wg_barrier();
 
-  // Tile 0 fixes the reference max m (per query): its scores are computed
-  // from zero and shifted once; later tiles start their accumulation at -m.
+  // The group's first tile fixes the reference max m (per query): its scores
+  // are computed from zero and shifted once; later tiles accumulate onto -m.
+  // A group with no tile (one-tile image, KG = 2) keeps m = -inf and O = 0.
   f32x16_t sa[2], sb[2], negm;
+  float m_use = -INFINITY;
 #pragma unroll
   for (int e = 0; e < 16; ++e) negm[e] = 0.f;
-  qk(sa, negm);
-  mask(sa, 0);
-  float m_use = rowmax(sa);
+  if (grp < ntiles) {
+    load_k(0);
+    qk(sa, negm);
+    mask(sa, grp);
+    m_use = rowmax(sa);
 #pragma unroll
-  for (int e = 0; e < 16; ++e) negm[e] = -m_use;
+    for (int e = 0; e < 16; ++e) negm[e] = -m_use;
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sa[b][e] -= m_use;
+      for (int e = 0; e < 16; ++e) sa[b][e] -= m_use;
+  }
 
-  // One tile; `cur` holds tile t's scores relative to m.  Tile t+1's score
-  // MFMAs are issued before tile t's exponentials so they run underneath.
-  auto body = [&](int t, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
-    // Every wave is done reading tile t-1 (V) and tile t (K); tile t+1 has landed.
+  // One round; `cur` holds the scores of the group's tile tc relative to m.
+  // The group's next tile's score MFMAs are issued before this tile's
+  // exponentials so they run underneath.
+  auto body = [&](int r, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
+    // Every wave is done reading round r-1 (V) and round r (K); round r+1 has landed.
     wait_vmcnt<0>();
     wait_lds_reads();
-    __builtin_amdgcn_s_barrier();
-    if (t + 2 < ntiles) issue(t + 2);  // into the stage tile t-1 used
-    if (t + 1 < ntiles) load_k(t + 1);
+    wg_barrier();
+    if (r + 2 < rounds) issue(r + 2);  // into the stage round r-1 used
+    const int tc = r * KG + grp, tn = tc + KG;
+    if (tn < ntiles) load_k(r + 1);
+    if (tc >= ntiles) return;
 
-    if (t > 0) {
-      mask(cur, t);
+    if (r > 0) {
+      mask(cur, tc);
       const float mx = rowmax(cur);  // relative to m
       // Lazy rescale: raise m only when some row's max grew by more than kLazy.
       if (__any(mx > kLazy)) {
@@ -330,11 +356,11 @@ __global__ void __launch_bounds__(256) attention_kernel(
       }
     }
 
-    if (t + 1 < ntiles) qk(nxt, negm);  // tile t+1's scores, in flight during the exponentials
+    if (tn < ntiles) qk(nxt, negm);  // next tile's scores, in flight during the exponentials
 
-    // V^T fragments of tile t: one 16-byte read per (key slice, dim block),
+    // V^T fragments of this tile: one 16-byte read per (key slice, dim block),
     // in two halves to bound the live registers.
-    const char* vst = lds + (t % NST) * STAGE_BYTES + voff;
+    const char* vst = lds + (r % NST) * STAGE + voff;
     f16x8_t vf[6];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -366,12 +392,38 @@ __global__ void __launch_bounds__(256) attention_kernel(
       for (int d = 0; d < 3; ++d)
         acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[3 * (ks - 2) + d], pf[ks], acc[d], 0, 0, 0);
   };
-  int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
-    body(t, sa, sb);
-    body(t + 1, sb, sa);
+  int r = 0;
+  for (; r + 1 < rounds; r += 2) {
+    body(r, sa, sb);
+    body(r + 1, sb, sa);
   }
-  if (t < ntiles) body(t, sa, sb);
+  if (r < rounds) body(r, sa, sb);
+
+  if constexpr (KG == 2) {
+    // Merge group 1 into group 0: O = O0 2^(m0-m) + O1 2^(m1-m), m = max(m0, m1),
+    // the row sum l (the ones-row element) included.  Exchange slots are
+    // [element][query wave][lane] floats, conflict-free.
+    float* xs = reinterpret_cast<float*>(lds);
+    wait_lds_reads();
+    wg_barrier();  // the ring is idle
+    const int slot = qw * 64 + lane;
+    if (grp == 1) {
+      xs[48 * 128 + slot] = m_use;
+#pragma unroll
+      for (int d = 0; d < 3; ++d)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xs[(16 * d + e) * 128 + slot] = acc[d][e];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = xs[48 * 128 + slot];
+    const float m = fmaxf(m_use, m1);
+    const float s0 = __builtin_amdgcn_exp2f(m_use - m), s1 = __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+    for (int d = 0; d < 3; ++d)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[d][e] = acc[d][e] * s0 + xs[(16 * d + e) * 128 + slot] * s1;
+  }
 
   // ---- normalise and store: acc[d][4g + r] is dim 32d + 8g + 4hf + r of query ln;
   // the row sum l (dim 80) is acc[2][8] in the lanes with hf == 0.
@@ -398,26 +450,33 @@ __global__ void __launch_bounds__(256) attention_kernel(
   }
 }
 
-hipError_t launch_attention(const uint16_t* qkv, const int32_t* cu_seqlens, const int32_t* pos_thw,
-                            const int32_t* order, const int32_t* tile_start,
-                            const int32_t* ktile_start, int32_t n_img, int32_t max_qtiles,
-                            int32_t max_ktiles, int32_t heads, int32_t n_pos, int32_t axis_code,
-                            const float2* rope_cs, float q_scale_log2, uint16_t* qpk, uint16_t* kv,
-                            void* out, bool out_f32, hipStream_t s) {
-  hipLaunchKernelGGL(attn_pack_kernel, dim3(max_ktiles, heads), dim3(320), 0, s, qkv, cu_seqlens,
-                     pos_thw, ktile_start, n_img, heads, n_pos, rope_cs, axis_code, q_scale_log2,
-                     qpk, kv);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const size_t lds = size_t(NST) * STAGE_BYTES;
+template <int KG>
+static hipError_t launch_attention_kernel(const uint16_t* qpk, const uint16_t* kv,
+                                          const int4* qdesc, int32_t max_qtiles, int32_t heads,
+                                          void* out, bool out_f32, hipStream_t s) {
+  const size_t lds = size_t(NST) * KG * STAGE_BYTES;
+  auto kern = attention_kernel<KG>;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(attention_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-      int(lds));
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (attr != hipSuccess) return attr;
   const int64_t blocks = int64_t(max_qtiles) * heads;
-  hipLaunchKernelGGL(attention_kernel, dim3(unsigned(blocks)), dim3(256), lds, s, qpk, kv,
-                     cu_seqlens, order, tile_start, ktile_start, n_img, heads, out, out_f32 ? 1 : 0);
+  hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(256), lds, s, qpk, kv, qdesc, heads, out,
+                     out_f32 ? 1 : 0);
   return hipGetLastError();
+}
+
+hipError_t launch_attention(const uint16_t* qkv, const int32_t* pos_thw, const int4* qdesc,
+                            const int2* kdesc, int32_t max_qtiles, int32_t max_ktiles,
+                            int32_t heads, int32_t n_pos, int32_t axis_code, const float2* rope_cs,
+                            float q_scale_log2, int32_t key_groups, uint16_t* qpk, uint16_t* kv,
+                            void* out, bool out_f32, hipStream_t s) {
+  hipLaunchKernelGGL(attn_pack_kernel, dim3(max_ktiles, heads), dim3(320), 0, s, qkv, pos_thw,
+                     kdesc, heads, n_pos, rope_cs, axis_code, q_scale_log2, qpk, kv);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (key_groups == 2)
+    return launch_attention_kernel<2>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, s);
+  return launch_attention_kernel<1>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, s);
 }
 
 }  // namespace vt

@@ -6,10 +6,14 @@
 // token tile, so each lane ends with one token and 4 runs of 4 consecutive
 // output features: epilogue stores are 8-byte (bf16) or 16-byte (fp32).
 //
-// Workgroup: 256 threads = 4 wavefronts in a 2x2 grid over a BM x BN tile,
-// K stepped by 64.  Tiles go global -> registers -> LDS (rows padded by 16
-// bytes so that the 16-byte fragment reads of 16 consecutive rows hit
-// distinct banks), double buffered, one barrier per K step.
+// Two kernels.  gemm_dl_kernel (K a multiple of 32, every GEMM of the
+// blocks and the projector) copies tiles global -> LDS directly; it is
+// described where it is defined.  gemm_kernel handles any K (the patch
+// embedding, K = 1176): 256 threads = 4 wavefronts in a 2x2 grid over a
+// BM x BN tile, K stepped by 64, tiles staged global -> registers -> LDS
+// (rows padded by 16 bytes so that the 16-byte fragment reads of 16
+// consecutive rows hit distinct banks), double buffered, one barrier per
+// K step.
 //
 // Epilogues (the bias/GELU/residual work of the blocks and the projector,
 // MiniMax-M3-Vision README Architecture table): bf16 out, GELU(tanh|erf) bf16
@@ -202,16 +206,18 @@ __device__ __forceinline__ void xcd_group_tile(int tiles_m, int tiles_n, int* tm
 __device__ __forceinline__ int swz4(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 
 // GWM x GWN wavefronts; each owns a (BM/GWM) x (BN/GWN) block of C.
-// K is consumed in steps of 32 through a ring of 4 LDS stages: three steps
-// are in flight while one is multiplied, one workgroup barrier per step.
-template <int BM, int BN, int GWM, int GWN, int EPI, bool SPLIT>
+// K is consumed in steps of 32 through a ring of NST LDS stages: NST - 1
+// steps are in flight while one is multiplied, one workgroup barrier per
+// step.  The finished tile is staged through the (then idle) ring so that
+// every global store writes whole 16-byte pieces of contiguous rows.
+template <int BM, int BN, int GWM, int GWN, int NST, int EPI, bool SPLIT>
 __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
     const uint16_t* __restrict__ A, int M, int K, const uint16_t* __restrict__ B, int N,
     const uint16_t* __restrict__ bias, void* __restrict__ out, float* __restrict__ part, int kper) {
   constexpr int NW = GWM * GWN;
   constexpr int WM = BM / GWM, WN = BN / GWN;
   constexpr int TB = WM / 32, FB = WN / 32;
-  constexpr int BK = 32, NST = 4;
+  constexpr int BK = 32;
   constexpr int LA = BM / (16 * NW), LB = BN / (16 * NW);  // copies per lane per K step
   constexpr int CP = LA + LB;
   constexpr int A_BYTES = BM * 64, STAGE = (BM + BN) * 64;
@@ -310,19 +316,19 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * FB * TB - 2 * (FB + TB), 0);
-    if (it + NST - 1 < nk) wait_vmcnt<CP>();
+    if (it + NST - 1 < nk) wait_vmcnt<(NST - 3) * CP>();  // step it+2 has landed
     else wait_vmcnt<0>();
     wait_lds_reads();
-    __builtin_amdgcn_s_barrier();
+    wg_barrier();
   };
 
 #pragma unroll
   for (int i = 0; i < NST - 1; ++i)
     if (i < nk) issue(i);
   if (nk > 0) {
-    if (NST - 1 < nk) wait_vmcnt<CP>();  // steps 0 and 1 landed, step 2 may be in flight
+    if (NST - 1 < nk) wait_vmcnt<(NST - 3) * CP>();  // steps 0 and 1 landed
     else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
+    wg_barrier();
     Frags F0, F1;
     load_frags(F0, 0);
     int it = 0;
@@ -333,28 +339,82 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
     if (it < nk) step(it, F0, F1);
   }
 
+  // ---- epilogue.  acc[f][t][4g + r] = C[token][feature] with token =
+  // wm*WM + 32t + lane%32 and feature = wn*WN + 32f + 8g + 4(lane/32) + r.
+  // Bias and the activation are applied in registers; the tile is written
+  // row-major into LDS (16-byte chunk c of row r at chunk c ^ (r % 16), which
+  // spreads the 32 rows one write instruction touches over all banks), then
+  // every thread moves whole 16-byte chunks to global memory, PASS_ROWS token
+  // rows at a time.  The ring is idle: the last step waited for every copy
+  // and, at its barrier, for every wave's fragment reads.
+  constexpr bool F32OUT = SPLIT || EPI == kEpiResid || EPI == kEpiF32;
+  constexpr int ESZ = F32OUT ? 4 : 2;
+  constexpr int ROWB = BN * ESZ, CHUNKS = ROWB / 16, EPC = 16 / ESZ;
+  constexpr int RING = NST * STAGE;
+  constexpr int PASS_ROWS = (BM * ROWB <= RING) ? BM : RING / ROWB;
+  static_assert(CHUNKS >= 16 && PASS_ROWS % WM == 0, "epilogue staging");
+  char* cs = reinterpret_cast<char*>(lds);
 #pragma unroll
-  for (int t = 0; t < TB; ++t) {
-    const int tok = m0 + wm * WM + t * 32 + fr;
-    if (tok >= M) continue;
+  for (int pass = 0; pass < BM / PASS_ROWS; ++pass) {
+    if (pass > 0) __syncthreads();  // the previous pass's reads are done
+    if (wm * WM / PASS_ROWS == pass) {
 #pragma unroll
-    for (int f = 0; f < FB; ++f) {
+      for (int t = 0; t < TB; ++t) {
+        const int r = wm * WM + 32 * t + fr - pass * PASS_ROWS;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = n0 + wn * WN + f * 32 + g * 8 + h * 4;
-        if (col >= N) continue;
-        float v0 = acc[f][t][4 * g + 0], v1 = acc[f][t][4 * g + 1];
-        float v2 = acc[f][t][4 * g + 2], v3 = acc[f][t][4 * g + 3];
-        if constexpr (SPLIT) {
-          *reinterpret_cast<float4*>(part + (int64_t(blockIdx.y) * M + tok) * N + col) =
-              make_float4(v0, v1, v2, v3);
-        } else {
-          if (bias) {
-            const uint2 bb = *reinterpret_cast<const uint2*>(bias + col);
-            v0 += bflo(bb.x); v1 += bfhi(bb.x); v2 += bflo(bb.y); v3 += bfhi(bb.y);
+        for (int f = 0; f < FB; ++f) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = n0 + wn * WN + 32 * f + 8 * g + 4 * h;
+            float v0 = acc[f][t][4 * g + 0], v1 = acc[f][t][4 * g + 1];
+            float v2 = acc[f][t][4 * g + 2], v3 = acc[f][t][4 * g + 3];
+            const int c = (wn * WN + 32 * f + 8 * g) / EPC;  // logical chunk of feature 8g
+            if constexpr (F32OUT) {
+              // 4 fp32 = one chunk; h selects the next chunk
+              const int pc = (c + h) ^ (r & 15);
+              *reinterpret_cast<float4*>(cs + r * ROWB + pc * 16) = make_float4(v0, v1, v2, v3);
+            } else {
+              if (bias) {
+                const uint2 bb = *reinterpret_cast<const uint2*>(bias + min(col, N - 4));
+                v0 += bflo(bb.x); v1 += bfhi(bb.x); v2 += bflo(bb.y); v3 += bfhi(bb.y);
+              }
+              if constexpr (EPI == kEpiGeluTanh) {
+                v0 = gelu_tanh(v0); v1 = gelu_tanh(v1); v2 = gelu_tanh(v2); v3 = gelu_tanh(v3);
+              } else if constexpr (EPI == kEpiGeluErf) {
+                v0 = gelu_erf(v0); v1 = gelu_erf(v1); v2 = gelu_erf(v2); v3 = gelu_erf(v3);
+              }
+              const int pc = c ^ (r & 15);
+              *reinterpret_cast<uint2*>(cs + r * ROWB + pc * 16 + 8 * h) =
+                  make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+            }
           }
-          epi_store4<EPI>(out, int64_t(tok) * N + col, v0, v1, v2, v3);
         }
+      }
+    }
+    __syncthreads();
+    constexpr int TOTAL = PASS_ROWS * CHUNKS;
+#pragma unroll
+    for (int i = tid; i < TOTAL; i += 64 * NW) {
+      const int r = i / CHUNKS, c = i % CHUNKS;
+      const int tok = m0 + pass * PASS_ROWS + r, col = n0 + c * EPC;
+      if (tok >= M || col >= N) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(cs + r * ROWB + ((c ^ (r & 15)) * 16));
+      if constexpr (SPLIT) {
+        *reinterpret_cast<uint4*>(part + (int64_t(blockIdx.y) * M + tok) * N + col) = v;
+      } else if constexpr (EPI == kEpiResid || EPI == kEpiF32) {
+        float4 a = __builtin_bit_cast(float4, v);
+        if (bias) {
+          const uint2 bb = *reinterpret_cast<const uint2*>(bias + col);
+          a.x += bflo(bb.x); a.y += bfhi(bb.x); a.z += bflo(bb.y); a.w += bfhi(bb.y);
+        }
+        float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + int64_t(tok) * N + col);
+        if constexpr (EPI == kEpiResid) {
+          const float4 r0 = *o;
+          a.x += r0.x; a.y += r0.y; a.z += r0.z; a.w += r0.w;
+        }
+        *o = a;
+      } else {
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + int64_t(tok) * N + col) = v;
       }
     }
   }
@@ -414,15 +474,15 @@ template <int BM, int BN, int EPI, bool SPLIT>
 static hipError_t launch_tile(const uint16_t* A, int M, int K, const uint16_t* B, int N,
                               const uint16_t* bias, void* out, float* part, const GemmPlan& p,
                               hipStream_t s) {
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (K % 32 == 0 && (!SPLIT || p.kper % 32 == 0)) {
-    // 256 x 256 tiles: 8 wavefronts (2 per SIMD, 128 x 64 each); 128 x 128: 4 (64 x 64 each)
-    constexpr int GWM = 2, GWN = (BM == 256) ? 4 : 2;
-    const size_t lds = size_t(4) * (BM + BN) * 64;
-    auto kern = gemm_dl_kernel<BM, BN, GWM, GWN, EPI, SPLIT>;
+    // 8 wavefronts (2 per SIMD): 128 x 64 each in a 256 x 256 tile, 32 x 64 in a 128 x 128 one
+    constexpr int GWM = (BM == 256) ? 2 : 4, GWN = (BM == 256) ? 4 : 2, NST = 4;
+    const size_t lds = size_t(NST) * (BM + BN) * 64;
+    auto kern = gemm_dl_kernel<BM, BN, GWM, GWN, NST, EPI, SPLIT>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (attr != hipSuccess) return attr;
-    const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     hipLaunchKernelGGL(kern, dim3(tiles, SPLIT ? p.splits : 1), dim3(64 * GWM * GWN), lds, s, A, M,
                        K, B, N, bias, out, part, p.kper);
     return hipGetLastError();
@@ -433,7 +493,6 @@ static hipError_t launch_tile(const uint16_t* A, int M, int K, const uint16_t* B
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (attr != hipSuccess) return attr;
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   hipLaunchKernelGGL(kern, dim3(tiles, SPLIT ? p.splits : 1), dim3(256), lds, s, A, M, K, B, N,
                      bias, out, part, p.kper);
   return hipGetLastError();

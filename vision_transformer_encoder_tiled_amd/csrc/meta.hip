@@ -97,13 +97,15 @@ __device__ void block_scan(int n, F f, int32_t* out, int32_t* part) {
 // q-tiles are dispatched before the cheap ones).  tile_start is the
 // exclusive prefix sum of ceil(n/q_tile) in rank order, with
 // tile_start[n_img] = the total number of q-tiles; ktile_start the prefix
-// sum of ceil(n/k_tile) in image order.
-__global__ void __launch_bounds__(1024) attn_schedule_kernel(const int32_t* __restrict__ cu,
-                                                             int32_t n_img, int32_t q_tile,
-                                                             int32_t k_tile,
-                                                             int32_t* __restrict__ order,
-                                                             int32_t* __restrict__ tile_start,
-                                                             int32_t* __restrict__ ktile_start) {
+// sum of ceil(n/k_tile) in image order.  From these, one descriptor per
+// q-tile slot (qdesc, max_qtiles entries) and per key-tile slot (kdesc,
+// max_ktiles entries), so that each attention / pack workgroup finds its
+// work with a single load; slots past the totals are marked unused (-1).
+__global__ void __launch_bounds__(1024) attn_schedule_kernel(
+    const int32_t* __restrict__ cu, int32_t n_img, int32_t q_tile, int32_t k_tile,
+    int32_t max_qtiles, int32_t max_ktiles, int32_t* __restrict__ order,
+    int32_t* __restrict__ tile_start, int32_t* __restrict__ ktile_start,
+    int4* __restrict__ qdesc, int2* __restrict__ kdesc) {
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x, nt = blockDim.x;
   for (int i = tid; i < n_img; i += nt) {
@@ -120,14 +122,42 @@ __global__ void __launch_bounds__(1024) attn_schedule_kernel(const int32_t* __re
              tile_start, part);
   block_scan(n_img, [&](int i) { return (cu[i + 1] - cu[i] + k_tile - 1) / k_tile; },
              ktile_start, part);
+  const int nq = tile_start[n_img], nk = ktile_start[n_img];
+  for (int t = tid; t < max_qtiles; t += nt) {
+    int4 d = make_int4(-1, 0, 0, 0);
+    if (t < nq) {
+      int lo = 0, hi = n_img - 1;  // largest rank r with tile_start[r] <= t
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tile_start[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      const int i = order[lo];
+      d = make_int4(cu[i] + (t - tile_start[lo]) * q_tile, cu[i], cu[i + 1], ktile_start[i]);
+    }
+    qdesc[t] = d;
+  }
+  for (int T = tid; T < max_ktiles; T += nt) {
+    int2 d = make_int2(-1, -1);
+    if (T < nk) {
+      int lo = 0, hi = n_img - 1;  // image of key tile T
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (ktile_start[mid] <= T) lo = mid; else hi = mid - 1;
+      }
+      d = make_int2(cu[lo] + (T - ktile_start[lo]) * k_tile, cu[lo + 1]);
+    }
+    kdesc[T] = d;
+  }
 }
 
 hipError_t launch_attn_schedule(const int32_t* cu_seqlens, int32_t n_img, int32_t q_tile,
-                                int32_t k_tile, int32_t* order, int32_t* tile_start,
-                                int32_t* ktile_start, hipStream_t s) {
+                                int32_t k_tile, int32_t max_qtiles, int32_t max_ktiles,
+                                int32_t* order, int32_t* tile_start, int32_t* ktile_start,
+                                int4* qdesc, int2* kdesc, hipStream_t s) {
+  // block_scan's serial step runs over the thread count: keep it near n_img.
   const int threads = n_img >= 1024 ? 1024 : (n_img >= 256 ? 256 : 64);
   hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(threads), 0, s, cu_seqlens, n_img, q_tile,
-                     k_tile, order, tile_start, ktile_start);
+                     k_tile, max_qtiles, max_ktiles, order, tile_start, ktile_start, qdesc, kdesc);
   return hipGetLastError();
 }
 

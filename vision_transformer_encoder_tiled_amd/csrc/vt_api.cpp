@@ -127,8 +127,10 @@ struct BlockBufs {
   int32_t* order;
   int32_t* tile_start;
   int32_t* ktile_start;
+  int4* qdesc;     // per q-tile slot (max_q_tiles at 64 queries)
+  int2* kdesc;     // per key-tile slot
   uint16_t* qpk;   // [N, heads, 80] fp16 rotated, scaled Q
-  uint16_t* kv;    // heads x max_ktiles K/V tile images (fp16)
+  uint16_t* kv;    // max_ktiles x heads K/V tile images (fp16)
   float2* rope;
   uint16_t* xn;    // [N, d] LayerNorm output
   uint16_t* act;   // [N, max(4d, mlp)]: qkv [N,3d] then attn [N,d]; later the MLP hidden [N, mlp]
@@ -148,10 +150,16 @@ int32_t max_k_tiles(int64_t N, int32_t n_img) {
   return int32_t((N + vt::kAttnKTile - 1) / vt::kAttnKTile + n_img);
 }
 
+int32_t max_q_tiles(int64_t N, int32_t n_img, int32_t q_tile) {
+  return int32_t((N + q_tile - 1) / q_tile + n_img);
+}
+
 void carve_block(Carver& c, const Dims& D, int32_t n_pos, BlockBufs* b) {
   b->order = c.take<int32_t>(D.n_img);
   b->tile_start = c.take<int32_t>(D.n_img + 1);
   b->ktile_start = c.take<int32_t>(D.n_img + 1);
+  b->qdesc = c.take<int4>(max_q_tiles(D.N, D.n_img, vt::attn_q_tile(2)));
+  b->kdesc = c.take<int2>(max_k_tiles(D.N, D.n_img));
   b->qpk = c.take<uint16_t>(size_t(D.N) * D.d);
   b->kv = reinterpret_cast<uint16_t*>(
       c.take<char>(size_t(D.heads) * max_k_tiles(D.N, D.n_img) * vt::kAttnTileBytes));
@@ -252,18 +260,24 @@ vt_status launch_meta(const vt_grid_thw* grid, int32_t n_img, int64_t total, int
   return VT_OK;
 }
 
+// Key groups of the attention kernel: two (64-query workgroups) when the
+// 128-query tiles would not give every CU a workgroup, else one.  A function
+// of the call's sizes only, so the schedule and the launch agree.
+int32_t attn_key_groups(int64_t N, int32_t n_img, int32_t heads) {
+  const int64_t tiles128 = (N + 127) / 128 + n_img;
+  return tiles128 * heads <= 256 ? 2 : 1;
+}
+
 // The per-call attention prologue: LPT schedule and RoPE cos/sin table.
-vt_status attn_prologue(const vt_config* cfg, const int32_t* cu, int32_t n_img, int32_t n_pos,
-                        const BlockBufs& b, int32_t* axis_code, hipStream_t s) {
-  VT_TRY_HIP(vt::launch_attn_schedule(cu, n_img, vt::kAttnQTile, vt::kAttnKTile, b.order,
-                                      b.tile_start, b.ktile_start, s));
+vt_status attn_prologue(const vt_config* cfg, const int32_t* cu, int32_t n_img, int64_t N,
+                        int32_t n_pos, const BlockBufs& b, int32_t* axis_code, hipStream_t s) {
+  const int q_tile = vt::attn_q_tile(attn_key_groups(N, n_img, cfg->heads));
+  VT_TRY_HIP(vt::launch_attn_schedule(cu, n_img, q_tile, vt::kAttnKTile,
+                                      max_q_tiles(N, n_img, q_tile), max_k_tiles(N, n_img),
+                                      b.order, b.tile_start, b.ktile_start, b.qdesc, b.kdesc, s));
   const vt::RopeFreq f = rope_freq(cfg, axis_code);
   VT_TRY_HIP(vt::launch_rope_table(f, n_pos, b.rope, s));
   return VT_OK;
-}
-
-int32_t max_q_tiles(int64_t N, int32_t n_img) {
-  return int32_t((N + vt::kAttnQTile - 1) / vt::kAttnQTile + n_img);
 }
 
 float q_scale_log2(const vt_config* cfg) {
@@ -274,9 +288,10 @@ vt_status run_attention(const vt_config* cfg, const uint16_t* qkv, const int32_t
                         const int32_t* pos, int32_t n_img, int64_t N, int32_t n_pos,
                         int32_t axis_code, const BlockBufs& b, void* out, bool f32,
                         hipStream_t s) {
-  VT_TRY_HIP(vt::launch_attention(qkv, cu, pos, b.order, b.tile_start, b.ktile_start, n_img,
-                                  max_q_tiles(N, n_img), max_k_tiles(N, n_img), cfg->heads, n_pos,
-                                  axis_code, b.rope, q_scale_log2(cfg), b.qpk, b.kv, out, f32, s));
+  const int32_t kg = attn_key_groups(N, n_img, cfg->heads);
+  VT_TRY_HIP(vt::launch_attention(qkv, pos, b.qdesc, b.kdesc, max_q_tiles(N, n_img, vt::attn_q_tile(kg)),
+                                  max_k_tiles(N, n_img), cfg->heads, n_pos, axis_code, b.rope,
+                                  q_scale_log2(cfg), kg, b.qpk, b.kv, out, f32, s));
   return VT_OK;
 }
 
@@ -496,7 +511,7 @@ VT_API vt_status vt_attention_varlen(const vt_config* cfg, const uint16_t* qkv,
   BlockBufs b;
   carve_block(c, dims_of(cfg, total_tokens, n_img), max_seqlen, &b);
   int32_t axis_code = 0;
-  if ((st = attn_prologue(cfg, cu_seqlens, n_img, max_seqlen, b, &axis_code, s)) != VT_OK) return st;
+  if ((st = attn_prologue(cfg, cu_seqlens, n_img, total_tokens, max_seqlen, b, &axis_code, s)) != VT_OK) return st;
   return run_attention(cfg, qkv, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen, axis_code, b,
                        out, out_dtype == VT_FP32, s);
 }
@@ -516,7 +531,7 @@ VT_API vt_status vt_block_forward(const vt_config* cfg, float* resid, const vt_b
   BlockBufs b;
   carve_block(c, dims_of(cfg, total_tokens, n_img), max_seqlen, &b);
   int32_t axis_code = 0;
-  if ((st = attn_prologue(cfg, cu_seqlens, n_img, max_seqlen, b, &axis_code, s)) != VT_OK) return st;
+  if ((st = attn_prologue(cfg, cu_seqlens, n_img, total_tokens, max_seqlen, b, &axis_code, s)) != VT_OK) return st;
   return run_block(cfg, resid, w, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen, axis_code, b, s);
 }
 
@@ -585,7 +600,7 @@ VT_API vt_status vt_tower_forward(const vt_config* cfg, const uint16_t* pixels,
   carve_tower(c, dims_of(cfg, N, n_img), gi.max_hw, &t);
   if ((st = launch_meta(grid, n_img, N, t.cu, t.info, t.pos, t.ridx, t.tok_img, s)) != VT_OK) return st;
   int32_t axis_code = 0;
-  if ((st = attn_prologue(cfg, t.cu, n_img, gi.max_hw, t.blk, &axis_code, s)) != VT_OK) return st;
+  if ((st = attn_prologue(cfg, t.cu, n_img, N, gi.max_hw, t.blk, &axis_code, s)) != VT_OK) return st;
   VT_TRY_HIP(vt::launch_patchify(pixels, t.info, t.cu, t.tok_img, int32_t(N), t.X, s));
   VT_TRY_HIP(vt::launch_gemm(t.X, int(N), 1176, w->w_patch, cfg->hidden, w->b_patch, vt::kEpiF32, t.R,
                              t.blk.gemm_ws, s));

@@ -84,6 +84,16 @@ __device__ __forceinline__ void wait_lds_reads() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Workgroup barrier without a memory fence or waits.  The compiler does not
+// treat s_barrier as a memory operation, so empty asm statements with a
+// memory clobber on both sides stop it from moving LDS accesses across; the
+// waits the barrier needs are issued explicitly before it.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // LDS byte offset of a pointer into __shared__ memory.
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));

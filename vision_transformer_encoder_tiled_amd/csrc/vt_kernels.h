@@ -27,9 +27,13 @@ hipError_t launch_cu_last(int32_t* cu_seqlens, int32_t n_img, int32_t total, hip
 // Attention work schedule: images ordered by token count (largest first),
 // tile_start[r] = first q-tile of the image of rank r; ktile_start[i] = first
 // 64-key tile of image i (image order) in the packed K/V tile images.
+// qdesc[t] = (first query, image begin, image end, first key tile of the
+// image) of q-tile slot t < max_qtiles; kdesc[T] = (first token, image end)
+// of key-tile slot T < max_ktiles; unused slots have .x = -1.
 hipError_t launch_attn_schedule(const int32_t* cu_seqlens, int32_t n_img, int32_t q_tile,
-                                int32_t k_tile, int32_t* order, int32_t* tile_start,
-                                int32_t* ktile_start, hipStream_t s);
+                                int32_t k_tile, int32_t max_qtiles, int32_t max_ktiles,
+                                int32_t* order, int32_t* tile_start, int32_t* ktile_start,
+                                int4* qdesc, int2* kdesc, hipStream_t s);
 // RoPE table cs[pos][j] = (cos, sin)(pos * inv_freq[j]), pos < n_pos, j < 40.
 struct RopeFreq { double inv_freq[64]; int32_t pairs; };
 hipError_t launch_rope_table(const RopeFreq& f, int32_t n_pos, float2* cs, hipStream_t s);
@@ -60,15 +64,18 @@ hipError_t launch_gemm(const uint16_t* A, int M, int K, const uint16_t* B, int N
                        const uint16_t* bias, int epi, void* out, void* ws, hipStream_t s);
 
 // ---- attention (attention.hip)
-constexpr int kAttnQTile = 128;        // queries per workgroup
 constexpr int kAttnKTile = 64;         // keys per tile
 constexpr int kAttnTileBytes = 24576;  // one (head, key tile) image: K [64][88] + V^T [81][72] fp16 + pad
-// qpk: [N, heads, 80] fp16 rotated+scaled Q; kv: heads x max_ktiles tile images.
-hipError_t launch_attention(const uint16_t* qkv, const int32_t* cu_seqlens, const int32_t* pos_thw,
-                            const int32_t* order, const int32_t* tile_start,
-                            const int32_t* ktile_start, int32_t n_img, int32_t max_qtiles,
-                            int32_t max_ktiles, int32_t heads, int32_t n_pos, int32_t axis_code,
-                            const float2* rope_cs, float q_scale_log2, uint16_t* qpk, uint16_t* kv,
+// Queries per workgroup: 128 with one key group, 64 with two (the kernel
+// splits each image's key tiles between two groups of 2 wavefronts).
+inline int attn_q_tile(int key_groups) { return key_groups == 2 ? 64 : 128; }
+// qpk: [N, heads, 80] fp16 rotated+scaled Q; kv: max_ktiles x heads tile
+// images.  qdesc / kdesc come from launch_attn_schedule with
+// attn_q_tile(key_groups) and the same max_qtiles / max_ktiles.
+hipError_t launch_attention(const uint16_t* qkv, const int32_t* pos_thw, const int4* qdesc,
+                            const int2* kdesc, int32_t max_qtiles, int32_t max_ktiles,
+                            int32_t heads, int32_t n_pos, int32_t axis_code, const float2* rope_cs,
+                            float q_scale_log2, int32_t key_groups, uint16_t* qpk, uint16_t* kv,
                             void* out, bool out_f32, hipStream_t s);
 
 }  // namespace vt
