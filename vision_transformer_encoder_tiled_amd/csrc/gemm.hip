@@ -420,22 +420,28 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
   }
 }
 
-// out = epilogue(sum_z part[z] + bias), summed in split order.
+// out = epilogue(sum_z part[z] + bias), summed in split order.  The loads of
+// up to 4 partials are issued together (indices clamped to the last split,
+// so they stay in bounds) before the valid ones are added in order.
 template <int EPI>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part,
                                                             int splits, int M, int N,
                                                             const uint16_t* __restrict__ bias,
                                                             void* __restrict__ out) {
   const int64_t n4 = int64_t(M) * N / 4;
-  const int64_t plane = int64_t(M) * N;
+  const float4* p4 = reinterpret_cast<const float4*>(part);
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n4;
        i += int64_t(gridDim.x) * blockDim.x) {
-    const int64_t off = i * 4;
-    float4 s = *reinterpret_cast<const float4*>(part + off);
-    for (int z = 1; z < splits; ++z) {
-      const float4 p = *reinterpret_cast<const float4*>(part + z * plane + off);
-      s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+    float4 s = p4[i];
+    for (int z0 = 1; z0 < splits; z0 += 4) {
+      float4 q[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) q[j] = p4[int64_t(min(z0 + j, splits - 1)) * n4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (z0 + j < splits) { s.x += q[j].x; s.y += q[j].y; s.z += q[j].z; s.w += q[j].w; }
     }
+    const int64_t off = i * 4;
     if (bias) {
       const int col = int(off % N);
       const uint2 bb = *reinterpret_cast<const uint2*>(bias + col);
@@ -454,8 +460,10 @@ GemmPlan plan_gemm(int M, int N, int K) {
   p.bn = 128;
   const int t128 = cdiv(M, 128) * cdiv(N, 128);
   if (t128 >= 200) return p;
-  int splits = cdiv(256, t128);
-  const int max_splits = K / 512;
+  // Split K so that the workgroups fill the 256 CUs once (one round), each
+  // split keeping at least 384 of K.
+  int splits = 256 / t128;
+  const int max_splits = K / 384;
   if (splits > max_splits) splits = max_splits;
   if (splits > 1) {
     p.splits = splits;
@@ -527,6 +535,14 @@ hipError_t launch_gemm(const uint16_t* A, int M, int K, const uint16_t* B, int N
     case kEpiF32: return launch_epi<kEpiF32>(A, M, K, B, N, bias, out, ws, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_partials(const uint16_t* A, int M, int K, const uint16_t* B, int N, void* ws,
+                                hipStream_t s) {
+  const GemmPlan p = plan_gemm(M, N, K);
+  if (p.splits < 2) return hipErrorInvalidValue;
+  return launch_tile<128, 128, kEpiResid, true>(A, M, K, B, N, nullptr, nullptr,
+                                                 reinterpret_cast<float*>(ws), p, s);
 }
 
 }  // namespace vt

@@ -1,4 +1,5 @@
-// LayerNorm over fp32 rows -> bf16 rows, one 64-lane wavefront per row.
+// LayerNorm over fp32 rows -> bf16 rows, one 64-lane wavefront per row, and
+// the same LayerNorm fused behind a split-K residual update.
 // Textbook form: biased variance over the row, eps inside the square root,
 // then gamma/beta (pre-LN blocks of the tower; eps 1e-6).  Two passes over
 // the row held in registers: mean, then the centred sum of squares, each
@@ -8,23 +9,15 @@
 
 namespace vt {
 
-template <int NV>  // float4 vectors per lane: width = 256 * NV
-__global__ void __launch_bounds__(256) layer_norm_kernel(const float* __restrict__ x, int32_t rows,
-                                                         const uint16_t* __restrict__ g,
-                                                         const uint16_t* __restrict__ b, float eps,
-                                                         uint16_t* __restrict__ out) {
+// LayerNorm of one row held by a wavefront: v[i] = elements 4(lane + 64 i) .. +3.
+template <int NV>
+__device__ __forceinline__ void ln_row(float4 (&v)[NV], int lane, const uint16_t* __restrict__ g,
+                                       const uint16_t* __restrict__ b, float eps,
+                                       uint16_t* __restrict__ out_row) {
   constexpr int W = 256 * NV;
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const float4* xr = reinterpret_cast<const float4*>(x + int64_t(row) * W);
-  float4 v[NV];
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    v[i] = xr[lane + 64 * i];
-    s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
-  }
+  for (int i = 0; i < NV; ++i) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
   const float mean = wave_sum(s) * (1.0f / W);
   float q = 0.f;
 #pragma unroll
@@ -36,7 +29,7 @@ __global__ void __launch_bounds__(256) layer_norm_kernel(const float* __restrict
   const float rstd = 1.0f / sqrtf(var + eps);
   const uint2* g2 = reinterpret_cast<const uint2*>(g);
   const uint2* b2 = reinterpret_cast<const uint2*>(b);
-  uint2* o2 = reinterpret_cast<uint2*>(out + int64_t(row) * W);
+  uint2* o2 = reinterpret_cast<uint2*>(out_row);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = lane + 64 * i;
@@ -49,6 +42,81 @@ __global__ void __launch_bounds__(256) layer_norm_kernel(const float* __restrict
   }
 }
 
+template <int NV>  // float4 vectors per lane: width = 256 * NV
+__global__ void __launch_bounds__(256) layer_norm_kernel(const float* __restrict__ x, int32_t rows,
+                                                         const uint16_t* __restrict__ g,
+                                                         const uint16_t* __restrict__ b, float eps,
+                                                         uint16_t* __restrict__ out) {
+  constexpr int W = 256 * NV;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float4* xr = reinterpret_cast<const float4*>(x + int64_t(row) * W);
+  float4 v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = xr[lane + 64 * i];
+  ln_row<NV>(v, lane, g, b, eps, out + int64_t(row) * W);
+}
+
+// Split-K residual update fused with the next LayerNorm, one wavefront per
+// row: R += (sum over z in order of part[z]) + bias, exactly the arithmetic
+// of the split-K reduction with the residual epilogue; then out = LN(R).
+template <int NV>
+__global__ void __launch_bounds__(256) resid_ln_kernel(const float* __restrict__ part,
+                                                       int32_t splits, int32_t rows,
+                                                       const uint16_t* __restrict__ bias,
+                                                       float* __restrict__ R,
+                                                       const uint16_t* __restrict__ g,
+                                                       const uint16_t* __restrict__ b, float eps,
+                                                       uint16_t* __restrict__ out) {
+  constexpr int W = 256 * NV;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int64_t plane4 = int64_t(rows) * W / 4;
+  float4* rr = reinterpret_cast<float4*>(R + int64_t(row) * W);
+  const float4* p0 = reinterpret_cast<const float4*>(part + int64_t(row) * W);
+  float4 v[NV], r[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    v[i] = p0[lane + 64 * i];
+    r[i] = rr[lane + 64 * i];
+  }
+  // Partials 1.. in groups of 4: the loads of a group are issued together
+  // (indices clamped to the last split, so they stay in bounds), then the
+  // valid ones are added in split order.
+  for (int z0 = 1; z0 < splits; z0 += 4) {
+    float4 q[4][NV];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t zz = min(z0 + j, splits - 1);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) q[j][i] = p0[zz * plane4 + lane + 64 * i];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (z0 + j < splits) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          v[i].x += q[j][i].x; v[i].y += q[j][i].y; v[i].z += q[j][i].z; v[i].w += q[j][i].w;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    if (bias) {
+      const uint2 bb = reinterpret_cast<const uint2*>(bias)[c];
+      v[i].x += bflo(bb.x); v[i].y += bfhi(bb.x); v[i].z += bflo(bb.y); v[i].w += bfhi(bb.y);
+    }
+    r[i].x += v[i].x; r[i].y += v[i].y; r[i].z += v[i].z; r[i].w += v[i].w;
+    rr[c] = r[i];
+    v[i] = r[i];
+  }
+  ln_row<NV>(v, lane, g, b, eps, out + int64_t(row) * W);
+}
+
 hipError_t launch_layer_norm(const float* x, int32_t rows, int32_t width, const uint16_t* g,
                              const uint16_t* b, float eps, uint16_t* out, hipStream_t s) {
   const dim3 grid((rows + 3) / 4), block(256);
@@ -59,6 +127,25 @@ hipError_t launch_layer_norm(const float* x, int32_t rows, int32_t width, const 
     VT_LN_CASE(7) VT_LN_CASE(8) VT_LN_CASE(9) VT_LN_CASE(10) VT_LN_CASE(11) VT_LN_CASE(12)
     VT_LN_CASE(13) VT_LN_CASE(14) VT_LN_CASE(15) VT_LN_CASE(16)
 #undef VT_LN_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_resid_ln(const float* part, int32_t splits, int32_t rows, int32_t width,
+                           const uint16_t* bias, float* R, const uint16_t* g, const uint16_t* b,
+                           float eps, uint16_t* out, hipStream_t s) {
+  const dim3 grid((rows + 3) / 4), block(256);
+  switch (width / 256) {
+#define VT_RLN_CASE(n)                                                                           \
+  case n:                                                                                        \
+    hipLaunchKernelGGL(resid_ln_kernel<n>, grid, block, 0, s, part, splits, rows, bias, R, g, b, \
+                       eps, out);                                                                \
+    break;
+    VT_RLN_CASE(1) VT_RLN_CASE(2) VT_RLN_CASE(3) VT_RLN_CASE(4) VT_RLN_CASE(5) VT_RLN_CASE(6)
+    VT_RLN_CASE(7) VT_RLN_CASE(8) VT_RLN_CASE(9) VT_RLN_CASE(10) VT_RLN_CASE(11) VT_RLN_CASE(12)
+    VT_RLN_CASE(13) VT_RLN_CASE(14) VT_RLN_CASE(15) VT_RLN_CASE(16)
+#undef VT_RLN_CASE
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -295,20 +295,42 @@ vt_status run_attention(const vt_config* cfg, const uint16_t* qkv, const int32_t
   return VT_OK;
 }
 
+// One block.  LN1 is skipped when the previous block already wrote LN1(R)
+// into xn (*xn_ready).  When a residual GEMM runs split-K, its reduction is
+// fused with the LayerNorm that follows it: LN2 of this block after O, LN1 of
+// the next block (next_ln1_g/b, when given) after FC2.
 vt_status run_block(const vt_config* cfg, float* R, const vt_block_weights* w, const int32_t* cu,
                     const int32_t* pos, int32_t n_img, int64_t N, int32_t n_pos, int32_t axis_code,
-                    const BlockBufs& b, hipStream_t s) {
+                    const BlockBufs& b, const uint16_t* next_ln1_g, const uint16_t* next_ln1_b,
+                    bool* xn_ready, hipStream_t s) {
   const int d = cfg->hidden, mlp = cfg->mlp, M = int(N);
   uint16_t* qkv = b.act;
   uint16_t* att = b.act + size_t(N) * 3 * d;
-  VT_TRY_HIP(vt::launch_layer_norm(R, M, d, w->ln1_g, w->ln1_b, cfg->ln_eps, b.xn, s));
+  if (!*xn_ready)
+    VT_TRY_HIP(vt::launch_layer_norm(R, M, d, w->ln1_g, w->ln1_b, cfg->ln_eps, b.xn, s));
   VT_TRY_HIP(vt::launch_gemm(b.xn, M, d, w->w_qkv, 3 * d, w->b_qkv, vt::kEpiBf16, qkv, b.gemm_ws, s));
   vt_status st = run_attention(cfg, qkv, cu, pos, n_img, N, n_pos, axis_code, b, att, false, s);
   if (st != VT_OK) return st;
-  VT_TRY_HIP(vt::launch_gemm(att, M, d, w->w_o, d, w->b_o, vt::kEpiResid, R, b.gemm_ws, s));
-  VT_TRY_HIP(vt::launch_layer_norm(R, M, d, w->ln2_g, w->ln2_b, cfg->ln_eps, b.xn, s));
+  const float* part = reinterpret_cast<const float*>(b.gemm_ws);
+  if (vt::plan_gemm(M, d, d).splits > 1) {
+    VT_TRY_HIP(vt::launch_gemm_partials(att, M, d, w->w_o, d, b.gemm_ws, s));
+    VT_TRY_HIP(vt::launch_resid_ln(part, vt::plan_gemm(M, d, d).splits, M, d, w->b_o, R, w->ln2_g,
+                                   w->ln2_b, cfg->ln_eps, b.xn, s));
+  } else {
+    VT_TRY_HIP(vt::launch_gemm(att, M, d, w->w_o, d, w->b_o, vt::kEpiResid, R, b.gemm_ws, s));
+    VT_TRY_HIP(vt::launch_layer_norm(R, M, d, w->ln2_g, w->ln2_b, cfg->ln_eps, b.xn, s));
+  }
   VT_TRY_HIP(vt::launch_gemm(b.xn, M, d, w->w_fc1, mlp, w->b_fc1, vt::kEpiGeluTanh, b.act, b.gemm_ws, s));
-  VT_TRY_HIP(vt::launch_gemm(b.act, M, mlp, w->w_fc2, d, w->b_fc2, vt::kEpiResid, R, b.gemm_ws, s));
+  *xn_ready = false;
+  const int fc2_splits = vt::plan_gemm(M, d, mlp).splits;
+  if (fc2_splits > 1 && next_ln1_g) {
+    VT_TRY_HIP(vt::launch_gemm_partials(b.act, M, mlp, w->w_fc2, d, b.gemm_ws, s));
+    VT_TRY_HIP(vt::launch_resid_ln(part, fc2_splits, M, d, w->b_fc2, R, next_ln1_g, next_ln1_b,
+                                   cfg->ln_eps, b.xn, s));
+    *xn_ready = true;
+  } else {
+    VT_TRY_HIP(vt::launch_gemm(b.act, M, mlp, w->w_fc2, d, w->b_fc2, vt::kEpiResid, R, b.gemm_ws, s));
+  }
   return VT_OK;
 }
 
@@ -532,7 +554,9 @@ VT_API vt_status vt_block_forward(const vt_config* cfg, float* resid, const vt_b
   carve_block(c, dims_of(cfg, total_tokens, n_img), max_seqlen, &b);
   int32_t axis_code = 0;
   if ((st = attn_prologue(cfg, cu_seqlens, n_img, total_tokens, max_seqlen, b, &axis_code, s)) != VT_OK) return st;
-  return run_block(cfg, resid, w, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen, axis_code, b, s);
+  bool xn_ready = false;
+  return run_block(cfg, resid, w, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen, axis_code, b,
+                   nullptr, nullptr, &xn_ready, s);
 }
 
 VT_API vt_status vt_merge_project(const vt_config* cfg, const uint16_t* tower, vt_order order,
@@ -604,8 +628,11 @@ VT_API vt_status vt_tower_forward(const vt_config* cfg, const uint16_t* pixels,
   VT_TRY_HIP(vt::launch_patchify(pixels, t.info, t.cu, t.tok_img, int32_t(N), t.X, s));
   VT_TRY_HIP(vt::launch_gemm(t.X, int(N), 1176, w->w_patch, cfg->hidden, w->b_patch, vt::kEpiF32, t.R,
                              t.blk.gemm_ws, s));
+  bool xn_ready = false;
   for (int l = 0; l < cfg->layers; ++l) {
-    st = run_block(cfg, t.R, &w->blocks[l], t.cu, t.pos, n_img, N, gi.max_hw, axis_code, t.blk, s);
+    const vt_block_weights* nx = l + 1 < cfg->layers ? &w->blocks[l + 1] : nullptr;
+    st = run_block(cfg, t.R, &w->blocks[l], t.cu, t.pos, n_img, N, gi.max_hw, axis_code, t.blk,
+                   nx ? nx->ln1_g : nullptr, nx ? nx->ln1_b : nullptr, &xn_ready, s);
     if (st != VT_OK) return st;
   }
   VT_TRY_HIP(vt::launch_f32_to_bf16(t.R, t.T, size_t(N) * cfg->hidden, s));

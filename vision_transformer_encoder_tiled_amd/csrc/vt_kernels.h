@@ -50,6 +50,11 @@ hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, size_t n, hipStre
 // ---- LayerNorm (layernorm.hip)
 hipError_t launch_layer_norm(const float* x, int32_t rows, int32_t width, const uint16_t* g,
                              const uint16_t* b, float eps, uint16_t* out, hipStream_t s);
+// R += sum_z part[z] (z = 0..splits-1 in order) + bias, then out = LN(R; g, b, eps);
+// part is [splits][rows][width] fp32 (the split-K partials of launch_gemm_partials).
+hipError_t launch_resid_ln(const float* part, int32_t splits, int32_t rows, int32_t width,
+                           const uint16_t* bias, float* R, const uint16_t* g, const uint16_t* b,
+                           float eps, uint16_t* out, hipStream_t s);
 
 // ---- GEMM (gemm.hip)
 enum Epi : int { kEpiBf16 = 0, kEpiGeluTanh = 1, kEpiGeluErf = 2, kEpiResid = 3, kEpiF32 = 4 };
@@ -62,6 +67,10 @@ GemmPlan plan_gemm(int M, int N, int K);
 size_t gemm_workspace_bytes(int M, int N, int K);
 hipError_t launch_gemm(const uint16_t* A, int M, int K, const uint16_t* B, int N,
                        const uint16_t* bias, int epi, void* out, void* ws, hipStream_t s);
+// Split-K GEMMs only: writes the fp32 partials part[z][M][N] of plan_gemm's
+// splits (> 1) to ws, no bias and no epilogue (launch_resid_ln finishes them).
+hipError_t launch_gemm_partials(const uint16_t* A, int M, int K, const uint16_t* B, int N, void* ws,
+                                hipStream_t s);
 
 // ---- attention (attention.hip)
 constexpr int kAttnKTile = 64;         // keys per tile
