@@ -6,11 +6,15 @@ raster-order tower output, the 2x2 merge and the projector -- over one batch
 of synthetic input that is already resident in device memory.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload tower_448]
+    python bench.py --kernel {fc1,attention,copy} [--workload ...]   # one kernel, for counter runs
 
 Prints one JSON line.  Beside the headline workload it times, with HIP events
-on the stream the kernels run on, the dominant kernel (the bf16 GEMM at the
-FC1 shape) and the attention kernel through their own entry points, and the
-2016x2016 single image as a secondary workload.  The CPU oracle is timed on a
+on the stream the kernels run on, the dominant kernel of the headline
+workload (the bf16 GEMM at the FC1 shape) and one vt_attention_varlen call
+through their own entry points, and the 2016x2016 single image as a
+secondary workload.  "traffic" (HBM-side bytes per launch) comes from the
+FETCH_SIZE / WRITE_SIZE counter summaries under profiles/, and is null when
+those were taken on other kernel sources.  The CPU oracle is timed on a
 bounded sample (one 448x448 image through the full tower) on the host.
 """
 from __future__ import annotations
@@ -56,6 +60,8 @@ def parse():
     ap.add_argument("--secondary", default="tower_2016", help="second workload ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-iters", type=int, default=20)
+    ap.add_argument("--kernel", choices=["fc1", "attention", "copy"], default=None,
+                    help="run only this kernel case (counter runs) and exit")
     return ap.parse_args()
 
 
@@ -105,8 +111,9 @@ def time_kernel(torch, fn, iters):
     return s.elapsed_time(e) / 1e3 / iters
 
 
-def gemm_roofline(vt, torch, M, iters):
-    """The FC1 GEMM (M x 5120 x 1280, bias + GELU epilogue) on its own."""
+def fc1_case(vt, torch, M):
+    """The FC1 GEMM of one block (M x 5120 x 1280, bias + GELU epilogue) as a
+    vt_linear call on seeded bf16 operands."""
     N, K = 5120, 1280
     g = np.random.Generator(np.random.PCG64(0))
     x = torch.from_numpy(synth.bf16_bits(g.standard_normal((M, K), dtype=np.float32)).view(np.int16)).cuda()
@@ -114,15 +121,10 @@ def gemm_roofline(vt, torch, M, iters):
     b = torch.zeros(N, dtype=torch.int16, device="cuda")
     out = torch.empty((M, N), dtype=torch.int16, device="cuda")
     ws = vt.workspace(vt.vt_linear_workspace_size(M, N, K))
-    t = time_kernel(torch, lambda: vt.vt_linear(x, M, K, w, N, b, vt.VT_EPI_GELU_TANH_BF16, out, ws), iters)
-    flops = 2.0 * M * N * K
-    return {"kernel": "gemm_kernel (FC1: %d x %d x %d, bias+GELU epilogue)" % (M, N, K),
-            "bound": "mfma", "achieved": flops / t / 1e12, "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": flops / t / 1e12 / PEAK_BF16_TFLOPS, "traffic": None,
-            "flops_per_launch": flops, "avg_launch_us": t * 1e6}
+    return (lambda: vt.vt_linear(x, M, K, w, N, b, vt.VT_EPI_GELU_TANH_BF16, out, ws)), 2.0 * M * N * K
 
 
-def attention_roofline(vt, torch, grids, iters):
+def attention_case(vt, torch, grids):
     """vt_attention_varlen on the workload's token layout (random bf16 q, k, v)."""
     N = sum(h * w for _, h, w in grids)
     g = np.random.Generator(np.random.PCG64(1))
@@ -134,13 +136,85 @@ def attention_roofline(vt, torch, grids, iters):
     max_seq = max(h * w for _, h, w in grids)
     ws = vt.workspace(vt.vt_block_workspace_size(cfg, N, len(grids), max_seq))
     out = torch.empty((N, 1280), dtype=torch.int16, device="cuda")
-    t = time_kernel(torch, lambda: vt.vt_attention_varlen(cfg, qkv, cu, pos, len(grids), N, max_seq,
-                                                          out, vt.VT_BF16, ws), iters)
     flops = float(sum(4 * (h * w) ** 2 * 1280 for _, h, w in grids))
+    return (lambda: vt.vt_attention_varlen(cfg, qkv, cu, pos, len(grids), N, max_seq, out, vt.VT_BF16, ws)), flops
+
+
+def copy_case(torch, nbytes=256 << 20):
+    """A plain device-to-device copy of nbytes (the HBM-counter calibration)."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    return (lambda: dst.copy_(src)), 0.0
+
+
+def profile_traffic(name, source):
+    """HBM bytes per launch of a kernel from the counter summary in
+    profiles/<name>.txt: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the
+    kernel and of a plain copy of known size, each scaled by the copy's
+    known bytes / its counter reading.  None if the summary is missing or
+    was taken on other kernel sources (sha1 recorded in the summary)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", name + ".txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith((" ", "#", "`")):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    sha = hashlib.sha1(open(os.path.join(ROOT, source), "rb").read()).hexdigest()
+    if kv.get("source_sha1") != sha:
+        return None
+    try:
+        fr = float(kv["copy_known_read_bytes"]) / (float(kv["copy_fetch_kib"]) * 1024)
+        fw = float(kv["copy_known_write_bytes"]) / (float(kv["copy_write_kib"]) * 1024)
+        return float(kv["kernel_fetch_kib"]) * 1024 * fr + float(kv["kernel_write_kib"]) * 1024 * fw
+    except (KeyError, ValueError):
+        return None
+
+
+def gemm_roofline(vt, torch, M, iters):
+    fn, flops = fc1_case(vt, torch, M)
+    t = time_kernel(torch, fn, iters)
+    return {"kernel": "gemm_dl_kernel (FC1: %d x 5120 x 1280, bias+GELU epilogue)" % M,
+            "bound": "mfma", "achieved": flops / t / 1e12, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": flops / t / 1e12 / PEAK_BF16_TFLOPS,
+            "traffic": profile_traffic("gemm_fc1_%d_traffic" % M, "vision_transformer_encoder_tiled_amd/csrc/gemm.hip"),
+            "flops_per_launch": flops, "avg_launch_us": t * 1e6}
+
+
+def attention_roofline(vt, torch, grids, iters, traffic_profile=None):
+    fn, flops = attention_case(vt, torch, grids)
+    t = time_kernel(torch, fn, iters)
+    N = sum(h * w for _, h, w in grids)
+    traffic = (profile_traffic(traffic_profile, "vision_transformer_encoder_tiled_amd/csrc/attention.hip")
+               if traffic_profile else None)
     return {"kernel": "attention_kernel (%d tokens, %d images)" % (N, len(grids)), "bound": "mfma",
             "achieved": flops / t / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": flops / t / 1e12 / PEAK_BF16_TFLOPS, "flops_per_launch": flops,
-            "avg_launch_us": t * 1e6, "note": "average includes the schedule and RoPE-table prologue kernels"}
+            "frac": flops / t / 1e12 / PEAK_BF16_TFLOPS, "traffic": traffic,
+            "traffic_note": "attention kernel only (not the pack kernel)" if traffic else None,
+            "flops_per_launch": flops,
+            "avg_launch_us": t * 1e6,
+            "note": "one vt_attention_varlen call: the RoPE/pack kernel and the attention kernel, "
+                    "plus the per-call schedule and RoPE-table kernels"}
+
+
+def kernel_only(a):
+    """--kernel: run one kernel case a fixed number of times (for counter runs)."""
+    import torch
+    import vision_transformer_encoder_tiled_amd as vt
+    wl = synth.WORKLOADS[a.workload]
+    if a.kernel == "fc1":
+        fn, _ = fc1_case(vt, torch, wl.tokens)
+    elif a.kernel == "attention":
+        fn, _ = attention_case(vt, torch, list(wl.grids))
+    else:
+        fn, _ = copy_case(torch)
+    fn()
+    torch.cuda.synchronize()
+    t = time_kernel(torch, fn, a.kernel_iters)
+    print(json.dumps({"kernel": a.kernel, "workload": wl.name, "iters": a.kernel_iters + 2,
+                      "avg_us": t * 1e6}), flush=True)
 
 
 def cpu_baseline(weights):
@@ -169,6 +243,8 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus %d is not supported "
                                    "(the multi-GPU sharding is a design note, not code)" % a.gpus}))
         sys.exit(2)
+    if a.kernel:
+        return kernel_only(a)
     import torch
     import vision_transformer_encoder_tiled_amd as vt
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -213,7 +289,9 @@ def main():
             "patches_per_s": wl2.tokens * k2 / s2, "images_per_s": wl2.n_img * k2 / s2,
             "ms_per_step": s2 / k2 * 1e3, "steps": k2,
             "tflops_total": (g2 + at2) / (s2 / k2) / 1e12,
-            "attention_roofline": attention_roofline(vt, torch, list(wl2.grids), max(3, a.kernel_iters // 4)),
+            "attention_roofline": attention_roofline(
+                vt, torch, list(wl2.grids), max(3, a.kernel_iters // 4),
+                "attention_2016_traffic" if wl2.name == "tower_2016" else None),
             "gemm_roofline": gemm_roofline(vt, torch, wl2.tokens, max(3, a.kernel_iters // 4)),
         }
         del run2
