@@ -78,11 +78,8 @@ constexpr int K_BYTES = BKV * KROW * 2;          // 11264
 constexpr int V_ROWS = HD + 1;                   // dims 0..79 and the ones row
 constexpr int IMG_BYTES = kAttnTileBytes;        // 24576: K + V^T rows 0..80 + pad
 constexpr int STAGE_BYTES = K_BYTES + 96 * VROW * 2;  // 25088: the MFMA reads V^T rows up to 95
-constexpr int NST = 3;
-constexpr int COPIES = IMG_BYTES / (1024 * 4);   // DMA instructions per wave per tile
 constexpr float kLazy = 8.0f;       // log2 growth of the row max tolerated before rescaling
 static_assert(K_BYTES + V_ROWS * VROW * 2 <= IMG_BYTES, "tile image size");
-static_assert(COPIES * 4 * 1024 == IMG_BYTES, "tile image must be whole 4 KB rounds");
 
 // V^T slot of key k inside its group of 16: swap bits 2 and 3.
 __device__ __forceinline__ int vslot(int k) {
@@ -190,11 +187,14 @@ __global__ void __launch_bounds__(320) attn_pack_kernel(
 // image (tile r*KG + g in round r).  With KG = 2 a workgroup holds 64
 // queries, so small images give twice as many workgroups; the groups'
 // partial (max, O, l) are merged through LDS at the end.
-template <int KG>
-__global__ void __launch_bounds__(256) attention_kernel(
+template <int NW, int KG, int NST>
+__global__ void __launch_bounds__(64 * NW) attention_kernel(
     const uint16_t* __restrict__ qpk, const uint16_t* __restrict__ kv,
     const int4* __restrict__ qdesc, int32_t heads, void* __restrict__ out, int32_t out_f32) {
-  constexpr int QW = 4 / KG;              // query wavefronts per group
+  static_assert(NST == 3 || (NST == 4 && KG == 1), "stage ring");
+  constexpr int QW = NW / KG;             // query wavefronts per group
+  constexpr int COPIES = IMG_BYTES / (1024 * NW);  // 1 KB DMA pieces per wave per tile
+  static_assert(COPIES * NW * 1024 == IMG_BYTES, "tile image must be whole rounds of copies");
   constexpr int WQ = 32 * QW;             // queries per workgroup
   constexpr int STAGE = KG * STAGE_BYTES; // one round: KG tiles
   extern __shared__ __align__(16) char lds[];
@@ -226,7 +226,7 @@ __global__ void __launch_bounds__(256) attention_kernel(
             __builtin_amdgcn_readfirstlane(lds_wave + (r % NST) * STAGE + j * STAGE_BYTES);
         const char* g = src + t * tile_stride + 1024 * wave + 16 * lane;
 #pragma unroll
-        for (int c = 0; c < COPIES; ++c) dma16(g + 4096 * c, base + 4096 * c);
+        for (int c = 0; c < COPIES; ++c) dma16(g + NW * 1024 * c, base + NW * 1024 * c);
       }
     }
   };
@@ -297,8 +297,9 @@ __global__ void __launch_bounds__(256) attention_kernel(
     return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
   };
 
-  issue(0);
-  if (rounds > 1) issue(1);
+#pragma unroll
+  for (int r = 0; r < NST - 1; ++r)
+    if (r < rounds) issue(r);
   wait_vmcnt<0>();
   wg_barrier();
 
@@ -326,11 +327,13 @@ __global__ void __launch_bounds__(256) attention_kernel(
   // The group's next tile's score MFMAs are issued before this tile's
   // exponentials so they run underneath.
   auto body = [&](int r, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
-    // Every wave is done reading round r-1 (V) and round r (K); round r+1 has landed.
-    wait_vmcnt<0>();
+    // Every wave is done reading round r-1 (V) and round r (K); round r+1 has
+    // landed (with 4 stages round r+2 may still be in flight).
+    if (NST == 4 && r + 2 < rounds) wait_vmcnt<(NST - 3) * COPIES * KG>();
+    else wait_vmcnt<0>();
     wait_lds_reads();
     wg_barrier();
-    if (r + 2 < rounds) issue(r + 2);  // into the stage round r-1 used
+    if (r + NST - 1 < rounds) issue(r + NST - 1);  // into the stage round r-1 used
     const int tc = r * KG + grp, tn = tc + KG;
     if (tn < ntiles) load_k(r + 1);
     if (tc >= ntiles) return;
@@ -408,21 +411,21 @@ __global__ void __launch_bounds__(256) attention_kernel(
     wg_barrier();  // the ring is idle
     const int slot = qw * 64 + lane;
     if (grp == 1) {
-      xs[48 * 128 + slot] = m_use;
+      xs[48 * 64 * QW + slot] = m_use;
 #pragma unroll
       for (int d = 0; d < 3; ++d)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) xs[(16 * d + e) * 128 + slot] = acc[d][e];
+        for (int e = 0; e < 16; ++e) xs[(16 * d + e) * 64 * QW + slot] = acc[d][e];
     }
     __syncthreads();
     if (grp == 1) return;
-    const float m1 = xs[48 * 128 + slot];
+    const float m1 = xs[48 * 64 * QW + slot];
     const float m = fmaxf(m_use, m1);
     const float s0 = __builtin_amdgcn_exp2f(m_use - m), s1 = __builtin_amdgcn_exp2f(m1 - m);
 #pragma unroll
     for (int d = 0; d < 3; ++d)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[d][e] = acc[d][e] * s0 + xs[(16 * d + e) * 128 + slot] * s1;
+      for (int e = 0; e < 16; ++e) acc[d][e] = acc[d][e] * s0 + xs[(16 * d + e) * 64 * QW + slot] * s1;
   }
 
   // ---- normalise and store: acc[d][4g + r] is dim 32d + 8g + 4hf + r of query ln;
@@ -450,18 +453,18 @@ __global__ void __launch_bounds__(256) attention_kernel(
   }
 }
 
-template <int KG>
+template <int NW, int KG, int NST>
 static hipError_t launch_attention_kernel(const uint16_t* qpk, const uint16_t* kv,
                                           const int4* qdesc, int32_t max_qtiles, int32_t heads,
                                           void* out, bool out_f32, hipStream_t s) {
   const size_t lds = size_t(NST) * KG * STAGE_BYTES;
-  auto kern = attention_kernel<KG>;
+  auto kern = attention_kernel<NW, KG, NST>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (attr != hipSuccess) return attr;
   const int64_t blocks = int64_t(max_qtiles) * heads;
-  hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(256), lds, s, qpk, kv, qdesc, heads, out,
-                     out_f32 ? 1 : 0);
+  hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(64 * NW), lds, s, qpk, kv, qdesc, heads,
+                     out, out_f32 ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -475,8 +478,8 @@ hipError_t launch_attention(const uint16_t* qkv, const int32_t* pos_thw, const i
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (key_groups == 2)
-    return launch_attention_kernel<2>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, s);
-  return launch_attention_kernel<1>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, s);
+    return launch_attention_kernel<4, 2, 3>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, s);
+  return launch_attention_kernel<kAttnWaves1, 1, kAttnStages1>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, s);
 }
 
 }  // namespace vt

@@ -205,6 +205,19 @@ __device__ __forceinline__ void xcd_group_tile(int tiles_m, int tiles_n, int* tm
 // 16-byte bank groups (64 banks) and any 8 aligned rows in 8 (32 banks).
 __device__ __forceinline__ int swz4(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 
+// LDS layout of one K step of gemm_dl_kernel: BM rows of A, then the B rows,
+// 64 bytes each; B is rounded up to whole copy rounds of 16 rows per wavefront.
+constexpr int dl_b_rows(int bn, int nw) { return (bn + 16 * nw - 1) / (16 * nw) * (16 * nw); }
+constexpr int dl_stage_bytes(int bm, int bn, int nw) { return (bm + dl_b_rows(bn, nw)) * 64; }
+
+// Token rows of the C tile staged per epilogue pass: BM halved until a pass
+// fits the LDS ring.
+constexpr int pass_rows(int bm, int row_bytes, int ring) {
+  int r = bm;
+  while (r > 1 && r * row_bytes > ring) r /= 2;
+  return r;
+}
+
 // GWM x GWN wavefronts; each owns a (BM/GWM) x (BN/GWN) block of C.
 // K is consumed in steps of 32 through a ring of NST LDS stages: NST - 1
 // steps are in flight while one is multiplied, one workgroup barrier per
@@ -218,10 +231,13 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
   constexpr int WM = BM / GWM, WN = BN / GWN;
   constexpr int TB = WM / 32, FB = WN / 32;
   constexpr int BK = 32;
-  constexpr int LA = BM / (16 * NW), LB = BN / (16 * NW);  // copies per lane per K step
+  // B rows copied per step: BN rounded up to whole copy rounds (16 rows per
+  // wavefront); the extra rows are copied and never read.
+  constexpr int BNP = dl_b_rows(BN, NW);
+  constexpr int LA = BM / (16 * NW), LB = BNP / (16 * NW);  // copies per lane per K step
   constexpr int CP = LA + LB;
-  constexpr int A_BYTES = BM * 64, STAGE = (BM + BN) * 64;
-  static_assert(WM % 32 == 0 && WN % 32 == 0 && LA * 16 * NW == BM && LB * 16 * NW == BN, "tiling");
+  constexpr int A_BYTES = BM * 64, STAGE = dl_stage_bytes(BM, BN, NW);
+  static_assert(WM % 32 == 0 && WN % 32 == 0 && LA * 16 * NW == BM && LB * 16 * NW == BNP, "tiling");
   static_assert(NST * STAGE <= 160 * 1024, "LDS");
   extern __shared__ __align__(16) uint16_t lds[];
   const char* smem = reinterpret_cast<const char*>(lds);
@@ -342,8 +358,9 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
   // ---- epilogue.  acc[f][t][4g + r] = C[token][feature] with token =
   // wm*WM + 32t + lane%32 and feature = wn*WN + 32f + 8g + 4(lane/32) + r.
   // Bias and the activation are applied in registers; the tile is written
-  // row-major into LDS (16-byte chunk c of row r at chunk c ^ (r % 16), which
-  // spreads the 32 rows one write instruction touches over all banks), then
+  // row-major into LDS (16-byte chunk c of row r at chunk (c + r % 16) mod
+  // CHUNKS, which spreads the 32 rows one write instruction touches over the
+  // banks), then
   // every thread moves whole 16-byte chunks to global memory, PASS_ROWS token
   // rows at a time.  The ring is idle: the last step waited for every copy
   // and, at its barrier, for every wave's fragment reads.
@@ -351,8 +368,8 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
   constexpr int ESZ = F32OUT ? 4 : 2;
   constexpr int ROWB = BN * ESZ, CHUNKS = ROWB / 16, EPC = 16 / ESZ;
   constexpr int RING = NST * STAGE;
-  constexpr int PASS_ROWS = (BM * ROWB <= RING) ? BM : RING / ROWB;
-  static_assert(CHUNKS >= 16 && PASS_ROWS % WM == 0, "epilogue staging");
+  constexpr int PASS_ROWS = pass_rows(BM, ROWB, RING);
+  static_assert(CHUNKS >= 16 && PASS_ROWS % WM == 0 && BM % PASS_ROWS == 0, "epilogue staging");
   char* cs = reinterpret_cast<char*>(lds);
 #pragma unroll
   for (int pass = 0; pass < BM / PASS_ROWS; ++pass) {
@@ -371,7 +388,7 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
             const int c = (wn * WN + 32 * f + 8 * g) / EPC;  // logical chunk of feature 8g
             if constexpr (F32OUT) {
               // 4 fp32 = one chunk; h selects the next chunk
-              const int pc = (c + h) ^ (r & 15);
+              const int pc = (c + h + (r & 15)) % CHUNKS;
               *reinterpret_cast<float4*>(cs + r * ROWB + pc * 16) = make_float4(v0, v1, v2, v3);
             } else {
               if (bias) {
@@ -383,7 +400,7 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
               } else if constexpr (EPI == kEpiGeluErf) {
                 v0 = gelu_erf(v0); v1 = gelu_erf(v1); v2 = gelu_erf(v2); v3 = gelu_erf(v3);
               }
-              const int pc = c ^ (r & 15);
+              const int pc = (c + (r & 15)) % CHUNKS;
               *reinterpret_cast<uint2*>(cs + r * ROWB + pc * 16 + 8 * h) =
                   make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
             }
@@ -398,7 +415,7 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
       const int r = i / CHUNKS, c = i % CHUNKS;
       const int tok = m0 + pass * PASS_ROWS + r, col = n0 + c * EPC;
       if (tok >= M || col >= N) continue;
-      const uint4 v = *reinterpret_cast<const uint4*>(cs + r * ROWB + ((c ^ (r & 15)) * 16));
+      const uint4 v = *reinterpret_cast<const uint4*>(cs + r * ROWB + ((c + (r & 15)) % CHUNKS) * 16);
       if constexpr (SPLIT) {
         *reinterpret_cast<uint4*>(part + (int64_t(blockIdx.y) * M + tok) * N + col) = v;
       } else if constexpr (EPI == kEpiResid || EPI == kEpiF32) {
@@ -458,7 +475,17 @@ GemmPlan plan_gemm(int M, int N, int K) {
   if (t256 >= 192) return p;
   p.bm = 128;
   p.bn = 128;
-  const int t128 = cdiv(M, 128) * cdiv(N, 128);
+  const int tm = cdiv(M, 128);
+  const int t128 = tm * cdiv(N, 128);
+  if (t128 > 256 && K % 32 == 0) {
+    // One round of wider tiles when N allows it (e.g. 1024 x 5120: 8 x 32 tiles of 128 x 160).
+    for (int bn : {160, 192})
+      if (N % bn == 0 && tm * (N / bn) <= 256) {
+        p.bn = bn;
+        return p;
+      }
+    return p;
+  }
   if (t128 >= 200) return p;
   // Split K so that the workgroups fill the 256 CUs once (one round), each
   // split keeping at least 384 of K.
@@ -484,9 +511,10 @@ static hipError_t launch_tile(const uint16_t* A, int M, int K, const uint16_t* B
                               hipStream_t s) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (K % 32 == 0 && (!SPLIT || p.kper % 32 == 0)) {
-    // 8 wavefronts (2 per SIMD): 128 x 64 each in a 256 x 256 tile, 32 x 64 in a 128 x 128 one
-    constexpr int GWM = (BM == 256) ? 2 : 4, GWN = (BM == 256) ? 4 : 2, NST = 4;
-    const size_t lds = size_t(NST) * (BM + BN) * 64;
+    // 256 x 256: 8 wavefronts (2 per SIMD) of 128 x 64; 128 x 128: 8 of 32 x 64;
+    // 128 x 160 and 128 x 192: 4 of 32 x BN.
+    constexpr int GWM = (BM == 256) ? 2 : 4, GWN = (BM == 256) ? 4 : (BN == 128 ? 2 : 1), NST = 4;
+    const size_t lds = size_t(NST) * dl_stage_bytes(BM, BN, GWM * GWN);
     auto kern = gemm_dl_kernel<BM, BN, GWM, GWN, NST, EPI, SPLIT>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
@@ -495,15 +523,19 @@ static hipError_t launch_tile(const uint16_t* A, int M, int K, const uint16_t* B
                        K, B, N, bias, out, part, p.kper);
     return hipGetLastError();
   }
-  const size_t lds = size_t(2) * (BM + BN) * kLdsRow * sizeof(uint16_t);
-  auto kern = gemm_kernel<BM, BN, EPI, SPLIT>;
-  // Set once per instantiation (thread-safe static initialisation).
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(tiles, SPLIT ? p.splits : 1), dim3(256), lds, s, A, M, K, B, N,
-                     bias, out, part, p.kper);
-  return hipGetLastError();
+  if constexpr (BN != BM) {
+    return hipErrorInvalidValue;  // the register-staged kernel has square tiles only
+  } else {
+    const size_t lds = size_t(2) * (BM + BN) * kLdsRow * sizeof(uint16_t);
+    auto kern = gemm_kernel<BM, BN, EPI, SPLIT>;
+    // Set once per instantiation (thread-safe static initialisation).
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(kern, dim3(tiles, SPLIT ? p.splits : 1), dim3(256), lds, s, A, M, K, B, N,
+                       bias, out, part, p.kper);
+    return hipGetLastError();
+  }
 }
 
 template <int EPI>
@@ -522,6 +554,8 @@ static hipError_t launch_epi(const uint16_t* A, int M, int K, const uint16_t* B,
     return hipGetLastError();
   }
   if (p.bm == 256) return launch_tile<256, 256, EPI, false>(A, M, K, B, N, bias, out, nullptr, p, s);
+  if (p.bn == 160) return launch_tile<128, 160, EPI, false>(A, M, K, B, N, bias, out, nullptr, p, s);
+  if (p.bn == 192) return launch_tile<128, 192, EPI, false>(A, M, K, B, N, bias, out, nullptr, p, s);
   return launch_tile<128, 128, EPI, false>(A, M, K, B, N, bias, out, nullptr, p, s);
 }
 

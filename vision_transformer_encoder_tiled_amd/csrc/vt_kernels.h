@@ -75,9 +75,13 @@ hipError_t launch_gemm_partials(const uint16_t* A, int M, int K, const uint16_t*
 // ---- attention (attention.hip)
 constexpr int kAttnKTile = 64;         // keys per tile
 constexpr int kAttnTileBytes = 24576;  // one (head, key tile) image: K [64][88] + V^T [81][72] fp16 + pad
-// Queries per workgroup: 128 with one key group, 64 with two (the kernel
-// splits each image's key tiles between two groups of 2 wavefronts).
-inline int attn_q_tile(int key_groups) { return key_groups == 2 ? 64 : 128; }
+// Wavefronts (of 32 queries) per workgroup and LDS stages with one key group
+// (8 wavefronts, or 4 stages with 8 wavefronts, measured no faster).
+constexpr int kAttnWaves1 = 4;
+constexpr int kAttnStages1 = 3;
+// Queries per workgroup: 32 * kAttnWaves1 with one key group, 64 with two
+// (the kernel splits each image's key tiles between two groups of 2 wavefronts).
+inline int attn_q_tile(int key_groups) { return key_groups == 2 ? 64 : 32 * kAttnWaves1; }
 // qpk: [N, heads, 80] fp16 rotated+scaled Q; kv: max_ktiles x heads tile
 // images.  qdesc / kdesc come from launch_attn_schedule with
 // attn_q_tile(key_groups) and the same max_qtiles / max_ktiles.
