@@ -20,6 +20,8 @@
 // out, fp32 residual update in place, fp32 out.  Split-K writes fp32 partial
 // tiles to the workspace and a second kernel sums them in split order (no
 // atomics: results are deterministic).
+#include <algorithm>
+
 #include "vt_device.h"
 #include "vt_kernels.h"
 
@@ -473,6 +475,16 @@ GemmPlan plan_gemm(int M, int N, int K) {
   GemmPlan p{256, 256, 1, K};
   const int t256 = cdiv(M, 256) * cdiv(N, 256);
   if (t256 >= 192) return p;
+  if (M <= 512 && K % 32 == 0) {
+    // Few rows, large weights (the merged MLP of a small image): 256 x 256
+    // tiles read each weight panel once; split K to fill the CUs.
+    const int sp = std::min(256 / t256, K / 512);
+    if (t256 * sp >= 192) {
+      p.kper = cdiv(cdiv(K, sp), 64) * 64;
+      p.splits = cdiv(K, p.kper);
+      return p;
+    }
+  }
   p.bm = 128;
   p.bn = 128;
   const int tm = cdiv(M, 128);
@@ -544,7 +556,8 @@ static hipError_t launch_epi(const uint16_t* A, int M, int K, const uint16_t* B,
   const GemmPlan p = plan_gemm(M, N, K);
   if (p.splits > 1) {
     float* part = reinterpret_cast<float*>(ws);
-    hipError_t e = launch_tile<128, 128, EPI, true>(A, M, K, B, N, bias, out, part, p, s);
+    hipError_t e = p.bm == 256 ? launch_tile<256, 256, EPI, true>(A, M, K, B, N, bias, out, part, p, s)
+                               : launch_tile<128, 128, EPI, true>(A, M, K, B, N, bias, out, part, p, s);
     if (e != hipSuccess) return e;
     const int64_t n4 = int64_t(M) * N / 4;
     int64_t blocks = (n4 + 255) / 256;
@@ -575,8 +588,9 @@ hipError_t launch_gemm_partials(const uint16_t* A, int M, int K, const uint16_t*
                                 hipStream_t s) {
   const GemmPlan p = plan_gemm(M, N, K);
   if (p.splits < 2) return hipErrorInvalidValue;
-  return launch_tile<128, 128, kEpiResid, true>(A, M, K, B, N, nullptr, nullptr,
-                                                 reinterpret_cast<float*>(ws), p, s);
+  float* part = reinterpret_cast<float*>(ws);
+  return p.bm == 256 ? launch_tile<256, 256, kEpiResid, true>(A, M, K, B, N, nullptr, nullptr, part, p, s)
+                     : launch_tile<128, 128, kEpiResid, true>(A, M, K, B, N, nullptr, nullptr, part, p, s);
 }
 
 }  // namespace vt
