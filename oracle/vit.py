@@ -24,7 +24,7 @@ Readings where the pages are silent (each is also listed in the design notes):
 attention scale 1/sqrt(80); RoPE rotate-half pairing (x_j, x_{j+40}); pairs
 [0,8) -> t, [8,24) -> h, [24,40) -> w with a per-axis ladder
 ``theta^(-2k/(2 n_axis))``; positions are integer patch coordinates per image
-(t=0, row, col); LayerNorm with biased variance and eps inside the sqrt;
+(t, row, col), t = 0 for a still image; LayerNorm with biased variance and eps inside the sqrt;
 GELU(tanh) in the blocks and the projector; W_qkv rows are [Q | K | V], each
 head-major 16 x 80; attention is block-diagonal per image, non-causal; tokens
 in raster order inside an image; merged token m = (r, c) gathers the 2x2 block
@@ -80,37 +80,52 @@ def positions(grids) -> np.ndarray:
 def merge_map(grids) -> np.ndarray:
     """[N/4, 4] global raster token indices gathered into each merged token.
 
-    Merged token m = (r, c) of an image (raster over the (h/2, w/2) grid)
-    takes patches (2r+dr, 2c+dc) in slot k = 2*dr + dc (2x2 spatial merge,
-    MiniMax-M3-Vision README, Architecture table)."""
+    Merged token m = (tt, r, c) of an image (raster over the (t, h/2, w/2)
+    grid) takes patches (tt, 2r+dr, 2c+dc) in slot k = 2*dr + dc (2x2
+    spatial merge, MiniMax-M3-Vision README, Architecture table; the merge is
+    spatial, so each temporal slice is merged on its own)."""
     out = []
     base = 0
     for t, h, w in grids:
-        for r in range(h // 2):
-            for c in range(w // 2):
-                out.append([base + (2 * r + dr) * w + (2 * c + dc)
-                            for dr in (0, 1) for dc in (0, 1)])
+        for tt in range(t):
+            for r in range(h // 2):
+                for c in range(w // 2):
+                    out.append([base + tt * h * w + (2 * r + dr) * w + (2 * c + dc)
+                                for dr in (0, 1) for dc in (0, 1)])
         base += t * h * w
     return np.asarray(out, dtype=np.int64).reshape(-1, 4)
 
 
 # ------------------------------------------------------------------ patchify
-def patchify(img: np.ndarray) -> np.ndarray:
-    """[3, 14h, 14w] -> [h*w, 3*2*14*14] rows in raster patch order.
+def frames_of(t: int) -> int:
+    """Frames stored per item: a still image (t = 1) is one frame, repeated
+    to fill the temporal patch of 2 ("v2_loaders FINDINGS" s.3); a clip with
+    t temporal patches is 2t frames (README Architecture: temporal patch 2)."""
+    return 1 if t == 1 else 2 * t
 
-    The single frame is repeated to fill the temporal patch of 2 ("v2_loaders
-    FINDINGS" s.3).  Row layout is (channel, tau, py, px), i.e. a Conv3d
-    weight [1280, 3, 2, 14, 14] flattened, so that ``X @ W.T`` is the Conv3d
-    with kernel = stride (README Architecture: Conv3d patch embed)."""
-    c, H, W = img.shape
-    h, w = H // PATCH, W // PATCH
-    p = img.reshape(c, h, PATCH, w, PATCH).transpose(1, 3, 0, 2, 4)  # h, w, c, py, px
-    p = np.stack([p, p], axis=3)                                       # h, w, c, tau, py, px
-    return np.ascontiguousarray(p.reshape(h * w, c * T_PATCH * PATCH * PATCH))
+
+def patchify(pix: np.ndarray) -> np.ndarray:
+    """[3, 14h, 14w] (still image) or [2t, 3, 14h, 14w] (clip) -> rows in
+    raster patch order over (temporal patch, row, col).
+
+    Row layout is (channel, tau, py, px), i.e. a Conv3d weight
+    [1280, 3, 2, 14, 14] flattened, so that ``X @ W.T`` is the Conv3d with
+    kernel = stride = (2, 14, 14) (README Architecture: Conv3d patch embed);
+    temporal patch tt covers frames 2tt and 2tt+1.  A still image's single
+    frame is repeated ("v2_loaders FINDINGS" s.3)."""
+    frames = pix[None] if pix.ndim == 3 else pix
+    if frames.shape[0] == 1:
+        frames = np.concatenate([frames, frames], axis=0)
+    F, c, H, W = frames.shape
+    assert F % T_PATCH == 0
+    t, h, w = F // T_PATCH, H // PATCH, W // PATCH
+    p = frames.reshape(t, T_PATCH, c, h, PATCH, w, PATCH)
+    p = p.transpose(0, 3, 5, 2, 1, 4, 6)  # t, h, w, c, tau, py, px
+    return np.ascontiguousarray(p.reshape(t * h * w, c * T_PATCH * PATCH * PATCH))
 
 
 def unpatchify(x: np.ndarray, h: int, w: int) -> np.ndarray:
-    """Inverse of :func:`patchify` using the tau = 0 slice."""
+    """Inverse of :func:`patchify` for a still image, using the tau = 0 slice."""
     p = x.reshape(h, w, 3, T_PATCH, PATCH, PATCH)[:, :, :, 0]
     return np.ascontiguousarray(p.transpose(2, 0, 3, 1, 4).reshape(3, h * PATCH, w * PATCH))
 
@@ -258,18 +273,22 @@ def block_forward(R, W, pos, cu, cfg: Config, prefix="l0.", return_attn=False):
 
 
 def patch_embed(images, W, grids):
-    """Patchify every image (raster order) and apply the Conv3d-as-Linear embed."""
+    """Patchify every item (raster order over (t, row, col)) and apply the
+    Conv3d-as-Linear embed."""
     X = np.concatenate([patchify(img) for img in images], axis=0)
     b = W.get("patch_b")
     return linear(X, W["patch_w"], b)
 
 
 def split_pixels(flat, grids):
-    """Cut the concatenated [3, 14h, 14w] images out of one flat array."""
+    """Cut the concatenated items out of one flat array: [3, 14h, 14w] for a
+    still image (t = 1), [2t, 3, 14h, 14w] for a clip."""
     out, o = [], 0
     for t, h, w in grids:
-        n = 3 * PATCH * h * PATCH * w
-        out.append(flat[o:o + n].reshape(3, PATCH * h, PATCH * w))
+        F = frames_of(t)
+        n = F * 3 * PATCH * h * PATCH * w
+        a = flat[o:o + n].reshape(F, 3, PATCH * h, PATCH * w)
+        out.append(a[0] if F == 1 else a)
         o += n
     return out
 

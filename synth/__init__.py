@@ -145,6 +145,12 @@ def make_pixels(h: int, w: int, seed: int) -> np.ndarray:
     return bf16_bits(g.random((3, PATCH * h, PATCH * w), dtype=np.float32))
 
 
+def make_clip(t: int, h: int, w: int, seed: int) -> np.ndarray:
+    """bf16 bits of one clip of 2t frames, [2t, 3, 14h, 14w], values ~U[0, 1)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    return bf16_bits(g.random((2 * t, 3, PATCH * h, PATCH * w), dtype=np.float32))
+
+
 # ---------------------------------------------------------------- workloads
 @dataclasses.dataclass(frozen=True)
 class Workload:

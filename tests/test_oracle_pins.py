@@ -75,6 +75,24 @@ def test_merge_map_is_a_bijection_of_2x2_blocks():
             assert tuple(p[k, 1:]) == (r0 + k // 2, c0 + k % 2)
 
 
+def test_positions_and_merge_map_for_clips():
+    # a clip with t = 3 temporal patches next to a still image
+    grids = [(3, 2, 4), (1, 2, 2)]
+    cu = oracle.cu_seqlens(grids)
+    assert list(cu) == [0, 24, 28]
+    pos = oracle.positions(grids)
+    for j in range(24):
+        assert tuple(pos[j]) == (j // 8, (j % 8) // 4, j % 4)
+    mm = oracle.merge_map(grids)
+    assert mm.shape == (7, 4)
+    assert sorted(mm.reshape(-1).tolist()) == list(range(28))
+    for m in range(7):
+        p = pos[mm[m]]
+        assert len(set(p[:, 0].tolist())) == 1  # the merge never crosses temporal patches
+        for k in range(4):
+            assert tuple(p[k, 1:]) == (p[0, 1] + k // 2, p[0, 2] + k % 2)
+
+
 # ---------------------------------------------------------------- patchify / embed
 def test_patchify_roundtrip_bit_exact():
     img = synth.make_pixels(6, 4, seed=7)
@@ -112,6 +130,35 @@ def test_patch_embed_equals_direct_conv3d_loops():
                                         torch.from_numpy(b), stride=14)[0]
     np.testing.assert_allclose(got, conv2d.permute(1, 2, 0).reshape(h * w, co).numpy(),
                                rtol=1e-12, atol=1e-12)
+
+
+def test_clip_patch_embed_equals_direct_conv3d_loops():
+    # Conv3d with kernel = stride = (2, 14, 14) over a 4-frame clip (t = 2),
+    # explicit float64 loops; temporal patch tt covers frames 2tt, 2tt+1.
+    t, h, w, co = 2, 2, 2, 3
+    clip = oracle.bf16_to_f32(synth.make_clip(t, h, w, seed=5)).astype(F64)  # [4, 3, H, W]
+    W5 = rng(4).standard_normal((co, 3, 2, 14, 14))
+    b = rng(5).standard_normal(co)
+    direct = np.zeros((t * h * w, co))
+    for o in range(co):
+        for tt in range(t):
+            for r in range(h):
+                for c in range(w):
+                    acc = b[o]
+                    for ch in range(3):
+                        for tau in range(2):
+                            blk = clip[2 * tt + tau, ch, 14 * r:14 * r + 14, 14 * c:14 * c + 14]
+                            acc += float(np.sum(W5[o, ch, tau] * blk))
+                    direct[(tt * h + r) * w + c, o] = acc
+    got = oracle.linear(oracle.patchify(clip), W5.reshape(co, -1), b)
+    np.testing.assert_allclose(got, direct, rtol=1e-12, atol=1e-12)
+    # a 2-frame clip of one repeated frame is the still image
+    img = synth.make_pixels(h, w, seed=6)
+    assert np.array_equal(oracle.patchify(np.stack([img, img])), oracle.patchify(img))
+    # flat split: a still image then a clip
+    flat = np.concatenate([img.reshape(-1), synth.make_clip(t, h, w, seed=5).reshape(-1)])
+    parts = oracle.split_pixels(flat, [(1, h, w), (t, h, w)])
+    assert parts[0].shape == img.shape and parts[1].shape == (4, 3, 14 * h, 14 * w)
 
 
 # ---------------------------------------------------------------- basic ops
