@@ -25,12 +25,13 @@
  * Alignment. Every device pointer must be 16-byte aligned; the workspace
  *            256-byte aligned.
  * Tokens.    Inside the library, and at every boundary that says "token
- *            order", the tokens of one image are stored in 2x2-window order:
- *            with w2 = w/2, token 4*(R*w2 + C) + 2*dr + dc is the patch at
- *            row 2R+dr, column 2C+dc.  The four patches of merged token
- *            m = R*w2 + C are therefore adjacent and the 2x2 merge is a
- *            reshape.  Images follow each other in grid-list order.  Outputs
- *            documented as "raster" use row-major patch order instead.
+ *            order", the tokens of one item are stored per temporal patch
+ *            tt in 2x2-window order: with w2 = w/2, token
+ *            tt*h*w + 4*(R*w2 + C) + 2*dr + dc is the patch at (tt, 2R+dr,
+ *            2C+dc).  The four patches of merged token tt*h*w/4 + R*w2 + C
+ *            are therefore adjacent and the 2x2 merge is a reshape.  Items
+ *            follow each other in grid-list order.  Outputs documented as
+ *            "raster" use (tt, row, col) row-major patch order instead.
  * Streams.   `stream` is a hipStream_t (NULL = the default stream).  Calls
  *            only enqueue work; they return before it finishes.  Inputs must
  *            stay valid until the stream reaches that point.
@@ -73,9 +74,11 @@ typedef enum vt_epilogue {
   VT_EPI_F32 = 4            /* out fp32 = y                                   */
 } vt_epilogue;
 
-/* One image: t frames x h x w patches.  The temporal patch is 2 and a single
- * frame is repeated to fill it ("v2_loaders FINDINGS", section 3), so t == 1
- * for still images; h and w must be even (2x2 merge). */
+/* One item: t temporal patches x h x w patches (README Architecture: temporal
+ * patch 2).  t == 1 is a still image, whose single frame is repeated to fill
+ * the temporal patch ("v2_loaders FINDINGS", section 3); t > 1 is a clip of
+ * 2t frames, temporal patch tt covering frames 2tt and 2tt+1.  h and w must
+ * be even (2x2 merge, applied within each temporal patch). */
 typedef struct vt_grid_thw { int32_t t, h, w; } vt_grid_thw;
 
 /* Tower shape.  vt_config_default() fills the MiniMax-M3 shape; the kernels
@@ -147,17 +150,18 @@ size_t vt_block_workspace_size(const vt_config* cfg, int32_t total_tokens, int32
  * Integer maps of a grid list, written on the device ("v2_loaders FINDINGS",
  * section 3: grid_thw; section 1: per-image native-resolution grids).
  *   cu_seqlens   [n_img+1] int32: cu[0] = 0, cu[i+1] = cu[i] + t*h*w.
- *   pos_thw      [N, 3] int32 in token order: (t, row, col) patch coordinates,
- *                restarting at 0 for each image.
+ *   pos_thw      [N, 3] int32 in token order: (tt, row, col) patch coordinates,
+ *                restarting at 0 for each item.
  *   raster_index [N] int32 in token order, or NULL: global raster index
- *                (cu[i] + row*w + col) of each token. */
+ *                (cu[i] + tt*h*w + row*w + col) of each token. */
 vt_status vt_build_metadata(const vt_grid_thw* grid, int32_t n_img, int32_t* cu_seqlens,
                             int32_t* pos_thw, int32_t* raster_index, void* stream);
 
 /* ---------------------------------------------------------------- steps */
-/* Patchify + patch embed (README Architecture: patch 14, Conv3d patch embed;
- * FINDINGS s.3: the frame is repeated to fill the temporal patch of 2).
- *   pixels    bf16, the images one after another, each [3, 14h, 14w] row-major.
+/* Patchify + patch embed (README Architecture: patch 14, Conv3d patch embed,
+ * temporal patch 2; FINDINGS s.3: a still frame is repeated to fill it).
+ *   pixels    bf16, the items one after another: [3, 14h, 14w] row-major for a
+ *             still image (t == 1), [2t, 3, 14h, 14w] for a clip (t > 1).
  *   resid_out fp32 [N, hidden] in token order: X W_patch^T + b_patch, where
  *             row X[j] = (channel, tau, py, px) of token j's 3x2x14x14 block. */
 vt_status vt_patch_embed(const vt_config* cfg, const uint16_t* pixels, const vt_grid_thw* grid,

@@ -58,3 +58,10 @@ def rng(seed):
 
 def random_bf16(shape, seed, scale=1.0):
     return synth.bf16_bits(rng(seed).standard_normal(shape, dtype=np.float32) * np.float32(scale))
+
+
+def item_pixels(grids, seeds) -> np.ndarray:
+    """Flat bf16 pixels of a list of items: a still image for t == 1
+    ([3, 14h, 14w]), a clip of 2t frames otherwise."""
+    return np.concatenate([(synth.make_pixels(h, w, s) if t == 1 else synth.make_clip(t, h, w, s)).reshape(-1)
+                           for (t, h, w), s in zip(grids, seeds)])

@@ -67,8 +67,13 @@ def test_workspace_size_reports_invalid_grids():
     cfg = vt.config()
     assert vt.vt_tower_workspace_size(cfg, [(1, 3, 4)]) == 0
     assert "even" in vt.last_error()
-    assert vt.vt_tower_workspace_size(cfg, [(2, 4, 4)]) == 0
-    assert "t = 2" in vt.last_error()
+    assert vt.vt_tower_workspace_size(cfg, [(0, 4, 4)]) == 0
+    assert "positive" in vt.last_error()
+    # a clip of t temporal patches is sized like any item of t*h*w tokens, up to
+    # the RoPE table (40 (cos, sin) pairs per position, positions < max(t, h, w))
+    a = vt.vt_tower_workspace_size(cfg, [(4, 8, 8)])
+    b = vt.vt_tower_workspace_size(cfg, [(1, 16, 16)])
+    assert a > 0 and abs(a - b) <= 40 * 8 * 16
     bad = vt.config(head_dim=64, hidden=1024, rope_pairs=(0, 16, 16))
     assert vt.vt_tower_workspace_size(bad, [(1, 4, 4)]) == 0
     assert "head_dim 80" in vt.last_error()
@@ -83,7 +88,7 @@ def _call_metadata(grids):
 def test_metadata_rejects_bad_grids_before_launch():
     assert _call_metadata([(1, 3, 4)]) == vt.VT_ERR_INVALID_ARG
     assert _call_metadata([(1, 4, 0)]) == vt.VT_ERR_INVALID_ARG
-    assert _call_metadata([(3, 4, 4)]) == vt.VT_ERR_UNSUPPORTED
+    assert _call_metadata([(-1, 4, 4)]) == vt.VT_ERR_INVALID_ARG
     g, _ = vt._lib._grid([(1, 4, 4)])
     assert vt.LIB.vt_build_metadata(g, 0, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None,
                                     None) == vt.VT_ERR_INVALID_ARG

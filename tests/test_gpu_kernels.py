@@ -11,8 +11,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import (bf16_f32, cosine_rows, dev_bits, host_bits, log, random_bf16, rel_l2,
-                      rng, window_to_raster)
+from gpu_util import (bf16_f32, cosine_rows, dev_bits, host_bits, item_pixels, log, random_bf16,
+                      rel_l2, rng, window_to_raster)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -32,10 +32,11 @@ def vt():
     [(1, 2, 2), (1, 6, 10), (1, 16, 18)],
     list(synth.WORKLOADS["tower_mixed8"].grids),
     [(1, 144, 144)],
+    [(3, 4, 6), (1, 2, 2), (2, 6, 4), (8, 16, 16)],   # clips (t > 1) and a still image
 ])
 def test_metadata_bit_exact(vt, grids):
     log(f"metadata {grids[:3]}")
-    N = sum(h * w for _, h, w in grids)
+    N = sum(t * h * w for t, h, w in grids)
     cu = torch.full((len(grids) + 1,), -1, dtype=torch.int32, device="cuda")
     pos = torch.full((N, 3), -1, dtype=torch.int32, device="cuda")
     ridx = torch.full((N,), -1, dtype=torch.int32, device="cuda")
@@ -48,13 +49,14 @@ def test_metadata_bit_exact(vt, grids):
 
 
 # ---------------------------------------------------------------- patch embed
-@pytest.mark.parametrize("grids", [[(1, 16, 16)], [(1, 2, 2), (1, 6, 10), (1, 4, 2)]])
+@pytest.mark.parametrize("grids", [[(1, 16, 16)], [(1, 2, 2), (1, 6, 10), (1, 4, 2)],
+                                   [(2, 4, 6), (1, 2, 2), (3, 2, 4)]])
 def test_patch_embed(vt, grids):
     log(f"patch_embed {grids}")
     cfg = vt.config(layers=0)
-    px = np.concatenate([synth.make_pixels(h, w, 10 + i).reshape(-1) for i, (_, h, w) in enumerate(grids)])
+    px = item_pixels(grids, [10 + i for i in range(len(grids))])
     w = synth.make_weights(0, projector=False, affine="random")
-    N = sum(h * ww for _, h, ww in grids)
+    N = sum(t * h * ww for t, h, ww in grids)
     ws = vt.workspace(vt.vt_tower_workspace_size(cfg, grids))
     R = torch.empty((N, 1280), dtype=torch.float32, device="cuda")
     vt.vt_patch_embed(cfg, dev_bits(px, torch), grids, dev_bits(w["patch_w"], torch),

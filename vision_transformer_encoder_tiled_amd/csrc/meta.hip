@@ -1,14 +1,16 @@
 // Integer metadata of a packed image batch, on the device.
 //
-// For each image i with grid (t=1, h, w) (grid_thw of "v2_loaders FINDINGS"
-// section 3; one native-resolution grid per image as in its section 1):
-//   cu_seqlens[i]  first token of the image (prefix sum of h*w),
-//   pos_thw[j]     (t, row, col) of token j, restarting at 0 per image,
-//   raster_index[j] cu[i] + row*w + col,
+// For each item i with grid (t, h, w) (grid_thw of "v2_loaders FINDINGS"
+// section 3; one native-resolution grid per image as in its section 1; t
+// temporal patches of 2 frames for a clip, t = 1 for a still image):
+//   cu_seqlens[i]  first token of the item (prefix sum of t*h*w),
+//   pos_thw[j]     (tt, row, col) of token j, restarting at 0 per item,
+//   raster_index[j] cu[i] + tt*h*w + row*w + col,
 //   tok_img[j]     i.
-// Tokens are stored in 2x2-window order: token 4*(R*(w/2) + C) + 2*dr + dc of
-// an image is the patch at (2R+dr, 2C+dc), so the 2x2 merge of the
-// MiniMax-M3-Vision README ("Token compression" row) is a reshape.
+// Tokens are stored per temporal patch in 2x2-window order: token
+// tt*h*w + 4*(R*(w/2) + C) + 2*dr + dc of an item is the patch at
+// (tt, 2R+dr, 2C+dc), so the 2x2 merge of the MiniMax-M3-Vision README
+// ("Token compression" row) is a reshape.
 #include "vt_device.h"
 #include "vt_kernels.h"
 
@@ -19,27 +21,28 @@ __global__ void __launch_bounds__(256) metadata_kernel(MetaChunk c, int32_t* __r
                                                        int32_t* __restrict__ pos_thw,
                                                        int32_t* __restrict__ raster_index,
                                                        int32_t* __restrict__ tok_img) {
-  const int li = blockIdx.y;  // image within the chunk
+  const int li = blockIdx.y;  // item within the chunk
   if (li >= c.count) return;
   const int img = c.first + li;
-  const int h = c.h[li], w = c.w[li], base = c.cu[li];
+  const int t = c.t[li], h = c.h[li], w = c.w[li], base = c.cu[li];
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     if (cu_seqlens) cu_seqlens[img] = base;
-    if (info) info[img] = ImgInfo{h, w, c.pix_off[li]};
+    if (info) info[img] = ImgInfo{t, h, w, c.pix_off[li]};
   }
-  const int n = h * w, w2 = w >> 1;
+  const int hw = h * w, n = t * hw, w2 = w >> 1;
   for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x) {
-    const int m = j >> 2, k = j & 3;
+    const int ti = j / hw, jj = j - ti * hw;
+    const int m = jj >> 2, k = jj & 3;
     const int row = 2 * (m / w2) + (k >> 1);
     const int col = 2 * (m % w2) + (k & 1);
-    const int t = base + j;
+    const int tk = base + j;
     if (pos_thw) {
-      pos_thw[3 * t + 0] = 0;
-      pos_thw[3 * t + 1] = row;
-      pos_thw[3 * t + 2] = col;
+      pos_thw[3 * tk + 0] = ti;
+      pos_thw[3 * tk + 1] = row;
+      pos_thw[3 * tk + 2] = col;
     }
-    if (raster_index) raster_index[t] = base + row * w + col;
-    if (tok_img) tok_img[t] = img;
+    if (raster_index) raster_index[tk] = base + ti * hw + row * w + col;
+    if (tok_img) tok_img[tk] = img;
   }
 }
 

@@ -6,9 +6,11 @@
 namespace vt {
 
 // One thread per (token, channel, py): reads the 14 pixels of that patch row
-// and writes them twice (tau = 0 and tau = 1: the single frame is repeated to
-// fill the temporal patch of 2, "v2_loaders FINDINGS" section 3).  Row layout
-// of X is (channel, tau, py, px), the flattened Conv3d weight order.
+// in the two frames of its temporal patch (tau = 0 and tau = 1: frames 2tt
+// and 2tt+1 of a clip; a still image's single frame is repeated to fill the
+// temporal patch of 2, "v2_loaders FINDINGS" section 3).  Row layout of X is
+// (channel, tau, py, px), the flattened Conv3d weight order.  Pixels of an
+// item: [frames][3][14h][14w] with 1 frame for t = 1 and 2t frames for t > 1.
 // Pixel rows start at even offsets (14 * col bf16), so the 14 values are read
 // as 7 aligned 32-bit words.
 __global__ void __launch_bounds__(256) patchify_kernel(const uint16_t* __restrict__ pix,
@@ -24,22 +26,31 @@ __global__ void __launch_bounds__(256) patchify_kernel(const uint16_t* __restric
   const int img = tok_img[tok];
   const ImgInfo in = info[img];
   const int j = tok - cu[img];
+  const int hw = in.h * in.w, ti = j / hw, jj = j - ti * hw;
   const int w2 = in.w >> 1;
-  const int m = j >> 2, k = j & 3;
+  const int m = jj >> 2, k = jj & 3;
   const int row = 2 * (m / w2) + (k >> 1);
   const int col = 2 * (m % w2) + (k & 1);
   const int64_t W = int64_t(in.w) * 14, H = int64_t(in.h) * 14;
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(
-      pix + in.pix_off + int64_t(ch) * H * W + (int64_t(row) * 14 + py) * W + int64_t(col) * 14);
-  uint32_t v[7];
+  // Frames 2ti and 2ti+1 of a clip; a still image's one frame serves both.
+  const int64_t frame = 3 * H * W;
+  const int64_t f0 = in.t == 1 ? 0 : int64_t(2 * ti) * frame;
+  const int64_t f1 = in.t == 1 ? 0 : f0 + frame;
+  const int64_t at = in.pix_off + int64_t(ch) * H * W + (int64_t(row) * 14 + py) * W + int64_t(col) * 14;
+  const uint32_t* src0 = reinterpret_cast<const uint32_t*>(pix + at + f0);
+  const uint32_t* src1 = reinterpret_cast<const uint32_t*>(pix + at + f1);
+  uint32_t v0[7], v1[7];
 #pragma unroll
-  for (int i = 0; i < 7; ++i) v[i] = src[i];
+  for (int i = 0; i < 7; ++i) {
+    v0[i] = src0[i];
+    v1[i] = src1[i];
+  }
   uint32_t* dst0 = reinterpret_cast<uint32_t*>(X + int64_t(tok) * 1176 + (ch * 2 + 0) * 196 + py * 14);
   uint32_t* dst1 = reinterpret_cast<uint32_t*>(X + int64_t(tok) * 1176 + (ch * 2 + 1) * 196 + py * 14);
 #pragma unroll
   for (int i = 0; i < 7; ++i) {
-    dst0[i] = v[i];
-    dst1[i] = v[i];
+    dst0[i] = v0[i];
+    dst1[i] = v1[i];
   }
 }
 

@@ -73,10 +73,13 @@ vt_status check_config(const vt_config* c) {
 
 struct GridInfo {
   int64_t tokens = 0;
-  int32_t max_hw = 0;     // largest h or w: RoPE positions lie in [0, max_hw)
+  int32_t max_hw = 0;     // largest t, h or w: RoPE positions lie in [0, max_hw)
   int32_t max_seq = 0;    // largest image token count
   int64_t pixels = 0;
 };
+
+// Frames stored per item: one still frame for t = 1, 2t frames for a clip.
+int64_t frames_of(int32_t t) { return t == 1 ? 1 : 2 * int64_t(t); }
 
 vt_status check_grid(const vt_grid_thw* grid, int32_t n_img, GridInfo* gi) {
   if (!grid) return fail(VT_ERR_INVALID_ARG, "grid is NULL");
@@ -90,16 +93,15 @@ vt_status check_grid(const vt_grid_thw* grid, int32_t n_img, GridInfo* gi) {
     if (x.h % 2 || x.w % 2)
       return fail(VT_ERR_INVALID_ARG, "image %d: h and w must be even for the 2x2 merge (got %d x %d)",
                   i, x.h, x.w);
-    if (x.t != 1)
-      return fail(VT_ERR_UNSUPPORTED, "image %d: t = %d; only still images (t = 1) are implemented",
-                  i, x.t);
-    const int64_t n = int64_t(x.h) * x.w;
+    const int64_t n = int64_t(x.t) * x.h * x.w;
+    if (n > kMaxTokens)
+      return fail(VT_ERR_UNSUPPORTED, "image %d: more than %lld tokens", i, (long long)kMaxTokens);
     g.tokens += n;
     if (g.tokens > kMaxTokens)
       return fail(VT_ERR_UNSUPPORTED, "more than %lld tokens in one call", (long long)kMaxTokens);
-    g.max_hw = std::max(g.max_hw, std::max(x.h, x.w));
+    g.max_hw = std::max(g.max_hw, std::max(x.t, std::max(x.h, x.w)));
     g.max_seq = std::max<int32_t>(g.max_seq, int32_t(n));
-    g.pixels += n * 3 * 196;
+    g.pixels += int64_t(frames_of(x.t)) * x.h * x.w * 3 * 196;
   }
   *gi = g;
   return VT_OK;
@@ -245,14 +247,15 @@ vt_status launch_meta(const vt_grid_thw* grid, int32_t n_img, int64_t total, int
     int32_t maxn = 0;
     for (int i = 0; i < c.count; ++i) {
       const vt_grid_thw& g = grid[first + i];
+      c.t[i] = g.t;
       c.h[i] = g.h;
       c.w[i] = g.w;
       c.cu[i] = int32_t(tok);
       c.pix_off[i] = pix;
-      const int64_t n = int64_t(g.h) * g.w;
+      const int64_t n = int64_t(g.t) * g.h * g.w;
       maxn = std::max<int32_t>(maxn, int32_t(n));
       tok += n;
-      pix += n * 3 * 196;
+      pix += frames_of(g.t) * g.h * g.w * 3 * 196;
     }
     VT_TRY_HIP(vt::launch_metadata(c, maxn, cu, info, pos, ridx, tok_img, s));
   }

@@ -10,13 +10,13 @@ namespace vt {
 
 // ---- metadata (meta.hip)
 constexpr int kMetaChunk = 128;  // images per metadata launch (kernel-argument table)
-struct ImgInfo {                 // one image as the device kernels see it
-  int32_t h, w;
-  int64_t pix_off;               // first pixel of the image in the packed pixel array
+struct ImgInfo {                 // one item (image or clip) as the device kernels see it
+  int32_t t, h, w;               // temporal patches and patch grid; t == 1: one still frame
+  int64_t pix_off;               // first pixel of the item in the packed pixel array
 };
 struct MetaChunk {
-  int32_t first, count;          // images [first, first+count)
-  int32_t h[kMetaChunk], w[kMetaChunk], cu[kMetaChunk];
+  int32_t first, count;          // items [first, first+count)
+  int32_t t[kMetaChunk], h[kMetaChunk], w[kMetaChunk], cu[kMetaChunk];
   int64_t pix_off[kMetaChunk];
 };
 hipError_t launch_metadata(const MetaChunk& c, int32_t max_tokens_in_chunk, int32_t* cu_seqlens,
