@@ -308,6 +308,15 @@ def projector(T, W, grids, cfg: Config):
     return linear(act(linear(z, W["p_w3"], W["p_b3"])), W["p_w4"], W["p_b4"])
 
 
+def mean_pool(T: np.ndarray, grids) -> np.ndarray:
+    """[n_img, d]: the mean of each item's tower tokens -- the sequence
+    mean-pooled to (1, 1280) per image ("v2_loaders FINDINGS" s.3,
+    preprocessing line).  Token order inside an item does not matter."""
+    cu = cu_seqlens(grids)
+    return np.stack([T[cu[i]:cu[i + 1]].mean(axis=0, dtype=np.float64) for i in range(len(grids))]
+                    ).astype(T.dtype)
+
+
 def tower_forward(pixels_bits, grids, weight_bits, cfg: Config = None, n_layers=None,
                   keep_layers=False, projector_on=True):
     """Full forward pass in fp32.  Returns a dict with

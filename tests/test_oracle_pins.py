@@ -465,3 +465,21 @@ def test_output_widths_printed_on_the_pages():
     # tower: 32 blocks x 16 tensors (q, k, v kept separate) + 3 = 515
     per_block_separate_qkv = len(synth.BLOCK_TENSORS) - 2 + 6
     assert g["tower_layers"] * per_block_separate_qkv + 3 == g["tensor_counts"]["tower"]
+
+
+# ---------------------------------------------------------------- mean pool
+def test_mean_pool_closed_forms():
+    grids = [(1, 2, 2), (2, 2, 4), (1, 4, 4)]
+    N = sum(t * h * w for t, h, w in grids)
+    cu = oracle.cu_seqlens(grids)
+    # constant rows per item pool to that constant
+    T = np.zeros((N, 8), np.float32)
+    for i in range(3):
+        T[cu[i]:cu[i + 1]] = i + 0.5
+    assert np.array_equal(oracle.mean_pool(T, grids), np.repeat(np.arange(3) + 0.5, 8).reshape(3, 8))
+    # an arithmetic ramp pools to its midpoint; shuffling rows inside an item changes nothing
+    T = np.arange(N, dtype=np.float64)[:, None] * np.ones((1, 4))
+    want = np.array([[(cu[i] + cu[i + 1] - 1) / 2] * 4 for i in range(3)])
+    np.testing.assert_allclose(oracle.mean_pool(T, grids), want, rtol=1e-15)
+    perm = np.concatenate([cu[i] + rng(i).permutation(cu[i + 1] - cu[i]) for i in range(3)])
+    np.testing.assert_allclose(oracle.mean_pool(T[perm], grids), want, rtol=1e-15)
