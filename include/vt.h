@@ -216,6 +216,17 @@ vt_status vt_tower_forward(const vt_config* cfg, const uint16_t* pixels, const v
                            uint16_t* merged_raw, uint16_t* out, void* ws, size_t ws_bytes,
                            void* stream);
 
+/* Mean-pooled feature ("v2_loaders FINDINGS" section 3: the tower's output
+ * sequence mean-pooled to (1, 1280) per image).
+ *   tower      bf16 [N, hidden] tower tokens in token or raster order (the
+ *              mean does not depend on the order inside an item).
+ *   cu_seqlens [n_img+1] int32 on the device (vt_build_metadata).
+ *   out        fp32 [n_img, hidden]: the mean of each item's rows, summed in
+ *              fp32 in a fixed order (deterministic).
+ * hidden must be a multiple of 128.  No workspace. */
+vt_status vt_mean_pool(const uint16_t* tower, const int32_t* cu_seqlens, int32_t n_img,
+                       int32_t hidden, float* out, void* stream);
+
 /* ---------------------------------------------------------------- kernels
  * The two non-attention kernels of the path, exposed on their own.
  * vt_linear: y = x W^T + b with x bf16 [M, K], W bf16 [N, K], b bf16 [N] or

@@ -325,3 +325,29 @@ def test_block_224(vt, affine):
     log(f"  block rel-L2 {e:.3e}, min cos {cosine_rows(got, ref['tower']).min():.6f}")
     assert e <= 1e-2
     assert cosine_rows(got, ref["tower"]).min() >= 0.999
+
+
+# ---------------------------------------------------------------- mean pool
+@pytest.mark.parametrize("grids", [[(1, 32, 32)], [(1, 2, 2), (3, 4, 6), (1, 144, 144)]])
+def test_mean_pool(vt, grids):
+    """Per-item mean of bf16 tower tokens against the oracle's float64 mean of
+    the same bits.  The tokens are small integers, so every fp32 partial sum
+    is exact and only the final scaling by 1/n rounds: a missing or repeated
+    token or a wrong column would show as an error of at least 1/n."""
+    N = sum(t * h * w for t, h, w in grids)
+    T = synth.bf16_bits(rng(31).integers(-8, 9, (N, 1280)).astype(np.float32))
+    cu = torch.empty(len(grids) + 1, dtype=torch.int32, device="cuda")
+    pos = torch.empty((N, 3), dtype=torch.int32, device="cuda")
+    vt.vt_build_metadata(grids, cu, pos)
+    out = torch.empty((len(grids), 1280), dtype=torch.float32, device="cuda")
+    vt.vt_mean_pool(dev_bits(T, torch), cu, len(grids), 1280, out)
+    torch.cuda.synchronize()
+    want = oracle.mean_pool(bf16_f32(T).astype(np.float64), grids)
+    got = out.cpu().numpy().astype(np.float64)
+    n_min = min(t * h * w for t, h, w in grids)
+    assert np.max(np.abs(got - want)) <= 4 * 2.0 ** -24 * np.max(np.abs(want)) + 2.0 ** -30
+    assert np.max(np.abs(got - want)) < 0.25 / n_min
+    b = torch.empty_like(out)
+    vt.vt_mean_pool(dev_bits(T, torch), cu, len(grids), 1280, b)
+    torch.cuda.synchronize()
+    assert torch.equal(out, b)  # deterministic

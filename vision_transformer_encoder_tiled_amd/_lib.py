@@ -23,7 +23,8 @@ VT_EPI_BF16, VT_EPI_GELU_TANH_BF16, VT_EPI_GELU_ERF_BF16, VT_EPI_RESID_F32, VT_E
 EXPORTED = ("vt_config_default", "vt_status_string", "vt_last_error", "vt_version",
             "vt_tower_workspace_size", "vt_block_workspace_size", "vt_build_metadata",
             "vt_patch_embed", "vt_attention_varlen", "vt_block_forward", "vt_merge_project",
-            "vt_tower_forward", "vt_linear_workspace_size", "vt_linear", "vt_layer_norm")
+            "vt_tower_forward", "vt_mean_pool", "vt_linear_workspace_size", "vt_linear",
+            "vt_layer_norm")
 
 
 class VtError(RuntimeError):
@@ -90,6 +91,7 @@ def _load():
         "vt_linear_workspace_size": (SZ, [I32, I32, I32]),
         "vt_linear": (ctypes.c_int, [_P, I32, I32, _P, I32, _P, ctypes.c_int, _P, _P, SZ, _P]),
         "vt_layer_norm": (ctypes.c_int, [_P, I32, I32, _P, _P, ctypes.c_float, _P, _P]),
+        "vt_mean_pool": (ctypes.c_int, [_P, _P, I32, I32, _P, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -250,6 +252,10 @@ def vt_tower_forward(cfg, pixels, grids, tw: TowerWeights, tower_out, merged_raw
 def vt_linear(x, M, K, w, N, bias, epi, out, ws=None, stream=None):
     _check(LIB.vt_linear(_ptr(x), M, K, _ptr(w), N, _ptr(bias), epi, _ptr(out), _ptr(ws),
                          ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def vt_mean_pool(tower, cu_seqlens, n_img, hidden, out, stream=None):
+    _check(LIB.vt_mean_pool(_ptr(tower), _ptr(cu_seqlens), n_img, hidden, _ptr(out), _stream(stream)))
 
 
 def vt_layer_norm(x, rows, width, g, b, eps, out, stream=None):

@@ -1,5 +1,6 @@
-// Memory-bound permutations: patchify (pixels -> patch rows in token order),
-// row permutation between token order and raster order, fp32 -> bf16 cast.
+// Memory-bound permutations and reductions: patchify (pixels -> patch rows in
+// token order), row permutation between token order and raster order,
+// fp32 -> bf16 cast, per-item mean pool of the tower tokens.
 #include "vt_device.h"
 #include "vt_kernels.h"
 
@@ -100,6 +101,44 @@ hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, size_t n, hipStre
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(unsigned(blocks)), dim3(256), 0, s,
                      reinterpret_cast<const float4*>(src), reinterpret_cast<uint2*>(dst), n4);
+  return hipGetLastError();
+}
+
+// Mean of each item's tower tokens ("v2_loaders FINDINGS" s.3: the sequence
+// mean-pooled to (1, 1280)).  Workgroup (item, 128-column slice) of 16
+// wavefronts: lane l of wave w sums columns 2l, 2l+1 of tokens w, w+16, ...
+// in order (fp32), then the 16 partial sums are added in wave order, so the
+// result is deterministic.
+__global__ void __launch_bounds__(1024) mean_pool_kernel(const uint16_t* __restrict__ T,
+                                                         const int32_t* __restrict__ cu,
+                                                         int32_t hidden, float* __restrict__ out) {
+  __shared__ float2 part[16][64];
+  const int img = blockIdx.x, col = blockIdx.y * 128 + 2 * (threadIdx.x & 63);
+  const int wave = threadIdx.x >> 6;
+  const int beg = cu[img], end = cu[img + 1];
+  float sx = 0.f, sy = 0.f;
+  for (int r = beg + wave; r < end; r += 16) {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(T + int64_t(r) * hidden + col);
+    sx += bflo(v);
+    sy += bfhi(v);
+  }
+  part[wave][threadIdx.x & 63] = make_float2(sx, sy);
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    float2 s = part[0][threadIdx.x];
+    for (int w = 1; w < 16; ++w) {
+      s.x += part[w][threadIdx.x].x;
+      s.y += part[w][threadIdx.x].y;
+    }
+    const float inv = 1.0f / float(end - beg);
+    *reinterpret_cast<float2*>(out + int64_t(img) * hidden + col) = make_float2(s.x * inv, s.y * inv);
+  }
+}
+
+hipError_t launch_mean_pool(const uint16_t* T, const int32_t* cu_seqlens, int32_t n_img,
+                            int32_t hidden, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(mean_pool_kernel, dim3(n_img, hidden / 128), dim3(1024), 0, s, T, cu_seqlens,
+                     hidden, out);
   return hipGetLastError();
 }
 

@@ -668,6 +668,19 @@ VT_API vt_status vt_linear(const uint16_t* x, int32_t M, int32_t K, const uint16
   return VT_OK;
 }
 
+VT_API vt_status vt_mean_pool(const uint16_t* tower, const int32_t* cu_seqlens, int32_t n_img,
+                              int32_t hidden, float* out, void* stream) {
+  vt_status st;
+  if ((st = check_ptr(tower, "tower")) != VT_OK) return st;
+  if ((st = check_ptr(cu_seqlens, "cu_seqlens")) != VT_OK) return st;
+  if ((st = check_ptr(out, "out")) != VT_OK) return st;
+  if (n_img <= 0 || hidden <= 0) return fail(VT_ERR_INVALID_ARG, "n_img and hidden must be positive");
+  if (hidden % 128) return fail(VT_ERR_UNSUPPORTED, "hidden must be a multiple of 128 (got %d)", hidden);
+  if (n_img > 65535) return fail(VT_ERR_UNSUPPORTED, "at most 65535 items per call");
+  VT_TRY_HIP(vt::launch_mean_pool(tower, cu_seqlens, n_img, hidden, out, static_cast<hipStream_t>(stream)));
+  return VT_OK;
+}
+
 VT_API vt_status vt_layer_norm(const float* x, int32_t rows, int32_t width, const uint16_t* g,
                                const uint16_t* b, float eps, uint16_t* out, void* stream) {
   vt_status st;
