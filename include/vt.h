@@ -216,6 +216,33 @@ vt_status vt_tower_forward(const vt_config* cfg, const uint16_t* pixels, const v
                            uint16_t* merged_raw, uint16_t* out, void* ws, size_t ws_bytes,
                            void* stream);
 
+/* ---------------------------------------------------------------- planning
+ * Host-only: no device work, no stream. */
+
+/* Patches one call can hold in a workspace budget: the analogue of the pages'
+ * derive_max_patches ("init.rs (VisionEncoder::new)": patches = area /
+ * patch^2, clamped to what memory affords, the clamp reported).  Scratch here
+ * is O(tokens), so the limit is the budget, not a fixed ceiling.
+ *   budget_bytes workspace bytes available to one call.
+ *   n_img        items per call.
+ *   max_pixels   an area bound in pixels per call, or 0 for none.
+ *   patches      out: min(max_pixels / patch^2, the largest token count, a
+ *                multiple of 4, that fits for any grid of n_img items).
+ *   wanted       out: max_pixels / patch^2 when that was clamped, else 0.
+ * VT_ERR_WORKSPACE if not even 4 tokens per item fit. */
+vt_status vt_plan_patches(const vt_config* cfg, size_t budget_bytes, int32_t n_img,
+                          int64_t max_pixels, int64_t* patches, int64_t* wanted);
+
+/* Greedy packing of the items, in list order, into calls whose workspace
+ * (vt_tower_workspace_size of the call's items) fits budget_bytes: a call
+ * takes items until the next one would not fit.
+ *   batch      out, [n_img] host array: call index of each item (0, 1, ...).
+ *   n_batches  out: number of calls.
+ * VT_ERR_WORKSPACE, naming the item, if one item alone does not fit (nothing
+ * is dropped or clamped). */
+vt_status vt_pack_items(const vt_config* cfg, const vt_grid_thw* grid, int32_t n_img,
+                        size_t budget_bytes, int32_t* batch, int32_t* n_batches);
+
 /* Mean-pooled feature ("v2_loaders FINDINGS" section 3: the tower's output
  * sequence mean-pooled to (1, 1280) per image).
  *   tower      bf16 [N, hidden] tower tokens in token or raster order (the

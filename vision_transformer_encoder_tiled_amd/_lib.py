@@ -23,8 +23,8 @@ VT_EPI_BF16, VT_EPI_GELU_TANH_BF16, VT_EPI_GELU_ERF_BF16, VT_EPI_RESID_F32, VT_E
 EXPORTED = ("vt_config_default", "vt_status_string", "vt_last_error", "vt_version",
             "vt_tower_workspace_size", "vt_block_workspace_size", "vt_build_metadata",
             "vt_patch_embed", "vt_attention_varlen", "vt_block_forward", "vt_merge_project",
-            "vt_tower_forward", "vt_mean_pool", "vt_linear_workspace_size", "vt_linear",
-            "vt_layer_norm")
+            "vt_tower_forward", "vt_plan_patches", "vt_pack_items", "vt_mean_pool",
+            "vt_linear_workspace_size", "vt_linear", "vt_layer_norm")
 
 
 class VtError(RuntimeError):
@@ -92,6 +92,8 @@ def _load():
         "vt_linear": (ctypes.c_int, [_P, I32, I32, _P, I32, _P, ctypes.c_int, _P, _P, SZ, _P]),
         "vt_layer_norm": (ctypes.c_int, [_P, I32, I32, _P, _P, ctypes.c_float, _P, _P]),
         "vt_mean_pool": (ctypes.c_int, [_P, _P, I32, I32, _P, _P]),
+        "vt_plan_patches": (ctypes.c_int, [_P, ctypes.c_size_t, I32, ctypes.c_int64, _P, _P]),
+        "vt_pack_items": (ctypes.c_int, [_P, _P, I32, ctypes.c_size_t, _P, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -252,6 +254,23 @@ def vt_tower_forward(cfg, pixels, grids, tw: TowerWeights, tower_out, merged_raw
 def vt_linear(x, M, K, w, N, bias, epi, out, ws=None, stream=None):
     _check(LIB.vt_linear(_ptr(x), M, K, _ptr(w), N, _ptr(bias), epi, _ptr(out), _ptr(ws),
                          ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def vt_plan_patches(cfg, budget_bytes, n_img=1, max_pixels=0):
+    """(patches, wanted): see include/vt.h."""
+    p, w = ctypes.c_int64(), ctypes.c_int64()
+    _check(LIB.vt_plan_patches(ctypes.byref(cfg), int(budget_bytes), n_img, int(max_pixels),
+                               ctypes.byref(p), ctypes.byref(w)))
+    return p.value, w.value
+
+
+def vt_pack_items(cfg, grids, budget_bytes):
+    """Call index of each item, greedy in list order (see include/vt.h)."""
+    g, n = _grid(grids)
+    batch = (ctypes.c_int32 * n)()
+    nb = ctypes.c_int32()
+    _check(LIB.vt_pack_items(ctypes.byref(cfg), g, n, int(budget_bytes), batch, ctypes.byref(nb)))
+    return list(batch), nb.value
 
 
 def vt_mean_pool(tower, cu_seqlens, n_img, hidden, out, stream=None):

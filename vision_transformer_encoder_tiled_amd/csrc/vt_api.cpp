@@ -122,7 +122,12 @@ struct Carver {
 
 struct Dims {
   int32_t N, n_img, d, mlp, heads, P, Pout;
+  bool ws_upper = false;  // size split-K partials at their bound for any M (capacity planning)
 };
+
+// Split-K partials never exceed 256 tiles of 256 x 256 fp32: tiles x splits
+// is kept <= 256 (gemm.hip plan_gemm).
+constexpr size_t kPartialsBound = size_t(256) * 256 * 256 * sizeof(float);
 
 // Buffers of one block, used by vt_block_forward and vt_tower_forward.
 struct BlockBufs {
@@ -168,7 +173,7 @@ void carve_block(Carver& c, const Dims& D, int32_t n_pos, BlockBufs* b) {
   b->rope = c.take<float2>(size_t(n_pos) * 40);
   b->xn = c.take<uint16_t>(size_t(D.N) * D.d);
   b->act = c.take<uint16_t>(size_t(D.N) * std::max(4 * D.d, D.mlp));
-  b->gemm_ws = c.take<char>(block_gemm_ws(D.N, D.d, D.mlp));
+  b->gemm_ws = c.take<char>(D.ws_upper ? kPartialsBound : block_gemm_ws(D.N, D.d, D.mlp));
 }
 
 struct TowerBufs {
@@ -209,7 +214,7 @@ void carve_tower(Carver& c, const Dims& D, int32_t n_pos, TowerBufs* t) {
   t->Y1 = c.take<uint16_t>(size_t(D.N) * D.P);
   t->Y2 = c.take<uint16_t>(size_t(D.N) * D.P);
   t->U = c.take<uint16_t>(size_t(D.N / 4) * D.Pout);
-  t->proj_ws = c.take<char>(proj_gemm_ws(D.N, D.d, D.P, D.Pout));
+  t->proj_ws = c.take<char>(D.ws_upper ? kPartialsBound : proj_gemm_ws(D.N, D.d, D.P, D.Pout));
 }
 
 Dims dims_of(const vt_config* cfg, int64_t N, int32_t n_img) {
@@ -391,6 +396,18 @@ size_t tower_ws_bytes(const vt_config* cfg, const GridInfo& gi, int32_t n_img) {
   Carver c(nullptr);
   TowerBufs t;
   carve_tower(c, dims_of(cfg, gi.tokens, n_img), gi.max_hw, &t);
+  return c.off;
+}
+
+// A bound on tower_ws_bytes over every grid list of n_img items with N tokens
+// in all: the RoPE table sized for positions up to N and the split-K
+// partials at their bound.  Non-decreasing in N.
+size_t tower_ws_upper(const vt_config* cfg, int64_t N, int32_t n_img) {
+  Carver c(nullptr);
+  TowerBufs t;
+  Dims D = dims_of(cfg, N, n_img);
+  D.ws_upper = true;
+  carve_tower(c, D, int32_t(N), &t);
   return c.off;
 }
 
@@ -665,6 +682,58 @@ VT_API vt_status vt_linear(const uint16_t* x, int32_t M, int32_t K, const uint16
   if (epi < VT_EPI_BF16 || epi > VT_EPI_F32) return fail(VT_ERR_INVALID_ARG, "bad epilogue %d", int(epi));
   if ((st = check_ws(ws, ws_bytes, vt::gemm_workspace_bytes(M, N, K))) != VT_OK) return st;
   VT_TRY_HIP(vt::launch_gemm(x, M, K, w, N, bias, int(epi), out, ws, static_cast<hipStream_t>(stream)));
+  return VT_OK;
+}
+
+VT_API vt_status vt_plan_patches(const vt_config* cfg, size_t budget_bytes, int32_t n_img,
+                                 int64_t max_pixels, int64_t* patches, int64_t* wanted) {
+  vt_status st;
+  if ((st = check_config(cfg)) != VT_OK) return st;
+  if (!patches || !wanted) return fail(VT_ERR_INVALID_ARG, "patches and wanted must not be NULL");
+  if (n_img <= 0) return fail(VT_ERR_INVALID_ARG, "n_img must be >= 1 (got %d)", n_img);
+  if (max_pixels < 0) return fail(VT_ERR_INVALID_ARG, "max_pixels must be >= 0");
+  const int64_t per = int64_t(cfg->patch) * cfg->patch;
+  // Largest multiple of 4 (whole merged tokens) whose bound fits the budget.
+  int64_t lo = 0, hi = kMaxTokens / 4;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (tower_ws_upper(cfg, 4 * mid, n_img) <= budget_bytes) lo = mid; else hi = mid - 1;
+  }
+  const int64_t fit = 4 * lo;
+  if (fit < 4 * int64_t(n_img))
+    return fail(VT_ERR_WORKSPACE, "a workspace of %zu bytes holds no %d-item call (%lld bytes for 4 "
+                "tokens per item)", budget_bytes, n_img, (long long)tower_ws_upper(cfg, 4 * n_img, n_img));
+  const int64_t want = max_pixels > 0 ? std::max<int64_t>(1, max_pixels / per) : fit;
+  *patches = std::min(want, fit);
+  *wanted = want > fit ? want : 0;
+  return VT_OK;
+}
+
+VT_API vt_status vt_pack_items(const vt_config* cfg, const vt_grid_thw* grid, int32_t n_img,
+                               size_t budget_bytes, int32_t* batch, int32_t* n_batches) {
+  vt_status st;
+  if ((st = check_config(cfg)) != VT_OK) return st;
+  GridInfo gi;
+  if ((st = check_grid(grid, n_img, &gi)) != VT_OK) return st;
+  if (!batch || !n_batches) return fail(VT_ERR_INVALID_ARG, "batch and n_batches must not be NULL");
+  auto need = [&](int32_t from, int32_t to) {  // workspace of items [from, to]
+    GridInfo g;
+    check_grid(grid + from, to - from + 1, &g);
+    return tower_ws_bytes(cfg, g, to - from + 1);
+  };
+  int32_t b = 0, first = 0;
+  for (int32_t i = 0; i < n_img; ++i) {
+    if (i > first && need(first, i) > budget_bytes) {
+      ++b;
+      first = i;
+    }
+    if (i == first && need(i, i) > budget_bytes)
+      return fail(VT_ERR_WORKSPACE, "item %d (%d x %d x %d) alone needs %zu workspace bytes, "
+                  "more than the %zu available", i, grid[i].t, grid[i].h, grid[i].w, need(i, i),
+                  budget_bytes);
+    batch[i] = b;
+  }
+  *n_batches = b + 1;
   return VT_OK;
 }
 
