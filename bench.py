@@ -47,7 +47,7 @@ def workload_flops(wl):
     N = wl.tokens
     block, proj = gemm_flops_per_token()
     gemm = N * (2 * 1176 * 1280 + wl.layers * block + (proj if wl.projector else 0))
-    attn = wl.layers * sum(4 * (h * w) ** 2 * 1280 for _, h, w in wl.grids)
+    attn = wl.layers * sum(4 * (t * h * w) ** 2 * 1280 for t, h, w in wl.grids)
     return gemm, attn
 
 
@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="tower_448", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--secondary", default="tower_2016", help="second workload ('' to skip)")
+    ap.add_argument("--more", default="tower_clip16",
+                    help="comma-separated further workloads, throughput only ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-iters", type=int, default=20)
     ap.add_argument("--kernel", choices=["fc1", "attention", "copy"], default=None,
@@ -126,17 +128,17 @@ def fc1_case(vt, torch, M):
 
 def attention_case(vt, torch, grids):
     """vt_attention_varlen on the workload's token layout (random bf16 q, k, v)."""
-    N = sum(h * w for _, h, w in grids)
+    N = sum(t * h * w for t, h, w in grids)
     g = np.random.Generator(np.random.PCG64(1))
     qkv = torch.from_numpy(synth.bf16_bits(g.standard_normal((N, 3840), dtype=np.float32) * 0.7).view(np.int16)).cuda()
     cfg = vt.config()
     cu = torch.empty(len(grids) + 1, dtype=torch.int32, device="cuda")
     pos = torch.empty((N, 3), dtype=torch.int32, device="cuda")
     vt.vt_build_metadata(grids, cu, pos)
-    max_seq = max(h * w for _, h, w in grids)
+    max_seq = max(t * h * w for t, h, w in grids)
     ws = vt.workspace(vt.vt_block_workspace_size(cfg, N, len(grids), max_seq))
     out = torch.empty((N, 1280), dtype=torch.int16, device="cuda")
-    flops = float(sum(4 * (h * w) ** 2 * 1280 for _, h, w in grids))
+    flops = float(sum(4 * (t * h * w) ** 2 * 1280 for t, h, w in grids))
     return (lambda: vt.vt_attention_varlen(cfg, qkv, cu, pos, len(grids), N, max_seq, out, vt.VT_BF16, ws)), flops
 
 
@@ -186,7 +188,7 @@ def gemm_roofline(vt, torch, M, iters):
 def attention_roofline(vt, torch, grids, iters, traffic_profile=None):
     fn, flops = attention_case(vt, torch, grids)
     t = time_kernel(torch, fn, iters)
-    N = sum(h * w for _, h, w in grids)
+    N = sum(t * h * w for t, h, w in grids)
     traffic = (profile_traffic(traffic_profile, "vision_transformer_encoder_tiled_amd/csrc/attention.hip")
                if traffic_profile else None)
     return {"kernel": "attention_kernel (%d tokens, %d images)" % (N, len(grids)), "bound": "mfma",
@@ -295,6 +297,22 @@ def main():
             "gemm_roofline": gemm_roofline(vt, torch, wl2.tokens, max(3, a.kernel_iters // 4)),
         }
         del run2
+
+    more = []
+    for name in [m for m in a.more.split(",") if m]:
+        wl3 = synth.WORKLOADS[name]
+        run3 = Runner(vt, torch, tw, wl3)
+        k3 = max(3, a.steps // 4)
+        s3, _ = run3.time(k3, 1)
+        g3, at3 = workload_flops(wl3)
+        more.append({"workload": wl3.name, "patches": wl3.tokens, "items": wl3.n_img,
+                     "grids": [list(g) for g in wl3.grids][:16],
+                     "patches_per_s": wl3.tokens * k3 / s3, "items_per_s": wl3.n_img * k3 / s3,
+                     "ms_per_step": s3 / k3 * 1e3, "steps": k3,
+                     "tflops_total": (g3 + at3) / (s3 / k3) / 1e12})
+        del run3
+    if more:
+        res["more_workloads"] = more
 
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(weights)

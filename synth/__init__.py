@@ -194,10 +194,14 @@ WORKLOADS = {
                              "8 native-resolution images, seeded even grids in [16, 96]"),
     "tower_2016": Workload("tower_2016", ((1, 144, 144),), (5,), LAYERS, True,
                            "one 2016x2016 image (144x144 patches) through the tower + projector"),
+    "tower_clip16": Workload("tower_clip16", ((8, 32, 32),), (6,), LAYERS, True,
+                             "one 16-frame 448x448 clip (8 temporal patches of 32x32) through the "
+                             "tower + projector"),
 }
 
 
 def make_batch_pixels(wl: Workload) -> np.ndarray:
-    """All images of a workload, flattened and concatenated (bf16 bits)."""
-    return np.concatenate([make_pixels(h, w, s).reshape(-1)
+    """All items of a workload, flattened and concatenated (bf16 bits): one
+    frame per still image (t = 1), 2t frames per clip."""
+    return np.concatenate([(make_pixels(h, w, s) if t == 1 else make_clip(t, h, w, s)).reshape(-1)
                            for (t, h, w), s in zip(wl.grids, wl.seeds)])
