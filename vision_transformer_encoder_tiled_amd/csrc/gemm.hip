@@ -412,6 +412,36 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
     }
     __syncthreads();
     constexpr int TOTAL = PASS_ROWS * CHUNKS;
+    constexpr int PER = (TOTAL + 64 * NW - 1) / (64 * NW);  // chunks per thread per pass
+    if constexpr (EPI == kEpiResid && !SPLIT) {
+      // Residual update: every old value this thread needs is loaded first,
+      // so the loads are in flight together rather than one store apart.
+      float4 old[PER];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = tid + j * 64 * NW;
+        const int r = i / CHUNKS, c = i % CHUNKS;
+        const int tok = m0 + pass * PASS_ROWS + r, col = n0 + c * EPC;
+        if (i < TOTAL && tok < M && col < N)
+          old[j] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(out) +
+                                                    int64_t(tok) * N + col);
+      }
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = tid + j * 64 * NW;
+        const int r = i / CHUNKS, c = i % CHUNKS;
+        const int tok = m0 + pass * PASS_ROWS + r, col = n0 + c * EPC;
+        if (i >= TOTAL || tok >= M || col >= N) continue;
+        float4 a = *reinterpret_cast<const float4*>(cs + r * ROWB + ((c + (r & 15)) % CHUNKS) * 16);
+        if (bias) {
+          const uint2 bb = *reinterpret_cast<const uint2*>(bias + col);
+          a.x += bflo(bb.x); a.y += bfhi(bb.x); a.z += bflo(bb.y); a.w += bfhi(bb.y);
+        }
+        a.x = old[j].x + a.x; a.y = old[j].y + a.y; a.z = old[j].z + a.z; a.w = old[j].w + a.w;
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + int64_t(tok) * N + col) = a;
+      }
+      continue;
+    }
 #pragma unroll
     for (int i = tid; i < TOTAL; i += 64 * NW) {
       const int r = i / CHUNKS, c = i % CHUNKS;
