@@ -11,6 +11,8 @@ of the forward pass of the MiniMax-M3 vision tower (MiniMax-M3-Vision README,
 temporal patch 2; the four-Linear projector).  It shares no code with the HIP
 path: the only common module is ``synth`` (seeded random inputs).
 
-Parity status per function is listed in ``oracle.vit``'s docstring.
+Parity status per function is listed in ``oracle.vit``'s docstring.  The
+gradients of one block (the backward pass) are in ``oracle.grad``.
 """
 from .vit import *  # noqa: F401,F403
+from . import grad  # noqa: F401
