@@ -183,6 +183,33 @@ vt_status vt_attention_varlen(const vt_config* cfg, const uint16_t* qkv, const i
                               int32_t max_seqlen, void* out, vt_dtype out_dtype, void* ws,
                               size_t ws_bytes, void* stream);
 
+/* Gradient of vt_attention_varlen with respect to its qkv input ("v2_loaders
+ * FINDINGS", section 3: the towers are differentiable; the probe's backward
+ * pass).  Per image and head, with P = softmax(q k^T / sqrt(head_dim)) of the
+ * rotated q, k and D_i = sum_d dO_id O_id:
+ *   dv = P^T dO,  dS = P * (dO v^T - D),  dq = dS k / sqrt(head_dim),
+ *   dk = dS^T q / sqrt(head_dim),
+ * then dq and dk rotated back by the opposite RoPE angle.
+ *   qkv, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen: as in
+ *              vt_attention_varlen (the forward is recomputed inside; its
+ *              output and per-query log-sum-exp stay in the workspace).
+ *   dout       bf16 [N, heads*head_dim]: dL/d(out), out as vt_attention_varlen's.
+ *   dqkv       [N, 3, heads, head_dim], bf16 or fp32 by dqkv_dtype: dL/d(qkv).
+ *              Every element is written; it may not overlap qkv or dout.
+ *   ws         device workspace of vt_attention_backward_workspace_size bytes
+ *              (about 36 KB per token at 16 heads, affine in the token count).
+ * Pointers are 16-byte aligned device memory owned by the caller; ws 256-byte
+ * aligned.  Errors as for vt_attention_varlen; nothing is launched on error. */
+vt_status vt_attention_backward(const vt_config* cfg, const uint16_t* qkv, const int32_t* cu_seqlens,
+                                const int32_t* pos_thw, int32_t n_img, int32_t total_tokens,
+                                int32_t max_seqlen, const uint16_t* dout, void* dqkv,
+                                vt_dtype dqkv_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for vt_attention_backward.
+ * Returns 0 and sets vt_last_error() if the arguments are invalid. */
+size_t vt_attention_backward_workspace_size(const vt_config* cfg, int32_t total_tokens,
+                                            int32_t n_img, int32_t max_seqlen);
+
 /* One pre-LN block on the fp32 residual, in place:
  *   R += O(attention(RoPE(LN1(R) W_qkv^T + b_qkv)))  with O(a) = a W_o^T + b_o
  *   R += GELU_tanh(LN2(R) W_fc1^T + b_fc1) W_fc2^T + b_fc2

@@ -122,3 +122,34 @@ def block_backward(R, W, pos, cu, cfg: vit.Config, dR2, prefix="l0."):
     dx1, grads["w_qkv"], grads["b_qkv"] = linear_backward(x1, g("w_qkv"), dqkv)
     dln1, grads["ln1_g"], grads["ln1_b"] = layer_norm_backward(R, g("ln1_g"), dx1, cfg.ln_eps)
     return dR1 + dln1, grads
+
+
+def attention_dq_rows(qkv, pos, cu, dout, rows, cfg: vit.Config = None):
+    """Rows ``rows`` (token indices) of the q part of attention_qkv_backward.
+    A query's gradient needs only its own softmax row, so this costs
+    O(len(rows) * n) per head and serves sampled checks of long images."""
+    cfg = cfg or vit.Config()
+    N = qkv.shape[0]
+    H, hd = cfg.heads, cfg.head_dim
+    axis, inv = vit.rope_tables(hd, cfg.rope_sections, cfg.rope_theta, cfg.rope_shared_ladder)
+    rows = np.asarray(rows)
+    out = np.empty((len(rows), H, hd), qkv.dtype)
+    d = dout.reshape(N, H, hd)
+    scale = 1.0 / np.sqrt(hd)
+    for i in range(len(cu) - 1):
+        a, b = int(cu[i]), int(cu[i + 1])
+        sel = np.nonzero((rows >= a) & (rows < b))[0]
+        if len(sel) == 0:
+            continue
+        r = rows[sel]
+        q = vit.apply_rope(qkv[r, 0], pos[r], axis, inv)                # m, H, hd
+        k = vit.apply_rope(qkv[a:b, 1], pos[a:b], axis, inv)           # n, H, hd
+        v = qkv[a:b, 2]
+        for h in range(H):
+            p = vit.softmax_rows(q[:, h] @ k[:, h].T * scale)          # m, n
+            o = p @ v[:, h]
+            dp = d[r, h] @ v[:, h].T
+            ds = p * (dp - (d[r, h] * o).sum(axis=-1, keepdims=True))
+            out[sel, h] = ds @ k[:, h] * scale
+        out[sel] = rope_backward(out[sel], pos[r], axis, inv)
+    return out

@@ -30,7 +30,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     declared = header_functions()
-    assert len(declared) == 18
+    assert len(declared) == 20
     assert sorted(vt.EXPORTED) == declared
     lib = ctypes.CDLL(vt.LIB_PATH)
     for name in declared:
@@ -122,6 +122,36 @@ def test_attention_validation():
     assert _attn(vt.config(head_dim=64, hidden=1024, rope_pairs=(0, 16, 16))) == vt.VT_ERR_UNSUPPORTED
     assert _attn(vt.config(rope_pairs=(8, 12, 20))) == vt.VT_ERR_UNSUPPORTED
     assert _attn(vt.config(rope_pairs=(8, 16, 8))) == vt.VT_ERR_INVALID_ARG
+
+
+def _attn_bwd(cfg, qkv=FAKE, dout=FAKE, dqkv=FAKE, n_img=1, total=64, max_seq=64, ws=FAKE,
+              ws_bytes=None, dtype=vt.VT_FP32):
+    if ws_bytes is None:
+        ws_bytes = vt.vt_attention_backward_workspace_size(cfg, total, n_img, max_seq)
+    P = lambda v: None if v is None else ctypes.c_void_p(v)
+    return vt.LIB.vt_attention_backward(ctypes.byref(cfg), P(qkv), P(FAKE), P(FAKE), n_img, total,
+                                        max_seq, P(dout), P(dqkv), dtype, P(ws), ws_bytes, None)
+
+
+@needs_no_gpu
+def test_attention_backward_validation():
+    cfg = vt.config()
+    need = vt.vt_attention_backward_workspace_size(cfg, 64, 1, 64)
+    assert need > vt.vt_block_workspace_size(cfg, 64, 1, 64) // 2
+    assert _attn_bwd(cfg, ws_bytes=need - 1) == vt.VT_ERR_WORKSPACE
+    assert _attn_bwd(cfg, dout=None) == vt.VT_ERR_INVALID_ARG
+    assert _attn_bwd(cfg, dqkv=FAKE + 4) == vt.VT_ERR_INVALID_ARG
+    assert _attn_bwd(cfg, n_img=0) == vt.VT_ERR_INVALID_ARG
+    assert _attn_bwd(cfg, dtype=5) == vt.VT_ERR_INVALID_ARG
+    assert _attn_bwd(vt.config(head_dim=64, hidden=1024, rope_pairs=(0, 16, 16))) == vt.VT_ERR_UNSUPPORTED
+    assert vt.vt_attention_backward_workspace_size(cfg, 0, 1, 1) == 0
+
+
+def test_attention_backward_workspace_is_affine():
+    cfg = vt.config()
+    s = [vt.vt_attention_backward_workspace_size(cfg, n, 1, n) for n in (4096, 8192, 16384)]
+    assert abs((s[2] - s[1]) - 2 * (s[1] - s[0])) <= 4096
+    assert (s[1] - s[0]) / 4096 < 40 * 1024       # about 36 KB per token at 16 heads
 
 
 @needs_no_gpu

@@ -1,0 +1,137 @@
+"""GPU parity of the attention backward pass (vt_attention_backward) against
+the float64 oracle of oracle/grad.py, through the C ABI.
+
+Tolerance: relative L2 error <= 1e-2 for each of dq, dk, dv (the bar used for
+one block's output).  The kernels round q, k, v, dO, P and dS to fp16 (2^-11
+relative) and accumulate in fp32, so the expected error is a few times 2^-11;
+the bf16 output adds 2^-9 relative.  The library orders tokens by 2x2
+windows; attention is equivariant under any permutation inside an image, so
+the oracle runs in the same order with the positions permuted alike."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import bf16_f32, dev_bits, host_bits, log, rel_l2, rng, window_to_raster
+from oracle import grad as G
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+H, HD = 16, 80
+
+
+@pytest.fixture(scope="module")
+def vt():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import vision_transformer_encoder_tiled_amd as m
+    return m
+
+
+def run_backward(vt, grids, qkv_bits, dout_bits, f32=True):
+    """vt_attention_backward on window-order bf16 inputs; returns dqkv
+    [N, 3, H, 80] as float32 (window order)."""
+    N = qkv_bits.shape[0]
+    cfg = vt.config()
+    cu = torch.empty(len(grids) + 1, dtype=torch.int32, device="cuda")
+    pos = torch.empty((N, 3), dtype=torch.int32, device="cuda")
+    vt.vt_build_metadata(grids, cu, pos)
+    max_seq = max(t * h * w for t, h, w in grids)
+    ws = vt.workspace(vt.vt_attention_backward_workspace_size(cfg, N, len(grids), max_seq))
+    dq = torch.full((N, 3, H, HD), float("nan"), dtype=torch.float32, device="cuda") if f32 else \
+        torch.full((N, 3, H, HD), -1, dtype=torch.int16, device="cuda")
+    vt.vt_attention_backward(cfg, dev_bits(qkv_bits, torch), cu, pos, len(grids), N, max_seq,
+                             dev_bits(dout_bits, torch), dq, vt.VT_FP32 if f32 else vt.VT_BF16, ws)
+    torch.cuda.synchronize()
+    return dq.cpu().numpy() if f32 else bf16_f32(host_bits(dq))
+
+
+def window_positions(grids):
+    return oracle.positions(grids)[window_to_raster(grids)]
+
+
+def random_inputs(N, seed, qk_scale=1.0):
+    g = rng(seed)
+    qkv = g.standard_normal((N, 3, H, HD), dtype=np.float32)
+    qkv[:, :2] *= np.float32(qk_scale)
+    dout = g.standard_normal((N, H * HD), dtype=np.float32)
+    return synth.bf16_bits(qkv), synth.bf16_bits(dout)
+
+
+def check_parts(got, want, tol, what):
+    errs = [rel_l2(got[:, i], want[:, i]) for i in range(3)]
+    log(f"  {what}: rel-L2 dq {errs[0]:.2e} dk {errs[1]:.2e} dv {errs[2]:.2e}")
+    assert np.all(np.isfinite(got))
+    assert max(errs) <= tol
+
+
+@pytest.mark.parametrize("grids,seed", [
+    ([(1, 12, 14)], 41),                         # 168 tokens: 2 full 64-key tiles + 40, 128-tile + 40
+    ([(1, 16, 18), (1, 2, 2), (3, 4, 6)], 42),   # several items, a 4-token image, a clip
+    ([(1, 2, 2)], 43),                           # one 4-token image: a single ragged tile
+])
+@pytest.mark.parametrize("out_dtype", ["fp32", "bf16"])
+def test_attention_backward_parity(vt, grids, seed, out_dtype):
+    log(f"attention backward {grids} {out_dtype}")
+    N = sum(t * h * w for t, h, w in grids)
+    qkv, dout = random_inputs(N, seed)
+    got = run_backward(vt, grids, qkv, dout, f32=out_dtype == "fp32")
+    want = G.attention_qkv_backward(bf16_f32(qkv).astype(np.float64), window_positions(grids),
+                                    oracle.cu_seqlens(grids), bf16_f32(dout).astype(np.float64))
+    check_parts(got, want, 1e-2, "full")
+
+
+def test_attention_backward_sharp_scores(vt):
+    """q, k ~ N(0, 9): peaked softmax rows (scores of std ~9)."""
+    grids = [(1, 10, 12)]
+    qkv, dout = random_inputs(120, 44, qk_scale=3.0)
+    got = run_backward(vt, grids, qkv, dout)
+    want = G.attention_qkv_backward(bf16_f32(qkv).astype(np.float64), window_positions(grids),
+                                    oracle.cu_seqlens(grids), bf16_f32(dout).astype(np.float64))
+    check_parts(got, want, 1e-2, "sharp")
+
+
+def test_attention_backward_block0_448(vt):
+    """The block-0 QKV activations of the 448x448 image (1024 tokens), whole."""
+    from test_gpu_kernels import layer0_qkv_bits
+    grids = [(1, 32, 32)]
+    perm = window_to_raster(grids)
+    qkv = layer0_qkv_bits(grids, [2])[perm].reshape(1024, 3, H, HD)
+    dout = synth.bf16_bits(rng(45).standard_normal((1024, H * HD), dtype=np.float32))
+    got = run_backward(vt, grids, qkv, dout)
+    want = G.attention_qkv_backward(bf16_f32(qkv).astype(np.float64), window_positions(grids),
+                                    oracle.cu_seqlens(grids), bf16_f32(dout).astype(np.float64))
+    check_parts(got, want, 1e-2, "block0 448")
+
+
+def test_attention_backward_2016_sampled(vt):
+    """One 2016x2016 image (20,736 tokens, the largest configuration): dq on
+    sampled rows against the oracle row by row; dv and dk through identities
+    that hold at any size -- sum over keys of dv = sum over queries of dO, and
+    the keys' dk rotated forward by RoPE sum to zero -- each to 1e-2 of the
+    root-sum-square of the summed gradients (the size that independent
+    relative errors of 1e-2 would leave)."""
+    grids = [(1, 144, 144)]
+    N = 20736
+    qkv, dout = random_inputs(N, 46)
+    got = run_backward(vt, grids, qkv, dout)
+    pos = window_positions(grids)
+    x = bf16_f32(qkv).astype(np.float64)
+    d = bf16_f32(dout).astype(np.float64)
+    rows = np.unique(np.r_[0:16, N - 16:N, rng(47).integers(0, N, 160)])
+    want_q = G.attention_dq_rows(x, pos, oracle.cu_seqlens(grids), d, rows)
+    e = rel_l2(got[rows, 0], want_q)
+    log(f"  2016 sampled dq rel-L2 {e:.2e}")
+    assert e <= 1e-2
+    dv = got[:, 2].astype(np.float64)
+    s_err = np.linalg.norm(dv.sum(0) - d.reshape(N, H, HD).sum(0))
+    rss = np.sqrt((dv ** 2).sum())
+    log(f"  dv sum error {s_err:.3e} (rss {rss:.3e})")
+    assert s_err <= 1e-2 * rss
+    axis, inv = oracle.rope_tables()
+    dk_rot = oracle.apply_rope(got[:, 1].astype(np.float64), pos, axis, inv)
+    k_sum = np.linalg.norm(dk_rot.sum(0))
+    rss_k = np.sqrt((dk_rot ** 2).sum())
+    log(f"  rotated dk sum {k_sum:.3e} (rss {rss_k:.3e})")
+    assert k_sum <= 1e-2 * rss_k

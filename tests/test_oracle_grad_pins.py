@@ -131,3 +131,42 @@ def test_block_gradient_finite_differences_and_autograd():
     np.testing.assert_allclose(dR, Rt.grad.numpy(), rtol=1e-9, atol=1e-10)
     for k, v in grads.items():
         np.testing.assert_allclose(v, T["l0." + k].grad.numpy(), rtol=1e-9, atol=1e-10, err_msg=k)
+
+
+def _qkv_attention(qkv, pos, cu, cfg):
+    axis, inv = oracle.rope_tables(cfg.head_dim, cfg.rope_sections, cfg.rope_theta, cfg.rope_shared_ladder)
+    q = oracle.apply_rope(qkv[:, 0], pos, axis, inv)
+    k = oracle.apply_rope(qkv[:, 1], pos, axis, inv)
+    return oracle.attention_varlen(q, k, np.ascontiguousarray(qkv[:, 2]), cu).reshape(qkv.shape[0], -1)
+
+
+def test_attention_qkv_gradient_and_sampled_rows():
+    """attention_qkv_backward (RoPE included) against central differences;
+    attention_dq_rows equals its q rows; and the two identities the sampled
+    GPU checks use: sum over keys of dv = sum over queries of dO (softmax rows
+    sum to 1), and sum over keys of the rotated-frame dk = 0 (each row of dS
+    sums to 0)."""
+    cfg = TINY
+    grids = [(1, 2, 4), (1, 2, 2)]
+    pos = oracle.positions(grids)
+    cu = oracle.cu_seqlens(grids)
+    N, H, hd = 12, cfg.heads, cfg.head_dim
+    qkv = rng(30).standard_normal((N, 3, H, hd))
+    do = rng(31).standard_normal((N, H * hd))
+    g = G.attention_qkv_backward(qkv, pos, cu, do, cfg)
+    fd_dot(lambda t: _qkv_attention(t, pos, cu, cfg), qkv, do, g)
+    rows = np.array([0, 5, 7, 9, 11])
+    np.testing.assert_allclose(G.attention_dq_rows(qkv, pos, cu, do, rows, cfg), g[rows, 0],
+                               rtol=1e-12, atol=1e-12)
+    axis, inv = oracle.rope_tables(hd, cfg.rope_sections, cfg.rope_theta, cfg.rope_shared_ladder)
+    dk_rot = oracle.apply_rope(g[:, 1], pos, axis, inv)
+    d3 = do.reshape(N, H, hd)
+    for i in range(len(cu) - 1):
+        a, b = cu[i], cu[i + 1]
+        np.testing.assert_allclose(g[a:b, 2].sum(0), d3[a:b].sum(0), rtol=1e-12, atol=1e-12)
+        assert np.max(np.abs(dk_rot[a:b].sum(0))) < 1e-12
+    # a planted sign error in dS breaks the finite-difference pin
+    bad = g.copy()
+    bad[:, 0] *= -1
+    with pytest.raises(AssertionError):
+        fd_dot(lambda t: _qkv_attention(t, pos, cu, cfg), qkv, do, bad)

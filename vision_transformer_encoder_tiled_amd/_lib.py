@@ -24,7 +24,8 @@ EXPORTED = ("vt_config_default", "vt_status_string", "vt_last_error", "vt_versio
             "vt_tower_workspace_size", "vt_block_workspace_size", "vt_build_metadata",
             "vt_patch_embed", "vt_attention_varlen", "vt_block_forward", "vt_merge_project",
             "vt_tower_forward", "vt_plan_patches", "vt_pack_items", "vt_mean_pool",
-            "vt_linear_workspace_size", "vt_linear", "vt_layer_norm")
+            "vt_linear_workspace_size", "vt_linear", "vt_layer_norm", "vt_attention_backward",
+            "vt_attention_backward_workspace_size")
 
 
 class VtError(RuntimeError):
@@ -81,6 +82,9 @@ def _load():
         "vt_patch_embed": (ctypes.c_int, [cfgp, _P, gridp, I32, _P, _P, _P, _P, SZ, _P]),
         "vt_attention_varlen": (ctypes.c_int, [cfgp, _P, _P, _P, I32, I32, I32, _P, ctypes.c_int,
                                                _P, SZ, _P]),
+        "vt_attention_backward": (ctypes.c_int, [cfgp, _P, _P, _P, I32, I32, I32, _P, _P,
+                                                 ctypes.c_int, _P, SZ, _P]),
+        "vt_attention_backward_workspace_size": (SZ, [cfgp, I32, I32, I32]),
         "vt_block_forward": (ctypes.c_int, [cfgp, _P, ctypes.POINTER(vt_block_weights), _P, _P,
                                             I32, I32, I32, _P, SZ, _P]),
         "vt_merge_project": (ctypes.c_int, [cfgp, _P, ctypes.c_int, gridp, I32,
@@ -191,6 +195,19 @@ def vt_attention_varlen(cfg, qkv, cu_seqlens, pos_thw, n_img, total_tokens, max_
     _check(LIB.vt_attention_varlen(ctypes.byref(cfg), _ptr(qkv), _ptr(cu_seqlens), _ptr(pos_thw),
                                    n_img, total_tokens, max_seqlen, _ptr(out), out_dtype, _ptr(ws),
                                    ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def vt_attention_backward_workspace_size(cfg, total_tokens, n_img, max_seqlen) -> int:
+    return int(LIB.vt_attention_backward_workspace_size(ctypes.byref(cfg), total_tokens, n_img,
+                                                        max_seqlen))
+
+
+def vt_attention_backward(cfg, qkv, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen, dout,
+                          dqkv, dqkv_dtype, ws, stream=None):
+    _check(LIB.vt_attention_backward(ctypes.byref(cfg), _ptr(qkv), _ptr(cu_seqlens), _ptr(pos_thw),
+                                     n_img, total_tokens, max_seqlen, _ptr(dout), _ptr(dqkv),
+                                     dqkv_dtype, _ptr(ws), ws.numel() if ws is not None else 0,
+                                     _stream(stream)))
 
 
 def block_weights(w: dict, prefix: str = "") -> vt_block_weights:

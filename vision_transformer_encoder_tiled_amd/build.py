@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libvt.so")
 OBJ = os.path.join(ROOT, "_build")
-SOURCES = ["meta.hip", "permute.hip", "layernorm.hip", "gemm.hip", "attention.hip", "vt_api.cpp"]
+SOURCES = ["meta.hip", "permute.hip", "layernorm.hip", "gemm.hip", "attention.hip", "attention_bwd.hip",
+           "vt_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 instructions are disabled: the compiler would otherwise form
 # v_pk_* fp32 ops from ordinary float code.
@@ -25,10 +26,12 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hi
          "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 
-# Per-file flags.  attention.hip keeps its MFMA accumulators in ordinary
-# VGPRs (its whole working set fits in 256), which avoids AGPR<->VGPR copies
-# around the softmax; the GEMM needs the AGPR file for its 256 accumulators.
-EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-file flags.  The attention kernels (forward and backward) keep their
+# MFMA accumulators in ordinary VGPRs (their working sets fit in 256, which
+# allows two wavefronts per SIMD), avoiding AGPR<->VGPR copies around the
+# softmax; the GEMM needs the AGPR file for its 256 accumulators.
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "attention_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:

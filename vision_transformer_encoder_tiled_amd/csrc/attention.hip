@@ -81,10 +81,6 @@ constexpr int STAGE_BYTES = K_BYTES + 96 * VROW * 2;  // 25088: the MFMA reads V
 constexpr float kLazy = 8.0f;       // log2 growth of the row max tolerated before rescaling
 static_assert(K_BYTES + V_ROWS * VROW * 2 <= IMG_BYTES, "tile image size");
 
-// V^T slot of key k inside its group of 16: swap bits 2 and 3.
-__device__ __forceinline__ int vslot(int k) {
-  return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
 }  // namespace
 
 // ---------------------------------------------------------------- pack
@@ -160,7 +156,7 @@ __global__ void __launch_bounds__(320) attn_pack_kernel(
   *reinterpret_cast<uint4*>(kimg + k * KROW + 8 * c) = make_uint4(kr[0], kr[1], kr[2], kr[3]);
   *reinterpret_cast<uint4*>(kimg + k * KROW + 40 + 8 * c) = make_uint4(kr[4], kr[5], kr[6], kr[7]);
   // V^T through LDS: element (dim, slot of key k).
-  const int s = vslot(k);
+  const int s = mfma_slot16(k);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     vs[(8 * c + 2 * j) * BKV + s] = uint16_t(vt[j] & 0xffffu);
@@ -190,7 +186,8 @@ __global__ void __launch_bounds__(320) attn_pack_kernel(
 template <int NW, int KG, int NST>
 __global__ void __launch_bounds__(64 * NW) attention_kernel(
     const uint16_t* __restrict__ qpk, const uint16_t* __restrict__ kv,
-    const int4* __restrict__ qdesc, int32_t heads, void* __restrict__ out, int32_t out_f32) {
+    const int4* __restrict__ qdesc, int32_t heads, void* __restrict__ out, int32_t out_f32,
+    float* __restrict__ lse) {
   static_assert(NST == 3 || (NST == 4 && KG == 1), "stage ring");
   constexpr int QW = NW / KG;             // query wavefronts per group
   constexpr int COPIES = IMG_BYTES / (1024 * NW);  // 1 KB DMA pieces per wave per tile
@@ -426,6 +423,7 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(
     for (int d = 0; d < 3; ++d)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[d][e] = acc[d][e] * s0 + xs[(16 * d + e) * 64 * QW + slot] * s1;
+    m_use = m;
   }
 
   // ---- normalise and store: acc[d][4g + r] is dim 32d + 8g + 4hf + r of query ln;
@@ -433,6 +431,8 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(
   const float l_half0 = __shfl(acc[2][8], ln, 64);
   const float inv = 1.0f / l_half0;
   if (!qvalid) return;
+  // log2-domain log-sum-exp of the query's scaled scores, for the backward pass.
+  if (lse && hf == 0) lse[int64_t(qrow) * heads + head] = m_use + log2f(l_half0);
   const int64_t orow = int64_t(qrow) * heads * HD + head * HD;
 #pragma unroll
   for (int d = 0; d < 3; ++d) {
@@ -456,7 +456,7 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(
 template <int NW, int KG, int NST>
 static hipError_t launch_attention_kernel(const uint16_t* qpk, const uint16_t* kv,
                                           const int4* qdesc, int32_t max_qtiles, int32_t heads,
-                                          void* out, bool out_f32, hipStream_t s) {
+                                          void* out, bool out_f32, float* lse, hipStream_t s) {
   const size_t lds = size_t(NST) * KG * STAGE_BYTES;
   auto kern = attention_kernel<NW, KG, NST>;
   static const hipError_t attr = hipFuncSetAttribute(
@@ -464,7 +464,7 @@ static hipError_t launch_attention_kernel(const uint16_t* qpk, const uint16_t* k
   if (attr != hipSuccess) return attr;
   const int64_t blocks = int64_t(max_qtiles) * heads;
   hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(64 * NW), lds, s, qpk, kv, qdesc, heads,
-                     out, out_f32 ? 1 : 0);
+                     out, out_f32 ? 1 : 0, lse);
   return hipGetLastError();
 }
 
@@ -472,14 +472,15 @@ hipError_t launch_attention(const uint16_t* qkv, const int32_t* pos_thw, const i
                             const int2* kdesc, int32_t max_qtiles, int32_t max_ktiles,
                             int32_t heads, int32_t n_pos, int32_t axis_code, const float2* rope_cs,
                             float q_scale_log2, int32_t key_groups, uint16_t* qpk, uint16_t* kv,
-                            void* out, bool out_f32, hipStream_t s) {
+                            void* out, bool out_f32, float* lse, hipStream_t s) {
   hipLaunchKernelGGL(attn_pack_kernel, dim3(max_ktiles, heads), dim3(320), 0, s, qkv, pos_thw,
                      kdesc, heads, n_pos, rope_cs, axis_code, q_scale_log2, qpk, kv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (key_groups == 2)
-    return launch_attention_kernel<4, 2, 3>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, s);
-  return launch_attention_kernel<kAttnWaves1, 1, kAttnStages1>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, s);
+    return launch_attention_kernel<4, 2, 3>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, lse, s);
+  return launch_attention_kernel<kAttnWaves1, 1, kAttnStages1>(qpk, kv, qdesc, max_qtiles, heads, out,
+                                                                out_f32, lse, s);
 }
 
 }  // namespace vt

@@ -161,7 +161,8 @@ int32_t max_q_tiles(int64_t N, int32_t n_img, int32_t q_tile) {
   return int32_t((N + q_tile - 1) / q_tile + n_img);
 }
 
-void carve_block(Carver& c, const Dims& D, int32_t n_pos, BlockBufs* b) {
+// The attention step's buffers (schedule, packed Q, tile images, RoPE table).
+void carve_attention(Carver& c, const Dims& D, int32_t n_pos, BlockBufs* b) {
   b->order = c.take<int32_t>(D.n_img);
   b->tile_start = c.take<int32_t>(D.n_img + 1);
   b->ktile_start = c.take<int32_t>(D.n_img + 1);
@@ -171,6 +172,10 @@ void carve_block(Carver& c, const Dims& D, int32_t n_pos, BlockBufs* b) {
   b->kv = reinterpret_cast<uint16_t*>(
       c.take<char>(size_t(D.heads) * max_k_tiles(D.N, D.n_img) * vt::kAttnTileBytes));
   b->rope = c.take<float2>(size_t(n_pos) * 40);
+}
+
+void carve_block(Carver& c, const Dims& D, int32_t n_pos, BlockBufs* b) {
+  carve_attention(c, D, n_pos, b);
   b->xn = c.take<uint16_t>(size_t(D.N) * D.d);
   b->act = c.take<uint16_t>(size_t(D.N) * std::max(4 * D.d, D.mlp));
   b->gemm_ws = c.take<char>(D.ws_upper ? kPartialsBound : block_gemm_ws(D.N, D.d, D.mlp));
@@ -295,11 +300,11 @@ float q_scale_log2(const vt_config* cfg) {
 vt_status run_attention(const vt_config* cfg, const uint16_t* qkv, const int32_t* cu,
                         const int32_t* pos, int32_t n_img, int64_t N, int32_t n_pos,
                         int32_t axis_code, const BlockBufs& b, void* out, bool f32,
-                        hipStream_t s) {
+                        hipStream_t s, float* lse = nullptr) {
   const int32_t kg = attn_key_groups(N, n_img, cfg->heads);
   VT_TRY_HIP(vt::launch_attention(qkv, pos, b.qdesc, b.kdesc, max_q_tiles(N, n_img, vt::attn_q_tile(kg)),
                                   max_k_tiles(N, n_img), cfg->heads, n_pos, axis_code, b.rope,
-                                  q_scale_log2(cfg), kg, b.qpk, b.kv, out, f32, s));
+                                  q_scale_log2(cfg), kg, b.qpk, b.kv, out, f32, lse, s));
   return VT_OK;
 }
 
@@ -556,6 +561,80 @@ VT_API vt_status vt_attention_varlen(const vt_config* cfg, const uint16_t* qkv,
   if ((st = attn_prologue(cfg, cu_seqlens, n_img, total_tokens, max_seqlen, b, &axis_code, s)) != VT_OK) return st;
   return run_attention(cfg, qkv, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen, axis_code, b,
                        out, out_dtype == VT_FP32, s);
+}
+
+// Buffers of vt_attention_backward: the forward's attention buffers, its
+// fp32 output and log-sum-exp, the 128-token schedule and both tile images.
+struct AttnBwdBufs {
+  BlockBufs fwd;
+  int4* bdesc;
+  float* o;
+  float* lse;
+  char* qimg;
+  char* kimg;
+};
+
+void carve_attn_bwd(Carver& c, const Dims& D, int32_t n_pos, AttnBwdBufs* a) {
+  carve_attention(c, D, n_pos, &a->fwd);
+  const size_t kt = size_t(max_k_tiles(D.N, D.n_img)) * D.heads;
+  a->bdesc = c.take<int4>(max_q_tiles(D.N, D.n_img, vt::kAttnBwdTile));
+  a->o = c.take<float>(size_t(D.N) * D.d);
+  a->lse = c.take<float>(size_t(D.N) * D.heads);
+  a->qimg = c.take<char>(kt * vt::kAttnBwdQBytes);
+  a->kimg = c.take<char>(kt * vt::kAttnBwdKBytes);
+}
+
+size_t attn_bwd_ws_bytes(const vt_config* cfg, int64_t N, int32_t n_img, int32_t n_pos) {
+  Carver c(nullptr);
+  AttnBwdBufs a;
+  carve_attn_bwd(c, dims_of(cfg, N, n_img), n_pos, &a);
+  return c.off;
+}
+
+VT_API size_t vt_attention_backward_workspace_size(const vt_config* cfg, int32_t total_tokens,
+                                                   int32_t n_img, int32_t max_seqlen) {
+  if (check_config(cfg) != VT_OK) return 0;
+  if (total_tokens <= 0 || n_img <= 0 || max_seqlen <= 0) {
+    fail(VT_ERR_INVALID_ARG, "total_tokens, n_img and max_seqlen must be positive");
+    return 0;
+  }
+  return attn_bwd_ws_bytes(cfg, total_tokens, n_img, max_seqlen);
+}
+
+VT_API vt_status vt_attention_backward(const vt_config* cfg, const uint16_t* qkv,
+                                       const int32_t* cu_seqlens, const int32_t* pos_thw,
+                                       int32_t n_img, int32_t total_tokens, int32_t max_seqlen,
+                                       const uint16_t* dout, void* dqkv, vt_dtype dqkv_dtype,
+                                       void* ws, size_t ws_bytes, void* stream) {
+  vt_status st = check_varlen(cfg, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen);
+  if (st != VT_OK) return st;
+  if ((st = check_ptr(qkv, "qkv")) != VT_OK) return st;
+  if ((st = check_ptr(dout, "dout")) != VT_OK) return st;
+  if ((st = check_ptr(dqkv, "dqkv")) != VT_OK) return st;
+  if (dqkv_dtype != VT_BF16 && dqkv_dtype != VT_FP32) return fail(VT_ERR_INVALID_ARG, "bad dqkv_dtype");
+  const size_t need = attn_bwd_ws_bytes(cfg, total_tokens, n_img, max_seqlen);
+  if ((st = check_ws(ws, ws_bytes, need)) != VT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver c(ws);
+  AttnBwdBufs a;
+  const int64_t N = total_tokens;
+  carve_attn_bwd(c, dims_of(cfg, N, n_img), max_seqlen, &a);
+  const BlockBufs& b = a.fwd;
+  int32_t axis_code = 0;
+  if ((st = attn_prologue(cfg, cu_seqlens, n_img, N, max_seqlen, b, &axis_code, s)) != VT_OK) return st;
+  // The 128-token schedule of the backward kernels (same key tiles: kdesc is rewritten unchanged).
+  const int32_t max_bt = max_q_tiles(N, n_img, vt::kAttnBwdTile);
+  VT_TRY_HIP(vt::launch_attn_schedule(cu_seqlens, n_img, vt::kAttnBwdTile, vt::kAttnKTile, max_bt,
+                                      max_k_tiles(N, n_img), b.order, b.tile_start, b.ktile_start,
+                                      a.bdesc, b.kdesc, s));
+  if ((st = run_attention(cfg, qkv, cu_seqlens, pos_thw, n_img, N, max_seqlen, axis_code, b, a.o, true,
+                          s, a.lse)) != VT_OK)
+    return st;
+  VT_TRY_HIP(vt::launch_attention_backward(qkv, dout, a.o, a.lse, pos_thw, b.kdesc, a.bdesc,
+                                           max_k_tiles(N, n_img), max_bt, cfg->heads, max_seqlen,
+                                           axis_code, b.rope, q_scale_log2(cfg), a.qimg, a.kimg, dqkv,
+                                           dqkv_dtype == VT_FP32, s));
+  return VT_OK;
 }
 
 VT_API vt_status vt_block_forward(const vt_config* cfg, float* resid, const vt_block_weights* w,

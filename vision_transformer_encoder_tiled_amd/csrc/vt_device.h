@@ -65,6 +65,15 @@ __device__ __forceinline__ float gelu_erf(float x) {
   return 0.5f * x * (1.0f + erff(x * 0.7071067811865476f));
 }
 
+// Slot of index k inside its group of 16 when a [.][16 k] operand is fed as
+// the k-slice of v_mfma_f32_32x32x16 from a 32x32 accumulator: the lane
+// half hf holds accumulator rows 8g + 4hf + r (g = 0, 1; r = 0..3) of the
+// slice, so storing the operand with bits 2 and 3 of k swapped makes those
+// 8 rows the lane's 8 contiguous k values (slots 8hf .. 8hf + 7).
+__device__ __forceinline__ int mfma_slot16(int k) {
+  return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
 // ---- LDS DMA and explicit waits (gfx950)
 
 // s_waitcnt immediate: vmcnt <= n, expcnt and lgkmcnt unconstrained (gfx9 encoding).

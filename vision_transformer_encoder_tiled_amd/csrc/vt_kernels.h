@@ -87,11 +87,30 @@ constexpr int kAttnStages1 = 3;
 inline int attn_q_tile(int key_groups) { return key_groups == 2 ? 64 : 32 * kAttnWaves1; }
 // qpk: [N, heads, 80] fp16 rotated+scaled Q; kv: max_ktiles x heads tile
 // images.  qdesc / kdesc come from launch_attn_schedule with
-// attn_q_tile(key_groups) and the same max_qtiles / max_ktiles.
+// attn_q_tile(key_groups) and the same max_qtiles / max_ktiles.  lse, when
+// not null, receives [N, heads] fp32: the log2-domain log-sum-exp of each
+// query's scaled scores (max + log2 of the row sum).
 hipError_t launch_attention(const uint16_t* qkv, const int32_t* pos_thw, const int4* qdesc,
                             const int2* kdesc, int32_t max_qtiles, int32_t max_ktiles,
                             int32_t heads, int32_t n_pos, int32_t axis_code, const float2* rope_cs,
                             float q_scale_log2, int32_t key_groups, uint16_t* qpk, uint16_t* kv,
-                            void* out, bool out_f32, hipStream_t s);
+                            void* out, bool out_f32, float* lse, hipStream_t s);
+
+// ---- attention backward (attention_bwd.hip)
+// Tile images of 64 tokens of one head: the key side (K, V, K^T) and the
+// query side (Q, dO, Q^T, dO^T, log-sum-exp, D).
+constexpr int kAttnBwdKBytes = 36864;
+constexpr int kAttnBwdQBytes = 49152;
+constexpr int kAttnBwdTile = 128;  // queries (dQ pass) or keys (dK/dV pass) per workgroup
+// o: the forward output [N, heads*80] fp32; lse: its [N, heads] log-sum-exp;
+// dout: [N, heads*80] bf16.  kdesc from launch_attn_schedule (key tiles of
+// 64), bdesc from a schedule with q_tile = kAttnBwdTile (max_btiles slots).
+// dqkv: [N, 3, heads, 80], bf16 or fp32.
+hipError_t launch_attention_backward(const uint16_t* qkv, const uint16_t* dout, const float* o,
+                                     const float* lse, const int32_t* pos_thw, const int2* kdesc,
+                                     const int4* bdesc, int32_t max_ktiles, int32_t max_btiles,
+                                     int32_t heads, int32_t n_pos, int32_t axis_code,
+                                     const float2* rope_cs, float q_scale_log2, char* qimg,
+                                     char* kimg, void* dqkv, bool out_f32, hipStream_t s);
 
 }  // namespace vt
