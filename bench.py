@@ -6,12 +6,13 @@ raster-order tower output, the 2x2 merge and the projector -- over one batch
 of synthetic input that is already resident in device memory.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload tower_448]
-    python bench.py --kernel {fc1,attention,copy} [--workload ...]   # one kernel, for counter runs
+    python bench.py --kernel {fc1,attention,attention_bwd,copy} [--workload ...]   # one case, for counter runs
 
 Prints one JSON line.  Beside the headline workload it times, with HIP events
 on the stream the kernels run on, the dominant kernel of the headline
 workload (the bf16 GEMM at the FC1 shape) and one vt_attention_varlen call
-through their own entry points, and the 2016x2016 single image as a
+through their own entry points, one vt_attention_backward call (the
+backward pass of the attention step), and the 2016x2016 single image as a
 secondary workload.  "traffic" (HBM-side bytes per launch) comes from the
 FETCH_SIZE / WRITE_SIZE counter summaries under profiles/, and is null when
 those were taken on other kernel sources.  The CPU oracle is timed on a
@@ -62,7 +63,7 @@ def parse():
                     help="comma-separated further workloads, throughput only ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-iters", type=int, default=20)
-    ap.add_argument("--kernel", choices=["fc1", "attention", "copy"], default=None,
+    ap.add_argument("--kernel", choices=["fc1", "attention", "attention_bwd", "copy"], default=None,
                     help="run only this kernel case (counter runs) and exit")
     return ap.parse_args()
 
@@ -142,6 +143,27 @@ def attention_case(vt, torch, grids):
     return (lambda: vt.vt_attention_varlen(cfg, qkv, cu, pos, len(grids), N, max_seq, out, vt.VT_BF16, ws)), flops
 
 
+def attention_backward_case(vt, torch, grids):
+    """vt_attention_backward on the workload's token layout (random bf16 q, k,
+    v and dO).  FLOPs counted: the gradient's four n^2 products (dP = dO V^T,
+    dV = P^T dO, dQ = dS K, dK = dS^T Q) per head; the call also recomputes
+    the forward (S and P V) and S once more in each backward kernel."""
+    N = sum(t * h * w for t, h, w in grids)
+    g = np.random.Generator(np.random.PCG64(2))
+    qkv = torch.from_numpy(synth.bf16_bits(g.standard_normal((N, 3840), dtype=np.float32) * 0.7).view(np.int16)).cuda()
+    dout = torch.from_numpy(synth.bf16_bits(g.standard_normal((N, 1280), dtype=np.float32)).view(np.int16)).cuda()
+    cfg = vt.config()
+    cu = torch.empty(len(grids) + 1, dtype=torch.int32, device="cuda")
+    pos = torch.empty((N, 3), dtype=torch.int32, device="cuda")
+    vt.vt_build_metadata(grids, cu, pos)
+    max_seq = max(t * h * w for t, h, w in grids)
+    ws = vt.workspace(vt.vt_attention_backward_workspace_size(cfg, N, len(grids), max_seq))
+    dqkv = torch.empty((N, 3840), dtype=torch.int16, device="cuda")
+    flops = float(sum(8 * (t * h * w) ** 2 * 1280 for t, h, w in grids))
+    return (lambda: vt.vt_attention_backward(cfg, qkv, cu, pos, len(grids), N, max_seq, dout, dqkv,
+                                             vt.VT_BF16, ws)), flops
+
+
 def copy_case(torch, nbytes=256 << 20):
     """A plain device-to-device copy of nbytes (the HBM-counter calibration)."""
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -201,6 +223,18 @@ def attention_roofline(vt, torch, grids, iters, traffic_profile=None):
                     "plus the per-call schedule and RoPE-table kernels"}
 
 
+def attention_backward_line(vt, torch, grids, iters):
+    fn, flops = attention_backward_case(vt, torch, grids)
+    t = time_kernel(torch, fn, iters)
+    N = sum(t_ * h * w for t_, h, w in grids)
+    return {"call": "vt_attention_backward (%d tokens, %d images, bf16 dqkv)" % (N, len(grids)),
+            "bound": "mfma", "achieved": flops / t / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": flops / t / 1e12 / PEAK_BF16_TFLOPS, "flops_per_call": flops,
+            "avg_call_us": t * 1e6,
+            "note": "whole call: schedule, forward recompute with log-sum-exp, both packs, the dQ "
+                    "and the dK/dV kernels; FLOPs are the four gradient products only"}
+
+
 def kernel_only(a):
     """--kernel: run one kernel case a fixed number of times (for counter runs)."""
     import torch
@@ -210,6 +244,8 @@ def kernel_only(a):
         fn, _ = fc1_case(vt, torch, wl.tokens)
     elif a.kernel == "attention":
         fn, _ = attention_case(vt, torch, list(wl.grids))
+    elif a.kernel == "attention_bwd":
+        fn, _ = attention_backward_case(vt, torch, list(wl.grids))
     else:
         fn, _ = copy_case(torch)
     fn()
@@ -278,6 +314,7 @@ def main():
     M = wl.tokens
     res["roofline"] = gemm_roofline(vt, torch, M, a.kernel_iters)
     res["attention_roofline"] = attention_roofline(vt, torch, list(wl.grids), a.kernel_iters)
+    res["attention_backward"] = attention_backward_line(vt, torch, list(wl.grids), a.kernel_iters)
 
     if a.secondary:
         wl2 = synth.WORKLOADS[a.secondary]
@@ -295,6 +332,8 @@ def main():
                 vt, torch, list(wl2.grids), max(3, a.kernel_iters // 4),
                 "attention_2016_traffic" if wl2.name == "tower_2016" else None),
             "gemm_roofline": gemm_roofline(vt, torch, wl2.tokens, max(3, a.kernel_iters // 4)),
+            "attention_backward": attention_backward_line(vt, torch, list(wl2.grids),
+                                                          max(3, a.kernel_iters // 4)),
         }
         del run2
 

@@ -220,6 +220,43 @@ vt_status vt_block_forward(const vt_config* cfg, float* resid, const vt_block_we
                            int32_t total_tokens, int32_t max_seqlen, void* ws, size_t ws_bytes,
                            void* stream);
 
+/* Gradients of one block's parameters, fp32, each shaped like its weight in
+ * vt_block_weights ([out, in] for the linears, [hidden] for LN gamma/beta).
+ * A NULL member is not formed. */
+typedef struct vt_block_grads {
+  float *ln1_g, *ln1_b;
+  float *w_qkv, *b_qkv;
+  float *w_o, *b_o;
+  float *ln2_g, *ln2_b;
+  float *w_fc1, *b_fc1;
+  float *w_fc2, *b_fc2;
+} vt_block_grads;
+
+/* Backward pass of vt_block_forward ("v2_loaders FINDINGS", section 3: the
+ * towers are differentiable): given the block's input and dL/d(output), form
+ * dL/d(input) and the parameter gradients.  The block's forward is
+ * recomputed from resid_in; per linear y = x W^T + b: dx = dy W, dW = dy^T x,
+ * db = column sums of dy; GELU(tanh) and LayerNorm by their derivatives;
+ * attention as in vt_attention_backward.  Activations and dL/d(activation)
+ * enter the products as bf16 (the forward's precision), accumulate in fp32.
+ *   resid_in  fp32 [N, hidden]: the block's input (not modified).
+ *   dresid    fp32 [N, hidden]: in, dL/d(block output); out, dL/d(resid_in).
+ *   grads     host struct of device pointers (members may be NULL); each
+ *             formed gradient is overwritten, not accumulated.
+ *   other arguments as in vt_block_forward; hidden <= 2048.
+ *   ws        vt_block_backward_workspace_size bytes (about 120 KB per token
+ *             at the MiniMax-M3 shape, affine in the token count).
+ * Errors as for vt_block_forward; nothing is launched on error. */
+vt_status vt_block_backward(const vt_config* cfg, const float* resid_in, const vt_block_weights* w,
+                            const int32_t* cu_seqlens, const int32_t* pos_thw, int32_t n_img,
+                            int32_t total_tokens, int32_t max_seqlen, float* dresid,
+                            const vt_block_grads* grads, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for vt_block_backward.
+ * Returns 0 and sets vt_last_error() if the arguments are invalid. */
+size_t vt_block_backward_workspace_size(const vt_config* cfg, int32_t total_tokens, int32_t n_img,
+                                        int32_t max_seqlen);
+
 /* 2x2 merge + projector (README Architecture, Projector row).
  *   tower      bf16 [N, hidden] tower tokens, rows in `order`.
  *   merged_raw bf16 [N/4, 4*hidden] or NULL: the 2x2 gather of the tower

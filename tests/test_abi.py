@@ -30,7 +30,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     declared = header_functions()
-    assert len(declared) == 20
+    assert len(declared) == 22
     assert sorted(vt.EXPORTED) == declared
     lib = ctypes.CDLL(vt.LIB_PATH)
     for name in declared:
@@ -147,11 +147,44 @@ def test_attention_backward_validation():
     assert vt.vt_attention_backward_workspace_size(cfg, 0, 1, 1) == 0
 
 
+@needs_no_gpu
+def test_block_backward_validation():
+    cfg = vt.config()
+    P = ctypes.c_void_p
+    need = vt.vt_block_backward_workspace_size(cfg, 64, 1, 64)
+    assert need > vt.vt_attention_backward_workspace_size(cfg, 64, 1, 64)
+    bw = vt.vt_block_weights()
+    for name, _ in vt.vt_block_weights._fields_:
+        setattr(bw, name, FAKE)
+    g = vt.vt_block_grads()
+
+    def call(cfg=cfg, resid=FAKE, dresid=FAKE, grads=g, ws_bytes=need, n_img=1, bw=bw):
+        return vt.LIB.vt_block_backward(ctypes.byref(cfg), P(resid), ctypes.byref(bw), P(FAKE), P(FAKE),
+                                        n_img, 64, 64, P(dresid),
+                                        ctypes.byref(grads) if grads is not None else None, P(FAKE),
+                                        ws_bytes, None)
+    assert call(ws_bytes=need - 1) == vt.VT_ERR_WORKSPACE
+    assert call(resid=None) == vt.VT_ERR_INVALID_ARG
+    assert call(dresid=FAKE + 4) == vt.VT_ERR_INVALID_ARG
+    assert call(grads=None) == vt.VT_ERR_INVALID_ARG
+    assert call(n_img=0) == vt.VT_ERR_INVALID_ARG
+    g2 = vt.vt_block_grads()
+    g2.w_o = FAKE + 8
+    assert call(grads=g2) == vt.VT_ERR_INVALID_ARG
+    bw2 = vt.vt_block_weights()
+    assert call(bw=bw2) == vt.VT_ERR_INVALID_ARG                       # NULL weights
+    wide = vt.config(hidden=2560, heads=32)
+    assert call(cfg=wide, ws_bytes=1 << 40) == vt.VT_ERR_UNSUPPORTED   # hidden > 2048
+
+
 def test_attention_backward_workspace_is_affine():
     cfg = vt.config()
     s = [vt.vt_attention_backward_workspace_size(cfg, n, 1, n) for n in (4096, 8192, 16384)]
     assert abs((s[2] - s[1]) - 2 * (s[1] - s[0])) <= 4096
     assert (s[1] - s[0]) / 4096 < 40 * 1024       # about 36 KB per token at 16 heads
+    b = [vt.vt_block_backward_workspace_size(cfg, n, 1, n) for n in (4096, 8192, 16384)]
+    assert abs((b[2] - b[1]) - 2 * (b[1] - b[0])) <= 4096
+    assert (b[1] - b[0]) / 4096 < 128 * 1024      # about 115 KB per token
 
 
 @needs_no_gpu

@@ -135,3 +135,70 @@ def test_attention_backward_2016_sampled(vt):
     rss_k = np.sqrt((dk_rot ** 2).sum())
     log(f"  rotated dk sum {k_sum:.3e} (rss {rss_k:.3e})")
     assert k_sum <= 1e-2 * rss_k
+
+
+# ---------------------------------------------------------------- one block
+GRAD_NAMES = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_g", "ln2_b", "w_fc1", "b_fc1",
+              "w_fc2", "b_fc2")
+
+
+def block_backward_case(vt, grids, R, dR2, affine, seed=0):
+    """vt_block_backward on window-order fp32 R and dL/d(output); returns
+    (dR, grads) from the GPU and from the float64 oracle."""
+    N = R.shape[0]
+    W = synth.make_weights(1, projector=False, affine=affine)
+    cfg = vt.config(layers=1)
+    dw = {k: dev_bits(v, torch) for k, v in W.items()}
+    bw = vt.block_weights(dw, "l0.")
+    cu = torch.empty(len(grids) + 1, dtype=torch.int32, device="cuda")
+    pos = torch.empty((N, 3), dtype=torch.int32, device="cuda")
+    vt.vt_build_metadata(grids, cu, pos)
+    max_seq = max(t * h * w for t, h, w in grids)
+    ws = vt.workspace(vt.vt_block_backward_workspace_size(cfg, N, len(grids), max_seq))
+    shapes = {k[3:]: v.shape for k, v in W.items() if k.startswith("l0.")}
+    gd = {n: torch.full(shapes[n], float("nan"), dtype=torch.float32, device="cuda") for n in GRAD_NAMES}
+    Rd = torch.from_numpy(R).cuda()
+    dRd = torch.from_numpy(dR2.copy()).cuda()
+    vt.vt_block_backward(cfg, Rd, bw, cu, pos, len(grids), N, max_seq, dRd, vt.block_grads(gd), ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(Rd.cpu().numpy(), R)                      # the input is not modified
+    got = {n: t.cpu().numpy() for n, t in gd.items()}
+    Wf = {k: v.astype(np.float64) for k, v in oracle.weights_f32(W).items()}
+    want_dR, want = G.block_backward(R.astype(np.float64), Wf, window_positions(grids),
+                                     oracle.cu_seqlens(grids), oracle.Config(),
+                                     dR2.astype(np.float64), prefix="l0.")
+    return dRd.cpu().numpy(), got, want_dR, want
+
+
+def check_block(got_dR, got, want_dR, want, what):
+    errs = {n: rel_l2(got[n], want[n]) for n in GRAD_NAMES}
+    e = rel_l2(got_dR, want_dR)
+    log(f"  {what}: dR rel-L2 {e:.2e}; " + " ".join(f"{n} {v:.1e}" for n, v in errs.items()))
+    assert np.all(np.isfinite(got_dR)) and all(np.all(np.isfinite(g)) for g in got.values())
+    assert e <= 1e-2
+    assert max(errs.values()) <= 1e-2
+
+
+@pytest.mark.parametrize("affine", ["canonical", "random"])
+def test_block_backward_224(vt, affine):
+    """One block on the 224x224 image's patch embedding, random dL/d(output)."""
+    log(f"block backward 224 {affine}")
+    wl = synth.WORKLOADS["block_224"]
+    W = synth.make_weights(1, projector=False, affine=affine)
+    px = synth.make_batch_pixels(wl)
+    R0 = oracle.patch_embed(oracle.split_pixels(bf16_f32(px), wl.grids), oracle.weights_f32(W),
+                            wl.grids).astype(np.float32)
+    perm = window_to_raster(wl.grids)
+    R = np.ascontiguousarray(R0[perm])
+    dR2 = rng(50).standard_normal(R.shape, dtype=np.float32)
+    check_block(*block_backward_case(vt, list(wl.grids), R, dR2, affine), "224")
+
+
+def test_block_backward_ragged_images(vt):
+    """Two images (168 + 4 tokens: the transposed token dimension padded to
+    192), random residual stream and dL/d(output)."""
+    grids = [(1, 12, 14), (1, 2, 2)]
+    N = 172
+    R = rng(51).standard_normal((N, 1280), dtype=np.float32)
+    dR2 = rng(52).standard_normal((N, 1280), dtype=np.float32)
+    check_block(*block_backward_case(vt, grids, R, dR2, "random"), "ragged")

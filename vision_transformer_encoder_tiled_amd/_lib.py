@@ -25,7 +25,8 @@ EXPORTED = ("vt_config_default", "vt_status_string", "vt_last_error", "vt_versio
             "vt_patch_embed", "vt_attention_varlen", "vt_block_forward", "vt_merge_project",
             "vt_tower_forward", "vt_plan_patches", "vt_pack_items", "vt_mean_pool",
             "vt_linear_workspace_size", "vt_linear", "vt_layer_norm", "vt_attention_backward",
-            "vt_attention_backward_workspace_size")
+            "vt_attention_backward_workspace_size", "vt_block_backward",
+            "vt_block_backward_workspace_size")
 
 
 class VtError(RuntimeError):
@@ -53,6 +54,10 @@ _P = ctypes.c_void_p
 class vt_block_weights(ctypes.Structure):
     _fields_ = [(n, _P) for n in ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_g",
                                   "ln2_b", "w_fc1", "b_fc1", "w_fc2", "b_fc2")]
+
+
+class vt_block_grads(ctypes.Structure):
+    _fields_ = list(vt_block_weights._fields_)
 
 
 class vt_projector_weights(ctypes.Structure):
@@ -85,6 +90,9 @@ def _load():
         "vt_attention_backward": (ctypes.c_int, [cfgp, _P, _P, _P, I32, I32, I32, _P, _P,
                                                  ctypes.c_int, _P, SZ, _P]),
         "vt_attention_backward_workspace_size": (SZ, [cfgp, I32, I32, I32]),
+        "vt_block_backward": (ctypes.c_int, [cfgp, _P, ctypes.POINTER(vt_block_weights), _P, _P, I32,
+                                             I32, I32, _P, ctypes.POINTER(vt_block_grads), _P, SZ, _P]),
+        "vt_block_backward_workspace_size": (SZ, [cfgp, I32, I32, I32]),
         "vt_block_forward": (ctypes.c_int, [cfgp, _P, ctypes.POINTER(vt_block_weights), _P, _P,
                                             I32, I32, I32, _P, SZ, _P]),
         "vt_merge_project": (ctypes.c_int, [cfgp, _P, ctypes.c_int, gridp, I32,
@@ -208,6 +216,28 @@ def vt_attention_backward(cfg, qkv, cu_seqlens, pos_thw, n_img, total_tokens, ma
                                      n_img, total_tokens, max_seqlen, _ptr(dout), _ptr(dqkv),
                                      dqkv_dtype, _ptr(ws), ws.numel() if ws is not None else 0,
                                      _stream(stream)))
+
+
+def block_grads(g: dict) -> vt_block_grads:
+    """vt_block_grads from a dict of fp32 device tensors keyed like the weights
+    (missing entries -> NULL, not formed)."""
+    b = vt_block_grads()
+    for name, _ in vt_block_grads._fields_:
+        t = g.get(name)
+        setattr(b, name, None if t is None else t.data_ptr())
+    return b
+
+
+def vt_block_backward_workspace_size(cfg, total_tokens, n_img, max_seqlen) -> int:
+    return int(LIB.vt_block_backward_workspace_size(ctypes.byref(cfg), total_tokens, n_img, max_seqlen))
+
+
+def vt_block_backward(cfg, resid_in, bw: vt_block_weights, cu_seqlens, pos_thw, n_img, total_tokens,
+                      max_seqlen, dresid, grads: vt_block_grads, ws, stream=None):
+    _check(LIB.vt_block_backward(ctypes.byref(cfg), _ptr(resid_in), ctypes.byref(bw), _ptr(cu_seqlens),
+                                 _ptr(pos_thw), n_img, total_tokens, max_seqlen, _ptr(dresid),
+                                 ctypes.byref(grads), _ptr(ws), ws.numel() if ws is not None else 0,
+                                 _stream(stream)))
 
 
 def block_weights(w: dict, prefix: str = "") -> vt_block_weights:

@@ -637,6 +637,173 @@ VT_API vt_status vt_attention_backward(const vt_config* cfg, const uint16_t* qkv
   return VT_OK;
 }
 
+// ---- one block's backward pass
+int32_t pad64(int64_t n) { return int32_t((n + 63) / 64 * 64); }
+
+// Buffers of vt_block_backward: the recomputed forward activations, the
+// backward activations, their token-major transposes (rows padded to 64
+// tokens, zero), one transposed weight at a time, and the GEMM partials.
+struct BlockBwdBufs {
+  AttnBwdBufs at;
+  uint16_t *x1, *qkv, *a, *x2, *h, *dh, *gb, *da, *dqkv;
+  float *R1, *dx;
+  uint16_t *gT, *hT, *xT, *dqkvT, *wT;
+  float* ln_scratch;  // gamma / beta gradients the caller did not ask for
+  void* gemm_ws;
+};
+
+size_t block_bwd_gemm_ws(int N, int d, int mlp) {
+  const int Np = pad64(N);
+  const int shapes[][3] = {{N, 3 * d, d}, {N, d, d}, {N, mlp, d}, {d, mlp, Np}, {mlp, d, Np},
+                           {N, d, mlp}, {d, d, Np}, {3 * d, d, Np}, {N, d, 3 * d}};
+  size_t w = 0;
+  for (const auto& x : shapes) w = std::max(w, vt::gemm_workspace_bytes(x[0], x[1], x[2]));
+  return w;
+}
+
+void carve_block_bwd(Carver& c, const Dims& D, int32_t n_pos, BlockBwdBufs* b) {
+  carve_attn_bwd(c, D, n_pos, &b->at);
+  const size_t N = D.N, d = D.d, mlp = D.mlp, Np = pad64(D.N);
+  b->x1 = c.take<uint16_t>(N * d);
+  b->qkv = c.take<uint16_t>(N * 3 * d);
+  b->a = c.take<uint16_t>(N * d);
+  b->x2 = c.take<uint16_t>(N * d);
+  b->h = c.take<uint16_t>(N * mlp);
+  b->dh = c.take<uint16_t>(N * mlp);
+  b->gb = c.take<uint16_t>(N * d);
+  b->da = c.take<uint16_t>(N * d);
+  b->dqkv = c.take<uint16_t>(N * 3 * d);
+  b->R1 = c.take<float>(N * d);
+  b->dx = c.take<float>(N * d);
+  b->gT = c.take<uint16_t>(d * Np);
+  b->hT = c.take<uint16_t>(mlp * Np);
+  b->xT = c.take<uint16_t>(d * Np);
+  b->dqkvT = c.take<uint16_t>(3 * d * Np);
+  b->wT = c.take<uint16_t>(std::max(mlp * d, 3 * d * d));
+  b->ln_scratch = c.take<float>(4 * d);
+  b->gemm_ws = c.take<char>(D.ws_upper ? kPartialsBound : block_bwd_gemm_ws(D.N, D.d, D.mlp));
+}
+
+size_t block_bwd_ws_bytes(const vt_config* cfg, int64_t N, int32_t n_img, int32_t n_pos) {
+  Carver c(nullptr);
+  BlockBwdBufs b;
+  carve_block_bwd(c, dims_of(cfg, N, n_img), n_pos, &b);
+  return c.off;
+}
+
+vt_status run_block_backward(const vt_config* cfg, const float* R, const vt_block_weights* w,
+                             const int32_t* cu, const int32_t* pos, int32_t n_img, int64_t N,
+                             int32_t n_pos, float* dR, const vt_block_grads* g, const BlockBwdBufs& B,
+                             hipStream_t s) {
+  const int d = cfg->hidden, mlp = cfg->mlp, M = int(N), Np = pad64(N);
+  const float eps = cfg->ln_eps;
+  void* ws = B.gemm_ws;
+  float* ln1g = g->ln1_g ? g->ln1_g : B.ln_scratch;
+  float* ln1b = g->ln1_b ? g->ln1_b : B.ln_scratch + d;
+  float* ln2g = g->ln2_g ? g->ln2_g : B.ln_scratch + 2 * d;
+  float* ln2b = g->ln2_b ? g->ln2_b : B.ln_scratch + 3 * d;
+  // Gradients formed by atomic accumulation start from zero.
+  float* zero_list[] = {ln1g, ln1b, ln2g, ln2b, g->b_qkv, g->b_o, g->b_fc1, g->b_fc2};
+  const int zero_len[] = {d, d, d, d, 3 * d, d, mlp, d};
+  for (int i = 0; i < 8; ++i)
+    if (zero_list[i]) VT_TRY_HIP(vt::launch_zero_f32(zero_list[i], zero_len[i], s));
+
+  // ---- the block's forward, keeping what the backward reads
+  const AttnBwdBufs& at = B.at;
+  VT_TRY_HIP(vt::launch_layer_norm(R, M, d, w->ln1_g, w->ln1_b, eps, B.x1, s));
+  VT_TRY_HIP(vt::launch_gemm(B.x1, M, d, w->w_qkv, 3 * d, w->b_qkv, vt::kEpiBf16, B.qkv, ws, s));
+  int32_t axis_code = 0;
+  vt_status st = attn_prologue(cfg, cu, n_img, N, n_pos, at.fwd, &axis_code, s);
+  if (st != VT_OK) return st;
+  const int32_t max_bt = max_q_tiles(N, n_img, vt::kAttnBwdTile);
+  VT_TRY_HIP(vt::launch_attn_schedule(cu, n_img, vt::kAttnBwdTile, vt::kAttnKTile, max_bt,
+                                      max_k_tiles(N, n_img), at.fwd.order, at.fwd.tile_start,
+                                      at.fwd.ktile_start, at.bdesc, at.fwd.kdesc, s));
+  if ((st = run_attention(cfg, B.qkv, cu, pos, n_img, N, n_pos, axis_code, at.fwd, at.o, true, s,
+                          at.lse)) != VT_OK)
+    return st;
+  VT_TRY_HIP(vt::launch_f32_to_bf16(at.o, B.a, size_t(N) * d, s));
+  VT_TRY_HIP(hipMemcpyAsync(B.R1, R, size_t(N) * d * sizeof(float), hipMemcpyDeviceToDevice, s));
+  VT_TRY_HIP(vt::launch_gemm(B.a, M, d, w->w_o, d, w->b_o, vt::kEpiResid, B.R1, ws, s));
+  VT_TRY_HIP(vt::launch_layer_norm(B.R1, M, d, w->ln2_g, w->ln2_b, eps, B.x2, s));
+  VT_TRY_HIP(vt::launch_gemm(B.x2, M, d, w->w_fc1, mlp, w->b_fc1, vt::kEpiBf16, B.h, ws, s));
+
+  // ---- MLP: dR holds dL/d(output) = dR2
+  VT_TRY_HIP(vt::launch_transpose(dR, true, 0, nullptr, M, d, Np, B.gb, B.gT, g->b_fc2, s));
+  VT_TRY_HIP(vt::launch_transpose(w->w_fc2, false, 0, nullptr, d, mlp, d, nullptr, B.wT, nullptr, s));
+  VT_TRY_HIP(vt::launch_gemm(B.gb, M, d, B.wT, mlp, nullptr, vt::kEpiBf16, B.dh, ws, s));  // du
+  if (g->w_fc2) {  // dW_fc2 = dR2^T GELU(h)
+    VT_TRY_HIP(vt::launch_transpose(B.h, false, 1, nullptr, M, mlp, Np, nullptr, B.hT, nullptr, s));
+    VT_TRY_HIP(vt::launch_gemm(B.gT, d, Np, B.hT, mlp, nullptr, vt::kEpiF32, g->w_fc2, ws, s));
+  }
+  // dh = du * GELU'(h), in place, with its transpose and column sums
+  VT_TRY_HIP(vt::launch_transpose(B.dh, false, 2, B.h, M, mlp, Np, B.dh, B.hT, g->b_fc1, s));
+  if (g->w_fc1) {  // dW_fc1 = dh^T x2
+    VT_TRY_HIP(vt::launch_transpose(B.x2, false, 0, nullptr, M, d, Np, nullptr, B.xT, nullptr, s));
+    VT_TRY_HIP(vt::launch_gemm(B.hT, mlp, Np, B.xT, d, nullptr, vt::kEpiF32, g->w_fc1, ws, s));
+  }
+  VT_TRY_HIP(vt::launch_transpose(w->w_fc1, false, 0, nullptr, mlp, d, mlp, nullptr, B.wT, nullptr, s));
+  VT_TRY_HIP(vt::launch_gemm(B.dh, M, mlp, B.wT, d, nullptr, vt::kEpiF32, B.dx, ws, s));  // dx2
+  VT_TRY_HIP(vt::launch_ln_backward(B.R1, w->ln2_g, B.dx, dR, M, d, eps, dR, ln2g, ln2b, s));
+
+  // ---- attention: dR now holds dR1
+  VT_TRY_HIP(vt::launch_transpose(dR, true, 0, nullptr, M, d, Np, B.gb, B.gT, g->b_o, s));
+  if (g->w_o) {  // dW_o = dR1^T a
+    VT_TRY_HIP(vt::launch_transpose(B.a, false, 0, nullptr, M, d, Np, nullptr, B.xT, nullptr, s));
+    VT_TRY_HIP(vt::launch_gemm(B.gT, d, Np, B.xT, d, nullptr, vt::kEpiF32, g->w_o, ws, s));
+  }
+  VT_TRY_HIP(vt::launch_transpose(w->w_o, false, 0, nullptr, d, d, d, nullptr, B.wT, nullptr, s));
+  VT_TRY_HIP(vt::launch_gemm(B.gb, M, d, B.wT, d, nullptr, vt::kEpiBf16, B.da, ws, s));
+  VT_TRY_HIP(vt::launch_attention_backward(B.qkv, B.da, at.o, at.lse, pos, at.fwd.kdesc, at.bdesc,
+                                           max_k_tiles(N, n_img), max_bt, cfg->heads, n_pos, axis_code,
+                                           at.fwd.rope, q_scale_log2(cfg), at.qimg, at.kimg, B.dqkv,
+                                           false, s));
+  VT_TRY_HIP(vt::launch_transpose(B.dqkv, false, 0, nullptr, M, 3 * d, Np, nullptr, B.dqkvT, g->b_qkv, s));
+  if (g->w_qkv) {  // dW_qkv = dqkv^T x1
+    VT_TRY_HIP(vt::launch_transpose(B.x1, false, 0, nullptr, M, d, Np, nullptr, B.xT, nullptr, s));
+    VT_TRY_HIP(vt::launch_gemm(B.dqkvT, 3 * d, Np, B.xT, d, nullptr, vt::kEpiF32, g->w_qkv, ws, s));
+  }
+  VT_TRY_HIP(vt::launch_transpose(w->w_qkv, false, 0, nullptr, 3 * d, d, 3 * d, nullptr, B.wT, nullptr, s));
+  VT_TRY_HIP(vt::launch_gemm(B.dqkv, M, 3 * d, B.wT, d, nullptr, vt::kEpiF32, B.dx, ws, s));  // dx1
+  VT_TRY_HIP(vt::launch_ln_backward(R, w->ln1_g, B.dx, dR, M, d, eps, dR, ln1g, ln1b, s));
+  return VT_OK;
+}
+
+VT_API size_t vt_block_backward_workspace_size(const vt_config* cfg, int32_t total_tokens,
+                                               int32_t n_img, int32_t max_seqlen) {
+  if (check_config(cfg) != VT_OK) return 0;
+  if (total_tokens <= 0 || n_img <= 0 || max_seqlen <= 0) {
+    fail(VT_ERR_INVALID_ARG, "total_tokens, n_img and max_seqlen must be positive");
+    return 0;
+  }
+  return block_bwd_ws_bytes(cfg, total_tokens, n_img, max_seqlen);
+}
+
+VT_API vt_status vt_block_backward(const vt_config* cfg, const float* resid_in,
+                                   const vt_block_weights* w, const int32_t* cu_seqlens,
+                                   const int32_t* pos_thw, int32_t n_img, int32_t total_tokens,
+                                   int32_t max_seqlen, float* dresid, const vt_block_grads* grads,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  vt_status st = check_varlen(cfg, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen);
+  if (st != VT_OK) return st;
+  if (cfg->hidden > 2048) return fail(VT_ERR_UNSUPPORTED, "the backward pass supports hidden <= 2048");
+  if ((st = check_ptr(resid_in, "resid_in")) != VT_OK) return st;
+  if ((st = check_ptr(dresid, "dresid")) != VT_OK) return st;
+  if ((st = check_block_weights(w, 0)) != VT_OK) return st;
+  if (!grads) return fail(VT_ERR_INVALID_ARG, "grads is NULL (its members may be NULL)");
+  const float* gp[] = {grads->ln1_g, grads->ln1_b, grads->w_qkv, grads->b_qkv, grads->w_o, grads->b_o,
+                       grads->ln2_g, grads->ln2_b, grads->w_fc1, grads->b_fc1, grads->w_fc2, grads->b_fc2};
+  for (const float* p : gp)
+    if (p && !aligned16(p)) return fail(VT_ERR_INVALID_ARG, "a gradient buffer is not 16-byte aligned");
+  const size_t need = block_bwd_ws_bytes(cfg, total_tokens, n_img, max_seqlen);
+  if ((st = check_ws(ws, ws_bytes, need)) != VT_OK) return st;
+  Carver c(ws);
+  BlockBwdBufs B;
+  carve_block_bwd(c, dims_of(cfg, total_tokens, n_img), max_seqlen, &B);
+  return run_block_backward(cfg, resid_in, w, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen,
+                            dresid, grads, B, static_cast<hipStream_t>(stream));
+}
+
 VT_API vt_status vt_block_forward(const vt_config* cfg, float* resid, const vt_block_weights* w,
                                   const int32_t* cu_seqlens, const int32_t* pos_thw, int32_t n_img,
                                   int32_t total_tokens, int32_t max_seqlen, void* ws,

@@ -96,6 +96,23 @@ hipError_t launch_attention(const uint16_t* qkv, const int32_t* pos_thw, const i
                             float q_scale_log2, int32_t key_groups, uint16_t* qpk, uint16_t* kv,
                             void* out, bool out_f32, float* lse, hipStream_t s);
 
+// ---- block backward helpers (backward.hip)
+// 64 x 64-tiled transpose of in [M, C] (fp32 or bf16; C, Mp multiples of 64,
+// Mp >= M) with v = op(in): op 0 identity, 1 GELU(tanh), 2 in * GELU'(aux)
+// (aux bf16 [M, C]; fp32 input only with op 0).  Optional outputs: copy
+// [M, C] bf16(v), outT [C, Mp] bf16(v)^T (rows M.. zero), colsum [C] += the
+// column sums of bf16(v) (fp32 atomics: zero it first).
+hipError_t launch_transpose(const void* in, bool in_f32, int op, const uint16_t* aux, int32_t M,
+                            int32_t C, int32_t Mp, uint16_t* copy, uint16_t* outT, float* colsum,
+                            hipStream_t s);
+// dx = dres + LayerNorm'(x; g)^T dy per row (width = 256 k, k <= 8); dg, db
+// += the gamma / beta gradients (fp32 atomics: zero them first).  dx may
+// alias dres.
+hipError_t launch_ln_backward(const float* x, const uint16_t* g, const float* dy, const float* dres,
+                              int32_t rows, int32_t width, float eps, float* dx, float* dg,
+                              float* db, hipStream_t s);
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
+
 // ---- attention backward (attention_bwd.hip)
 // Tile images of 64 tokens of one head: the key side (K, V, K^T) and the
 // query side (Q, dO, Q^T, dO^T, log-sum-exp, D).
