@@ -6,13 +6,14 @@ raster-order tower output, the 2x2 merge and the projector -- over one batch
 of synthetic input that is already resident in device memory.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload tower_448]
-    python bench.py --kernel {fc1,attention,attention_bwd,copy} [--workload ...]   # one case, for counter runs
+    python bench.py --kernel {fc1,attention,attention_bwd,block_bwd,copy} [--workload ...]   # one case
 
 Prints one JSON line.  Beside the headline workload it times, with HIP events
 on the stream the kernels run on, the dominant kernel of the headline
 workload (the bf16 GEMM at the FC1 shape) and one vt_attention_varlen call
 through their own entry points, one vt_attention_backward call (the
-backward pass of the attention step), and the 2016x2016 single image as a
+backward pass of the attention step) and one vt_block_backward call (a
+whole block's backward pass), and the 2016x2016 single image as a
 secondary workload.  "traffic" (HBM-side bytes per launch) comes from the
 FETCH_SIZE / WRITE_SIZE counter summaries under profiles/, and is null when
 those were taken on other kernel sources.  The CPU oracle is timed on a
@@ -63,7 +64,8 @@ def parse():
                     help="comma-separated further workloads, throughput only ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-iters", type=int, default=20)
-    ap.add_argument("--kernel", choices=["fc1", "attention", "attention_bwd", "copy"], default=None,
+    ap.add_argument("--kernel", choices=["fc1", "attention", "attention_bwd", "block_bwd", "copy"],
+                    default=None,
                     help="run only this kernel case (counter runs) and exit")
     return ap.parse_args()
 
@@ -164,6 +166,35 @@ def attention_backward_case(vt, torch, grids):
                                              vt.VT_BF16, ws)), flops
 
 
+def block_backward_case(vt, torch, grids):
+    """vt_block_backward of one block (random-init bf16 weights, a random fp32
+    residual stream and dL/d(output), all gradients formed).  FLOPs counted:
+    the block's forward (which the call recomputes) plus its backward -- three
+    times the linear layers' products and 12 n^2 d for attention (forward
+    S and P V, backward dP, dV, dQ, dK)."""
+    N = sum(t * h * w for t, h, w in grids)
+    W = synth.make_weights(1, projector=False)
+    dev = {k: torch.from_numpy(v.view(np.int16)).cuda() for k, v in W.items()}
+    bw = vt.block_weights(dev, "l0.")
+    g = np.random.Generator(np.random.PCG64(3))
+    R = torch.from_numpy(g.standard_normal((N, 1280), dtype=np.float32)).cuda()
+    dR0 = torch.from_numpy(g.standard_normal((N, 1280), dtype=np.float32)).cuda()
+    dR = dR0.clone()
+    grads = {k[3:]: torch.empty(v.shape, dtype=torch.float32, device="cuda")
+             for k, v in W.items() if k.startswith("l0.")}
+    gs = vt.block_grads(grads)
+    cfg = vt.config(layers=1)
+    cu = torch.empty(len(grids) + 1, dtype=torch.int32, device="cuda")
+    pos = torch.empty((N, 3), dtype=torch.int32, device="cuda")
+    vt.vt_build_metadata(grids, cu, pos)
+    max_seq = max(t * h * w for t, h, w in grids)
+    ws = vt.workspace(vt.vt_block_backward_workspace_size(cfg, N, len(grids), max_seq))
+    block, _ = gemm_flops_per_token()
+    flops = 3.0 * N * block + float(sum(12 * (t * h * w) ** 2 * 1280 for t, h, w in grids))
+    # dR is overwritten with dL/d(input) each call; the work does not depend on its values
+    return (lambda: vt.vt_block_backward(cfg, R, bw, cu, pos, len(grids), N, max_seq, dR, gs, ws)), flops
+
+
 def copy_case(torch, nbytes=256 << 20):
     """A plain device-to-device copy of nbytes (the HBM-counter calibration)."""
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -235,6 +266,18 @@ def attention_backward_line(vt, torch, grids, iters):
                     "and the dK/dV kernels; FLOPs are the four gradient products only"}
 
 
+def block_backward_line(vt, torch, grids, iters):
+    fn, flops = block_backward_case(vt, torch, grids)
+    t = time_kernel(torch, fn, iters)
+    N = sum(t_ * h * w for t_, h, w in grids)
+    return {"call": "vt_block_backward (%d tokens, %d images, all gradients)" % (N, len(grids)),
+            "achieved": flops / t / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": flops / t / 1e12 / PEAK_BF16_TFLOPS, "flops_per_call": flops,
+            "avg_call_us": t * 1e6, "tokens_per_s": N / t,
+            "note": "one block's recomputed forward and backward; FLOPs = forward + backward "
+                    "(3x the linear products, 12 n^2 d attention)"}
+
+
 def kernel_only(a):
     """--kernel: run one kernel case a fixed number of times (for counter runs)."""
     import torch
@@ -246,6 +289,8 @@ def kernel_only(a):
         fn, _ = attention_case(vt, torch, list(wl.grids))
     elif a.kernel == "attention_bwd":
         fn, _ = attention_backward_case(vt, torch, list(wl.grids))
+    elif a.kernel == "block_bwd":
+        fn, _ = block_backward_case(vt, torch, list(wl.grids))
     else:
         fn, _ = copy_case(torch)
     fn()
@@ -315,6 +360,7 @@ def main():
     res["roofline"] = gemm_roofline(vt, torch, M, a.kernel_iters)
     res["attention_roofline"] = attention_roofline(vt, torch, list(wl.grids), a.kernel_iters)
     res["attention_backward"] = attention_backward_line(vt, torch, list(wl.grids), a.kernel_iters)
+    res["block_backward"] = block_backward_line(vt, torch, list(wl.grids), a.kernel_iters)
 
     if a.secondary:
         wl2 = synth.WORKLOADS[a.secondary]
@@ -334,6 +380,7 @@ def main():
             "gemm_roofline": gemm_roofline(vt, torch, wl2.tokens, max(3, a.kernel_iters // 4)),
             "attention_backward": attention_backward_line(vt, torch, list(wl2.grids),
                                                           max(3, a.kernel_iters // 4)),
+            "block_backward": block_backward_line(vt, torch, list(wl2.grids), max(3, a.kernel_iters // 4)),
         }
         del run2
 

@@ -70,6 +70,7 @@ def check_parts(got, want, tol, what):
     ([(1, 12, 14)], 41),                         # 168 tokens: 2 full 64-key tiles + 40, 128-tile + 40
     ([(1, 16, 18), (1, 2, 2), (3, 4, 6)], 42),   # several items, a 4-token image, a clip
     ([(1, 2, 2)], 43),                           # one 4-token image: a single ragged tile
+    ([(1, 4, 4)] * 62 + [(1, 16, 18), (1, 6, 8)], 48),  # 64 items: the 8-wavefront dK/dV pass
 ])
 @pytest.mark.parametrize("out_dtype", ["fp32", "bf16"])
 def test_attention_backward_parity(vt, grids, seed, out_dtype):

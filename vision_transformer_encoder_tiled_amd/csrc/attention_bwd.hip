@@ -380,8 +380,11 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_kernel(
 
 // ---------------------------------------------------------------- dK, dV
 // Lane (ln, hf) of wavefront w: key k0 + 32w + ln; accumulator rows are
-// queries (S, dP) or dims (dK^T, dV^T).
-__global__ void __launch_bounds__(64 * NW) bwd_dkv_kernel(
+// queries (S, dP) or dims (dK^T, dV^T).  KW wavefronts (4 or 8) share one
+// stream of query-side images: the 96 KB ring allows one workgroup per CU,
+// so 8 wavefronts (256 keys) put two on each SIMD when the image is large.
+template <int KW>
+__global__ void __launch_bounds__(64 * KW) bwd_dkv_kernel(
     const char* __restrict__ qimg, const char* __restrict__ kimg, const int4* __restrict__ bdesc,
     int32_t heads, const int32_t* __restrict__ pos, int32_t n_pos, const float2* __restrict__ rope_cs,
     int32_t axis_code, float dk_scale, void* __restrict__ dqkv, int32_t out_f32) {
@@ -396,11 +399,12 @@ __global__ void __launch_bounds__(64 * NW) bwd_dkv_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, ln = lane & 31;
   const uint32_t lds_wave = lds_offset(lds) + 1024 * wave;
+  static_assert(QS_BYTES % (1024 * KW) == 0, "whole rounds of copies");
   auto issue = [&](int t) {
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_wave + (t & 1) * QS_BYTES);
     const char* g = src + t * tile_stride + 1024 * wave + 16 * lane;
 #pragma unroll
-    for (int c = 0; c < QS_BYTES / (1024 * NW); ++c) dma16(g + NW * 1024 * c, base + NW * 1024 * c);
+    for (int c = 0; c < QS_BYTES / (1024 * KW); ++c) dma16(g + KW * 1024 * c, base + KW * 1024 * c);
   };
 
   const int krow = k0 + 32 * wave + ln;
@@ -488,11 +492,14 @@ hipError_t launch_attention_backward(const uint16_t* qkv, const uint16_t* dout, 
                                      const int4* bdesc, int32_t max_ktiles, int32_t max_btiles,
                                      int32_t heads, int32_t n_pos, int32_t axis_code,
                                      const float2* rope_cs, float q_scale_log2, char* qimg,
-                                     char* kimg, void* dqkv, bool out_f32, hipStream_t s) {
+                                     char* kimg, void* dqkv, bool out_f32, const int4* kdesc256,
+                                     int32_t max_ktiles256, hipStream_t s) {
   static const hipError_t a1 = set_lds(bwd_dq_kernel, 2 * KS_BYTES);
-  static const hipError_t a2 = set_lds(bwd_dkv_kernel, 2 * QS_BYTES);
+  static const hipError_t a2 = set_lds(bwd_dkv_kernel<4>, 2 * QS_BYTES);
+  static const hipError_t a3 = set_lds(bwd_dkv_kernel<8>, 2 * QS_BYTES);
   if (a1 != hipSuccess) return a1;
   if (a2 != hipSuccess) return a2;
+  if (a3 != hipSuccess) return a3;
   hipLaunchKernelGGL(bwd_pack_k_kernel, dim3(max_ktiles, heads), dim3(320), 0, s, qkv, pos_thw, kdesc,
                      heads, n_pos, rope_cs, axis_code, kimg);
   hipLaunchKernelGGL(bwd_pack_q_kernel, dim3(max_ktiles, heads), dim3(320), 0, s, qkv, dout, o, lse,
@@ -502,8 +509,13 @@ hipError_t launch_attention_backward(const uint16_t* qkv, const uint16_t* dout, 
   const float ln2 = 0.6931471805599453f;  // dK from the log2(e)/sqrt(80)-scaled Q: times sqrt(80)/log2(e)/sqrt(80)
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(blocks), dim3(64 * NW), 2 * KS_BYTES, s, qimg, kimg, bdesc,
                      heads, pos_thw, n_pos, rope_cs, axis_code, rsqrt_hd, dqkv, out_f32 ? 1 : 0);
-  hipLaunchKernelGGL(bwd_dkv_kernel, dim3(blocks), dim3(64 * NW), 2 * QS_BYTES, s, qimg, kimg, bdesc,
-                     heads, pos_thw, n_pos, rope_cs, axis_code, ln2, dqkv, out_f32 ? 1 : 0);
+  if (kdesc256)
+    hipLaunchKernelGGL(bwd_dkv_kernel<8>, dim3(unsigned(int64_t(max_ktiles256) * heads)), dim3(512),
+                       2 * QS_BYTES, s, qimg, kimg, kdesc256, heads, pos_thw, n_pos, rope_cs, axis_code,
+                       ln2, dqkv, out_f32 ? 1 : 0);
+  else
+    hipLaunchKernelGGL(bwd_dkv_kernel<4>, dim3(blocks), dim3(256), 2 * QS_BYTES, s, qimg, kimg, bdesc,
+                       heads, pos_thw, n_pos, rope_cs, axis_code, ln2, dqkv, out_f32 ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -568,6 +568,7 @@ VT_API vt_status vt_attention_varlen(const vt_config* cfg, const uint16_t* qkv,
 struct AttnBwdBufs {
   BlockBufs fwd;
   int4* bdesc;
+  int4* bdesc256;  // 256-key schedule of the wide dK/dV pass
   float* o;
   float* lse;
   char* qimg;
@@ -578,10 +579,41 @@ void carve_attn_bwd(Carver& c, const Dims& D, int32_t n_pos, AttnBwdBufs* a) {
   carve_attention(c, D, n_pos, &a->fwd);
   const size_t kt = size_t(max_k_tiles(D.N, D.n_img)) * D.heads;
   a->bdesc = c.take<int4>(max_q_tiles(D.N, D.n_img, vt::kAttnBwdTile));
+  a->bdesc256 = c.take<int4>(max_q_tiles(D.N, D.n_img, vt::kAttnBwdWideTile));
   a->o = c.take<float>(size_t(D.N) * D.d);
   a->lse = c.take<float>(size_t(D.N) * D.heads);
   a->qimg = c.take<char>(kt * vt::kAttnBwdQBytes);
   a->kimg = c.take<char>(kt * vt::kAttnBwdKBytes);
+}
+
+// The backward kernels' schedules (128-token tiles; 256-key tiles for the
+// wide dK/dV pass) after attn_prologue: kdesc is rewritten unchanged.
+vt_status attn_bwd_schedule(const int32_t* cu, int32_t n_img, int64_t N, int32_t heads,
+                            const AttnBwdBufs& a, hipStream_t s) {
+  const BlockBufs& b = a.fwd;
+  VT_TRY_HIP(vt::launch_attn_schedule(cu, n_img, vt::kAttnBwdTile, vt::kAttnKTile,
+                                      max_q_tiles(N, n_img, vt::kAttnBwdTile), max_k_tiles(N, n_img),
+                                      b.order, b.tile_start, b.ktile_start, a.bdesc, b.kdesc, s));
+  if (vt::attn_bwd_wide(N, n_img, heads))
+    VT_TRY_HIP(vt::launch_attn_schedule(cu, n_img, vt::kAttnBwdWideTile, vt::kAttnKTile,
+                                        max_q_tiles(N, n_img, vt::kAttnBwdWideTile),
+                                        max_k_tiles(N, n_img), b.order, b.tile_start, b.ktile_start,
+                                        a.bdesc256, b.kdesc, s));
+  return VT_OK;
+}
+
+// Packs, dQ and dK/dV passes of the attention backward (forward already run
+// into a.o and a.lse).
+vt_status run_attn_bwd(const vt_config* cfg, const uint16_t* qkv, const uint16_t* dout,
+                       const int32_t* pos, int32_t n_img, int64_t N, int32_t n_pos, int32_t axis_code,
+                       const AttnBwdBufs& a, void* dqkv, bool f32, hipStream_t s) {
+  const bool wide = vt::attn_bwd_wide(N, n_img, cfg->heads);
+  VT_TRY_HIP(vt::launch_attention_backward(
+      qkv, dout, a.o, a.lse, pos, a.fwd.kdesc, a.bdesc, max_k_tiles(N, n_img),
+      max_q_tiles(N, n_img, vt::kAttnBwdTile), cfg->heads, n_pos, axis_code, a.fwd.rope,
+      q_scale_log2(cfg), a.qimg, a.kimg, dqkv, f32, wide ? a.bdesc256 : nullptr,
+      max_q_tiles(N, n_img, vt::kAttnBwdWideTile), s));
+  return VT_OK;
 }
 
 size_t attn_bwd_ws_bytes(const vt_config* cfg, int64_t N, int32_t n_img, int32_t n_pos) {
@@ -622,19 +654,12 @@ VT_API vt_status vt_attention_backward(const vt_config* cfg, const uint16_t* qkv
   const BlockBufs& b = a.fwd;
   int32_t axis_code = 0;
   if ((st = attn_prologue(cfg, cu_seqlens, n_img, N, max_seqlen, b, &axis_code, s)) != VT_OK) return st;
-  // The 128-token schedule of the backward kernels (same key tiles: kdesc is rewritten unchanged).
-  const int32_t max_bt = max_q_tiles(N, n_img, vt::kAttnBwdTile);
-  VT_TRY_HIP(vt::launch_attn_schedule(cu_seqlens, n_img, vt::kAttnBwdTile, vt::kAttnKTile, max_bt,
-                                      max_k_tiles(N, n_img), b.order, b.tile_start, b.ktile_start,
-                                      a.bdesc, b.kdesc, s));
+  if ((st = attn_bwd_schedule(cu_seqlens, n_img, N, cfg->heads, a, s)) != VT_OK) return st;
   if ((st = run_attention(cfg, qkv, cu_seqlens, pos_thw, n_img, N, max_seqlen, axis_code, b, a.o, true,
                           s, a.lse)) != VT_OK)
     return st;
-  VT_TRY_HIP(vt::launch_attention_backward(qkv, dout, a.o, a.lse, pos_thw, b.kdesc, a.bdesc,
-                                           max_k_tiles(N, n_img), max_bt, cfg->heads, max_seqlen,
-                                           axis_code, b.rope, q_scale_log2(cfg), a.qimg, a.kimg, dqkv,
-                                           dqkv_dtype == VT_FP32, s));
-  return VT_OK;
+  return run_attn_bwd(cfg, qkv, dout, pos_thw, n_img, N, max_seqlen, axis_code, a, dqkv,
+                      dqkv_dtype == VT_FP32, s);
 }
 
 // ---- one block's backward pass
@@ -715,10 +740,7 @@ vt_status run_block_backward(const vt_config* cfg, const float* R, const vt_bloc
   int32_t axis_code = 0;
   vt_status st = attn_prologue(cfg, cu, n_img, N, n_pos, at.fwd, &axis_code, s);
   if (st != VT_OK) return st;
-  const int32_t max_bt = max_q_tiles(N, n_img, vt::kAttnBwdTile);
-  VT_TRY_HIP(vt::launch_attn_schedule(cu, n_img, vt::kAttnBwdTile, vt::kAttnKTile, max_bt,
-                                      max_k_tiles(N, n_img), at.fwd.order, at.fwd.tile_start,
-                                      at.fwd.ktile_start, at.bdesc, at.fwd.kdesc, s));
+  if ((st = attn_bwd_schedule(cu, n_img, N, cfg->heads, at, s)) != VT_OK) return st;
   if ((st = run_attention(cfg, B.qkv, cu, pos, n_img, N, n_pos, axis_code, at.fwd, at.o, true, s,
                           at.lse)) != VT_OK)
     return st;
@@ -754,10 +776,8 @@ vt_status run_block_backward(const vt_config* cfg, const float* R, const vt_bloc
   }
   VT_TRY_HIP(vt::launch_transpose(w->w_o, false, 0, nullptr, d, d, d, nullptr, B.wT, nullptr, s));
   VT_TRY_HIP(vt::launch_gemm(B.gb, M, d, B.wT, d, nullptr, vt::kEpiBf16, B.da, ws, s));
-  VT_TRY_HIP(vt::launch_attention_backward(B.qkv, B.da, at.o, at.lse, pos, at.fwd.kdesc, at.bdesc,
-                                           max_k_tiles(N, n_img), max_bt, cfg->heads, n_pos, axis_code,
-                                           at.fwd.rope, q_scale_log2(cfg), at.qimg, at.kimg, B.dqkv,
-                                           false, s));
+  if ((st = run_attn_bwd(cfg, B.qkv, B.da, pos, n_img, N, n_pos, axis_code, at, B.dqkv, false, s)) != VT_OK)
+    return st;
   VT_TRY_HIP(vt::launch_transpose(B.dqkv, false, 0, nullptr, M, 3 * d, Np, nullptr, B.dqkvT, g->b_qkv, s));
   if (g->w_qkv) {  // dW_qkv = dqkv^T x1
     VT_TRY_HIP(vt::launch_transpose(B.x1, false, 0, nullptr, M, d, Np, nullptr, B.xT, nullptr, s));

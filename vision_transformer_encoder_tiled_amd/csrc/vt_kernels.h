@@ -122,12 +122,19 @@ constexpr int kAttnBwdTile = 128;  // queries (dQ pass) or keys (dK/dV pass) per
 // o: the forward output [N, heads*80] fp32; lse: its [N, heads] log-sum-exp;
 // dout: [N, heads*80] bf16.  kdesc from launch_attn_schedule (key tiles of
 // 64), bdesc from a schedule with q_tile = kAttnBwdTile (max_btiles slots).
-// dqkv: [N, 3, heads, 80], bf16 or fp32.
+// kdesc256, when not null, is a schedule with q_tile = kAttnBwdWideTile
+// (max_ktiles256 slots): the dK/dV pass then runs 8 wavefronts of 256 keys
+// (attn_bwd_wide decides).  dqkv: [N, 3, heads, 80], bf16 or fp32.
+constexpr int kAttnBwdWideTile = 256;
+inline bool attn_bwd_wide(int64_t N, int32_t n_img, int32_t heads) {
+  return ((N + kAttnBwdWideTile - 1) / kAttnBwdWideTile + n_img) * heads >= 1024;
+}
 hipError_t launch_attention_backward(const uint16_t* qkv, const uint16_t* dout, const float* o,
                                      const float* lse, const int32_t* pos_thw, const int2* kdesc,
                                      const int4* bdesc, int32_t max_ktiles, int32_t max_btiles,
                                      int32_t heads, int32_t n_pos, int32_t axis_code,
                                      const float2* rope_cs, float q_scale_log2, char* qimg,
-                                     char* kimg, void* dqkv, bool out_f32, hipStream_t s);
+                                     char* kimg, void* dqkv, bool out_f32, const int4* kdesc256,
+                                     int32_t max_ktiles256, hipStream_t s);
 
 }  // namespace vt
