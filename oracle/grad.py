@@ -153,3 +153,26 @@ def attention_dq_rows(qkv, pos, cu, dout, rows, cfg: vit.Config = None):
             out[sel, h] = ds @ k[:, h] * scale
         out[sel] = rope_backward(out[sel], pos[r], axis, inv)
     return out
+
+
+def tower_backward(images, grids, W, cfg: vit.Config, n_layers, d_tower):
+    """Gradients of the tower -- patch embed, then n_layers blocks -- given
+    dL/d(tower output) ``d_tower`` [N, d] (raster order).  ``images`` are the
+    items as vit.split_pixels returns them, ``W`` float weights.  Returns
+    {"patch_w", "patch_b", "l<i>.<name>"} (the bias gradient even where the
+    bias is absent)."""
+    pos = vit.positions(grids)
+    cu = vit.cu_seqlens(grids)
+    X = np.concatenate([vit.patchify(img) for img in images], axis=0)
+    R = vit.linear(X, W["patch_w"], W.get("patch_b"))
+    inputs = []
+    for i in range(n_layers):
+        inputs.append(R)
+        R = vit.block_forward(R, W, pos, cu, cfg, prefix=f"l{i}.")
+    dR = d_tower
+    grads = {}
+    for i in reversed(range(n_layers)):
+        dR, g = block_backward(inputs[i], W, pos, cu, cfg, dR, prefix=f"l{i}.")
+        grads.update({f"l{i}.{k}": v for k, v in g.items()})
+    _, grads["patch_w"], grads["patch_b"] = linear_backward(X, W["patch_w"], dR)
+    return grads

@@ -170,3 +170,41 @@ def test_attention_qkv_gradient_and_sampled_rows():
     bad[:, 0] *= -1
     with pytest.raises(AssertionError):
         fd_dot(lambda t: _qkv_attention(t, pos, cu, cfg), qkv, do, bad)
+
+
+def test_tower_gradient_finite_differences():
+    """tower_backward (patch embed + 2 tiny blocks, two items) against central
+    differences of the forward oracle along random directions of the patch
+    weight, a first-layer weight (its gradient crosses the second block) and
+    the last layer's LN gamma."""
+    cfg = TINY
+    grids = [(1, 2, 2), (1, 2, 4)]
+    g0 = rng(40)
+    d, mlp, H, hd = cfg.hidden, cfg.mlp, cfg.heads, cfg.head_dim
+    W = {"patch_w": g0.standard_normal((d, 1176)) * 0.03, "patch_b": g0.standard_normal(d) * 0.1}
+    for i in range(2):
+        p = f"l{i}."
+        W.update({p + "ln1_g": 1 + 0.1 * g0.standard_normal(d), p + "ln1_b": 0.1 * g0.standard_normal(d),
+                  p + "w_qkv": g0.standard_normal((3 * d, d)) * 0.3, p + "b_qkv": 0.1 * g0.standard_normal(3 * d),
+                  p + "w_o": g0.standard_normal((d, d)) * 0.3, p + "b_o": 0.1 * g0.standard_normal(d),
+                  p + "ln2_g": 1 + 0.1 * g0.standard_normal(d), p + "ln2_b": 0.1 * g0.standard_normal(d),
+                  p + "w_fc1": g0.standard_normal((mlp, d)) * 0.3, p + "b_fc1": 0.1 * g0.standard_normal(mlp),
+                  p + "w_fc2": g0.standard_normal((d, mlp)) * 0.3, p + "b_fc2": 0.1 * g0.standard_normal(d)})
+    images = [g0.random((3, 14 * h, 14 * w)) for _, h, w in grids]
+    N = sum(h * w for _, h, w in grids)
+    dT = g0.standard_normal((N, d))
+    pos, cu = oracle.positions(grids), oracle.cu_seqlens(grids)
+
+    def tower(Wx):
+        R = oracle.patch_embed(images, Wx, grids)
+        for i in range(2):
+            R = oracle.block_forward(R, Wx, pos, cu, cfg, prefix=f"l{i}.")
+        return R
+
+    grads = G.tower_backward(images, grids, W, cfg, 2, dT)
+    for name in ("patch_w", "patch_b", "l0.w_qkv", "l1.ln2_g"):
+        def f(t, name=name):
+            Wx = dict(W)
+            Wx[name] = t
+            return tower(Wx)
+        fd_dot(f, W[name], dT, grads[name])
