@@ -195,6 +195,27 @@ def block_backward_case(vt, torch, grids):
     return (lambda: vt.vt_block_backward(cfg, R, bw, cu, pos, len(grids), N, max_seq, dR, gs, ws)), flops
 
 
+def tower_backward_case(vt, torch, wl, tw, W):
+    """vt_tower_backward of the 32-layer tower on the workload's items, with
+    dL/d(tower output) = 1/n per token (the mean-pool probe).  FLOPs counted:
+    the tower's forward (patch embed + blocks) plus its backward (2x the block
+    products, dW of the patch embed, 8 n^2 d attention per layer); the call
+    also recomputes each block's forward."""
+    N = wl.tokens
+    px = torch.from_numpy(synth.make_batch_pixels(wl).view(np.int16)).cuda()
+    grids = list(wl.grids)
+    dT = torch.cat([torch.full((t * h * w, 1280), 1.0 / (t * h * w), device="cuda") for t, h, w in grids])
+    grads = {k: torch.empty(v.shape, dtype=torch.float32, device="cuda") for k, v in W.items()
+             if not k.startswith("p_")}
+    tg = vt.TowerGrads(grads, 32)
+    cfg = vt.config()
+    ws = vt.workspace(vt.vt_tower_backward_workspace_size(cfg, grids))
+    block, _ = gemm_flops_per_token()
+    flops = N * (2 * 2 * 1176 * 1280 + 32 * 3 * block) + 32 * float(
+        sum(12 * (t * h * w) ** 2 * 1280 for t, h, w in grids))
+    return (lambda: vt.vt_tower_backward(cfg, px, grids, tw, dT, tg, ws)), flops
+
+
 def copy_case(torch, nbytes=256 << 20):
     """A plain device-to-device copy of nbytes (the HBM-counter calibration)."""
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -361,6 +382,15 @@ def main():
     res["attention_roofline"] = attention_roofline(vt, torch, list(wl.grids), a.kernel_iters)
     res["attention_backward"] = attention_backward_line(vt, torch, list(wl.grids), a.kernel_iters)
     res["block_backward"] = block_backward_line(vt, torch, list(wl.grids), a.kernel_iters)
+    fn, fl = tower_backward_case(vt, torch, wl, tw, weights)
+    tt = time_kernel(torch, fn, max(2, a.kernel_iters // 5))
+    res["tower_backward"] = {
+        "call": "vt_tower_backward (%s: 32 layers + patch embed, all gradients)" % wl.name,
+        "achieved": fl / tt / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "frac": fl / tt / 1e12 / PEAK_BF16_TFLOPS, "flops_per_call": fl, "ms_per_call": tt * 1e3,
+        "patches_per_s": wl.tokens / tt,
+        "note": "forward with every block input kept, then the backward of each block (which "
+                "recomputes that block's forward) and of the patch embed"}
 
     if a.secondary:
         wl2 = synth.WORKLOADS[a.secondary]

@@ -257,6 +257,34 @@ vt_status vt_block_backward(const vt_config* cfg, const float* resid_in, const v
 size_t vt_block_backward_workspace_size(const vt_config* cfg, int32_t total_tokens, int32_t n_img,
                                         int32_t max_seqlen);
 
+/* Gradients of the tower's parameters (fp32): the patch embed and a host
+ * array of cfg->layers block gradients.  NULL members are not formed. */
+typedef struct vt_tower_grads {
+  float *w_patch, *b_patch;          /* [hidden, 1176], [hidden] */
+  const vt_block_grads* blocks;      /* host array of cfg->layers entries */
+} vt_tower_grads;
+
+/* Backward pass of the tower -- patch embed and cfg->layers blocks -- from
+ * dL/d(tower output) ("v2_loaders FINDINGS", section 3: the probe mean-pools
+ * the tower output and runs a backward pass through the tower).  Runs the
+ * forward of vt_tower_forward keeping each block's input, then
+ * vt_block_backward from the last block to the first, then the patch
+ * embed's dW = dR0^T X and db = column sums of dR0.  The bf16 rounding of the
+ * tower output is passed through as the identity.
+ *   pixels, grid, n_img, w: as vt_tower_forward (w->proj is not read).
+ *   d_tower   fp32 [N, hidden], raster order per item (the order of
+ *             vt_tower_forward's tower_out): dL/d(tower output).
+ *   grads     host struct; every formed gradient is overwritten.
+ *   ws        vt_tower_backward_workspace_size bytes (about 320 KB per token at
+ *             32 layers: each block's fp32 input is kept).
+ * Errors as for vt_tower_forward; hidden <= 2048; nothing is launched on error. */
+vt_status vt_tower_backward(const vt_config* cfg, const uint16_t* pixels, const vt_grid_thw* grid,
+                            int32_t n_img, const vt_tower_weights* w, const float* d_tower,
+                            const vt_tower_grads* grads, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for vt_tower_backward; 0 (and vt_last_error()) if invalid. */
+size_t vt_tower_backward_workspace_size(const vt_config* cfg, const vt_grid_thw* grid, int32_t n_img);
+
 /* 2x2 merge + projector (README Architecture, Projector row).
  *   tower      bf16 [N, hidden] tower tokens, rows in `order`.
  *   merged_raw bf16 [N/4, 4*hidden] or NULL: the 2x2 gather of the tower

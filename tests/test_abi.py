@@ -30,7 +30,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     declared = header_functions()
-    assert len(declared) == 22
+    assert len(declared) == 24
     assert sorted(vt.EXPORTED) == declared
     lib = ctypes.CDLL(vt.LIB_PATH)
     for name in declared:
@@ -175,6 +175,45 @@ def test_block_backward_validation():
     assert call(bw=bw2) == vt.VT_ERR_INVALID_ARG                       # NULL weights
     wide = vt.config(hidden=2560, heads=32)
     assert call(cfg=wide, ws_bytes=1 << 40) == vt.VT_ERR_UNSUPPORTED   # hidden > 2048
+
+
+@needs_no_gpu
+def test_tower_backward_validation():
+    cfg = vt.config(layers=2)
+    P = ctypes.c_void_p
+    grids = [(1, 4, 4)]
+    need = vt.vt_tower_backward_workspace_size(cfg, grids)
+    assert need > 0
+    blocks = (vt.vt_block_weights * 2)()
+    for b in blocks:
+        for name, _ in vt.vt_block_weights._fields_:
+            setattr(b, name, FAKE)
+    tw = vt.vt_tower_weights()
+    tw.w_patch = FAKE
+    tw.blocks = ctypes.cast(blocks, ctypes.POINTER(vt.vt_block_weights))
+    bg = (vt.vt_block_grads * 2)()
+    tg = vt.vt_tower_grads()
+    tg.blocks = ctypes.cast(bg, ctypes.POINTER(vt.vt_block_grads))
+
+    def call(grids=grids, d_tower=FAKE, tg=tg, ws_bytes=need, tw=tw, cfg=cfg):
+        g, n = vt._lib._grid(grids)
+        return vt.LIB.vt_tower_backward(ctypes.byref(cfg), P(FAKE), g, n, ctypes.byref(tw), P(d_tower),
+                                        ctypes.byref(tg) if tg is not None else None, P(FAKE), ws_bytes,
+                                        None)
+    assert call(ws_bytes=need - 1) == vt.VT_ERR_WORKSPACE
+    assert call(d_tower=None) == vt.VT_ERR_INVALID_ARG
+    assert call(tg=None) == vt.VT_ERR_INVALID_ARG
+    assert call(grids=[(1, 3, 4)]) == vt.VT_ERR_INVALID_ARG
+    tg2 = vt.vt_tower_grads()                                       # blocks missing
+    assert call(tg=tg2) == vt.VT_ERR_INVALID_ARG
+    bg[1].w_o = FAKE + 4                                            # misaligned gradient
+    assert call() == vt.VT_ERR_INVALID_ARG
+    assert "block 1" in vt.last_error()
+    bg[1].w_o = None
+    tw2 = vt.vt_tower_weights()
+    tw2.w_patch = FAKE
+    assert call(tw=tw2) == vt.VT_ERR_INVALID_ARG                    # blocks NULL
+    assert vt.vt_tower_backward_workspace_size(cfg, [(1, 3, 3)]) == 0
 
 
 def test_attention_backward_workspace_is_affine():

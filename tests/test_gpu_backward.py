@@ -203,3 +203,59 @@ def test_block_backward_ragged_images(vt):
     R = rng(51).standard_normal((N, 1280), dtype=np.float32)
     dR2 = rng(52).standard_normal((N, 1280), dtype=np.float32)
     check_block(*block_backward_case(vt, grids, R, dR2, "random"), "ragged")
+
+
+# ---------------------------------------------------------------- the tower
+def tower_backward_case(vt, grids, seeds, n_layers, d_tower, affine="random"):
+    """vt_tower_backward (n_layers blocks) on seeded items and dL/d(tower
+    output) (raster order); returns (gpu grads, oracle grads), keyed like the
+    oracle's."""
+    W = synth.make_weights(n_layers, projector=False, affine=affine)
+    px = np.concatenate([(synth.make_pixels(h, w, s) if t == 1 else synth.make_clip(t, h, w, s)).reshape(-1)
+                         for (t, h, w), s in zip(grids, seeds)])
+    cfg = vt.config(layers=n_layers)
+    dw = {k: dev_bits(v, torch) for k, v in W.items()}
+    tw = vt.TowerWeights(dw, n_layers)
+    gd = {k: torch.full(v.shape, float("nan"), dtype=torch.float32, device="cuda") for k, v in W.items()}
+    tg = vt.TowerGrads(gd, n_layers)
+    ws = vt.workspace(vt.vt_tower_backward_workspace_size(cfg, grids))
+    vt.vt_tower_backward(cfg, dev_bits(px, torch), grids, tw, torch.from_numpy(d_tower).cuda(), tg, ws)
+    torch.cuda.synchronize()
+    got = {k: t.cpu().numpy() for k, t in gd.items()}
+    Wf = {k: v.astype(np.float64) for k, v in oracle.weights_f32(W).items()}
+    imgs = [x.astype(np.float64) for x in oracle.split_pixels(bf16_f32(px), grids)]
+    want = G.tower_backward(imgs, grids, Wf, oracle.Config(), n_layers, d_tower.astype(np.float64))
+    return got, want
+
+
+def check_tower(got, want, what, tol=1e-2):
+    errs = {k: rel_l2(got[k], want[k]) for k in want}
+    worst = max(errs, key=errs.get)
+    log(f"  {what}: patch_w {errs['patch_w']:.1e} patch_b {errs['patch_b']:.1e}; worst {worst} {errs[worst]:.1e}")
+    assert all(np.all(np.isfinite(got[k])) for k in want)
+    assert errs[worst] <= tol
+
+
+def test_tower_backward_two_layers(vt):
+    """Two blocks over two items (224x224 and a 6x8-patch image), random
+    dL/d(tower output): every parameter gradient of both blocks and of the
+    patch embed."""
+    grids = [(1, 16, 16), (1, 6, 8)]
+    N = 256 + 48
+    dT = rng(53).standard_normal((N, 1280), dtype=np.float32)
+    check_tower(*tower_backward_case(vt, grids, [1, 7], 2, dT), "2 layers")
+
+
+def test_tower_backward_mean_pool_probe(vt):
+    """The pages' probe (mean-pool the tower output, then a backward pass) on
+    a 4-layer tower of one 224x224 image, with the loss sum over features of
+    the pooled feature: dL/d(token) = 1/n for every token and feature.  The
+    gradient norm over all parameters is compared with the oracle's."""
+    grids = [(1, 16, 16)]
+    dT = np.full((256, 1280), 1.0 / 256, np.float32)
+    got, want = tower_backward_case(vt, grids, [1], 4, dT, affine="canonical")
+    check_tower(got, want, "probe 4 layers")
+    g_gpu = np.sqrt(sum(float((got[k].astype(np.float64) ** 2).sum()) for k in want))
+    g_ref = np.sqrt(sum(float((want[k] ** 2).sum()) for k in want))
+    log(f"  grad_l2 {g_gpu:.6g} (oracle {g_ref:.6g})")
+    assert abs(g_gpu - g_ref) <= 1e-2 * g_ref

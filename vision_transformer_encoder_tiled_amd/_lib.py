@@ -26,7 +26,8 @@ EXPORTED = ("vt_config_default", "vt_status_string", "vt_last_error", "vt_versio
             "vt_tower_forward", "vt_plan_patches", "vt_pack_items", "vt_mean_pool",
             "vt_linear_workspace_size", "vt_linear", "vt_layer_norm", "vt_attention_backward",
             "vt_attention_backward_workspace_size", "vt_block_backward",
-            "vt_block_backward_workspace_size")
+            "vt_block_backward_workspace_size", "vt_tower_backward",
+            "vt_tower_backward_workspace_size")
 
 
 class VtError(RuntimeError):
@@ -58,6 +59,10 @@ class vt_block_weights(ctypes.Structure):
 
 class vt_block_grads(ctypes.Structure):
     _fields_ = list(vt_block_weights._fields_)
+
+
+class vt_tower_grads(ctypes.Structure):
+    _fields_ = [("w_patch", _P), ("b_patch", _P), ("blocks", ctypes.POINTER(vt_block_grads))]
 
 
 class vt_projector_weights(ctypes.Structure):
@@ -100,6 +105,9 @@ def _load():
                                             _P]),
         "vt_tower_forward": (ctypes.c_int, [cfgp, _P, gridp, I32, ctypes.POINTER(vt_tower_weights),
                                             _P, _P, _P, _P, SZ, _P]),
+        "vt_tower_backward": (ctypes.c_int, [cfgp, _P, gridp, I32, ctypes.POINTER(vt_tower_weights), _P,
+                                             ctypes.POINTER(vt_tower_grads), _P, SZ, _P]),
+        "vt_tower_backward_workspace_size": (SZ, [cfgp, gridp, I32]),
         "vt_linear_workspace_size": (SZ, [I32, I32, I32]),
         "vt_linear": (ctypes.c_int, [_P, I32, I32, _P, I32, _P, ctypes.c_int, _P, _P, SZ, _P]),
         "vt_layer_norm": (ctypes.c_int, [_P, I32, I32, _P, _P, ctypes.c_float, _P, _P]),
@@ -296,6 +304,36 @@ def vt_tower_forward(cfg, pixels, grids, tw: TowerWeights, tower_out, merged_raw
     _check(LIB.vt_tower_forward(ctypes.byref(cfg), _ptr(pixels), g, n, ctypes.byref(tw.struct),
                                 _ptr(tower_out), _ptr(merged_raw), _ptr(out), _ptr(ws),
                                 ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+class TowerGrads:
+    """Keeps the ctypes structs of a tower gradient set alive: ``g`` maps
+    "patch_w", "patch_b" and "l<i>.<name>" to fp32 device tensors (missing
+    entries are not formed)."""
+
+    def __init__(self, g: dict, n_layers: int):
+        self.g = g
+        self.blocks = (vt_block_grads * max(1, n_layers))()
+        for i in range(n_layers):
+            p = f"l{i}."
+            self.blocks[i] = block_grads({k[len(p):]: v for k, v in g.items() if k.startswith(p)})
+        self.struct = vt_tower_grads()
+        for name in ("w_patch", "b_patch"):
+            t = g.get("patch_" + name[0])
+            setattr(self.struct, name, None if t is None else t.data_ptr())
+        self.struct.blocks = ctypes.cast(self.blocks, ctypes.POINTER(vt_block_grads))
+
+
+def vt_tower_backward_workspace_size(cfg, grids) -> int:
+    g, n = _grid(grids)
+    return int(LIB.vt_tower_backward_workspace_size(ctypes.byref(cfg), g, n))
+
+
+def vt_tower_backward(cfg, pixels, grids, tw: TowerWeights, d_tower, tg: TowerGrads, ws, stream=None):
+    g, n = _grid(grids)
+    _check(LIB.vt_tower_backward(ctypes.byref(cfg), _ptr(pixels), g, n, ctypes.byref(tw.struct),
+                                 _ptr(d_tower), ctypes.byref(tg.struct), _ptr(ws),
+                                 ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def vt_linear(x, M, K, w, N, bias, epi, out, ws=None, stream=None):

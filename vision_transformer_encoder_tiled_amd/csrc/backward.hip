@@ -42,10 +42,11 @@ __device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float* v) {
 }
 }  // namespace
 
-// One 64 x 64 tile of in [M, C] per block (256 threads): v = op(in) (op 1:
-// GELU; op 2: in * GELU'(aux)), rows M .. Mp-1 read as zero.  Writes, each
-// when its pointer is set: copy [M, C] = bf16(v); outT [C, Mp] = bf16(v)^T;
-// colsum[c] += sum over rows of v (fp32 atomics, the buffer zeroed before).
+// One 64 x 64 tile of in [M, C] per block (256 threads; C a multiple of 4,
+// the last column tile partial): v = op(in) (op 1: GELU; op 2: in *
+// GELU'(aux)), rows M .. Mp-1 read as zero.  Writes, each when its pointer is
+// set: copy [M, C] = bf16(v); outT [C, Mp] = bf16(v)^T; colsum[c] += sum over
+// rows of v (fp32 atomics, the buffer zeroed before).
 template <class TIN, int OP>
 __global__ void __launch_bounds__(256) transpose_kernel(const TIN* in,
                                                         const uint16_t* __restrict__ aux,
@@ -60,7 +61,7 @@ __global__ void __launch_bounds__(256) transpose_kernel(const TIN* in,
   for (int r = 0; r < 4; ++r) {
     const int row = rq + 16 * r, m = m0 + row;
     float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (m < M) {
+    if (m < M && c0 + cq < C) {
       const int64_t off = int64_t(m) * C + c0 + cq;
       load4<TIN>(in + off, v);
       if constexpr (OP == 1) {
@@ -81,12 +82,12 @@ __global__ void __launch_bounds__(256) transpose_kernel(const TIN* in,
     for (int j = 0; j < 4; ++j) tile[row][cq + j] = v[j];
   }
   __syncthreads();
-  if (colsum && tid < 64) {
+  if (colsum && tid < 64 && c0 + tid < C) {
     float s = 0.f;
     for (int r = 0; r < 64; ++r) s += tile[r][tid];
     atomicAdd(colsum + c0 + tid, s);
   }
-  if (outT) {
+  if (outT && c0 + (tid >> 2) < C) {
     // thread -> (column tid / 4, rows 16 (tid % 4) .. +15): two 16-byte stores
     const int c = tid >> 2, r0 = 16 * (tid & 3);
     uint32_t w[8];
@@ -185,6 +186,19 @@ __global__ void __launch_bounds__(256) ln_backward_kernel(
   }
 }
 
+// out [C, R] = in [R, C]^T, fp32, 32 x 32 tiles through LDS (any R, C).
+__global__ void __launch_bounds__(256) transpose_f32_kernel(const float* __restrict__ in, int32_t R,
+                                                            int32_t C, float* __restrict__ out) {
+  __shared__ float tile[32][33];
+  const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int i = ty; i < 32; i += 8)
+    if (r0 + i < R && c0 + tx < C) tile[i][tx] = in[int64_t(r0 + i) * C + c0 + tx];
+  __syncthreads();
+  for (int i = ty; i < 32; i += 8)
+    if (c0 + i < C && r0 + tx < R) out[int64_t(c0 + i) * R + r0 + tx] = tile[tx][i];
+}
+
 __global__ void __launch_bounds__(256) zero_f32_kernel(float* __restrict__ p, int64_t n) {
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256)
     p[i] = 0.f;
@@ -193,9 +207,9 @@ __global__ void __launch_bounds__(256) zero_f32_kernel(float* __restrict__ p, in
 hipError_t launch_transpose(const void* in, bool in_f32, int op, const uint16_t* aux, int32_t M,
                             int32_t C, int32_t Mp, uint16_t* copy, uint16_t* outT, float* colsum,
                             hipStream_t s) {
-  if (C % 64 || Mp % 64 || Mp < M || (in_f32 && op != 0) || op < 0 || op > 2 || (op == 2 && !aux))
+  if (C % 4 || Mp % 64 || Mp < M || (in_f32 && op != 0) || op < 0 || op > 2 || (op == 2 && !aux))
     return hipErrorInvalidValue;
-  const dim3 grid(C / 64, Mp / 64);
+  const dim3 grid((C + 63) / 64, Mp / 64);
   if (in_f32)
     hipLaunchKernelGGL((transpose_kernel<float, 0>), grid, dim3(256), 0, s,
                        static_cast<const float*>(in), aux, M, C, Mp, copy, outT, colsum);
@@ -227,6 +241,12 @@ hipError_t launch_ln_backward(const float* x, const uint16_t* g, const float* dy
 #undef VT_LNB_CASE
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_f32(const float* in, int32_t R, int32_t C, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(transpose_f32_kernel, dim3((C + 31) / 32, (R + 31) / 32), dim3(256), 0, s, in, R,
+                     C, out);
   return hipGetLastError();
 }
 

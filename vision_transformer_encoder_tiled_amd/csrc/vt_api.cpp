@@ -927,6 +927,130 @@ VT_API vt_status vt_tower_forward(const vt_config* cfg, const uint16_t* pixels,
   return run_tail(cfg, t, t.T, N, &w->proj, merged_raw, out, s);
 }
 
+// ---- the tower's backward pass
+// Buffers of vt_tower_backward: metadata, patches, the running residual and
+// every block's input, the forward block buffers, the block backward's
+// buffers, dL/dR, and the patch-weight gradient's operands.
+struct TowerBwdBufs {
+  int32_t *cu, *pos, *ridx, *tok_img;
+  vt::ImgInfo* info;
+  uint16_t* X;      // [N, 1176] patches
+  float* R;         // [N, d] running residual
+  float* Rsave;     // [layers, N, d] the input of each block
+  float* dR;        // [N, d]
+  uint16_t* XT;     // [1176, Np]
+  float* dwT;       // [1176, d]
+  BlockBufs blk;
+  BlockBwdBufs bb;
+  void* patch_ws;
+};
+
+void carve_tower_bwd(Carver& c, const vt_config* cfg, const Dims& D, int32_t n_pos, TowerBwdBufs* t) {
+  const size_t N = D.N, d = D.d, Np = pad64(D.N);
+  t->cu = c.take<int32_t>(D.n_img + 1);
+  t->info = c.take<vt::ImgInfo>(D.n_img);
+  t->pos = c.take<int32_t>(N * 3);
+  t->ridx = c.take<int32_t>(N);
+  t->tok_img = c.take<int32_t>(N);
+  t->X = c.take<uint16_t>(N * 1176);
+  t->R = c.take<float>(N * d);
+  t->Rsave = c.take<float>(size_t(std::max(cfg->layers, 1)) * N * d);
+  t->dR = c.take<float>(N * d);
+  t->XT = c.take<uint16_t>(1176 * Np);
+  t->dwT = c.take<float>(1176 * d);
+  carve_block(c, D, n_pos, &t->blk);
+  carve_block_bwd(c, D, n_pos, &t->bb);
+  t->patch_ws = c.take<char>(D.ws_upper ? kPartialsBound : vt::gemm_workspace_bytes(1176, D.d, int(Np)));
+}
+
+size_t tower_bwd_ws_bytes(const vt_config* cfg, const GridInfo& gi, int32_t n_img) {
+  Carver c(nullptr);
+  TowerBwdBufs t;
+  carve_tower_bwd(c, cfg, dims_of(cfg, gi.tokens, n_img), gi.max_hw, &t);
+  return c.off;
+}
+
+VT_API size_t vt_tower_backward_workspace_size(const vt_config* cfg, const vt_grid_thw* grid,
+                                               int32_t n_img) {
+  if (check_config(cfg) != VT_OK) return 0;
+  GridInfo gi;
+  if (check_grid(grid, n_img, &gi) != VT_OK) return 0;
+  return tower_bwd_ws_bytes(cfg, gi, n_img);
+}
+
+VT_API vt_status vt_tower_backward(const vt_config* cfg, const uint16_t* pixels,
+                                   const vt_grid_thw* grid, int32_t n_img, const vt_tower_weights* w,
+                                   const float* d_tower, const vt_tower_grads* grads, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  vt_status st = check_config(cfg);
+  if (st != VT_OK) return st;
+  if (cfg->hidden > 2048) return fail(VT_ERR_UNSUPPORTED, "the backward pass supports hidden <= 2048");
+  GridInfo gi;
+  if ((st = check_grid(grid, n_img, &gi)) != VT_OK) return st;
+  if ((st = check_ptr(pixels, "pixels")) != VT_OK) return st;
+  if ((st = check_ptr(d_tower, "d_tower")) != VT_OK) return st;
+  if (!w) return fail(VT_ERR_INVALID_ARG, "weights are NULL");
+  if ((st = check_ptr(w->w_patch, "w_patch")) != VT_OK) return st;
+  if (w->b_patch && !aligned16(w->b_patch)) return fail(VT_ERR_INVALID_ARG, "b_patch is not 16-byte aligned");
+  if (cfg->layers > 0 && !w->blocks) return fail(VT_ERR_INVALID_ARG, "blocks is NULL");
+  for (int l = 0; l < cfg->layers; ++l)
+    if ((st = check_block_weights(&w->blocks[l], l)) != VT_OK) return st;
+  if (!grads) return fail(VT_ERR_INVALID_ARG, "grads is NULL (its members may be NULL)");
+  if (cfg->layers > 0 && !grads->blocks) return fail(VT_ERR_INVALID_ARG, "grads->blocks is NULL");
+  if ((grads->w_patch && !aligned16(grads->w_patch)) || (grads->b_patch && !aligned16(grads->b_patch)))
+    return fail(VT_ERR_INVALID_ARG, "a patch gradient buffer is not 16-byte aligned");
+  for (int l = 0; l < cfg->layers; ++l) {
+    const vt_block_grads& g = grads->blocks[l];
+    const float* gp[] = {g.ln1_g, g.ln1_b, g.w_qkv, g.b_qkv, g.w_o, g.b_o,
+                         g.ln2_g, g.ln2_b, g.w_fc1, g.b_fc1, g.w_fc2, g.b_fc2};
+    for (const float* p : gp)
+      if (p && !aligned16(p)) return fail(VT_ERR_INVALID_ARG, "block %d: a gradient buffer is not 16-byte aligned", l);
+  }
+  const size_t need = tower_bwd_ws_bytes(cfg, gi, n_img);
+  if ((st = check_ws(ws, ws_bytes, need)) != VT_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver c(ws);
+  TowerBwdBufs t;
+  const int64_t N = gi.tokens;
+  const int d = cfg->hidden, M = int(N), Np = pad64(N);
+  carve_tower_bwd(c, cfg, dims_of(cfg, N, n_img), gi.max_hw, &t);
+  // forward, keeping each block's input
+  if ((st = launch_meta(grid, n_img, N, t.cu, t.info, t.pos, t.ridx, t.tok_img, s)) != VT_OK) return st;
+  int32_t axis_code = 0;
+  if ((st = attn_prologue(cfg, t.cu, n_img, N, gi.max_hw, t.blk, &axis_code, s)) != VT_OK) return st;
+  VT_TRY_HIP(vt::launch_patchify(pixels, t.info, t.cu, t.tok_img, M, t.X, s));
+  VT_TRY_HIP(vt::launch_gemm(t.X, M, 1176, w->w_patch, d, w->b_patch, vt::kEpiF32, t.R, t.blk.gemm_ws, s));
+  bool xn_ready = false;
+  const size_t plane = size_t(N) * d;
+  for (int l = 0; l < cfg->layers; ++l) {
+    VT_TRY_HIP(hipMemcpyAsync(t.Rsave + l * plane, t.R, plane * sizeof(float), hipMemcpyDeviceToDevice, s));
+    const vt_block_weights* nx = l + 1 < cfg->layers ? &w->blocks[l + 1] : nullptr;
+    st = run_block(cfg, t.R, &w->blocks[l], t.cu, t.pos, n_img, N, gi.max_hw, axis_code, t.blk,
+                   nx ? nx->ln1_g : nullptr, nx ? nx->ln1_b : nullptr, &xn_ready, s);
+    if (st != VT_OK) return st;
+  }
+  // dL/dR after the last block, in token order (rows of 2 * d 16-bit units)
+  VT_TRY_HIP(vt::launch_row_permute(reinterpret_cast<const uint16_t*>(d_tower),
+                                    reinterpret_cast<uint16_t*>(t.dR), t.ridx, M, 2 * d, false, s));
+  for (int l = cfg->layers - 1; l >= 0; --l) {
+    st = run_block_backward(cfg, t.Rsave + l * plane, &w->blocks[l], t.cu, t.pos, n_img, N, gi.max_hw,
+                            t.dR, &grads->blocks[l], t.bb, s);
+    if (st != VT_OK) return st;
+  }
+  // patch embed: dW = dR0^T X (formed as X^T dR0, then transposed), db = column sums of dR0
+  if (grads->b_patch) VT_TRY_HIP(vt::launch_zero_f32(grads->b_patch, d, s));
+  if (grads->w_patch || grads->b_patch)
+    VT_TRY_HIP(vt::launch_transpose(t.dR, true, 0, nullptr, M, d, Np, nullptr,
+                                    grads->w_patch ? t.bb.gT : nullptr, grads->b_patch, s));
+  if (grads->w_patch) {
+    VT_TRY_HIP(vt::launch_transpose(t.X, false, 0, nullptr, M, 1176, Np, nullptr, t.XT, nullptr, s));
+    VT_TRY_HIP(vt::launch_gemm(t.XT, 1176, Np, t.bb.gT, d, nullptr, vt::kEpiF32, t.dwT, t.patch_ws, s));
+    VT_TRY_HIP(vt::launch_transpose_f32(t.dwT, 1176, d, grads->w_patch, s));
+  }
+  return VT_OK;
+}
+
 VT_API size_t vt_linear_workspace_size(int32_t M, int32_t N, int32_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   return vt::gemm_workspace_bytes(M, N, K);

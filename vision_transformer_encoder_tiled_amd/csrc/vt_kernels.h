@@ -97,8 +97,8 @@ hipError_t launch_attention(const uint16_t* qkv, const int32_t* pos_thw, const i
                             void* out, bool out_f32, float* lse, hipStream_t s);
 
 // ---- block backward helpers (backward.hip)
-// 64 x 64-tiled transpose of in [M, C] (fp32 or bf16; C, Mp multiples of 64,
-// Mp >= M) with v = op(in): op 0 identity, 1 GELU(tanh), 2 in * GELU'(aux)
+// 64 x 64-tiled transpose of in [M, C] (fp32 or bf16; C a multiple of 4, Mp
+// a multiple of 64, Mp >= M) with v = op(in): op 0 identity, 1 GELU(tanh), 2 in * GELU'(aux)
 // (aux bf16 [M, C]; fp32 input only with op 0).  Optional outputs: copy
 // [M, C] bf16(v), outT [C, Mp] bf16(v)^T (rows M.. zero), colsum [C] += the
 // column sums of bf16(v) (fp32 atomics: zero it first).
@@ -112,6 +112,8 @@ hipError_t launch_ln_backward(const float* x, const uint16_t* g, const float* dy
                               int32_t rows, int32_t width, float eps, float* dx, float* dg,
                               float* db, hipStream_t s);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
+// out [C, R] = in [R, C]^T, fp32.
+hipError_t launch_transpose_f32(const float* in, int32_t R, int32_t C, float* out, hipStream_t s);
 
 // ---- attention backward (attention_bwd.hip)
 // Tile images of 64 tokens of one head: the key side (K, V, K^T) and the
