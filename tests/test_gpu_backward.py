@@ -259,3 +259,58 @@ def test_tower_backward_mean_pool_probe(vt):
     g_ref = np.sqrt(sum(float((want[k] ** 2).sum()) for k in want))
     log(f"  grad_l2 {g_gpu:.6g} (oracle {g_ref:.6g})")
     assert abs(g_gpu - g_ref) <= 1e-2 * g_ref
+
+
+def test_block_backward_is_reproducible(vt):
+    """Two calls on the same inputs give bitwise-equal gradients: every sum
+    (split-K, bias and LayerNorm gradients) runs in a fixed order, with no
+    atomics."""
+    grids = [(1, 12, 14), (1, 2, 2)]
+    N = 172
+    W = synth.make_weights(1, projector=False, affine="random")
+    cfg = vt.config(layers=1)
+    bw = vt.block_weights({k: dev_bits(v, torch) for k, v in W.items()}, "l0.")
+    cu = torch.empty(3, dtype=torch.int32, device="cuda")
+    pos = torch.empty((N, 3), dtype=torch.int32, device="cuda")
+    vt.vt_build_metadata(grids, cu, pos)
+    ws = vt.workspace(vt.vt_block_backward_workspace_size(cfg, N, 2, 168))
+    R = torch.from_numpy(rng(54).standard_normal((N, 1280), dtype=np.float32)).cuda()
+    dR0 = torch.from_numpy(rng(55).standard_normal((N, 1280), dtype=np.float32)).cuda()
+    runs = []
+    for _ in range(2):
+        gd = {k[3:]: torch.empty(v.shape, dtype=torch.float32, device="cuda")
+              for k, v in W.items() if k.startswith("l0.")}
+        dR = dR0.clone()
+        vt.vt_block_backward(cfg, R, bw, cu, pos, 2, N, 168, dR, vt.block_grads(gd), ws)
+        torch.cuda.synchronize()
+        runs.append({"dR": dR.cpu().numpy(), **{k: t.cpu().numpy() for k, t in gd.items()}})
+    diff = {k: float(np.max(np.abs(runs[0][k] - runs[1][k]))) for k in runs[0]
+            if not np.array_equal(runs[0][k], runs[1][k])}
+    log(f"  differing outputs: {diff}")
+    assert not diff
+
+
+def test_block_backward_partial_gradients(vt):
+    """Gradients left NULL are not formed; the others are unchanged by it."""
+    grids = [(1, 16, 16)]
+    N = 256
+    W = synth.make_weights(1, projector=False, affine="random")
+    cfg = vt.config(layers=1)
+    bw = vt.block_weights({k: dev_bits(v, torch) for k, v in W.items()}, "l0.")
+    cu = torch.empty(2, dtype=torch.int32, device="cuda")
+    pos = torch.empty((N, 3), dtype=torch.int32, device="cuda")
+    vt.vt_build_metadata(grids, cu, pos)
+    ws = vt.workspace(vt.vt_block_backward_workspace_size(cfg, N, 1, N))
+    R = torch.from_numpy(rng(56).standard_normal((N, 1280), dtype=np.float32)).cuda()
+    dR0 = torch.from_numpy(rng(57).standard_normal((N, 1280), dtype=np.float32)).cuda()
+    full = {k[3:]: torch.empty(v.shape, dtype=torch.float32, device="cuda") for k, v in W.items()
+            if k.startswith("l0.")}
+    dR_full = dR0.clone()
+    vt.vt_block_backward(cfg, R, bw, cu, pos, 1, N, N, dR_full, vt.block_grads(full), ws)
+    some = {k: torch.full_like(full[k], 7.0) for k in ("w_o", "b_fc1", "ln1_g")}
+    dR_some = dR0.clone()
+    vt.vt_block_backward(cfg, R, bw, cu, pos, 1, N, N, dR_some, vt.block_grads(some), ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dR_full, dR_some)
+    for k, t in some.items():
+        assert torch.equal(t, full[k]), k

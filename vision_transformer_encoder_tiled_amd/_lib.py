@@ -230,9 +230,12 @@ def block_grads(g: dict) -> vt_block_grads:
     """vt_block_grads from a dict of fp32 device tensors keyed like the weights
     (missing entries -> NULL, not formed)."""
     b = vt_block_grads()
+    keep = []
     for name, _ in vt_block_grads._fields_:
         t = g.get(name)
         setattr(b, name, None if t is None else t.data_ptr())
+        keep.append(t)
+    b._tensors = keep
     return b
 
 
@@ -249,19 +252,26 @@ def vt_block_backward(cfg, resid_in, bw: vt_block_weights, cu_seqlens, pos_thw, 
 
 
 def block_weights(w: dict, prefix: str = "") -> vt_block_weights:
-    """vt_block_weights from a dict of device tensors (missing biases -> NULL)."""
+    """vt_block_weights from a dict of device tensors (missing biases -> NULL).
+    The struct keeps references to the tensors it points to."""
     b = vt_block_weights()
+    keep = []
     for name, _ in vt_block_weights._fields_:
         t = w.get(prefix + name)
         setattr(b, name, None if t is None else t.data_ptr())
+        keep.append(t)
+    b._tensors = keep
     return b
 
 
 def projector_weights(w: dict) -> vt_projector_weights:
     p = vt_projector_weights()
+    keep = []
     for name, _ in vt_projector_weights._fields_:
         t = w.get("p_" + name)
         setattr(p, name, None if t is None else t.data_ptr())
+        keep.append(t)
+    p._tensors = keep
     return p
 
 

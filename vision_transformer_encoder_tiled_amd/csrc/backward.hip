@@ -45,15 +45,16 @@ __device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float* v) {
 // One 64 x 64 tile of in [M, C] per block (256 threads; C a multiple of 4,
 // the last column tile partial): v = op(in) (op 1: GELU; op 2: in *
 // GELU'(aux)), rows M .. Mp-1 read as zero.  Writes, each when its pointer is
-// set: copy [M, C] = bf16(v); outT [C, Mp] = bf16(v)^T; colsum[c] += sum over
-// rows of v (fp32 atomics, the buffer zeroed before).
+// set: copy [M, C] = bf16(v); outT [C, Mp] = bf16(v)^T; colpart[y][c] = the
+// sum of bf16(v) over the tile's 64 rows (y = the row tile), summed in order
+// by colsum_reduce_kernel, so column sums are reproducible bit for bit.
 template <class TIN, int OP>
 __global__ void __launch_bounds__(256) transpose_kernel(const TIN* in,
                                                         const uint16_t* __restrict__ aux,
                                                         int32_t M, int32_t C, int32_t Mp,
                                                         uint16_t* copy,
                                                         uint16_t* __restrict__ outT,
-                                                        float* __restrict__ colsum) {
+                                                        float* __restrict__ colpart) {
   __shared__ float tile[64][65];
   const int c0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
   const int tid = threadIdx.x, cq = 4 * (tid & 15), rq = tid >> 4;
@@ -82,10 +83,10 @@ __global__ void __launch_bounds__(256) transpose_kernel(const TIN* in,
     for (int j = 0; j < 4; ++j) tile[row][cq + j] = v[j];
   }
   __syncthreads();
-  if (colsum && tid < 64 && c0 + tid < C) {
+  if (colpart && tid < 64 && c0 + tid < C) {
     float s = 0.f;
     for (int r = 0; r < 64; ++r) s += tile[r][tid];
-    atomicAdd(colsum + c0 + tid, s);
+    colpart[int64_t(blockIdx.y) * C + c0 + tid] = s;
   }
   if (outT && c0 + (tid >> 2) < C) {
     // thread -> (column tid / 4, rows 16 (tid % 4) .. +15): two 16-byte stores
@@ -102,13 +103,14 @@ __global__ void __launch_bounds__(256) transpose_kernel(const TIN* in,
 // LayerNorm backward, one wavefront per row (rows strided over the grid):
 //   xh = (x - mean) rstd,  dxh = dy * g,
 //   dx = dres + rstd (dxh - mean(dxh) - xh mean(dxh xh)),
-//   dg += dy xh,  db += dy  (per-lane partial sums, then fp32 atomics).
+//   and per block part[block] = (sum of dy xh, sum of dy) over its rows
+//   (per-lane sums, then the 4 wavefronts in order), reduced in block order
+//   by colsum_reduce_kernel.
 // dx may alias dres (each element is read before it is written, by one lane).
 template <int NV>
 __global__ void __launch_bounds__(256) ln_backward_kernel(
     const float* __restrict__ x, const uint16_t* __restrict__ g, const float* __restrict__ dy,
-    const float* dres, int32_t rows, float eps, float* dx, float* __restrict__ dg,
-    float* __restrict__ db) {
+    const float* dres, int32_t rows, float eps, float* dx, float* __restrict__ part) {
   constexpr int W = 256 * NV;
   __shared__ float red[2][W];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -180,10 +182,22 @@ __global__ void __launch_bounds__(256) ln_backward_kernel(
     }
     __syncthreads();
   }
+  float* pb = part + int64_t(blockIdx.x) * 2 * W;
   for (int c = threadIdx.x; c < W; c += 256) {
-    atomicAdd(dg + c, red[0][c]);
-    atomicAdd(db + c, red[1][c]);
+    pb[c] = red[0][c];
+    pb[W + c] = red[1][c];
   }
+}
+
+// out[c] = sum over p = 0 .. parts-1, in order, of part[p * ld + c]  (c < C).
+__global__ void __launch_bounds__(256) colsum_reduce_kernel(const float* __restrict__ part,
+                                                            int32_t parts, int32_t ld, int32_t C,
+                                                            float* __restrict__ out) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= C) return;
+  float s = 0.f;
+  for (int p = 0; p < parts; ++p) s += part[int64_t(p) * ld + c];
+  out[c] = s;
 }
 
 // out [C, R] = in [R, C]^T, fp32, 32 x 32 tiles through LDS (any R, C).
@@ -199,61 +213,66 @@ __global__ void __launch_bounds__(256) transpose_f32_kernel(const float* __restr
     if (c0 + i < C && r0 + tx < R) out[int64_t(c0 + i) * R + r0 + tx] = tile[tx][i];
 }
 
-__global__ void __launch_bounds__(256) zero_f32_kernel(float* __restrict__ p, int64_t n) {
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256)
-    p[i] = 0.f;
-}
-
 hipError_t launch_transpose(const void* in, bool in_f32, int op, const uint16_t* aux, int32_t M,
                             int32_t C, int32_t Mp, uint16_t* copy, uint16_t* outT, float* colsum,
-                            hipStream_t s) {
+                            float* colpart, hipStream_t s) {
+  if (colsum && !colpart) return hipErrorInvalidValue;
+  float* cp = colsum ? colpart : nullptr;
   if (C % 4 || Mp % 64 || Mp < M || (in_f32 && op != 0) || op < 0 || op > 2 || (op == 2 && !aux))
     return hipErrorInvalidValue;
   const dim3 grid((C + 63) / 64, Mp / 64);
   if (in_f32)
     hipLaunchKernelGGL((transpose_kernel<float, 0>), grid, dim3(256), 0, s,
-                       static_cast<const float*>(in), aux, M, C, Mp, copy, outT, colsum);
+                       static_cast<const float*>(in), aux, M, C, Mp, copy, outT, cp);
   else if (op == 0)
     hipLaunchKernelGGL((transpose_kernel<uint16_t, 0>), grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(in), aux, M, C, Mp, copy, outT, colsum);
+                       static_cast<const uint16_t*>(in), aux, M, C, Mp, copy, outT, cp);
   else if (op == 1)
     hipLaunchKernelGGL((transpose_kernel<uint16_t, 1>), grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(in), aux, M, C, Mp, copy, outT, colsum);
+                       static_cast<const uint16_t*>(in), aux, M, C, Mp, copy, outT, cp);
   else
     hipLaunchKernelGGL((transpose_kernel<uint16_t, 2>), grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(in), aux, M, C, Mp, copy, outT, colsum);
+                       static_cast<const uint16_t*>(in), aux, M, C, Mp, copy, outT, cp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !colsum) return e;
+  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((C + 255) / 256), dim3(256), 0, s, colpart, Mp / 64, C,
+                     C, colsum);
   return hipGetLastError();
+}
+
+int ln_backward_blocks(int32_t rows) {
+  return int(std::min<int64_t>((int64_t(rows) + 3) / 4, kLnBwdMaxBlocks));
 }
 
 hipError_t launch_ln_backward(const float* x, const uint16_t* g, const float* dy, const float* dres,
                               int32_t rows, int32_t width, float eps, float* dx, float* dg,
-                              float* db, hipStream_t s) {
-  const int blocks = int(std::min<int64_t>((int64_t(rows) + 3) / 4, 1024));
+                              float* db, float* part, hipStream_t s) {
+  const int blocks = ln_backward_blocks(rows);
   if (width % 256) return hipErrorInvalidValue;
   switch (width / 256) {
 #define VT_LNB_CASE(n)                                                                            \
   case n:                                                                                         \
     hipLaunchKernelGGL(ln_backward_kernel<n>, dim3(blocks), dim3(256), 0, s, x, g, dy, dres, rows, \
-                       eps, dx, dg, db);                                                          \
+                       eps, dx, part);                                                            \
     break;
     VT_LNB_CASE(1) VT_LNB_CASE(2) VT_LNB_CASE(3) VT_LNB_CASE(4) VT_LNB_CASE(5) VT_LNB_CASE(6)
     VT_LNB_CASE(7) VT_LNB_CASE(8)
 #undef VT_LNB_CASE
     default: return hipErrorInvalidValue;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // part is [blocks][2][width]: the gamma sums, then the beta sums, of each block
+  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((width + 255) / 256), dim3(256), 0, s, part, blocks,
+                     2 * width, width, dg);
+  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((width + 255) / 256), dim3(256), 0, s, part + width,
+                     blocks, 2 * width, width, db);
   return hipGetLastError();
 }
 
 hipError_t launch_transpose_f32(const float* in, int32_t R, int32_t C, float* out, hipStream_t s) {
   hipLaunchKernelGGL(transpose_f32_kernel, dim3((C + 31) / 32, (R + 31) / 32), dim3(256), 0, s, in, R,
                      C, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
-  const int blocks = int(std::min<int64_t>((n + 255) / 256, 1024));
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(zero_f32_kernel, dim3(blocks), dim3(256), 0, s, p, n);
   return hipGetLastError();
 }
 

@@ -674,6 +674,7 @@ struct BlockBwdBufs {
   float *R1, *dx;
   uint16_t *gT, *hT, *xT, *dqkvT, *wT;
   float* ln_scratch;  // gamma / beta gradients the caller did not ask for
+  float* part;        // per-tile / per-block partial sums of the bias and LN gradients
   void* gemm_ws;
 };
 
@@ -706,6 +707,7 @@ void carve_block_bwd(Carver& c, const Dims& D, int32_t n_pos, BlockBwdBufs* b) {
   b->dqkvT = c.take<uint16_t>(3 * d * Np);
   b->wT = c.take<uint16_t>(std::max(mlp * d, 3 * d * d));
   b->ln_scratch = c.take<float>(4 * d);
+  b->part = c.take<float>(size_t(Np / 64) * std::max(mlp, 3 * d) + size_t(vt::kLnBwdMaxBlocks) * 2 * d);
   b->gemm_ws = c.take<char>(D.ws_upper ? kPartialsBound : block_bwd_gemm_ws(D.N, D.d, D.mlp));
 }
 
@@ -727,11 +729,6 @@ vt_status run_block_backward(const vt_config* cfg, const float* R, const vt_bloc
   float* ln1b = g->ln1_b ? g->ln1_b : B.ln_scratch + d;
   float* ln2g = g->ln2_g ? g->ln2_g : B.ln_scratch + 2 * d;
   float* ln2b = g->ln2_b ? g->ln2_b : B.ln_scratch + 3 * d;
-  // Gradients formed by atomic accumulation start from zero.
-  float* zero_list[] = {ln1g, ln1b, ln2g, ln2b, g->b_qkv, g->b_o, g->b_fc1, g->b_fc2};
-  const int zero_len[] = {d, d, d, d, 3 * d, d, mlp, d};
-  for (int i = 0; i < 8; ++i)
-    if (zero_list[i]) VT_TRY_HIP(vt::launch_zero_f32(zero_list[i], zero_len[i], s));
 
   // ---- the block's forward, keeping what the backward reads
   const AttnBwdBufs& at = B.at;
@@ -751,41 +748,42 @@ vt_status run_block_backward(const vt_config* cfg, const float* R, const vt_bloc
   VT_TRY_HIP(vt::launch_gemm(B.x2, M, d, w->w_fc1, mlp, w->b_fc1, vt::kEpiBf16, B.h, ws, s));
 
   // ---- MLP: dR holds dL/d(output) = dR2
-  VT_TRY_HIP(vt::launch_transpose(dR, true, 0, nullptr, M, d, Np, B.gb, B.gT, g->b_fc2, s));
-  VT_TRY_HIP(vt::launch_transpose(w->w_fc2, false, 0, nullptr, d, mlp, d, nullptr, B.wT, nullptr, s));
+  VT_TRY_HIP(vt::launch_transpose(dR, true, 0, nullptr, M, d, Np, B.gb, B.gT, g->b_fc2, B.part, s));
+  VT_TRY_HIP(vt::launch_transpose(w->w_fc2, false, 0, nullptr, d, mlp, d, nullptr, B.wT, nullptr, nullptr, s));
   VT_TRY_HIP(vt::launch_gemm(B.gb, M, d, B.wT, mlp, nullptr, vt::kEpiBf16, B.dh, ws, s));  // du
   if (g->w_fc2) {  // dW_fc2 = dR2^T GELU(h)
-    VT_TRY_HIP(vt::launch_transpose(B.h, false, 1, nullptr, M, mlp, Np, nullptr, B.hT, nullptr, s));
+    VT_TRY_HIP(vt::launch_transpose(B.h, false, 1, nullptr, M, mlp, Np, nullptr, B.hT, nullptr, nullptr, s));
     VT_TRY_HIP(vt::launch_gemm(B.gT, d, Np, B.hT, mlp, nullptr, vt::kEpiF32, g->w_fc2, ws, s));
   }
   // dh = du * GELU'(h), in place, with its transpose and column sums
-  VT_TRY_HIP(vt::launch_transpose(B.dh, false, 2, B.h, M, mlp, Np, B.dh, B.hT, g->b_fc1, s));
+  VT_TRY_HIP(vt::launch_transpose(B.dh, false, 2, B.h, M, mlp, Np, B.dh, B.hT, g->b_fc1, B.part, s));
   if (g->w_fc1) {  // dW_fc1 = dh^T x2
-    VT_TRY_HIP(vt::launch_transpose(B.x2, false, 0, nullptr, M, d, Np, nullptr, B.xT, nullptr, s));
+    VT_TRY_HIP(vt::launch_transpose(B.x2, false, 0, nullptr, M, d, Np, nullptr, B.xT, nullptr, nullptr, s));
     VT_TRY_HIP(vt::launch_gemm(B.hT, mlp, Np, B.xT, d, nullptr, vt::kEpiF32, g->w_fc1, ws, s));
   }
-  VT_TRY_HIP(vt::launch_transpose(w->w_fc1, false, 0, nullptr, mlp, d, mlp, nullptr, B.wT, nullptr, s));
+  VT_TRY_HIP(vt::launch_transpose(w->w_fc1, false, 0, nullptr, mlp, d, mlp, nullptr, B.wT, nullptr, nullptr, s));
   VT_TRY_HIP(vt::launch_gemm(B.dh, M, mlp, B.wT, d, nullptr, vt::kEpiF32, B.dx, ws, s));  // dx2
-  VT_TRY_HIP(vt::launch_ln_backward(B.R1, w->ln2_g, B.dx, dR, M, d, eps, dR, ln2g, ln2b, s));
+  VT_TRY_HIP(vt::launch_ln_backward(B.R1, w->ln2_g, B.dx, dR, M, d, eps, dR, ln2g, ln2b, B.part, s));
 
   // ---- attention: dR now holds dR1
-  VT_TRY_HIP(vt::launch_transpose(dR, true, 0, nullptr, M, d, Np, B.gb, B.gT, g->b_o, s));
+  VT_TRY_HIP(vt::launch_transpose(dR, true, 0, nullptr, M, d, Np, B.gb, B.gT, g->b_o, B.part, s));
   if (g->w_o) {  // dW_o = dR1^T a
-    VT_TRY_HIP(vt::launch_transpose(B.a, false, 0, nullptr, M, d, Np, nullptr, B.xT, nullptr, s));
+    VT_TRY_HIP(vt::launch_transpose(B.a, false, 0, nullptr, M, d, Np, nullptr, B.xT, nullptr, nullptr, s));
     VT_TRY_HIP(vt::launch_gemm(B.gT, d, Np, B.xT, d, nullptr, vt::kEpiF32, g->w_o, ws, s));
   }
-  VT_TRY_HIP(vt::launch_transpose(w->w_o, false, 0, nullptr, d, d, d, nullptr, B.wT, nullptr, s));
+  VT_TRY_HIP(vt::launch_transpose(w->w_o, false, 0, nullptr, d, d, d, nullptr, B.wT, nullptr, nullptr, s));
   VT_TRY_HIP(vt::launch_gemm(B.gb, M, d, B.wT, d, nullptr, vt::kEpiBf16, B.da, ws, s));
   if ((st = run_attn_bwd(cfg, B.qkv, B.da, pos, n_img, N, n_pos, axis_code, at, B.dqkv, false, s)) != VT_OK)
     return st;
-  VT_TRY_HIP(vt::launch_transpose(B.dqkv, false, 0, nullptr, M, 3 * d, Np, nullptr, B.dqkvT, g->b_qkv, s));
+  VT_TRY_HIP(vt::launch_transpose(B.dqkv, false, 0, nullptr, M, 3 * d, Np, nullptr, B.dqkvT, g->b_qkv,
+                                  B.part, s));
   if (g->w_qkv) {  // dW_qkv = dqkv^T x1
-    VT_TRY_HIP(vt::launch_transpose(B.x1, false, 0, nullptr, M, d, Np, nullptr, B.xT, nullptr, s));
+    VT_TRY_HIP(vt::launch_transpose(B.x1, false, 0, nullptr, M, d, Np, nullptr, B.xT, nullptr, nullptr, s));
     VT_TRY_HIP(vt::launch_gemm(B.dqkvT, 3 * d, Np, B.xT, d, nullptr, vt::kEpiF32, g->w_qkv, ws, s));
   }
-  VT_TRY_HIP(vt::launch_transpose(w->w_qkv, false, 0, nullptr, 3 * d, d, 3 * d, nullptr, B.wT, nullptr, s));
+  VT_TRY_HIP(vt::launch_transpose(w->w_qkv, false, 0, nullptr, 3 * d, d, 3 * d, nullptr, B.wT, nullptr, nullptr, s));
   VT_TRY_HIP(vt::launch_gemm(B.dqkv, M, 3 * d, B.wT, d, nullptr, vt::kEpiF32, B.dx, ws, s));  // dx1
-  VT_TRY_HIP(vt::launch_ln_backward(R, w->ln1_g, B.dx, dR, M, d, eps, dR, ln1g, ln1b, s));
+  VT_TRY_HIP(vt::launch_ln_backward(R, w->ln1_g, B.dx, dR, M, d, eps, dR, ln1g, ln1b, B.part, s));
   return VT_OK;
 }
 
@@ -1039,12 +1037,11 @@ VT_API vt_status vt_tower_backward(const vt_config* cfg, const uint16_t* pixels,
     if (st != VT_OK) return st;
   }
   // patch embed: dW = dR0^T X (formed as X^T dR0, then transposed), db = column sums of dR0
-  if (grads->b_patch) VT_TRY_HIP(vt::launch_zero_f32(grads->b_patch, d, s));
   if (grads->w_patch || grads->b_patch)
     VT_TRY_HIP(vt::launch_transpose(t.dR, true, 0, nullptr, M, d, Np, nullptr,
-                                    grads->w_patch ? t.bb.gT : nullptr, grads->b_patch, s));
+                                    grads->w_patch ? t.bb.gT : nullptr, grads->b_patch, t.bb.part, s));
   if (grads->w_patch) {
-    VT_TRY_HIP(vt::launch_transpose(t.X, false, 0, nullptr, M, 1176, Np, nullptr, t.XT, nullptr, s));
+    VT_TRY_HIP(vt::launch_transpose(t.X, false, 0, nullptr, M, 1176, Np, nullptr, t.XT, nullptr, nullptr, s));
     VT_TRY_HIP(vt::launch_gemm(t.XT, 1176, Np, t.bb.gT, d, nullptr, vt::kEpiF32, t.dwT, t.patch_ws, s));
     VT_TRY_HIP(vt::launch_transpose_f32(t.dwT, 1176, d, grads->w_patch, s));
   }

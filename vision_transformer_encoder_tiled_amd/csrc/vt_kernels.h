@@ -100,18 +100,20 @@ hipError_t launch_attention(const uint16_t* qkv, const int32_t* pos_thw, const i
 // 64 x 64-tiled transpose of in [M, C] (fp32 or bf16; C a multiple of 4, Mp
 // a multiple of 64, Mp >= M) with v = op(in): op 0 identity, 1 GELU(tanh), 2 in * GELU'(aux)
 // (aux bf16 [M, C]; fp32 input only with op 0).  Optional outputs: copy
-// [M, C] bf16(v), outT [C, Mp] bf16(v)^T (rows M.. zero), colsum [C] += the
-// column sums of bf16(v) (fp32 atomics: zero it first).
+// [M, C] bf16(v), outT [C, Mp] bf16(v)^T (rows M.. zero), colsum [C] = the
+// column sums of bf16(v), formed per 64-row tile in colpart [Mp/64][C] and
+// summed in tile order (reproducible bit for bit).
 hipError_t launch_transpose(const void* in, bool in_f32, int op, const uint16_t* aux, int32_t M,
                             int32_t C, int32_t Mp, uint16_t* copy, uint16_t* outT, float* colsum,
-                            hipStream_t s);
-// dx = dres + LayerNorm'(x; g)^T dy per row (width = 256 k, k <= 8); dg, db
-// += the gamma / beta gradients (fp32 atomics: zero them first).  dx may
-// alias dres.
+                            float* colpart, hipStream_t s);
+// dx = dres + LayerNorm'(x; g)^T dy per row (width = 256 k, k <= 8); dg, db =
+// the gamma / beta gradients, summed per block into part
+// [ln_backward_blocks(rows)][2][width] and then in block order.  dx may alias dres.
+constexpr int kLnBwdMaxBlocks = 256;
+int ln_backward_blocks(int32_t rows);
 hipError_t launch_ln_backward(const float* x, const uint16_t* g, const float* dy, const float* dres,
                               int32_t rows, int32_t width, float eps, float* dx, float* dg,
-                              float* db, hipStream_t s);
-hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
+                              float* db, float* part, hipStream_t s);
 // out [C, R] = in [R, C]^T, fp32.
 hipError_t launch_transpose_f32(const float* in, int32_t R, int32_t C, float* out, hipStream_t s);
 
