@@ -10,7 +10,7 @@
 // streams that image's keys in tiles of 64 through LDS with an online
 // softmax, so memory is O(tokens).
 //
-// Two kernels:
+// Three kernels:
 //
 // attn_pack_kernel (the Q/K/V load stage, once per token and head):
 //   rotate q and k with 3D RoPE (rotate-half pairs (j, j+40), angle
@@ -29,10 +29,14 @@
 //   RoPE and conversion work out of the inner loop, which is VALU-bound at
 //   head_dim 80.
 //
-// attention_kernel: 4 wavefronts, each with 32 queries.  KG = 1: one
-//   workgroup = 128 queries, every wavefront walks all key tiles.  KG = 2
-//   (small images, so that every CU gets a workgroup): 64 queries, two
-//   groups of 2 wavefronts take alternate key tiles and merge at the end.
+// attention_kernel (calls with few query tiles): 4 wavefronts, each with 32
+//   queries, in two key groups (KG = 2): 64 queries per workgroup, two
+//   groups of 2 wavefronts take alternate key tiles and merge at the end, so
+//   that small images still give every CU a workgroup.  (KG = 1, one group
+//   of 128 queries, is the same code with the merge left out.)
+// attention_lean_kernel (calls with many query tiles): the same arithmetic
+//   per tile without the score pipelining described below, in fewer
+//   registers, so that 3 or 4 wavefronts share each SIMD (see there).
 //   S^T = K Q^T   v_mfma_f32_32x32x16_f16, 2 key blocks x 5 dim slices of
 //                 16 (head_dim 80 = 5 x 16 exactly).  Each lane holds one
 //                 query and 16 keys of each 32-key block.
@@ -453,6 +457,153 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(
   }
 }
 
+// ---------------------------------------------------------------- lean attention
+// The kernel for calls with many query tiles: the same per-tile arithmetic
+// as attention_kernel with one key group (S^T onto -m, lazy rescale, P from
+// the score registers, the ones row for l), but register-lean so that more
+// wavefronts share each SIMD and hide one another's latencies: one set of
+// scores (no one-tile-ahead pipelining), K and V^T fragments read as they are
+// consumed, and a 2-stage ring (50 KB of LDS).  142 VGPRs with 4 wavefronts
+// (128 queries, three workgroups per CU) or 128 with 8 wavefronts (256
+// queries sharing one K/V stream, two workgroups per CU: four wavefronts per
+// SIMD).  WPE is the wavefronts per SIMD the register budget is set for.
+template <int NW, int NST, int WPE>
+__global__ void __launch_bounds__(64 * NW, WPE) attention_lean_kernel(
+    const uint16_t* __restrict__ qpk, const uint16_t* __restrict__ kv,
+    const int4* __restrict__ qdesc, int32_t heads, void* __restrict__ out, int32_t out_f32,
+    float* __restrict__ lse) {
+  constexpr int COPIES = IMG_BYTES / (1024 * NW);
+  constexpr int WQ = 32 * NW;
+  extern __shared__ __align__(16) char lds[];
+  const int head = blockIdx.x % heads;
+  const int4 desc = qdesc[blockIdx.x / heads];
+  if (desc.x < 0) return;
+  const int q0 = desc.x, kbeg = desc.y, kend = desc.z;
+  const int qend = min(q0 + WQ, kend);
+  const int ntiles = (kend - kbeg + BKV - 1) / BKV;
+  const char* src = reinterpret_cast<const char*>(kv) + (int64_t(desc.w) * heads + head) * IMG_BYTES;
+  const int64_t tile_stride = int64_t(heads) * IMG_BYTES;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hf = lane >> 5, ln = lane & 31;
+  const uint32_t lds_wave = lds_offset(lds) + 1024 * wave;
+  auto issue = [&](int t) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_wave + (t % NST) * STAGE_BYTES);
+    const char* g = src + t * tile_stride + 1024 * wave + 16 * lane;
+#pragma unroll
+    for (int c = 0; c < COPIES; ++c) dma16(g + NW * 1024 * c, base + NW * 1024 * c);
+  };
+  const int qrow = q0 + wave * 32 + ln;
+  const bool qvalid = qrow < qend;
+  const int qr = qvalid ? qrow : qend - 1;
+  f16x8_t qfrag[5];
+  {
+    const uint4* q = reinterpret_cast<const uint4*>(qpk + (int64_t(qr) * heads + head) * HD);
+#pragma unroll
+    for (int s = 0; s < 5; ++s) qfrag[s] = __builtin_bit_cast(f16x8_t, q[2 * s + hf]);
+  }
+  const int koff = ln * KROW * 2 + 16 * hf;
+  const int voff = K_BYTES + ln * VROW * 2 + 16 * hf;
+  f32x16_t acc[3];
+#pragma unroll
+  for (int d = 0; d < 3; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[d][e] = 0.f;
+  f32x16_t negm;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) negm[e] = 0.f;
+  float m_use = 0.f;
+#pragma unroll
+  for (int r = 0; r < NST - 1; ++r)
+    if (r < ntiles) issue(r);
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vmcnt<0>();
+    wait_lds_reads();
+    wg_barrier();
+    if (t + NST - 1 < ntiles) issue(t + NST - 1);
+    const char* st = lds + (t % NST) * STAGE_BYTES;
+    f32x16_t sc[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+      sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+          *reinterpret_cast<const f16x8_t*>(st + koff + b * 32 * KROW * 2), qfrag[0], negm, 0, 0, 0);
+#pragma unroll
+    for (int sl = 1; sl < 5; ++sl)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            *reinterpret_cast<const f16x8_t*>(st + koff + b * 32 * KROW * 2 + 32 * sl), qfrag[sl], sc[b], 0,
+            0, 0);
+    const int kt = kbeg + t * BKV;
+    if (kt + BKV > kend) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (kt + 32 * b + 8 * (e >> 2) + 4 * hf + (e & 3) >= kend) sc[b][e] = -INFINITY;
+    }
+    float mx = fmaxf(sc[0][0], sc[0][1]);
+#pragma unroll
+    for (int e = 2; e < 16; ++e) mx = fmaxf(mx, sc[0][e]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[1][e]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    if (t == 0 || __any(mx > kLazy)) {
+      const float delta = t == 0 ? mx : fmaxf(mx, 0.f);
+      m_use += delta;
+      if (t > 0) {
+        const float alpha = __builtin_amdgcn_exp2f(-delta);
+#pragma unroll
+        for (int d = 0; d < 3; ++d)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[d][e] *= alpha;
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[b][e] -= delta;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) negm[e] = -m_use;
+    }
+    const char* vst = st + voff;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      f16x8_t pf[2];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) pf[e >> 3][e & 7] = (_Float16)__builtin_amdgcn_exp2f(sc[b][e]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int d = 0; d < 3; ++d)
+          acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              *reinterpret_cast<const f16x8_t*>(vst + 32 * d * VROW * 2 + 32 * (2 * b + h)), pf[h], acc[d], 0,
+              0, 0);
+    }
+  }
+  const float l_half0 = __shfl(acc[2][8], ln, 64);
+  const float inv = 1.0f / l_half0;
+  if (!qvalid) return;
+  if (lse && hf == 0) lse[int64_t(qrow) * heads + head] = m_use + log2f(l_half0);
+  const int64_t orow = int64_t(qrow) * heads * HD + head * HD;
+#pragma unroll
+  for (int d = 0; d < 3; ++d) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dim = 32 * d + 8 * g + 4 * hf;
+      if (dim >= HD) continue;
+      const float o0 = acc[d][4 * g] * inv, o1 = acc[d][4 * g + 1] * inv;
+      const float o2 = acc[d][4 * g + 2] * inv, o3 = acc[d][4 * g + 3] * inv;
+      if (out_f32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + orow + dim) = make_float4(o0, o1, o2, o3);
+      } else {
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + orow + dim) =
+            make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+      }
+    }
+  }
+}
 template <int NW, int KG, int NST>
 static hipError_t launch_attention_kernel(const uint16_t* qpk, const uint16_t* kv,
                                           const int4* qdesc, int32_t max_qtiles, int32_t heads,
@@ -468,19 +619,37 @@ static hipError_t launch_attention_kernel(const uint16_t* qpk, const uint16_t* k
   return hipGetLastError();
 }
 
+template <int NW, int WPE>
+static hipError_t launch_lean(const uint16_t* qpk, const uint16_t* kv, const int4* qdesc,
+                              int32_t max_qtiles, int32_t heads, void* out, bool out_f32, float* lse,
+                              hipStream_t s) {
+  const size_t lds = size_t(2) * STAGE_BYTES;
+  auto kern = attention_lean_kernel<NW, 2, WPE>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (attr != hipSuccess) return attr;
+  const int64_t blocks = int64_t(max_qtiles) * heads;
+  hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(64 * NW), lds, s, qpk, kv, qdesc, heads, out,
+                     out_f32 ? 1 : 0, lse);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(const uint16_t* qkv, const int32_t* pos_thw, const int4* qdesc,
                             const int2* kdesc, int32_t max_qtiles, int32_t max_ktiles,
                             int32_t heads, int32_t n_pos, int32_t axis_code, const float2* rope_cs,
-                            float q_scale_log2, int32_t key_groups, uint16_t* qpk, uint16_t* kv,
+                            float q_scale_log2, int32_t variant, uint16_t* qpk, uint16_t* kv,
                             void* out, bool out_f32, float* lse, hipStream_t s) {
   hipLaunchKernelGGL(attn_pack_kernel, dim3(max_ktiles, heads), dim3(320), 0, s, qkv, pos_thw,
                      kdesc, heads, n_pos, rope_cs, axis_code, q_scale_log2, qpk, kv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (key_groups == 2)
-    return launch_attention_kernel<4, 2, 3>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, lse, s);
-  return launch_attention_kernel<kAttnWaves1, 1, kAttnStages1>(qpk, kv, qdesc, max_qtiles, heads, out,
-                                                                out_f32, lse, s);
+  switch (variant) {
+    case kAttnSmall:
+      return launch_attention_kernel<4, 2, 3>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, lse, s);
+    case kAttnLean4: return launch_lean<4, 3>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, lse, s);
+    case kAttnLean8: return launch_lean<8, 4>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, lse, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace vt

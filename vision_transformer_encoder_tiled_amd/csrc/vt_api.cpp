@@ -166,7 +166,7 @@ void carve_attention(Carver& c, const Dims& D, int32_t n_pos, BlockBufs* b) {
   b->order = c.take<int32_t>(D.n_img);
   b->tile_start = c.take<int32_t>(D.n_img + 1);
   b->ktile_start = c.take<int32_t>(D.n_img + 1);
-  b->qdesc = c.take<int4>(max_q_tiles(D.N, D.n_img, vt::attn_q_tile(2)));
+  b->qdesc = c.take<int4>(max_q_tiles(D.N, D.n_img, vt::attn_q_tile(vt::kAttnSmall)));
   b->kdesc = c.take<int2>(max_k_tiles(D.N, D.n_img));
   b->qpk = c.take<uint16_t>(size_t(D.N) * D.d);
   b->kv = reinterpret_cast<uint16_t*>(
@@ -273,18 +273,21 @@ vt_status launch_meta(const vt_grid_thw* grid, int32_t n_img, int64_t total, int
   return VT_OK;
 }
 
-// Key groups of the attention kernel: two (64-query workgroups) when the
-// 128-query tiles would not give every CU a workgroup, else one.  A function
-// of the call's sizes only, so the schedule and the launch agree.
-int32_t attn_key_groups(int64_t N, int32_t n_img, int32_t heads) {
-  const int64_t tiles128 = (N + 127) / 128 + n_img;
-  return tiles128 * heads <= 256 ? 2 : 1;
+// Attention kernel variant (vt_kernels.h): 64-query workgroups with two key
+// groups when 128-query tiles would not give every CU a workgroup; 256-query
+// workgroups when those still fill the chip twice over at two per CU; else
+// 128-query workgroups.  A function of the call's sizes only, so the
+// schedule and the launch agree.
+int32_t attn_variant(int64_t N, int32_t n_img, int32_t heads) {
+  const int64_t tiles128 = (N + 127) / 128 + n_img, tiles256 = (N + 255) / 256 + n_img;
+  if (tiles128 * heads <= 256) return vt::kAttnSmall;
+  return tiles256 * heads >= 1024 ? vt::kAttnLean8 : vt::kAttnLean4;
 }
 
 // The per-call attention prologue: LPT schedule and RoPE cos/sin table.
 vt_status attn_prologue(const vt_config* cfg, const int32_t* cu, int32_t n_img, int64_t N,
                         int32_t n_pos, const BlockBufs& b, int32_t* axis_code, hipStream_t s) {
-  const int q_tile = vt::attn_q_tile(attn_key_groups(N, n_img, cfg->heads));
+  const int q_tile = vt::attn_q_tile(attn_variant(N, n_img, cfg->heads));
   VT_TRY_HIP(vt::launch_attn_schedule(cu, n_img, q_tile, vt::kAttnKTile,
                                       max_q_tiles(N, n_img, q_tile), max_k_tiles(N, n_img),
                                       b.order, b.tile_start, b.ktile_start, b.qdesc, b.kdesc, s));
@@ -301,10 +304,10 @@ vt_status run_attention(const vt_config* cfg, const uint16_t* qkv, const int32_t
                         const int32_t* pos, int32_t n_img, int64_t N, int32_t n_pos,
                         int32_t axis_code, const BlockBufs& b, void* out, bool f32,
                         hipStream_t s, float* lse = nullptr) {
-  const int32_t kg = attn_key_groups(N, n_img, cfg->heads);
-  VT_TRY_HIP(vt::launch_attention(qkv, pos, b.qdesc, b.kdesc, max_q_tiles(N, n_img, vt::attn_q_tile(kg)),
+  const int32_t var = attn_variant(N, n_img, cfg->heads);
+  VT_TRY_HIP(vt::launch_attention(qkv, pos, b.qdesc, b.kdesc, max_q_tiles(N, n_img, vt::attn_q_tile(var)),
                                   max_k_tiles(N, n_img), cfg->heads, n_pos, axis_code, b.rope,
-                                  q_scale_log2(cfg), kg, b.qpk, b.kv, out, f32, lse, s));
+                                  q_scale_log2(cfg), var, b.qpk, b.kv, out, f32, lse, s));
   return VT_OK;
 }
 

@@ -78,22 +78,26 @@ hipError_t launch_gemm_partials(const uint16_t* A, int M, int K, const uint16_t*
 // ---- attention (attention.hip)
 constexpr int kAttnKTile = 64;         // keys per tile
 constexpr int kAttnTileBytes = 24576;  // one (head, key tile) image: K [64][88] + V^T [81][72] fp16 + pad
-// Wavefronts (of 32 queries) per workgroup and LDS stages with one key group
-// (8 wavefronts, or 4 stages with 8 wavefronts, measured no faster).
-constexpr int kAttnWaves1 = 4;
-constexpr int kAttnStages1 = 3;
-// Queries per workgroup: 32 * kAttnWaves1 with one key group, 64 with two
-// (the kernel splits each image's key tiles between two groups of 2 wavefronts).
-inline int attn_q_tile(int key_groups) { return key_groups == 2 ? 64 : 32 * kAttnWaves1; }
+// Attention kernel variants, chosen by the size of the call:
+//   kAttnSmall  attention_kernel, two key groups of 2 wavefronts, 64 queries
+//               per workgroup (few query tiles: every CU gets work);
+//   kAttnLean4  attention_lean_kernel, 4 wavefronts = 128 queries, three
+//               workgroups per CU;
+//   kAttnLean8  attention_lean_kernel, 8 wavefronts = 256 queries, two
+//               workgroups per CU (many query tiles).
+enum AttnVariant : int { kAttnSmall = 0, kAttnLean4 = 1, kAttnLean8 = 2 };
+inline int attn_q_tile(int variant) {
+  return variant == kAttnSmall ? 64 : variant == kAttnLean4 ? 128 : 256;
+}
 // qpk: [N, heads, 80] fp16 rotated+scaled Q; kv: max_ktiles x heads tile
 // images.  qdesc / kdesc come from launch_attn_schedule with
-// attn_q_tile(key_groups) and the same max_qtiles / max_ktiles.  lse, when
+// attn_q_tile(variant) and the same max_qtiles / max_ktiles.  lse, when
 // not null, receives [N, heads] fp32: the log2-domain log-sum-exp of each
 // query's scaled scores (max + log2 of the row sum).
 hipError_t launch_attention(const uint16_t* qkv, const int32_t* pos_thw, const int4* qdesc,
                             const int2* kdesc, int32_t max_qtiles, int32_t max_ktiles,
                             int32_t heads, int32_t n_pos, int32_t axis_code, const float2* rope_cs,
-                            float q_scale_log2, int32_t key_groups, uint16_t* qpk, uint16_t* kv,
+                            float q_scale_log2, int32_t variant, uint16_t* qpk, uint16_t* kv,
                             void* out, bool out_f32, float* lse, hipStream_t s);
 
 // ---- block backward helpers (backward.hip)
