@@ -189,15 +189,36 @@ __global__ void __launch_bounds__(256) ln_backward_kernel(
   }
 }
 
-// out[c] = sum over p = 0 .. parts-1, in order, of part[p * ld + c]  (c < C).
+// sum over p < parts of part[p * ld + c]  (c < C) in a fixed order, to
+// out[c] for c < split and out2[c - split] beyond: thread group g (of 4) sums
+// parts g, g + 4, g + 8, ... in turn, eight loads in flight, and the four
+// group sums are added in group order.
 __global__ void __launch_bounds__(256) colsum_reduce_kernel(const float* __restrict__ part,
                                                             int32_t parts, int32_t ld, int32_t C,
-                                                            float* __restrict__ out) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= C) return;
+                                                            float* __restrict__ out, int32_t split,
+                                                            float* __restrict__ out2) {
+  __shared__ float gs[4][64];
+  const int cl = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + cl;
   float s = 0.f;
-  for (int p = 0; p < parts; ++p) s += part[int64_t(p) * ld + c];
-  out[c] = s;
+  if (c < C) {
+    int p = g;
+    for (; p + 28 < parts; p += 32) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = part[int64_t(p + 4 * j) * ld + c];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s += v[j];
+    }
+    for (; p < parts; p += 4) s += part[int64_t(p) * ld + c];
+  }
+  gs[g][cl] = s;
+  __syncthreads();
+  if (g == 0 && c < C) {
+    const float v = ((gs[0][cl] + gs[1][cl]) + gs[2][cl]) + gs[3][cl];
+    if (c < split) out[c] = v;
+    else out2[c - split] = v;
+  }
 }
 
 // out [C, R] = in [R, C]^T, fp32, 32 x 32 tiles through LDS (any R, C).
@@ -235,8 +256,8 @@ hipError_t launch_transpose(const void* in, bool in_f32, int op, const uint16_t*
                        static_cast<const uint16_t*>(in), aux, M, C, Mp, copy, outT, cp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !colsum) return e;
-  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((C + 255) / 256), dim3(256), 0, s, colpart, Mp / 64, C,
-                     C, colsum);
+  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((C + 63) / 64), dim3(256), 0, s, colpart, Mp / 64, C, C,
+                     colsum, C, nullptr);
   return hipGetLastError();
 }
 
@@ -263,10 +284,8 @@ hipError_t launch_ln_backward(const float* x, const uint16_t* g, const float* dy
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // part is [blocks][2][width]: the gamma sums, then the beta sums, of each block
-  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((width + 255) / 256), dim3(256), 0, s, part, blocks,
-                     2 * width, width, dg);
-  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((width + 255) / 256), dim3(256), 0, s, part + width,
-                     blocks, 2 * width, width, db);
+  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((2 * width + 63) / 64), dim3(256), 0, s, part, blocks,
+                     2 * width, 2 * width, dg, width, db);
   return hipGetLastError();
 }
 
