@@ -61,7 +61,9 @@ __global__ void __launch_bounds__(256) layer_norm_kernel(const float* __restrict
 // Split-K residual update fused with the next LayerNorm, one wavefront per
 // row: R += (sum over z in order of part[z]) + bias, exactly the arithmetic
 // of the split-K reduction with the residual epilogue; then out = LN(R).
-template <int NV>
+// SPL > 0: exactly SPL partials, all loads of a row issued at once (one
+// memory round trip); SPL = 0: any count, in groups of 4.
+template <int NV, int SPL>
 __global__ void __launch_bounds__(256) resid_ln_kernel(const float* __restrict__ part,
                                                        int32_t splits, int32_t rows,
                                                        const uint16_t* __restrict__ bias,
@@ -82,10 +84,23 @@ __global__ void __launch_bounds__(256) resid_ln_kernel(const float* __restrict__
     v[i] = p0[lane + 64 * i];
     r[i] = rr[lane + 64 * i];
   }
+  if constexpr (SPL > 0) {
+    float4 q[SPL - 1][NV];
+#pragma unroll
+    for (int j = 0; j < SPL - 1; ++j)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) q[j][i] = p0[(j + 1) * plane4 + lane + 64 * i];
+#pragma unroll
+    for (int j = 0; j < SPL - 1; ++j)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        v[i].x += q[j][i].x; v[i].y += q[j][i].y; v[i].z += q[j][i].z; v[i].w += q[j][i].w;
+      }
+  }
   // Partials 1.. in groups of 4: the loads of a group are issued together
   // (indices clamped to the last split, so they stay in bounds), then the
   // valid ones are added in split order.
-  for (int z0 = 1; z0 < splits; z0 += 4) {
+  for (int z0 = 1; SPL == 0 && z0 < splits; z0 += 4) {
     float4 q[4][NV];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -136,11 +151,20 @@ hipError_t launch_resid_ln(const float* part, int32_t splits, int32_t rows, int3
                            const uint16_t* bias, float* R, const uint16_t* g, const uint16_t* b,
                            float eps, uint16_t* out, hipStream_t s) {
   const dim3 grid((rows + 3) / 4), block(256);
+  if (width == 1280 && splits >= 2 && splits <= 4) {  // the tower's width: one round trip per row
+    if (splits == 2)
+      hipLaunchKernelGGL((resid_ln_kernel<5, 2>), grid, block, 0, s, part, splits, rows, bias, R, g, b, eps, out);
+    else if (splits == 3)
+      hipLaunchKernelGGL((resid_ln_kernel<5, 3>), grid, block, 0, s, part, splits, rows, bias, R, g, b, eps, out);
+    else
+      hipLaunchKernelGGL((resid_ln_kernel<5, 4>), grid, block, 0, s, part, splits, rows, bias, R, g, b, eps, out);
+    return hipGetLastError();
+  }
   switch (width / 256) {
-#define VT_RLN_CASE(n)                                                                           \
-  case n:                                                                                        \
-    hipLaunchKernelGGL(resid_ln_kernel<n>, grid, block, 0, s, part, splits, rows, bias, R, g, b, \
-                       eps, out);                                                                \
+#define VT_RLN_CASE(n)                                                                              \
+  case n:                                                                                           \
+    hipLaunchKernelGGL((resid_ln_kernel<n, 0>), grid, block, 0, s, part, splits, rows, bias, R, g, b, \
+                       eps, out);                                                                   \
     break;
     VT_RLN_CASE(1) VT_RLN_CASE(2) VT_RLN_CASE(3) VT_RLN_CASE(4) VT_RLN_CASE(5) VT_RLN_CASE(6)
     VT_RLN_CASE(7) VT_RLN_CASE(8) VT_RLN_CASE(9) VT_RLN_CASE(10) VT_RLN_CASE(11) VT_RLN_CASE(12)
