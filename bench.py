@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--more", default="tower_clip16",
                     help="comma-separated further workloads, throughput only ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward-pass lines (forward-only kernel profiles)")
     ap.add_argument("--kernel-iters", type=int, default=20)
     ap.add_argument("--kernel", choices=["fc1", "attention", "attention_bwd", "block_bwd", "copy"],
                     default=None,
@@ -299,6 +301,17 @@ def block_backward_line(vt, torch, grids, iters):
                     "(3x the linear products, 12 n^2 d attention)"}
 
 
+def tower_backward_line(vt, torch, wl, tw, weights, iters):
+    fn, fl = tower_backward_case(vt, torch, wl, tw, weights)
+    tt = time_kernel(torch, fn, max(2, iters // 5))
+    return {"call": "vt_tower_backward (%s: 32 layers + patch embed, all gradients)" % wl.name,
+            "achieved": fl / tt / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": fl / tt / 1e12 / PEAK_BF16_TFLOPS, "flops_per_call": fl, "ms_per_call": tt * 1e3,
+            "patches_per_s": wl.tokens / tt,
+            "note": "forward with every block input kept, then the backward of each block (which "
+                    "recomputes that block's forward) and of the patch embed"}
+
+
 def kernel_only(a):
     """--kernel: run one kernel case a fixed number of times (for counter runs)."""
     import torch
@@ -380,17 +393,10 @@ def main():
     M = wl.tokens
     res["roofline"] = gemm_roofline(vt, torch, M, a.kernel_iters)
     res["attention_roofline"] = attention_roofline(vt, torch, list(wl.grids), a.kernel_iters)
-    res["attention_backward"] = attention_backward_line(vt, torch, list(wl.grids), a.kernel_iters)
-    res["block_backward"] = block_backward_line(vt, torch, list(wl.grids), a.kernel_iters)
-    fn, fl = tower_backward_case(vt, torch, wl, tw, weights)
-    tt = time_kernel(torch, fn, max(2, a.kernel_iters // 5))
-    res["tower_backward"] = {
-        "call": "vt_tower_backward (%s: 32 layers + patch embed, all gradients)" % wl.name,
-        "achieved": fl / tt / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-        "frac": fl / tt / 1e12 / PEAK_BF16_TFLOPS, "flops_per_call": fl, "ms_per_call": tt * 1e3,
-        "patches_per_s": wl.tokens / tt,
-        "note": "forward with every block input kept, then the backward of each block (which "
-                "recomputes that block's forward) and of the patch embed"}
+    if not a.no_backward:
+        res["attention_backward"] = attention_backward_line(vt, torch, list(wl.grids), a.kernel_iters)
+        res["block_backward"] = block_backward_line(vt, torch, list(wl.grids), a.kernel_iters)
+        res["tower_backward"] = tower_backward_line(vt, torch, wl, tw, weights, a.kernel_iters)
 
     if a.secondary:
         wl2 = synth.WORKLOADS[a.secondary]
@@ -408,10 +414,12 @@ def main():
                 vt, torch, list(wl2.grids), max(3, a.kernel_iters // 4),
                 "attention_2016_traffic" if wl2.name == "tower_2016" else None),
             "gemm_roofline": gemm_roofline(vt, torch, wl2.tokens, max(3, a.kernel_iters // 4)),
-            "attention_backward": attention_backward_line(vt, torch, list(wl2.grids),
-                                                          max(3, a.kernel_iters // 4)),
-            "block_backward": block_backward_line(vt, torch, list(wl2.grids), max(3, a.kernel_iters // 4)),
         }
+        if not a.no_backward:
+            res["secondary"]["attention_backward"] = attention_backward_line(
+                vt, torch, list(wl2.grids), max(3, a.kernel_iters // 4))
+            res["secondary"]["block_backward"] = block_backward_line(vt, torch, list(wl2.grids),
+                                                                     max(3, a.kernel_iters // 4))
         del run2
 
     more = []
