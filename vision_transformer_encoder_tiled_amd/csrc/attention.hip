@@ -463,10 +463,12 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(
 // the score registers, the ones row for l), but register-lean so that more
 // wavefronts share each SIMD and hide one another's latencies: one set of
 // scores (no one-tile-ahead pipelining), K and V^T fragments read as they are
-// consumed, and a 2-stage ring (50 KB of LDS).  142 VGPRs with 4 wavefronts
-// (128 queries, three workgroups per CU) or 128 with 8 wavefronts (256
-// queries sharing one K/V stream, two workgroups per CU: four wavefronts per
-// SIMD).  WPE is the wavefronts per SIMD the register budget is set for.
+// consumed, -m written into the score accumulators before each tile's first
+// MFMA (32 moves instead of a loop-carried 16-register C operand), and a
+// 2-stage ring (50 KB of LDS): 126 VGPRs.  4 wavefronts = 128 queries, three
+// workgroups per CU (LDS-bound), or 8 wavefronts = 256 queries sharing one
+// K/V stream, two workgroups per CU: four wavefronts per SIMD.  WPE is the
+// wavefronts per SIMD the register budget is set for.
 template <int NW, int NST, int WPE>
 __global__ void __launch_bounds__(64 * NW, WPE) attention_lean_kernel(
     const uint16_t* __restrict__ qpk, const uint16_t* __restrict__ kv,
@@ -508,9 +510,6 @@ __global__ void __launch_bounds__(64 * NW, WPE) attention_lean_kernel(
   for (int d = 0; d < 3; ++d)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[d][e] = 0.f;
-  f32x16_t negm;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) negm[e] = 0.f;
   float m_use = 0.f;
 #pragma unroll
   for (int r = 0; r < NST - 1; ++r)
@@ -523,9 +522,12 @@ __global__ void __launch_bounds__(64 * NW, WPE) attention_lean_kernel(
     const char* st = lds + (t % NST) * STAGE_BYTES;
     f32x16_t sc[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[b][e] = -m_use;
       sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-          *reinterpret_cast<const f16x8_t*>(st + koff + b * 32 * KROW * 2), qfrag[0], negm, 0, 0, 0);
+          *reinterpret_cast<const f16x8_t*>(st + koff + b * 32 * KROW * 2), qfrag[0], sc[b], 0, 0, 0);
+    }
 #pragma unroll
     for (int sl = 1; sl < 5; ++sl)
 #pragma unroll
@@ -564,8 +566,6 @@ __global__ void __launch_bounds__(64 * NW, WPE) attention_lean_kernel(
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sc[b][e] -= delta;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) negm[e] = -m_use;
     }
     const char* vst = st + voff;
 #pragma unroll
