@@ -246,6 +246,27 @@ def test_tower_backward_two_layers(vt):
     check_tower(*tower_backward_case(vt, grids, [1, 7], 2, dT), "2 layers")
 
 
+def test_tower_backward_clip(vt):
+    """A 4-frame clip (t = 2, the temporal RoPE pairs rotate) beside a still
+    image, two blocks: every gradient against the oracle."""
+    grids = [(2, 6, 8), (1, 4, 6)]
+    N = 96 + 24
+    dT = rng(58).standard_normal((N, 1280), dtype=np.float32)
+    check_tower(*tower_backward_case(vt, grids, [8, 9], 2, dT), "clip 2 layers")
+
+
+def test_attention_backward_many_items(vt):
+    """300 small items (4 and 8 tokens), so the schedule spans several
+    metadata chunks and many one-tile images."""
+    grids = [(1, 2, 2) if i % 3 else (1, 2, 4) for i in range(300)]
+    N = sum(t * h * w for t, h, w in grids)
+    qkv, dout = random_inputs(N, 59)
+    got = run_backward(vt, grids, qkv, dout)
+    want = G.attention_qkv_backward(bf16_f32(qkv).astype(np.float64), window_positions(grids),
+                                    oracle.cu_seqlens(grids), bf16_f32(dout).astype(np.float64))
+    check_parts(got, want, 1e-2, f"{len(grids)} items")
+
+
 def test_tower_backward_mean_pool_probe(vt):
     """The pages' probe (mean-pool the tower output, then a backward pass) on
     a 4-layer tower of one 224x224 image, with the loss sum over features of
