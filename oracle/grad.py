@@ -155,12 +155,13 @@ def attention_dq_rows(qkv, pos, cu, dout, rows, cfg: vit.Config = None):
     return out
 
 
-def tower_backward(images, grids, W, cfg: vit.Config, n_layers, d_tower):
+def tower_backward(images, grids, W, cfg: vit.Config, n_layers, d_tower, progress=None):
     """Gradients of the tower -- patch embed, then n_layers blocks -- given
     dL/d(tower output) ``d_tower`` [N, d] (raster order).  ``images`` are the
     items as vit.split_pixels returns them, ``W`` float weights.  Returns
     {"patch_w", "patch_b", "l<i>.<name>"} (the bias gradient even where the
-    bias is absent)."""
+    bias is absent).  ``progress(i)``, if given, is called after block i's
+    backward."""
     pos = vit.positions(grids)
     cu = vit.cu_seqlens(grids)
     X = np.concatenate([vit.patchify(img) for img in images], axis=0)
@@ -174,5 +175,7 @@ def tower_backward(images, grids, W, cfg: vit.Config, n_layers, d_tower):
     for i in reversed(range(n_layers)):
         dR, g = block_backward(inputs[i], W, pos, cu, cfg, dR, prefix=f"l{i}.")
         grads.update({f"l{i}.{k}": v for k, v in g.items()})
+        if progress:
+            progress(i)
     _, grads["patch_w"], grads["patch_b"] = linear_backward(X, W["patch_w"], dR)
     return grads

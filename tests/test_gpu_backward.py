@@ -206,7 +206,7 @@ def test_block_backward_ragged_images(vt):
 
 
 # ---------------------------------------------------------------- the tower
-def tower_backward_case(vt, grids, seeds, n_layers, d_tower, affine="random"):
+def tower_backward_case(vt, grids, seeds, n_layers, d_tower, affine="random", progress=None):
     """vt_tower_backward (n_layers blocks) on seeded items and dL/d(tower
     output) (raster order); returns (gpu grads, oracle grads), keyed like the
     oracle's."""
@@ -224,7 +224,8 @@ def tower_backward_case(vt, grids, seeds, n_layers, d_tower, affine="random"):
     got = {k: t.cpu().numpy() for k, t in gd.items()}
     Wf = {k: v.astype(np.float64) for k, v in oracle.weights_f32(W).items()}
     imgs = [x.astype(np.float64) for x in oracle.split_pixels(bf16_f32(px), grids)]
-    want = G.tower_backward(imgs, grids, Wf, oracle.Config(), n_layers, d_tower.astype(np.float64))
+    want = G.tower_backward(imgs, grids, Wf, oracle.Config(), n_layers, d_tower.astype(np.float64),
+                            progress=progress)
     return got, want
 
 
@@ -335,3 +336,19 @@ def test_block_backward_partial_gradients(vt):
     assert torch.equal(dR_full, dR_some)
     for k, t in some.items():
         assert torch.equal(t, full[k]), k
+
+
+def test_tower_backward_448_full(vt):
+    """The configuration bench.py times: the whole 32-layer tower on the
+    448x448 image (1,024 tokens) under the mean-pool probe, every one of the
+    386 gradients and the gradient norm against the float64 oracle (about a
+    minute of host time; progress is logged every 8 blocks)."""
+    grids = [(1, 32, 32)]
+    dT = np.full((1024, 1280), 1.0 / 1024, np.float32)
+    got, want = tower_backward_case(vt, grids, [2], 32, dT, affine="canonical",
+                                    progress=lambda i: i % 8 == 0 and log(f"  oracle block {i} done"))
+    check_tower(got, want, "448 32 layers")
+    g_gpu = np.sqrt(sum(float((got[k].astype(np.float64) ** 2).sum()) for k in want))
+    g_ref = np.sqrt(sum(float((want[k] ** 2).sum()) for k in want))
+    log(f"  grad_l2 {g_gpu:.6g} (oracle {g_ref:.6g})")
+    assert abs(g_gpu - g_ref) <= 1e-2 * g_ref
