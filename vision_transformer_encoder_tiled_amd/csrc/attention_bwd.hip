@@ -28,9 +28,10 @@
 //     S^T  = K Q^T - L        (the MFMAs accumulate onto -L: P = 2^(S^T))
 //     dP^T = V dO^T - D
 //     dQ^T += K^T dS^T        (dS^T straight from the registers in slot order)
-// bwd_dkv_kernel key-major: a workgroup owns 128 keys and streams the
-//   image's query-side images; per tile, with L and D per accumulator row
-//   loaded from LDS into the MFMA's initial value,
+// bwd_dkv_kernel key-major: a workgroup owns 128 keys (4 wavefronts), or 256
+//   (8 wavefronts sharing the stream) when the call has many key tiles, and
+//   streams the image's query-side images; per tile, with L and D per
+//   accumulator row loaded from LDS into the MFMA's initial value,
 //     S  = Q K^T - L,  dP = dO V^T - D,  dV^T += dO^T P,  dK^T += Q^T dS.
 // Both end by un-rotating (dq, dk) in registers -- the pair (j, j + 40) of a
 // lane's dims always sits in the same lane -- and store dqkv rows.
@@ -38,9 +39,9 @@
 // Precision: fp16 MFMA operands (q, k, v, dO, P, dS) with fp32 accumulation,
 // as in the forward.  P <= 1 after the log-sum-exp shift.
 //
-// Grid of both main kernels: one workgroup per (128-token tile, head), head
-// fastest, largest images first (the forward's schedule with 128-token
-// tiles).  Each image's tiles start on a fresh 64-token tile image.
+// Grid of both main kernels: one workgroup per (128- or 256-token tile,
+// head), head fastest, largest images first (the forward's schedule with
+// that tile size).  Each image's tiles start on a fresh 64-token tile image.
 #include "vt_device.h"
 #include "vt_kernels.h"
 
