@@ -335,7 +335,8 @@ def kernel_only(a):
 
 
 def cpu_baseline(weights):
-    """The oracle, untuned, on one 448x448 image through the full tower."""
+    """The oracle, untuned, on the 448x448 image through the full tower,
+    repeated until about 10 s of host work."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -344,12 +345,15 @@ def cpu_baseline(weights):
         threads = os.cpu_count()
     wl = synth.WORKLOADS["tower_448"]
     px = synth.make_batch_pixels(wl)
-    t0 = time.perf_counter()
-    oracle.tower_forward(px, list(wl.grids), weights)
+    # Whole passes over the 448x448 image until at least 10 s of host work.
+    passes, t0 = 0, time.perf_counter()
+    while passes < 8 and (passes == 0 or time.perf_counter() - t0 < 10.0):
+        oracle.tower_forward(px, list(wl.grids), weights)
+        passes += 1
     dt = time.perf_counter() - t0
-    return {"value": wl.tokens / dt, "unit": "patches/s", "cores": int(threads), "kind": "oracle",
-            "sample": "one 448x448 image (1024 patches) through the 32-layer tower, merge and "
-                      "projector, numpy fp32 on the host, %.1f s" % dt,
+    return {"value": passes * wl.tokens / dt, "unit": "patches/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%d passes of one 448x448 image (1024 patches) through the 32-layer tower, merge "
+                      "and projector, numpy fp32 on the host, %.1f s in all" % (passes, dt),
             "host_cpus": os.cpu_count(),
             "usable_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
