@@ -21,6 +21,7 @@
 // tiles to the workspace and a second kernel sums them in split order (no
 // atomics: results are deterministic).
 #include <algorithm>
+#include <type_traits>
 
 #include "vt_device.h"
 #include "vt_kernels.h"
@@ -207,10 +208,19 @@ __device__ __forceinline__ void xcd_group_tile(int tiles_m, int tiles_n, int* tm
 // 16-byte bank groups (64 banks) and any 8 aligned rows in 8 (32 banks).
 __device__ __forceinline__ int swz4(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 
-// LDS layout of one K step of gemm_dl_kernel: BM rows of A, then the B rows,
-// 64 bytes each; B is rounded up to whole copy rounds of 16 rows per wavefront.
-constexpr int dl_b_rows(int bn, int nw) { return (bn + 16 * nw - 1) / (16 * nw) * (16 * nw); }
-constexpr int dl_stage_bytes(int bm, int bn, int nw) { return (bm + dl_b_rows(bn, nw)) * 64; }
+// LDS layout of one K step of gemm_dl_kernel: BM rows of A, then BN rows of
+// B, 2 BK bytes each, copied in groups of 1 KB (one copy instruction).
+constexpr int dl_stage_bytes(int bm, int bn, int bk) { return (bm + bn) * 2 * bk; }
+
+// Chunk swizzle of the LDS rows: 64-byte rows (BK = 32) use swz4; 128-byte
+// rows (8 chunks) use (r mod 8) ^ bit 3 of r, so that 8 aligned consecutive
+// rows read at one logical chunk fall in 8 distinct 16-byte bank groups and
+// 16 aligned rows (two per 128-byte bank line) in 16.
+template <int BK>
+__device__ __forceinline__ int dl_swz(int r) {
+  if constexpr (BK == 32) return swz4(r);
+  else return (r & 7) ^ ((r >> 3) & 1);
+}
 
 // Token rows of the C tile staged per epilogue pass: BM halved until a pass
 // fits the LDS ring.
@@ -221,26 +231,32 @@ constexpr int pass_rows(int bm, int row_bytes, int ring) {
 }
 
 // GWM x GWN wavefronts; each owns a (BM/GWM) x (BN/GWN) block of C.
-// K is consumed in steps of 32 through a ring of NST LDS stages: NST - 1
-// steps are in flight while one is multiplied, one workgroup barrier per
-// step.  The finished tile is staged through the (then idle) ring so that
-// every global store writes whole 16-byte pieces of contiguous rows.
-template <int BM, int BN, int GWM, int GWN, int NST, int EPI, bool SPLIT>
+// K is consumed in steps of BK (32 or 64) through a ring of NST LDS stages,
+// one workgroup barrier per step.  BK = 32: 64-byte rows, NST - 1 steps in
+// flight while one is multiplied.  BK = 64: 128-byte rows (a copy reads whole
+// 128-byte lines), each step multiplied as two halves of 32 with the barrier
+// between them, NST - 1 steps in flight.  The finished tile is staged through
+// the (then idle) ring so that every global store writes whole 16-byte pieces
+// of contiguous rows.
+template <int BM, int BN, int GWM, int GWN, int NST, int EPI, bool SPLIT, int BK = 32>
 __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
     const uint16_t* __restrict__ A, int M, int K, const uint16_t* __restrict__ B, int N,
     const uint16_t* __restrict__ bias, void* __restrict__ out, float* __restrict__ part, int kper) {
   constexpr int NW = GWM * GWN;
   constexpr int WM = BM / GWM, WN = BN / GWN;
   constexpr int TB = WM / 32, FB = WN / 32;
-  constexpr int BK = 32;
-  // B rows copied per step: BN rounded up to whole copy rounds (16 rows per
-  // wavefront); the extra rows are copied and never read.
-  constexpr int BNP = dl_b_rows(BN, NW);
-  constexpr int LA = BM / (16 * NW), LB = BNP / (16 * NW);  // copies per lane per K step
-  constexpr int CP = LA + LB;
-  constexpr int A_BYTES = BM * 64, STAGE = dl_stage_bytes(BM, BN, NW);
-  static_assert(WM % 32 == 0 && WN % 32 == 0 && LA * 16 * NW == BM && LB * 16 * NW == BNP, "tiling");
+  static_assert(BK == 32 || BK == 64, "K step");
+  constexpr int RB = 2 * BK, CH = RB / 16, RPG = 1024 / RB;  // row bytes, chunks per row, rows per copy
+  // Copy groups of one K step (RPG rows, 1 KB, one copy instruction): BM/RPG
+  // of A, then BN/RPG of B; group g is copied by wavefront g % NW, so the
+  // first G % NW wavefronts copy one group more (CP_HI against CP_LO) when G
+  // is not a multiple of NW.
+  constexpr int GA = BM / RPG, G = (BM + BN) / RPG;
+  constexpr int CP_HI = (G + NW - 1) / NW, CP_LO = G / NW;
+  constexpr int A_BYTES = BM * RB, STAGE = dl_stage_bytes(BM, BN, BK);
+  static_assert(WM % 32 == 0 && WN % 32 == 0 && BM % 16 == 0 && BN % 16 == 0, "tiling");
   static_assert(NST * STAGE <= 160 * 1024, "LDS");
+  static_assert(BK == 32 ? NST >= 3 : NST >= 2, "ring depth");
   extern __shared__ __align__(16) uint16_t lds[];
   const char* smem = reinterpret_cast<const char*>(lds);
 
@@ -253,29 +269,41 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
   const int kend = SPLIT ? min(K, kbeg + kper) : K;
   const int nk = (kend - kbeg) / BK;
 
-  // Copy j of this lane: tile row 16 (wave + NW j) + lane / 4, logical chunk
-  // (lane % 4) ^ swz4(row), landing in physical chunk lane % 4.  Rows past M
-  // (N) read the last valid row; their results are never stored.
-  const int lrow = 16 * wave + (lane >> 2);
-  const int lchunk = (lane & 3) ^ swz4(lrow);
-  const uint16_t* ga = A + int64_t(min(m0 + lrow, M - 1)) * K + kbeg + 8 * lchunk;
-  const uint16_t* gb = B + int64_t(min(n0 + lrow, N - 1)) * K + kbeg + 8 * lchunk;
-  int64_t oa[LA], ob[LB];
+  // Copy j of this lane: group g = wave + NW j, i.e. row RPG g + lane / CH of
+  // the stage (an A row while g < GA, else B row RPG (g - GA) + lane / CH),
+  // logical chunk (lane % CH) ^ swz(row), landing in physical chunk lane % CH
+  // of LDS bytes 1024 g + RB (lane / CH) of the stage.  Rows past M (N) read
+  // the last valid row; their results are never stored.
+  const int lq = lane / CH;
+  const bool hi = wave < G % NW;  // copies CP_HI groups (else CP_LO)
+  const uint16_t* src[CP_HI];
 #pragma unroll
-  for (int j = 0; j < LA; ++j)
-    oa[j] = int64_t(min(m0 + lrow + 16 * NW * j, M - 1) - min(m0 + lrow, M - 1)) * K;
-#pragma unroll
-  for (int j = 0; j < LB; ++j)
-    ob[j] = int64_t(min(n0 + lrow + 16 * NW * j, N - 1) - min(n0 + lrow, N - 1)) * K;
+  for (int j = 0; j < CP_HI; ++j) {
+    const int g = min(wave + NW * j, G - 1);
+    const int lchunk = (lane % CH) ^ dl_swz<BK>(RPG * g + lq);
+    src[j] = g < GA ? A + int64_t(min(m0 + RPG * g + lq, M - 1)) * K + kbeg + 8 * lchunk
+                    : B + int64_t(min(n0 + RPG * (g - GA) + lq, N - 1)) * K + kbeg + 8 * lchunk;
+  }
   const uint32_t lds0 = lds_offset(lds) + 1024 * wave;
 
   auto issue = [&](int it) {
     const uint32_t sa = __builtin_amdgcn_readfirstlane(lds0 + (it % NST) * STAGE);
 #pragma unroll
-    for (int j = 0; j < LA; ++j) dma16(ga + oa[j] + it * BK, sa + 1024 * NW * j);
-#pragma unroll
-    for (int j = 0; j < LB; ++j) dma16(gb + ob[j] + it * BK, sa + A_BYTES + 1024 * NW * j);
+    for (int j = 0; j < CP_LO; ++j) dma16(src[j] + it * BK, sa + 1024 * NW * j);
+    if constexpr (CP_HI > CP_LO)
+      if (hi) dma16(src[CP_LO] + it * BK, sa + 1024 * NW * CP_LO);
   };
+  // vmcnt <= the copies of the newest `steps` issued steps.
+  auto wait_steps = [&](auto steps) {
+    constexpr int n = decltype(steps)::value;
+    if constexpr (CP_HI > CP_LO) {
+      if (hi) wait_vmcnt<n * CP_HI>();
+      else wait_vmcnt<n * CP_LO>();
+    } else {
+      wait_vmcnt<n * CP_LO>();
+    }
+  };
+  using None = std::integral_constant<int, 0>;
 
   f32x16_t acc[FB][TB];
 #pragma unroll
@@ -286,25 +314,26 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
       for (int e = 0; e < 16; ++e) acc[f][t][e] = 0.f;
 
   const int fr = lane & 31, h = lane >> 5;
-  const int sw = swz4(fr);
-  const int choff0 = 16 * ((0 + h) ^ sw), choff1 = 16 * ((2 + h) ^ sw);
+  const int sw = dl_swz<BK>(fr);
 
-  // Fragments of one K step (two MFMA k slices of 16).
+  // Fragments of 32 of K (two MFMA k slices of 16): half u of step `step`
+  // (u = 0 for BK = 32).  Slice q of half u is logical chunk 4u + 2q + h.
   struct Frags {
     bf16x8_t w0[FB], t0[TB], w1[FB], t1[TB];
   };
-  auto load_frags = [&](Frags& F, int step) {
+  auto load_frags = [&](Frags& F, int step, int u) {
     const char* st = smem + (step % NST) * STAGE;
-    const char* a_base = st + (wm * WM + fr) * 64;
-    const char* b_base = st + A_BYTES + (wn * WN + fr) * 64;
+    const char* a_base = st + (wm * WM + fr) * RB;
+    const char* b_base = st + A_BYTES + (wn * WN + fr) * RB;
+    const int choff0 = 16 * ((4 * u + h) ^ sw), choff1 = 16 * ((4 * u + 2 + h) ^ sw);
 #pragma unroll
-    for (int f = 0; f < FB; ++f) F.w0[f] = *reinterpret_cast<const bf16x8_t*>(b_base + f * 2048 + choff0);
+    for (int f = 0; f < FB; ++f) F.w0[f] = *reinterpret_cast<const bf16x8_t*>(b_base + f * 32 * RB + choff0);
 #pragma unroll
-    for (int t = 0; t < TB; ++t) F.t0[t] = *reinterpret_cast<const bf16x8_t*>(a_base + t * 2048 + choff0);
+    for (int t = 0; t < TB; ++t) F.t0[t] = *reinterpret_cast<const bf16x8_t*>(a_base + t * 32 * RB + choff0);
 #pragma unroll
-    for (int f = 0; f < FB; ++f) F.w1[f] = *reinterpret_cast<const bf16x8_t*>(b_base + f * 2048 + choff1);
+    for (int f = 0; f < FB; ++f) F.w1[f] = *reinterpret_cast<const bf16x8_t*>(b_base + f * 32 * RB + choff1);
 #pragma unroll
-    for (int t = 0; t < TB; ++t) F.t1[t] = *reinterpret_cast<const bf16x8_t*>(a_base + t * 2048 + choff1);
+    for (int t = 0; t < TB; ++t) F.t1[t] = *reinterpret_cast<const bf16x8_t*>(a_base + t * 32 * RB + choff1);
   };
   auto mma = [&](const Frags& F) {
 #pragma unroll
@@ -318,43 +347,87 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
       for (int t = 0; t < TB; ++t)
         acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.w1[f], F.t1[t], acc[f][t], 0, 0, 0);
   };
-  // One K step: copies for step it+3 go out, step it+1's fragments are read
-  // while step it's are multiplied; then step it+2's copies must have landed
-  // (by every wave) before the next step reads them.
-  // The fragment reads are unconditional (on the last step they read a
-  // stale, never used stage): a branch around them makes the compiler wait
-  // for every outstanding LDS read before the first MFMA of the step.
-  auto step = [&](int it, const Frags& cur, Frags& nxt) {
-    if (it + NST - 1 < nk) issue(it + NST - 1);  // into the stage step it-1 used
-    load_frags(nxt, it + 1);
-    mma(cur);
+  // The MFMAs of one half interleaved with the next half's fragment reads.
+  auto interleave = [&]() {
 #pragma unroll
     for (int i = 0; i < 2 * (FB + TB); ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * FB * TB - 2 * (FB + TB), 0);
-    if (it + NST - 1 < nk) wait_vmcnt<(NST - 3) * CP>();  // step it+2 has landed
-    else wait_vmcnt<0>();
-    wait_lds_reads();
-    wg_barrier();
   };
 
+  if constexpr (BK == 32) {
+    using InFlight = std::integral_constant<int, NST - 3>;
+    // One K step: copies for step it+NST-1 go out, step it+1's fragments are
+    // read while step it's are multiplied; then step it+2's copies must have
+    // landed (by every wave) before the next step reads them.
+    // The fragment reads are unconditional (on the last step they read a
+    // stale, never used stage): a branch around them makes the compiler wait
+    // for every outstanding LDS read before the first MFMA of the step.
+    auto step = [&](int it, const Frags& cur, Frags& nxt) {
+      if (it + NST - 1 < nk) issue(it + NST - 1);  // into the stage step it-1 used
+      load_frags(nxt, it + 1, 0);
+      mma(cur);
+      interleave();
+      if (it + NST - 1 < nk) wait_steps(InFlight{});  // step it+2 has landed
+      else wait_steps(None{});
+      wait_lds_reads();
+      wg_barrier();
+    };
+
 #pragma unroll
-  for (int i = 0; i < NST - 1; ++i)
-    if (i < nk) issue(i);
-  if (nk > 0) {
-    if (NST - 1 < nk) wait_vmcnt<(NST - 3) * CP>();  // steps 0 and 1 landed
-    else wait_vmcnt<0>();
-    wg_barrier();
-    Frags F0, F1;
-    load_frags(F0, 0);
-    int it = 0;
-    for (; it + 1 < nk; it += 2) {
-      step(it, F0, F1);
-      step(it + 1, F1, F0);
+    for (int i = 0; i < NST - 1; ++i)
+      if (i < nk) issue(i);
+    if (nk > 0) {
+      if (NST - 1 < nk) wait_steps(InFlight{});  // steps 0 and 1 landed
+      else wait_steps(None{});
+      wg_barrier();
+      Frags F0, F1;
+      load_frags(F0, 0, 0);
+      int it = 0;
+      for (; it + 1 < nk; it += 2) {
+        step(it, F0, F1);
+        step(it + 1, F1, F0);
+      }
+      if (it < nk) step(it, F0, F1);
     }
-    if (it < nk) step(it, F0, F1);
+  } else {
+    using InFlight = std::integral_constant<int, NST - 2>;
+#pragma unroll
+    for (int i = 0; i < NST - 1; ++i)
+      if (i < nk) issue(i);
+    if (nk > 0) {
+      if (NST - 1 <= nk) wait_steps(InFlight{});  // step 0 landed
+      else wait_steps(None{});
+      wg_barrier();
+      Frags F0, F1;
+      load_frags(F0, 0, 0);
+      for (int it = 0; it < nk; ++it) {
+        // First half of step it.  The copies for step it+NST-1 go into the
+        // stage of step it-1, whose last reads (its second half) came before
+        // the previous barrier.
+        if (it + NST - 1 < nk) issue(it + NST - 1);
+        load_frags(F1, it, 1);
+        mma(F0);
+        interleave();
+        // Step it+1 must have landed (by every wave) before the second half
+        // reads its first fragments; the barrier also releases step it's
+        // stage, all of whose reads are done.
+        if (it + NST - 1 < nk) wait_steps(InFlight{});
+        else wait_steps(None{});
+        wait_lds_reads();
+        wg_barrier();
+        // Second half of step it (on the last step the read is of a stale,
+        // never used stage).
+        load_frags(F0, it + 1, 0);
+        mma(F1);
+        interleave();
+      }
+      // The epilogue reuses the ring: every wave's reads must be done.
+      wait_lds_reads();
+      wg_barrier();
+    }
   }
 
   // ---- epilogue.  acc[f][t][4g + r] = C[token][feature] with token =
@@ -522,7 +595,7 @@ GemmPlan plan_gemm(int M, int N, int K) {
   if (t128 > 256 && K % 32 == 0) {
     // One round of wider tiles when N allows it (e.g. 1024 x 5120: 8 x 32 tiles of 128 x 160).
     for (int bn : {160, 192})
-      if (N % bn == 0 && tm * (N / bn) <= 256) {
+      if (N % bn == 0 && tm * (N / bn) <= 256 && K % 64 == 0) {
         p.bn = bn;
         return p;
       }
@@ -547,27 +620,45 @@ size_t gemm_workspace_bytes(int M, int N, int K) {
   return p.splits > 1 ? size_t(p.splits) * M * N * sizeof(float) : 0;
 }
 
+template <int BM, int BN, int EPI, bool SPLIT, int BK>
+static hipError_t launch_dl(const uint16_t* A, int M, int K, const uint16_t* B, int N,
+                            const uint16_t* bias, void* out, float* part, const GemmPlan& p,
+                            int tiles, hipStream_t s) {
+  // 256 x 256: 8 wavefronts (2 per SIMD) of 128 x 64; 128 x 128: 8 of 32 x 64;
+  // 128 x 160 and 128 x 192: 4 of 32 x BN.  K steps of 32 go through 4
+  // stages, K steps of 64 through 3.
+  constexpr int GWM = (BM == 256) ? 2 : 4, GWN = (BM == 256) ? 4 : (BN == 128 ? 2 : 1);
+  constexpr int NST = BK == 64 ? 3 : 4;
+  const size_t lds = size_t(NST) * dl_stage_bytes(BM, BN, BK);
+  auto kern = gemm_dl_kernel<BM, BN, GWM, GWN, NST, EPI, SPLIT, BK>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3(tiles, SPLIT ? p.splits : 1), dim3(64 * GWM * GWN), lds, s, A, M, K,
+                     B, N, bias, out, part, p.kper);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int EPI, bool SPLIT>
 static hipError_t launch_tile(const uint16_t* A, int M, int K, const uint16_t* B, int N,
                               const uint16_t* bias, void* out, float* part, const GemmPlan& p,
                               hipStream_t s) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  if (K % 32 == 0 && (!SPLIT || p.kper % 32 == 0)) {
-    // 256 x 256: 8 wavefronts (2 per SIMD) of 128 x 64; 128 x 128: 8 of 32 x 64;
-    // 128 x 160 and 128 x 192: 4 of 32 x BN.
-    constexpr int GWM = (BM == 256) ? 2 : 4, GWN = (BM == 256) ? 4 : (BN == 128 ? 2 : 1), NST = 4;
-    const size_t lds = size_t(NST) * dl_stage_bytes(BM, BN, GWM * GWN);
-    auto kern = gemm_dl_kernel<BM, BN, GWM, GWN, NST, EPI, SPLIT>;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(kern, dim3(tiles, SPLIT ? p.splits : 1), dim3(64 * GWM * GWN), lds, s, A, M,
-                       K, B, N, bias, out, part, p.kper);
-    return hipGetLastError();
-  }
-  if constexpr (BN != BM) {
-    return hipErrorInvalidValue;  // the register-staged kernel has square tiles only
+  const auto k_step_ok = [&](int bk) { return K % bk == 0 && (!SPLIT || p.kper % bk == 0); };
+  if constexpr (BN == 160 || BN == 192) {
+    // The wide tiles are planned only for one round of workgroups, K % 64 == 0.
+    if (!k_step_ok(64)) return hipErrorInvalidValue;
+    return launch_dl<BM, BN, EPI, SPLIT, 64>(A, M, K, B, N, bias, out, part, p, tiles, s);
   } else {
+    // 128 x 128 in one round of workgroups: K steps of 64 (96 KB of LDS, one
+    // workgroup per CU).  More rounds: K steps of 32 (64 KB, two per CU).
+    // 256 x 256 keeps K steps of 32: with 64 only a 2-stage ring fits, and
+    // inside the tower (weights not hot in cache) that measured slower.
+    if constexpr (BM == 128)
+      if (tiles * (SPLIT ? p.splits : 1) <= 256 && k_step_ok(64))
+        return launch_dl<BM, BN, EPI, SPLIT, 64>(A, M, K, B, N, bias, out, part, p, tiles, s);
+    if (k_step_ok(32))
+      return launch_dl<BM, BN, EPI, SPLIT, 32>(A, M, K, B, N, bias, out, part, p, tiles, s);
     const size_t lds = size_t(2) * (BM + BN) * kLdsRow * sizeof(uint16_t);
     auto kern = gemm_kernel<BM, BN, EPI, SPLIT>;
     // Set once per instantiation (thread-safe static initialisation).
