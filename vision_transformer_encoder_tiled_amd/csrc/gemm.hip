@@ -238,29 +238,34 @@ constexpr int pass_rows(int bm, int row_bytes, int ring) {
 // between them, NST - 1 steps in flight.  The finished tile is staged through
 // the (then idle) ring so that every global store writes whole 16-byte pieces
 // of contiguous rows.
-template <int BM, int BN, int GWM, int GWN, int NST, int EPI, bool SPLIT, int BK = 32>
-__global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
+template <int BM, int BN, int GWM, int GWN, int NST, int EPI, bool SPLIT, int BK = 32, int CW = 0>
+__global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
     const uint16_t* __restrict__ A, int M, int K, const uint16_t* __restrict__ B, int N,
     const uint16_t* __restrict__ bias, void* __restrict__ out, float* __restrict__ part, int kper) {
-  constexpr int NW = GWM * GWN;
+  constexpr int NW = GWM * GWN;  // wavefronts that multiply
+  constexpr int NWC = NW + CW;   // wavefronts that copy: all of them
   constexpr int WM = BM / GWM, WN = BN / GWN;
   constexpr int TB = WM / 32, FB = WN / 32;
   static_assert(BK == 32 || BK == 64, "K step");
+  static_assert(CW == 0 || BK == 64, "copy-only wavefronts with K steps of 64 only");
   constexpr int RB = 2 * BK, CH = RB / 16, RPG = 1024 / RB;  // row bytes, chunks per row, rows per copy
   // Copy groups of one K step (RPG rows, 1 KB, one copy instruction): BM/RPG
-  // of A, then BN/RPG of B; group g is copied by wavefront g % NW, so the
-  // first G % NW wavefronts copy one group more (CP_HI against CP_LO) when G
-  // is not a multiple of NW.
+  // of A, then BN/RPG of B; group g is copied by wavefront g % NWC, so the
+  // first G % NWC wavefronts copy one group more (CP_HI against CP_LO) when G
+  // is not a multiple of NWC.  A wavefront issues copies at a limited rate
+  // (~21 GB/s each, up to ~140 GB/s per CU from 8 wavefronts), so tiles with
+  // 4 multiplying wavefronts add CW = 4 that only copy.
   constexpr int GA = BM / RPG, G = (BM + BN) / RPG;
-  constexpr int CP_HI = (G + NW - 1) / NW, CP_LO = G / NW;
+  constexpr int CP_HI = (G + NWC - 1) / NWC, CP_LO = G / NWC;
   constexpr int A_BYTES = BM * RB, STAGE = dl_stage_bytes(BM, BN, BK);
   static_assert(WM % 32 == 0 && WN % 32 == 0 && BM % 16 == 0 && BN % 16 == 0, "tiling");
   static_assert(NST * STAGE <= 160 * 1024, "LDS");
-  static_assert(BK == 32 ? NST >= 3 : NST >= 2, "ring depth");
+  static_assert(NST >= 3, "ring depth");
   extern __shared__ __align__(16) uint16_t lds[];
   const char* smem = reinterpret_cast<const char*>(lds);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool mw = CW == 0 || wave < NW;  // a multiplying wavefront
   const int wm = wave / GWN, wn = wave % GWN;
   int tm, tn;
   xcd_group_tile((M + BM - 1) / BM, (N + BN - 1) / BN, &tm, &tn);
@@ -269,17 +274,17 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
   const int kend = SPLIT ? min(K, kbeg + kper) : K;
   const int nk = (kend - kbeg) / BK;
 
-  // Copy j of this lane: group g = wave + NW j, i.e. row RPG g + lane / CH of
+  // Copy j of this lane: group g = wave + NWC j, i.e. row RPG g + lane / CH of
   // the stage (an A row while g < GA, else B row RPG (g - GA) + lane / CH),
   // logical chunk (lane % CH) ^ swz(row), landing in physical chunk lane % CH
   // of LDS bytes 1024 g + RB (lane / CH) of the stage.  Rows past M (N) read
   // the last valid row; their results are never stored.
   const int lq = lane / CH;
-  const bool hi = wave < G % NW;  // copies CP_HI groups (else CP_LO)
+  const bool hi = wave < G % NWC;  // copies CP_HI groups (else CP_LO)
   const uint16_t* src[CP_HI];
 #pragma unroll
   for (int j = 0; j < CP_HI; ++j) {
-    const int g = min(wave + NW * j, G - 1);
+    const int g = min(wave + NWC * j, G - 1);
     const int lchunk = (lane % CH) ^ dl_swz<BK>(RPG * g + lq);
     src[j] = g < GA ? A + int64_t(min(m0 + RPG * g + lq, M - 1)) * K + kbeg + 8 * lchunk
                     : B + int64_t(min(n0 + RPG * (g - GA) + lq, N - 1)) * K + kbeg + 8 * lchunk;
@@ -289,9 +294,9 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
   auto issue = [&](int it) {
     const uint32_t sa = __builtin_amdgcn_readfirstlane(lds0 + (it % NST) * STAGE);
 #pragma unroll
-    for (int j = 0; j < CP_LO; ++j) dma16(src[j] + it * BK, sa + 1024 * NW * j);
+    for (int j = 0; j < CP_LO; ++j) dma16(src[j] + it * BK, sa + 1024 * NWC * j);
     if constexpr (CP_HI > CP_LO)
-      if (hi) dma16(src[CP_LO] + it * BK, sa + 1024 * NW * CP_LO);
+      if (hi) dma16(src[CP_LO] + it * BK, sa + 1024 * NWC * CP_LO);
   };
   // vmcnt <= the copies of the newest `steps` issued steps.
   auto wait_steps = [&](auto steps) {
@@ -402,15 +407,17 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
       else wait_steps(None{});
       wg_barrier();
       Frags F0, F1;
-      load_frags(F0, 0, 0);
+      if (mw) load_frags(F0, 0, 0);
       for (int it = 0; it < nk; ++it) {
         // First half of step it.  The copies for step it+NST-1 go into the
         // stage of step it-1, whose last reads (its second half) came before
         // the previous barrier.
         if (it + NST - 1 < nk) issue(it + NST - 1);
-        load_frags(F1, it, 1);
-        mma(F0);
-        interleave();
+        if (mw) {
+          load_frags(F1, it, 1);
+          mma(F0);
+          interleave();
+        }
         // Step it+1 must have landed (by every wave) before the second half
         // reads its first fragments; the barrier also releases step it's
         // stage, all of whose reads are done.
@@ -420,9 +427,11 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
         wg_barrier();
         // Second half of step it (on the last step the read is of a stale,
         // never used stage).
-        load_frags(F0, it + 1, 0);
-        mma(F1);
-        interleave();
+        if (mw) {
+          load_frags(F0, it + 1, 0);
+          mma(F1);
+          interleave();
+        }
       }
       // The epilogue reuses the ring: every wave's reads must be done.
       wait_lds_reads();
@@ -449,7 +458,7 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
 #pragma unroll
   for (int pass = 0; pass < BM / PASS_ROWS; ++pass) {
     if (pass > 0) __syncthreads();  // the previous pass's reads are done
-    if (wm * WM / PASS_ROWS == pass) {
+    if (mw && wm * WM / PASS_ROWS == pass) {
 #pragma unroll
       for (int t = 0; t < TB; ++t) {
         const int r = wm * WM + 32 * t + fr - pass * PASS_ROWS;
@@ -485,14 +494,14 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
     }
     __syncthreads();
     constexpr int TOTAL = PASS_ROWS * CHUNKS;
-    constexpr int PER = (TOTAL + 64 * NW - 1) / (64 * NW);  // chunks per thread per pass
+    constexpr int PER = (TOTAL + 64 * NWC - 1) / (64 * NWC);  // chunks per thread per pass
     if constexpr (EPI == kEpiResid && !SPLIT) {
       // Residual update: every old value this thread needs is loaded first,
       // so the loads are in flight together rather than one store apart.
       float4 old[PER];
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
-        const int i = tid + j * 64 * NW;
+        const int i = tid + j * 64 * NWC;
         const int r = i / CHUNKS, c = i % CHUNKS;
         const int tok = m0 + pass * PASS_ROWS + r, col = n0 + c * EPC;
         if (i < TOTAL && tok < M && col < N)
@@ -501,7 +510,7 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
       }
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
-        const int i = tid + j * 64 * NW;
+        const int i = tid + j * 64 * NWC;
         const int r = i / CHUNKS, c = i % CHUNKS;
         const int tok = m0 + pass * PASS_ROWS + r, col = n0 + c * EPC;
         if (i >= TOTAL || tok >= M || col >= N) continue;
@@ -516,7 +525,7 @@ __global__ void __launch_bounds__(64 * GWM * GWN) gemm_dl_kernel(
       continue;
     }
 #pragma unroll
-    for (int i = tid; i < TOTAL; i += 64 * NW) {
+    for (int i = tid; i < TOTAL; i += 64 * NWC) {
       const int r = i / CHUNKS, c = i % CHUNKS;
       const int tok = m0 + pass * PASS_ROWS + r, col = n0 + c * EPC;
       if (tok >= M || col >= N) continue;
@@ -625,17 +634,18 @@ static hipError_t launch_dl(const uint16_t* A, int M, int K, const uint16_t* B, 
                             const uint16_t* bias, void* out, float* part, const GemmPlan& p,
                             int tiles, hipStream_t s) {
   // 256 x 256: 8 wavefronts (2 per SIMD) of 128 x 64; 128 x 128: 8 of 32 x 64;
-  // 128 x 160 and 128 x 192: 4 of 32 x BN.  K steps of 32 go through 4
-  // stages, K steps of 64 through 3.
+  // 128 x 160 and 128 x 192: 4 of 32 x BN plus 4 that only copy.  K steps of
+  // 32 go through 4 stages, K steps of 64 through 3.
   constexpr int GWM = (BM == 256) ? 2 : 4, GWN = (BM == 256) ? 4 : (BN == 128 ? 2 : 1);
+  constexpr int CW = (BK == 64 && GWM * GWN == 4) ? 4 : 0;
   constexpr int NST = BK == 64 ? 3 : 4;
   const size_t lds = size_t(NST) * dl_stage_bytes(BM, BN, BK);
-  auto kern = gemm_dl_kernel<BM, BN, GWM, GWN, NST, EPI, SPLIT, BK>;
+  auto kern = gemm_dl_kernel<BM, BN, GWM, GWN, NST, EPI, SPLIT, BK, CW>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(tiles, SPLIT ? p.splits : 1), dim3(64 * GWM * GWN), lds, s, A, M, K,
-                     B, N, bias, out, part, p.kper);
+  hipLaunchKernelGGL(kern, dim3(tiles, SPLIT ? p.splits : 1), dim3(64 * (GWM * GWN + CW)), lds, s, A,
+                     M, K, B, N, bias, out, part, p.kper);
   return hipGetLastError();
 }
 
@@ -652,8 +662,9 @@ static hipError_t launch_tile(const uint16_t* A, int M, int K, const uint16_t* B
   } else {
     // 128 x 128 in one round of workgroups: K steps of 64 (96 KB of LDS, one
     // workgroup per CU).  More rounds: K steps of 32 (64 KB, two per CU).
-    // 256 x 256 keeps K steps of 32: with 64 only a 2-stage ring fits, and
-    // inside the tower (weights not hot in cache) that measured slower.
+    // 256 x 256 keeps K steps of 32: with 64 only a 2-stage ring fits, whose
+    // single step of slack does not cover weights read from HBM inside the
+    // tower (measured slower there, though faster with cache-hot operands).
     if constexpr (BM == 128)
       if (tiles * (SPLIT ? p.splits : 1) <= 256 && k_step_ok(64))
         return launch_dl<BM, BN, EPI, SPLIT, 64>(A, M, K, B, N, bias, out, part, p, tiles, s);
