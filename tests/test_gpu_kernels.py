@@ -101,6 +101,7 @@ GEMM_SHAPES = [  # (M, N, K, what)
     (77, 192, 72, "ragged M, K tail"),
     (1000, 5120, 1280, "ragged M, 128x160 tiles"),
     (968, 6144, 640, "ragged M, 128x192 tiles"),
+    (300, 960, 640, "ragged M and N, one round of 128x128 tiles, K steps of 64"),
     (200, 6144, 24576, "ragged M, 256x256 split-K"),
     (1024, 1280, 1216, "split-K, K not a multiple of the split"),
     (20736, 5120, 1280, "FC1, 2016x2016 (256 tile)"),
@@ -130,7 +131,7 @@ def test_linear_shapes(vt, M, N, K, what):
 
 @pytest.mark.parametrize("epi", ["bf16", "gelu_tanh", "gelu_erf", "resid"])
 @pytest.mark.parametrize("M,N,K", [(200, 512, 320), (1024, 1280, 5120), (1000, 5120, 1280),
-                                   (200, 6144, 6144)])
+                                   (968, 6144, 640), (200, 6144, 6144)])
 def test_linear_epilogues(vt, epi, M, N, K):
     log(f"linear epilogue {epi} {M}x{N}x{K}")
     x = random_bf16((M, K), 7)
