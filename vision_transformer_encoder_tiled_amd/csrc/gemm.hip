@@ -320,6 +320,22 @@ __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
 
   const int fr = lane & 31, h = lane >> 5;
   const int sw = dl_swz<BK>(fr);
+  // bf16-output epilogues of the 128 x 128 and 128 x 160 tiles: this lane's
+  // bias values (features 32f + 8g + 4h .. + 3 of its wavefront's columns),
+  // loaded before the K loop so that their latency is hidden behind it (the
+  // wider tiles have no registers to spare and load them in the epilogue).
+  constexpr bool F32OUT = SPLIT || EPI == kEpiResid || EPI == kEpiF32;
+  constexpr bool PRE = !F32OUT && BM == 128 && BN <= 160;
+  uint2 bpre[PRE ? FB : 1][4];
+  if constexpr (PRE) {
+#pragma unroll
+    for (int f = 0; f < FB; ++f)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        bpre[f][g] = (bias && mw) ? *reinterpret_cast<const uint2*>(
+                                        bias + min(n0 + wn * WN + 32 * f + 8 * g + 4 * h, N - 4))
+                                  : make_uint2(0, 0);
+  }
 
   // Fragments of 32 of K (two MFMA k slices of 16): half u of step `step`
   // (u = 0 for BK = 32).  Slice q of half u is logical chunk 4u + 2q + h.
@@ -448,7 +464,6 @@ __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
   // every thread moves whole 16-byte chunks to global memory, PASS_ROWS token
   // rows at a time.  The ring is idle: the last step waited for every copy
   // and, at its barrier, for every wave's fragment reads.
-  constexpr bool F32OUT = SPLIT || EPI == kEpiResid || EPI == kEpiF32;
   constexpr int ESZ = F32OUT ? 4 : 2;
   constexpr int ROWB = BN * ESZ, CHUNKS = ROWB / 16, EPC = 16 / ESZ;
   constexpr int RING = NST * STAGE;
@@ -466,7 +481,6 @@ __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
         for (int f = 0; f < FB; ++f) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int col = n0 + wn * WN + 32 * f + 8 * g + 4 * h;
             float v0 = acc[f][t][4 * g + 0], v1 = acc[f][t][4 * g + 1];
             float v2 = acc[f][t][4 * g + 2], v3 = acc[f][t][4 * g + 3];
             const int c = (wn * WN + 32 * f + 8 * g) / EPC;  // logical chunk of feature 8g
@@ -476,7 +490,9 @@ __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
               *reinterpret_cast<float4*>(cs + r * ROWB + pc * 16) = make_float4(v0, v1, v2, v3);
             } else {
               if (bias) {
-                const uint2 bb = *reinterpret_cast<const uint2*>(bias + min(col, N - 4));
+                uint2 bb;
+                if constexpr (PRE) bb = bpre[f][g];
+                else bb = *reinterpret_cast<const uint2*>(bias + min(n0 + wn * WN + 32 * f + 8 * g + 4 * h, N - 4));
                 v0 += bflo(bb.x); v1 += bfhi(bb.x); v2 += bflo(bb.y); v3 += bfhi(bb.y);
               }
               if constexpr (EPI == kEpiGeluTanh) {
