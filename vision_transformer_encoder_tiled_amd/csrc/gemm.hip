@@ -230,7 +230,8 @@ constexpr int pass_rows(int bm, int row_bytes, int ring) {
   return r;
 }
 
-// GWM x GWN wavefronts; each owns a (BM/GWM) x (BN/GWN) block of C.
+// GWM x GWN multiplying wavefronts, each owning a (BM/GWM) x (BN/GWN) block
+// of C, plus CW wavefronts that only copy (and help store the tile).
 // K is consumed in steps of BK (32 or 64) through a ring of NST LDS stages,
 // one workgroup barrier per step.  BK = 32: 64-byte rows, NST - 1 steps in
 // flight while one is multiplied.  BK = 64: 128-byte rows (a copy reads whole
