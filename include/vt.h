@@ -362,6 +362,24 @@ vt_status vt_linear(const uint16_t* x, int32_t M, int32_t K, const uint16_t* w, 
 vt_status vt_layer_norm(const float* x, int32_t rows, int32_t width, const uint16_t* g,
                         const uint16_t* b, float eps, uint16_t* out, void* stream);
 
+/* ---------------------------------------------------------------- measurement
+ * vt_clock_probe: the core clock while other work runs (not part of the
+ * path; the benchmark uses it to state each roofline fraction also against
+ * the clock the chip actually ran at, since the published bf16 peak assumes
+ * the 2.4 GHz peak engine clock).  Enqueues on `stream` one wavefront that
+ * reads the shader-clock counter and the constant-rate real-time counter,
+ * waits until wait_us microseconds of real time have passed (a wait on a
+ * counter that always advances), and reads both again.
+ *   wait_us      1 .. 10,000,000.
+ *   out          device, 8-byte aligned, 4 x uint64 written when the kernel
+ *                ends: clock ticks at start and end, real-time ticks at
+ *                start and end.
+ *   realtime_hz  host, written during the call: the real-time counter rate.
+ * Core clock (Hz) = (out[1] - out[0]) / (out[3] - out[2]) * realtime_hz.
+ * Launch it on a second stream just before the work to be measured. */
+vt_status vt_clock_probe(int64_t wait_us, unsigned long long* out, int64_t* realtime_hz,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     declared = header_functions()
-    assert len(declared) == 24
+    assert len(declared) == 25
     assert sorted(vt.EXPORTED) == declared
     lib = ctypes.CDLL(vt.LIB_PATH)
     for name in declared:
@@ -242,6 +242,18 @@ def test_linear_and_layer_norm_validation():
     assert L.vt_layer_norm(P(FAKE), 4, 1000, P(FAKE), P(FAKE), 1e-6, P(FAKE), None) == vt.VT_ERR_UNSUPPORTED
     assert L.vt_layer_norm(P(FAKE), 4, 1280, P(FAKE), P(FAKE), 0.0, P(FAKE), None) == vt.VT_ERR_INVALID_ARG
     assert L.vt_layer_norm(None, 4, 1280, P(FAKE), P(FAKE), 1e-6, P(FAKE), None) == vt.VT_ERR_INVALID_ARG
+
+
+@needs_no_gpu
+def test_clock_probe_validation():
+    P = ctypes.c_void_p
+    hz = ctypes.c_int64(0)
+    L = vt.LIB
+    assert L.vt_clock_probe(0, P(FAKE), ctypes.byref(hz), None) == vt.VT_ERR_INVALID_ARG
+    assert L.vt_clock_probe(10_000_001, P(FAKE), ctypes.byref(hz), None) == vt.VT_ERR_INVALID_ARG
+    assert L.vt_clock_probe(1000, P(FAKE + 4), ctypes.byref(hz), None) == vt.VT_ERR_INVALID_ARG
+    assert L.vt_clock_probe(1000, None, ctypes.byref(hz), None) == vt.VT_ERR_INVALID_ARG
+    assert L.vt_clock_probe(1000, P(FAKE), None, None) == vt.VT_ERR_INVALID_ARG
 
 
 @needs_no_gpu

@@ -87,6 +87,18 @@ def test_layer_norm(vt, rows, width):
     assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -8 + 1e-5)
 
 
+# ---------------------------------------------------------------- clock probe
+def test_clock_probe(vt):
+    log("clock probe, 2 ms")
+    out = torch.zeros(4, dtype=torch.int64, device="cuda")
+    hz = vt.vt_clock_probe(2000, out)
+    torch.cuda.synchronize()
+    c0, c1, r0, r1 = out.cpu().tolist()
+    assert hz > 0 and r1 - r0 >= 2000e-6 * hz
+    f = (c1 - c0) / (r1 - r0) * hz
+    assert 0.3e9 < f < 3.0e9, f
+
+
 # ---------------------------------------------------------------- GEMM
 GEMM_SHAPES = [  # (M, N, K, what)
     (256, 1280, 1176, "patch embed, 224x224"),

@@ -27,7 +27,7 @@ EXPORTED = ("vt_config_default", "vt_status_string", "vt_last_error", "vt_versio
             "vt_linear_workspace_size", "vt_linear", "vt_layer_norm", "vt_attention_backward",
             "vt_attention_backward_workspace_size", "vt_block_backward",
             "vt_block_backward_workspace_size", "vt_tower_backward",
-            "vt_tower_backward_workspace_size")
+            "vt_tower_backward_workspace_size", "vt_clock_probe")
 
 
 class VtError(RuntimeError):
@@ -114,6 +114,7 @@ def _load():
         "vt_mean_pool": (ctypes.c_int, [_P, _P, I32, I32, _P, _P]),
         "vt_plan_patches": (ctypes.c_int, [_P, ctypes.c_size_t, I32, ctypes.c_int64, _P, _P]),
         "vt_pack_items": (ctypes.c_int, [_P, _P, I32, ctypes.c_size_t, _P, _P]),
+        "vt_clock_probe": (ctypes.c_int, [ctypes.c_int64, _P, ctypes.POINTER(ctypes.c_int64), _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -370,6 +371,15 @@ def vt_pack_items(cfg, grids, budget_bytes):
 
 def vt_mean_pool(tower, cu_seqlens, n_img, hidden, out, stream=None):
     _check(LIB.vt_mean_pool(_ptr(tower), _ptr(cu_seqlens), n_img, hidden, _ptr(out), _stream(stream)))
+
+
+def vt_clock_probe(wait_us, out, stream=None) -> int:
+    """Enqueue the core-clock probe on ``stream`` (out: 4 int64 on the device);
+    returns the real-time counter rate in Hz.  The core clock is
+    (out[1] - out[0]) / (out[3] - out[2]) * rate once the probe has ended."""
+    hz = ctypes.c_int64(0)
+    _check(LIB.vt_clock_probe(int(wait_us), _ptr(out), ctypes.byref(hz), _stream(stream)))
+    return hz.value
 
 
 def vt_layer_norm(x, rows, width, g, b, eps, out, stream=None):

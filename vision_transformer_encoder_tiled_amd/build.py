@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libvt.so")
 OBJ = os.path.join(ROOT, "_build")
 SOURCES = ["meta.hip", "permute.hip", "layernorm.hip", "gemm.hip", "attention.hip", "attention_bwd.hip",
-           "backward.hip", "vt_api.cpp"]
+           "backward.hip", "clock.hip", "vt_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 instructions are disabled: the compiler would otherwise form
 # v_pk_* fp32 ops from ordinary float code.

@@ -1140,6 +1140,25 @@ VT_API vt_status vt_mean_pool(const uint16_t* tower, const int32_t* cu_seqlens, 
   return VT_OK;
 }
 
+VT_API vt_status vt_clock_probe(int64_t wait_us, unsigned long long* out, int64_t* realtime_hz,
+                                void* stream) {
+  vt_status st;
+  if ((st = check_ptr(out, "out")) != VT_OK) return st;
+  if (!realtime_hz) return fail(VT_ERR_INVALID_ARG, "realtime_hz is NULL");
+  if ((reinterpret_cast<uintptr_t>(out) & 7u) != 0)
+    return fail(VT_ERR_INVALID_ARG, "out is not 8-byte aligned");
+  if (wait_us <= 0 || wait_us > 10000000)
+    return fail(VT_ERR_INVALID_ARG, "wait_us must be in 1 .. 10,000,000 (got %lld)", (long long)wait_us);
+  int dev = 0, khz = 0;
+  VT_TRY_HIP(hipGetDevice(&dev));
+  VT_TRY_HIP(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev));
+  if (khz <= 0) return fail(VT_ERR_UNSUPPORTED, "the device reports no real-time counter rate");
+  *realtime_hz = int64_t(khz) * 1000;
+  const uint64_t ticks = uint64_t(wait_us) * uint64_t(khz) / 1000u;
+  VT_TRY_HIP(vt::launch_clock_probe(ticks, out, static_cast<hipStream_t>(stream)));
+  return VT_OK;
+}
+
 VT_API vt_status vt_layer_norm(const float* x, int32_t rows, int32_t width, const uint16_t* g,
                                const uint16_t* b, float eps, uint16_t* out, void* stream) {
   vt_status st;

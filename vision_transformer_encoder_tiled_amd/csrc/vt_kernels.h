@@ -46,6 +46,7 @@ hipError_t launch_patchify(const uint16_t* pixels, const ImgInfo* info, const in
 // out[i] = mean of rows cu[i] .. cu[i+1]-1 of T (bf16 [N, hidden]), fp32; hidden % 128 == 0.
 hipError_t launch_mean_pool(const uint16_t* T, const int32_t* cu_seqlens, int32_t n_img,
                             int32_t hidden, float* out, hipStream_t s);
+hipError_t launch_clock_probe(uint64_t ticks, unsigned long long* out, hipStream_t s);
 hipError_t launch_row_permute(const uint16_t* src, uint16_t* dst, const int32_t* raster_index,
                               int32_t rows, int32_t width, bool scatter, hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t s);
