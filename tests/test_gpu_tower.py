@@ -117,6 +117,44 @@ def test_tower_deterministic(vt, dev):
     assert all(np.array_equal(a[k], b[k]) for k in ("tower", "merged_raw", "out"))
 
 
+def test_tower_graph_capture(vt, dev):
+    # vt_tower_forward only enqueues kernels and device copies on the caller's
+    # stream (no allocation, no memset), so it can be captured into a HIP graph;
+    # every replay, with eager work and synchronisation between replays, must
+    # give the eager call's bits.
+    wl = synth.WORKLOADS["tower_448"]
+    grids, N = list(wl.grids), wl.tokens
+    cfg = vt.config(layers=2)
+    px = dev_bits(synth.make_batch_pixels(wl), torch)
+    ws = vt.workspace(vt.vt_tower_workspace_size(cfg, grids))
+    tower = torch.empty((N, 1280), dtype=torch.int16, device="cuda")
+    mraw = torch.empty((N // 4, 5120), dtype=torch.int16, device="cuda")
+    out = torch.empty((N // 4, 6144), dtype=torch.int16, device="cuda")
+    step = lambda: vt.vt_tower_forward(cfg, px, grids, dev[1], tower, mraw, out, ws)
+    step()
+    torch.cuda.synchronize()
+    ref = [tower.clone(), mraw.clone(), out.clone()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for i in range(3):
+        log(f"graph replay {i}")
+        for t in (tower, mraw, out):
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip((tower, mraw, out), ref)), i
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+
+
 # ---------------------------------------------------------------- batches
 @pytest.mark.parametrize("name,sample", [("tower_448x16", [0, 11]), ("tower_mixed8", None)])
 def test_tower_batched_sampled_images(vt, weights, dev, name, sample):
