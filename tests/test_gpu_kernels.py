@@ -311,6 +311,22 @@ def test_attention_2016_sampled(vt):
     assert err <= 2e-3
 
 
+def test_attention_4096_sampled(vt):
+    # The pages' ceiling case: a 4096x4096 image, 65,536 patches, for which the
+    # untiled per-head score buffers they describe take 26.7 GB.  The tiled
+    # call's whole workspace stays O(N); sampled query rows against the oracle.
+    grids = [(1, 256, 256)]
+    N = 65536
+    ws_bytes = vt.vt_block_workspace_size(vt.config(), N, 1, N)
+    log(f"attention 4096x4096 ({N} tokens): block workspace {ws_bytes / 2**30:.2f} GiB")
+    assert ws_bytes < 8 * 2**30
+    rows = np.unique(np.r_[0:32, N - 32:N, rng(8).integers(0, N, 96)])
+    got, want = attention_case(vt, grids, 9, rows=rows)
+    err = np.max(np.abs(got - want))
+    log(f"attention 4096 ({N} tokens): max abs err {err:.3e}")
+    assert err <= 2e-3
+
+
 # ---------------------------------------------------------------- one block
 @pytest.mark.parametrize("affine", ["canonical", "random"])
 def test_block_224(vt, affine):
