@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="tower_448", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--secondary", default="tower_2016", help="second workload ('' to skip)")
-    ap.add_argument("--more", default="tower_clip16,tower_448x16,tower_mixed8",
+    ap.add_argument("--more", default="tower_clip16,tower_448x16,tower_mixed8,tower_4096",
                     help="comma-separated further workloads, throughput only ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",

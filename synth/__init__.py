@@ -197,6 +197,9 @@ WORKLOADS = {
     "tower_clip16": Workload("tower_clip16", ((8, 32, 32),), (6,), LAYERS, True,
                              "one 16-frame 448x448 clip (8 temporal patches of 32x32) through the "
                              "tower + projector"),
+    "tower_4096": Workload("tower_4096", ((1, 256, 256),), (7,), LAYERS, True,
+                           "one 4096x4096 image (256x256 patches, 65,536 tokens) through the tower + "
+                           "projector"),
 }
 
 
