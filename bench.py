@@ -307,6 +307,22 @@ def attention_roofline(vt, torch, grids, iters, traffic_profile=None):
                     "plus the per-call schedule and RoPE-table kernels"}
 
 
+def layernorm_roofline(vt, torch, rows, iters):
+    """vt_layer_norm (a3/a7) on rows x 1280: 7,680 algorithmic bytes per row
+    (the fp32 row read, the bf16 row written) per launch time, against HBM."""
+    g = np.random.Generator(np.random.PCG64(3))
+    x = torch.from_numpy(g.standard_normal((rows, 1280), dtype=np.float32)).cuda()
+    gam = torch.from_numpy(synth.bf16_bits(np.ones(1280, np.float32)).view(np.int16)).cuda()
+    bet = torch.zeros(1280, dtype=torch.int16, device="cuda")
+    out = torch.empty((rows, 1280), dtype=torch.int16, device="cuda")
+    fn = lambda: vt.vt_layer_norm(x, rows, 1280, gam, bet, 1e-6, out)
+    t = time_kernel(torch, fn, iters)
+    gbs = rows * 7680 / t / 1e9
+    return {"kernel": "layer_norm_kernel (%d x 1280, fp32 in, bf16 out)" % rows, "bound": "hbm",
+            "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+            "bytes_per_launch": rows * 7680, "avg_launch_us": t * 1e6}
+
+
 def attention_backward_line(vt, torch, grids, iters):
     fn, flops = attention_backward_case(vt, torch, grids)
     t = time_kernel(torch, fn, iters)
@@ -448,6 +464,7 @@ def main():
                 vt, torch, list(wl2.grids), max(3, a.kernel_iters // 4),
                 "attention_2016_traffic" if wl2.name == "tower_2016" else None),
             "gemm_roofline": gemm_roofline(vt, torch, wl2.tokens, max(3, a.kernel_iters // 4)),
+            "layernorm_roofline": layernorm_roofline(vt, torch, wl2.tokens, a.kernel_iters),
         }
         if not a.no_backward:
             res["secondary"]["attention_backward"] = attention_backward_line(

@@ -42,9 +42,13 @@ __global__ void __launch_bounds__(256) patchify_kernel(const uint16_t* __restric
   const uint32_t* src1 = reinterpret_cast<const uint32_t*>(pix + at + f1);
   uint32_t v0[7], v1[7];
 #pragma unroll
-  for (int i = 0; i < 7; ++i) {
-    v0[i] = src0[i];
-    v1[i] = src1[i];
+  for (int i = 0; i < 7; ++i) v0[i] = src0[i];
+  if (in.t == 1) {  // a still image: both temporal slots hold the same frame
+#pragma unroll
+    for (int i = 0; i < 7; ++i) v1[i] = v0[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 7; ++i) v1[i] = src1[i];
   }
   uint32_t* dst0 = reinterpret_cast<uint32_t*>(X + int64_t(tok) * 1176 + (ch * 2 + 0) * 196 + py * 14);
   uint32_t* dst1 = reinterpret_cast<uint32_t*>(X + int64_t(tok) * 1176 + (ch * 2 + 1) * 196 + py * 14);
