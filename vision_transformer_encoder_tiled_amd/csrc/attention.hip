@@ -100,7 +100,10 @@ __global__ void __launch_bounds__(320) attn_pack_kernel(
     const float2* __restrict__ rope_cs, int32_t axis_code, float q_scale_log2,
     uint16_t* __restrict__ qpk, uint16_t* __restrict__ kv) {
   __shared__ __align__(16) uint16_t vs[HD * BKV];  // V^T [dim][slot], 128 B rows
-  const int T = blockIdx.x, head = blockIdx.y;
+  // Block b = (key tile b / heads, head b % heads): the heads of one tile go
+  // out together, so the 128-byte lines that two heads' 160-byte q/k/v
+  // segments share are read from memory once.
+  const int T = blockIdx.x / heads, head = blockIdx.x % heads;
   const int2 desc = kdesc[T];
   if (desc.x < 0) return;
   const int k = threadIdx.x / 5, c = threadIdx.x % 5;
@@ -639,8 +642,8 @@ hipError_t launch_attention(const uint16_t* qkv, const int32_t* pos_thw, const i
                             int32_t heads, int32_t n_pos, int32_t axis_code, const float2* rope_cs,
                             float q_scale_log2, int32_t variant, uint16_t* qpk, uint16_t* kv,
                             void* out, bool out_f32, float* lse, hipStream_t s) {
-  hipLaunchKernelGGL(attn_pack_kernel, dim3(max_ktiles, heads), dim3(320), 0, s, qkv, pos_thw,
-                     kdesc, heads, n_pos, rope_cs, axis_code, q_scale_log2, qpk, kv);
+  hipLaunchKernelGGL(attn_pack_kernel, dim3(unsigned(int64_t(max_ktiles) * heads)), dim3(320), 0, s,
+                     qkv, pos_thw, kdesc, heads, n_pos, rope_cs, axis_code, q_scale_log2, qpk, kv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (variant) {

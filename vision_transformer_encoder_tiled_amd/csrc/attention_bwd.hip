@@ -145,7 +145,7 @@ __global__ void __launch_bounds__(320) bwd_pack_k_kernel(
     int32_t heads, int32_t n_pos, const float2* __restrict__ rope_cs, int32_t axis_code,
     char* __restrict__ kimg) {
   __shared__ __align__(16) uint16_t ts[HD * BT];
-  const int T = blockIdx.x, head = blockIdx.y;
+  const int T = blockIdx.x / heads, head = blockIdx.x % heads;  // the heads of a tile together
   const int2 desc = kdesc[T];
   if (desc.x < 0) return;
   const int t = threadIdx.x / 5, c = threadIdx.x % 5;
@@ -182,7 +182,7 @@ __global__ void __launch_bounds__(320) bwd_pack_q_kernel(
     float q_scale_log2, char* __restrict__ qimg) {
   __shared__ __align__(16) uint16_t ts[2][HD * BT];
   __shared__ float dpart[BT * 5];
-  const int T = blockIdx.x, head = blockIdx.y;
+  const int T = blockIdx.x / heads, head = blockIdx.x % heads;  // the heads of a tile together
   const int2 desc = kdesc[T];
   if (desc.x < 0) return;
   const int t = threadIdx.x / 5, c = threadIdx.x % 5;
@@ -501,9 +501,10 @@ hipError_t launch_attention_backward(const uint16_t* qkv, const uint16_t* dout, 
   if (a1 != hipSuccess) return a1;
   if (a2 != hipSuccess) return a2;
   if (a3 != hipSuccess) return a3;
-  hipLaunchKernelGGL(bwd_pack_k_kernel, dim3(max_ktiles, heads), dim3(320), 0, s, qkv, pos_thw, kdesc,
+  const dim3 pack_grid(unsigned(int64_t(max_ktiles) * heads));
+  hipLaunchKernelGGL(bwd_pack_k_kernel, pack_grid, dim3(320), 0, s, qkv, pos_thw, kdesc,
                      heads, n_pos, rope_cs, axis_code, kimg);
-  hipLaunchKernelGGL(bwd_pack_q_kernel, dim3(max_ktiles, heads), dim3(320), 0, s, qkv, dout, o, lse,
+  hipLaunchKernelGGL(bwd_pack_q_kernel, pack_grid, dim3(320), 0, s, qkv, dout, o, lse,
                      pos_thw, kdesc, heads, n_pos, rope_cs, axis_code, q_scale_log2, qimg);
   const unsigned blocks = unsigned(int64_t(max_btiles) * heads);
   const float rsqrt_hd = 1.0f / sqrtf(float(HD));
