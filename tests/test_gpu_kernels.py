@@ -87,6 +87,30 @@ def test_layer_norm(vt, rows, width):
     assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -8 + 1e-5)
 
 
+def test_layer_norm_many_rows(vt):
+    """Width 1280 over 2^20 + 37 rows (a grid of 262,154 workgroups), checked
+    on sampled rows: 4099 distinct seeded rows tiled over the whole input, so
+    that an output written from the wrong row (off by a multiple of 2^k) lands
+    on different content, 4099 being odd and prime."""
+    rows, width, distinct = (1 << 20) + 37, 1280, 4099
+    log(f"layer_norm {rows}x{width}")
+    x = rng(4).standard_normal((distinct, width), dtype=np.float32) * 2 - 0.25
+    g = synth.bf16_bits(bf16_f32(random_bf16(width, 5, 0.2)) + 1)
+    b = random_bf16(width, 6, 0.1)
+    reps = -(-rows // distinct)
+    xd = torch.from_numpy(x).cuda().repeat(reps, 1)[:rows].contiguous()
+    out = torch.empty((rows, width), dtype=torch.int16, device="cuda")
+    vt.vt_layer_norm(xd, rows, width, dev_bits(g, torch), dev_bits(b, torch), 1e-6, out)
+    torch.cuda.synchronize()
+    del xd
+    want_all = oracle.layer_norm(x, bf16_f32(g), bf16_f32(b), 1e-6)
+    pick = [0, 1, distinct, (1 << 20) - 1, 1 << 20, (1 << 20) + 1, rows - 1] + \
+        list(rng(7).integers(0, rows, 40))
+    got = bf16_f32(host_bits(out[torch.tensor(pick, device="cuda")]))
+    want = want_all[np.array(pick) % distinct]
+    assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -8 + 1e-5)
+
+
 # ---------------------------------------------------------------- clock probe
 def test_clock_probe(vt):
     log("clock probe, 2 ms")
