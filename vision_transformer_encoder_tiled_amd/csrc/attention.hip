@@ -471,7 +471,11 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(
 // 2-stage ring (50 KB of LDS): 126 VGPRs.  4 wavefronts = 128 queries, three
 // workgroups per CU (LDS-bound), or 8 wavefronts = 256 queries sharing one
 // K/V stream, two workgroups per CU: four wavefronts per SIMD.  WPE is the
-// wavefronts per SIMD the register budget is set for.
+// wavefronts per SIMD the register budget is set for.  A wavefront raises
+// its issue priority (s_setprio) over its two MFMA sections, so that of the
+// wavefronts sharing a SIMD, one with a matrix product ready goes ahead of
+// one in the softmax arithmetic and the matrix unit idles less (about 1% at
+// 20,736 tokens; scheduling only, the results are the same bits).
 template <int NW, int NST, int WPE>
 __global__ void __launch_bounds__(64 * NW, WPE) attention_lean_kernel(
     const uint16_t* __restrict__ qpk, const uint16_t* __restrict__ kv,
@@ -524,6 +528,7 @@ __global__ void __launch_bounds__(64 * NW, WPE) attention_lean_kernel(
     if (t + NST - 1 < ntiles) issue(t + NST - 1);
     const char* st = lds + (t % NST) * STAGE_BYTES;
     f32x16_t sc[2];
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
@@ -538,6 +543,7 @@ __global__ void __launch_bounds__(64 * NW, WPE) attention_lean_kernel(
         sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
             *reinterpret_cast<const f16x8_t*>(st + koff + b * 32 * KROW * 2 + 32 * sl), qfrag[sl], sc[b], 0,
             0, 0);
+    __builtin_amdgcn_s_setprio(0);
     const int kt = kbeg + t * BKV;
     if (kt + BKV > kend) {
 #pragma unroll
@@ -571,6 +577,7 @@ __global__ void __launch_bounds__(64 * NW, WPE) attention_lean_kernel(
         for (int e = 0; e < 16; ++e) sc[b][e] -= delta;
     }
     const char* vst = st + voff;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       f16x8_t pf[2];
@@ -584,6 +591,7 @@ __global__ void __launch_bounds__(64 * NW, WPE) attention_lean_kernel(
               *reinterpret_cast<const f16x8_t*>(vst + 32 * d * VROW * 2 + 32 * (2 * b + h)), pf[h], acc[d], 0,
               0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
   const float l_half0 = __shfl(acc[2][8], ln, 64);
   const float inv = 1.0f / l_half0;
