@@ -318,3 +318,35 @@ def test_tower_tiny_items(vt, weights, dev):
     assert err <= 1e-2
     assert cos.min() >= 0.999
     assert np.array_equal(res["merged_raw"], res["tower"][oracle.merge_map(grids)].reshape(-1, 5120))
+
+
+@pytest.mark.parametrize("grids,seeds", [
+    ([(1, 2, 2), (1, 2, 4), (1, 6, 10), (2, 4, 4), (1, 2, 2)], [81, 82, 83, 84, 85]),
+    ([(1, 16, 16)], [86]),
+])
+def test_tower_fused_equals_blockwise_small(vt, weights, dev, grids, seeds):
+    """At 108 and 256 tokens the residual GEMMs run split-K (3 splits for O,
+    12 or 13 for FC2, the latter summed by the any-count loop of the fused
+    reduce + LayerNorm).  The tower entry point, which fuses each reduction
+    with the next LayerNorm, gives the same tower output bits as patch embed
+    followed by the blocks one call at a time, whose LayerNorms run alone."""
+    px = item_pixels(grids, seeds)
+    L = 3
+    N = sum(t * h * w for t, h, w in grids)
+    max_seq = max(t * h * w for t, h, w in grids)
+    d, _ = dev
+    res = gpu_tower(vt, vt.TowerWeights(d, L), grids, px, layers=L)
+    cfg = vt.config(layers=L)
+    ws = vt.workspace(vt.vt_tower_workspace_size(cfg, grids))
+    R = torch.empty((N, 1280), dtype=torch.float32, device="cuda")
+    vt.vt_patch_embed(cfg, dev_bits(px, torch), grids, d["patch_w"], d["patch_b"], R, ws)
+    cu = torch.empty(len(grids) + 1, dtype=torch.int32, device="cuda")
+    pos = torch.empty((N, 3), dtype=torch.int32, device="cuda")
+    vt.vt_build_metadata(grids, cu, pos)
+    bws = vt.workspace(vt.vt_block_workspace_size(cfg, N, len(grids), max_seq))
+    log(f"block by block, {L} layers, {N} tokens")
+    for l in range(L):
+        vt.vt_block_forward(cfg, R, vt.block_weights(d, f"l{l}."), cu, pos, len(grids), N, max_seq, bws)
+    got = np.empty((N, 1280), np.float32)
+    got[window_to_raster(grids)] = R.cpu().numpy()
+    assert np.array_equal(synth.bf16_bits(got), res["tower"])
