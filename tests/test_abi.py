@@ -280,3 +280,34 @@ def test_tower_validation():
     assert L.vt_tower_forward(ctypes.byref(cfg1), P(FAKE), g, n, ctypes.byref(tw), P(FAKE), None,
                               None, P(FAKE), need, None) == vt.VT_ERR_INVALID_ARG
     assert vt.LIB.vt_status_string(3) == b"VT_ERR_WORKSPACE"
+
+
+def test_package_fails_loudly_without_library(tmp_path):
+    """A copy of the package without libvt.so refuses to import (no CPU
+    fallback exists to route to)."""
+    import shutil
+    import subprocess
+    import sys
+    src = os.path.dirname(vt.__file__)
+    dst = tmp_path / "vision_transformer_encoder_tiled_amd"
+    dst.mkdir()
+    for f in os.listdir(src):
+        if f.endswith(".py"):
+            shutil.copy(os.path.join(src, f), dst / f)
+    r = subprocess.run([sys.executable, "-c", "import vision_transformer_encoder_tiled_amd"],
+                       cwd=tmp_path, capture_output=True, text=True, timeout=120,
+                       env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert r.returncode != 0
+    assert "libvt.so is missing" in r.stderr
+
+
+def test_package_does_not_load_the_oracle():
+    """Importing the library binding loads no oracle module: the product path
+    never reaches the CPU oracle."""
+    import subprocess
+    import sys
+    code = ("import sys, vision_transformer_encoder_tiled_amd; "
+            "print(sorted(m for m in sys.modules if m == 'oracle' or m.startswith('oracle.')))")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "[]"
