@@ -267,6 +267,10 @@ __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool mw = CW == 0 || wave < NW;  // a multiplying wavefront
+  // Copy-only wavefronts issue at raised priority: the copies set the pace
+  // of these tiles, and each shares its SIMD with one multiplying wavefront
+  // (FC1 at 1,024 tokens: 22.3 -> 21.9 us; scheduling only, same bits).
+  if (!mw) __builtin_amdgcn_s_setprio(1);
   const int wm = wave / GWN, wn = wave % GWN;
   int tm, tn;
   xcd_group_tile((M + BM - 1) / BM, (N + BN - 1) / BN, &tm, &tn);
