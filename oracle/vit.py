@@ -318,18 +318,23 @@ def mean_pool(T: np.ndarray, grids) -> np.ndarray:
 
 
 def tower_forward(pixels_bits, grids, weight_bits, cfg: Config = None, n_layers=None,
-                  keep_layers=False, projector_on=True):
-    """Full forward pass in fp32.  Returns a dict with
+                  keep_layers=False, projector_on=True, dtype=np.float32):
+    """Full forward pass, fp32 by default.  Returns a dict with
     ``tower`` [N, d] (last_hidden_state, raster order), ``merged_raw`` [N/4, 4d],
     ``out`` [N/4, proj] (if the projector runs) and ``layers`` (list of the
-    residual after each block, if requested)."""
+    residual after each block, if requested).
+
+    Block l reads the weights named ``l{l}.*``; the projector takes the last
+    block's output.  ``dtype`` = np.float64 runs the same steps on the exactly
+    decoded bf16 values in float64 (used to pin this composition against an
+    independent float64 implementation)."""
     cfg = cfg or Config()
-    W = weights_f32(weight_bits)
+    W = {k: v.astype(dtype, copy=False) for k, v in weights_f32(weight_bits).items()}
     L = cfg.layers if n_layers is None else n_layers
-    imgs = split_pixels(bf16_to_f32(pixels_bits), grids)
+    imgs = [x.astype(dtype, copy=False) for x in split_pixels(bf16_to_f32(pixels_bits), grids)]
     pos = positions(grids)
     cu = cu_seqlens(grids)
-    R = patch_embed(imgs, W, grids).astype(np.float32)
+    R = patch_embed(imgs, W, grids).astype(dtype)
     layers = []
     for i in range(L):
         R = block_forward(R, W, pos, cu, cfg, prefix=f"l{i}.")

@@ -483,3 +483,110 @@ def test_mean_pool_closed_forms():
     np.testing.assert_allclose(oracle.mean_pool(T, grids), want, rtol=1e-15)
     perm = np.concatenate([cu[i] + rng(i).permutation(cu[i + 1] - cu[i]) for i in range(3)])
     np.testing.assert_allclose(oracle.mean_pool(T[perm], grids), want, rtol=1e-15)
+
+
+# ---------------------------------------------------------------- the whole tower
+def _torch_tower_f64(px_bits, grids, w_bits, cfg, n_layers):
+    """An independent float64 implementation of the whole forward pass, from
+    the pages' description (MiniMax-M3-Vision README, Architecture table:
+    Conv3d patch embed with temporal patch 2, pre-LN blocks with 3D RoPE,
+    2x2 merge, the four-Linear projector) and torch library routines:
+    conv3d with kernel = stride = (2, 14, 14) for the patch embed,
+    layer_norm, scaled_dot_product_attention per item, GELU(tanh).  It
+    shares no step with the oracle: bf16 decoding, pixel splitting,
+    positions, RoPE angles and the 2x2 gather are written out here."""
+    F = torch.nn.functional
+
+    def dec(bits):  # bf16 bits -> float64: the 16 bits are the high half of an fp32 word
+        return torch.from_numpy(bits.astype(np.int32) << 16).view(torch.float32).double()
+
+    W = {k: dec(v) for k, v in w_bits.items()}
+    pix = dec(px_bits)
+    d, H, hd = cfg.hidden, cfg.heads, cfg.head_dim
+    half = hd // 2
+    kconv = W["patch_w"].reshape(d, 3, 2, 14, 14)
+    tokens, pos, off = [], [], 0
+    for t, h, w in grids:
+        nf = 1 if t == 1 else 2 * t
+        n = nf * 3 * 14 * h * 14 * w
+        frames = pix[off:off + n].reshape(nf, 3, 14 * h, 14 * w)
+        off += n
+        if nf == 1:  # a still image fills the temporal patch with its one frame twice
+            frames = torch.cat([frames, frames])
+        y = F.conv3d(frames.permute(1, 0, 2, 3)[None], kconv, W["patch_b"], stride=(2, 14, 14))
+        tokens.append(y[0].permute(1, 2, 3, 0).reshape(-1, d))  # (t, row, col) raster
+        tt, rr, cc = torch.meshgrid(torch.arange(t), torch.arange(h), torch.arange(w), indexing="ij")
+        pos.append(torch.stack([tt.reshape(-1), rr.reshape(-1), cc.reshape(-1)], 1))
+    R = torch.cat(tokens)
+    pos = torch.cat(pos).double()
+    # rotation angle of pair j: the position on its axis times theta^(-k/n),
+    # k = index of the pair within that axis's n pairs
+    ang = torch.cat([pos[:, a:a + 1] * cfg.rope_theta ** (-torch.arange(n, dtype=torch.float64) / n)
+                     for a, n in enumerate(cfg.rope_sections)], 1)[:, None, :]
+    cos, sin = torch.cos(ang), torch.sin(ang)
+
+    def rope(x):
+        z = torch.complex(x[..., :half], x[..., half:]) * torch.complex(cos, sin)
+        return torch.cat([z.real, z.imag], -1)
+
+    sizes = [t * h * w for t, h, w in grids]
+    layers = []
+    for l in range(n_layers):
+        g = lambda k: W[f"l{l}.{k}"]
+        x = F.layer_norm(R, (d,), g("ln1_g"), g("ln1_b"), cfg.ln_eps)
+        qkv = F.linear(x, g("w_qkv"), g("b_qkv")).reshape(-1, 3, H, hd)
+        q, k, v = rope(qkv[:, 0]), rope(qkv[:, 1]), qkv[:, 2]
+        att = torch.cat([F.scaled_dot_product_attention(qi.transpose(0, 1), ki.transpose(0, 1),
+                                                        vi.transpose(0, 1)).transpose(0, 1)
+                         for qi, ki, vi in zip(q.split(sizes), k.split(sizes), v.split(sizes))])
+        R = R + F.linear(att.reshape(-1, d), g("w_o"), g("b_o"))
+        y = F.layer_norm(R, (d,), g("ln2_g"), g("ln2_b"), cfg.ln_eps)
+        R = R + F.linear(F.gelu(F.linear(y, g("w_fc1"), g("b_fc1")), approximate="tanh"), g("w_fc2"), g("b_fc2"))
+        layers.append(R)
+    Y = F.linear(F.gelu(F.linear(R, W["p_w1"], W["p_b1"]), approximate="tanh"), W["p_w2"], W["p_b2"])
+    raw, Z, base = [], [], 0
+    for t, h, w in grids:
+        for tt in range(t):
+            for r in range(h // 2):
+                for c in range(w // 2):
+                    ids = [base + tt * h * w + (2 * r + dr) * w + 2 * c + dc for dr in (0, 1) for dc in (0, 1)]
+                    raw.append(torch.cat([R[i] for i in ids]))
+                    Z.append(torch.cat([Y[i] for i in ids]))
+        base += t * h * w
+    Z = torch.stack(Z)
+    out = F.linear(F.gelu(F.linear(Z, W["p_w3"], W["p_b3"]), approximate="tanh"), W["p_w4"], W["p_b4"])
+    return {"tower": R.numpy(), "merged_raw": torch.stack(raw).numpy(), "out": out.numpy(),
+            "layers": [x.numpy() for x in layers]}
+
+
+def test_tower_forward_composition_against_independent_float64():
+    """oracle.tower_forward (run in float64) against the independent torch
+    float64 tower above, on two still images and a clip with a 3-layer tower
+    whose layers all differ: the composition (patch rows of several items
+    concatenated in item order, block l reading the l-th weights, blocks in
+    order, the projector on the last block's output, the 2x2 gather) agrees
+    to rounding.  The same comparison fails for a tower whose first two layers
+    are swapped, and for one missing its last layer."""
+    cfg = tiny_cfg(layers=3)
+    L = 3
+    W = {k: synth.bf16_bits(v.astype(np.float32)) for k, v in tiny_weights(cfg, n_layers=L, seed=91).items()}
+    grids = [(1, 4, 6), (2, 2, 4), (1, 2, 2)]
+    px = np.concatenate([synth.make_pixels(4, 6, 92).reshape(-1), synth.make_clip(2, 2, 4, 93).reshape(-1),
+                         synth.make_pixels(2, 2, 94).reshape(-1)])
+    want = _torch_tower_f64(px, grids, W, cfg, L)
+    got = oracle.tower_forward(px, grids, W, cfg, n_layers=L, keep_layers=True, dtype=np.float64)
+    for key in ("tower", "merged_raw", "out"):
+        np.testing.assert_allclose(got[key], want[key], rtol=1e-10, atol=1e-12, err_msg=key)
+    for l in range(L):
+        np.testing.assert_allclose(got["layers"][l], want["layers"][l], rtol=1e-10, atol=1e-12)
+    # the fp32 default follows the same composition to fp32 rounding
+    f32 = oracle.tower_forward(px, grids, W, cfg, n_layers=L)
+    assert np.linalg.norm(f32["out"] - want["out"]) <= 1e-5 * np.linalg.norm(want["out"])
+    # planted composition mistakes are caught
+    Wsw = dict(W)
+    for k in synth.BLOCK_TENSORS:
+        Wsw[f"l0.{k}"], Wsw[f"l1.{k}"] = W[f"l1.{k}"], W[f"l0.{k}"]
+    bad = oracle.tower_forward(px, grids, Wsw, cfg, n_layers=L, dtype=np.float64)
+    assert np.linalg.norm(bad["tower"] - want["tower"]) > 1e-3 * np.linalg.norm(want["tower"])
+    short = oracle.tower_forward(px, grids, W, cfg, n_layers=L - 1, dtype=np.float64)
+    assert np.linalg.norm(short["out"] - want["out"]) > 1e-3 * np.linalg.norm(want["out"])
