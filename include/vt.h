@@ -17,8 +17,9 @@
  * Memory.    Every device pointer is owned by the caller.  The library never
  *            allocates or frees device memory; scratch comes from the caller's
  *            workspace (`ws`, `ws_bytes`), sized by the *_workspace_size
- *            functions.  Host arrays (the grid list) are read during the call
- *            and not kept.
+ *            functions -- except vt_attention_varlen_noalloc, whose scratch is
+ *            a fixed array inside the library.  Host arrays (the grid list)
+ *            are read during the call and not kept.
  * Dtypes.    "bf16" tensors are uint16 bit patterns of bfloat16.  Weights are
  *            bf16 in PyTorch Linear layout [out, in] (row-major, the input
  *            dimension contiguous).  The residual stream is fp32.
@@ -40,7 +41,9 @@
  *            code, with details in vt_last_error() (thread-local).  Launch
  *            failures return VT_ERR_HIP.  Nothing is clamped silently.
  * Threads.   Calls are reentrant; there is no global mutable state other
- *            than the thread-local error string.
+ *            than the thread-local error string, and the per-GPU scratch
+ *            array of vt_attention_varlen_noalloc (with its device address,
+ *            cached per GPU under a lock).
  */
 #ifndef VT_H
 #define VT_H
@@ -182,6 +185,32 @@ vt_status vt_attention_varlen(const vt_config* cfg, const uint16_t* qkv, const i
                               const int32_t* pos_thw, int32_t n_img, int32_t total_tokens,
                               int32_t max_seqlen, void* out, vt_dtype out_dtype, void* ws,
                               size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- no allocation
+ * For callers that can neither allocate device memory nor pass a workspace:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  vt_attention_varlen_noalloc computes exactly what
+ * vt_attention_varlen computes (the same kernels, the same bits) with its
+ * scratch -- the attention schedule, the rotated fp16 Q, the K/V tile images
+ * and the RoPE table, about 8.5 KB per token plus 384 KB per image at 16
+ * heads -- in one fixed device array of VT_NOALLOC_SCRATCH_BYTES inside the
+ * library.  Each GPU the library runs on holds its own copy of that array
+ * from the first use of the library on that GPU until the process ends.
+ *   Arguments, layouts and errors as vt_attention_varlen, without ws.
+ *   A call whose scratch would exceed the array returns VT_ERR_WORKSPACE
+ *   (one image fits up to about 7,300 tokens; 448x448 images, up to 7 per
+ *   call).
+ * The call enqueues kernels only: no hipMalloc, hipFree or memset.  Its
+ * first call on each GPU resolves the array's device address
+ * (hipGetSymbolAddress); make that first call outside graph capture.
+ * Every call on one GPU uses the same array and leaves its contents there;
+ * nothing in it needs to start at zero.  Calls that overlap on one GPU
+ * (on different streams, or from threads without ordering) race on it. */
+#define VT_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+vt_status vt_attention_varlen_noalloc(const vt_config* cfg, const uint16_t* qkv,
+                                      const int32_t* cu_seqlens, const int32_t* pos_thw,
+                                      int32_t n_img, int32_t total_tokens, int32_t max_seqlen,
+                                      void* out, vt_dtype out_dtype, void* stream);
 
 /* Gradient of vt_attention_varlen with respect to its qkv input ("v2_loaders
  * FINDINGS", section 3: the towers are differentiable; the probe's backward

@@ -30,7 +30,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     declared = header_functions()
-    assert len(declared) == 25
+    assert len(declared) == 26
     assert sorted(vt.EXPORTED) == declared
     lib = ctypes.CDLL(vt.LIB_PATH)
     for name in declared:
@@ -311,3 +311,30 @@ def test_package_does_not_load_the_oracle():
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     assert r.stdout.strip() == "[]"
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    m = re.search(r"#define\s+VT_NOALLOC_SCRATCH_BYTES\s+\((\d+)u \* (\d+)u \* (\d+)u\)", open(HEADER).read())
+    assert m and int(m[1]) * int(m[2]) * int(m[3]) == vt.VT_NOALLOC_SCRATCH_BYTES
+
+
+@needs_no_gpu
+def test_attention_noalloc_validation():
+    """Rejections happen on the host before the fixed array's address is
+    looked up: sizes whose attention scratch exceeds the array, and the
+    argument errors of vt_attention_varlen."""
+    cfg = vt.config()
+    P = lambda v: None if v is None else ctypes.c_void_p(v)
+
+    def call(qkv=FAKE, out=FAKE, n_img=1, total=64, max_seq=64, dtype=vt.VT_BF16, cfg=cfg):
+        return vt.LIB.vt_attention_varlen_noalloc(ctypes.byref(cfg), P(qkv), P(FAKE), P(FAKE), n_img, total,
+                                                  max_seq, P(out), dtype, None)
+    assert call(total=8192, max_seq=8192) == vt.VT_ERR_WORKSPACE       # one image of 8,192 tokens
+    assert "fixed array" in vt.last_error()
+    assert call(n_img=8, total=8192, max_seq=1024) == vt.VT_ERR_WORKSPACE   # eight 448x448 images
+    assert call(qkv=None) == vt.VT_ERR_INVALID_ARG
+    assert call(out=FAKE + 8) == vt.VT_ERR_INVALID_ARG
+    assert call(n_img=0) == vt.VT_ERR_INVALID_ARG
+    assert call(max_seq=65) == vt.VT_ERR_INVALID_ARG
+    assert call(dtype=7) == vt.VT_ERR_INVALID_ARG
+    assert call(cfg=vt.config(head_dim=64, hidden=1024, rope_pairs=(0, 16, 16))) == vt.VT_ERR_UNSUPPORTED

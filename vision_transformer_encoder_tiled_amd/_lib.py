@@ -19,6 +19,7 @@ VT_OK, VT_ERR_INVALID_ARG, VT_ERR_UNSUPPORTED, VT_ERR_WORKSPACE, VT_ERR_HIP = ra
 VT_BF16, VT_FP32 = 0, 1
 VT_ORDER_WINDOW, VT_ORDER_RASTER = 0, 1
 VT_EPI_BF16, VT_EPI_GELU_TANH_BF16, VT_EPI_GELU_ERF_BF16, VT_EPI_RESID_F32, VT_EPI_F32 = range(5)
+VT_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 EXPORTED = ("vt_config_default", "vt_status_string", "vt_last_error", "vt_version",
             "vt_tower_workspace_size", "vt_block_workspace_size", "vt_build_metadata",
@@ -27,7 +28,7 @@ EXPORTED = ("vt_config_default", "vt_status_string", "vt_last_error", "vt_versio
             "vt_linear_workspace_size", "vt_linear", "vt_layer_norm", "vt_attention_backward",
             "vt_attention_backward_workspace_size", "vt_block_backward",
             "vt_block_backward_workspace_size", "vt_tower_backward",
-            "vt_tower_backward_workspace_size", "vt_clock_probe")
+            "vt_tower_backward_workspace_size", "vt_clock_probe", "vt_attention_varlen_noalloc")
 
 
 class VtError(RuntimeError):
@@ -92,6 +93,8 @@ def _load():
         "vt_patch_embed": (ctypes.c_int, [cfgp, _P, gridp, I32, _P, _P, _P, _P, SZ, _P]),
         "vt_attention_varlen": (ctypes.c_int, [cfgp, _P, _P, _P, I32, I32, I32, _P, ctypes.c_int,
                                                _P, SZ, _P]),
+        "vt_attention_varlen_noalloc": (ctypes.c_int, [cfgp, _P, _P, _P, I32, I32, I32, _P, ctypes.c_int,
+                                                       _P]),
         "vt_attention_backward": (ctypes.c_int, [cfgp, _P, _P, _P, I32, I32, I32, _P, _P,
                                                  ctypes.c_int, _P, SZ, _P]),
         "vt_attention_backward_workspace_size": (SZ, [cfgp, I32, I32, I32]),
@@ -212,6 +215,13 @@ def vt_attention_varlen(cfg, qkv, cu_seqlens, pos_thw, n_img, total_tokens, max_
     _check(LIB.vt_attention_varlen(ctypes.byref(cfg), _ptr(qkv), _ptr(cu_seqlens), _ptr(pos_thw),
                                    n_img, total_tokens, max_seqlen, _ptr(out), out_dtype, _ptr(ws),
                                    ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def vt_attention_varlen_noalloc(cfg, qkv, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen, out,
+                                out_dtype, stream=None):
+    _check(LIB.vt_attention_varlen_noalloc(ctypes.byref(cfg), _ptr(qkv), _ptr(cu_seqlens), _ptr(pos_thw),
+                                           n_img, total_tokens, max_seqlen, _ptr(out), out_dtype,
+                                           _stream(stream)))
 
 
 def vt_attention_backward_workspace_size(cfg, total_tokens, n_img, max_seqlen) -> int:

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -400,6 +401,15 @@ size_t block_ws_bytes(const vt_config* cfg, int64_t N, int32_t n_img, int32_t n_
   return c.off;
 }
 
+// The attention step's own buffers (schedule, packed Q, tile images, RoPE
+// table): what vt_attention_varlen_noalloc carves from its fixed array.
+size_t attn_ws_bytes(const vt_config* cfg, int64_t N, int32_t n_img, int32_t n_pos) {
+  Carver c(nullptr);
+  BlockBufs b;
+  carve_attention(c, dims_of(cfg, N, n_img), n_pos, &b);
+  return c.off;
+}
+
 size_t tower_ws_bytes(const vt_config* cfg, const GridInfo& gi, int32_t n_img) {
   Carver c(nullptr);
   TowerBufs t;
@@ -564,6 +574,66 @@ VT_API vt_status vt_attention_varlen(const vt_config* cfg, const uint16_t* qkv,
   if ((st = attn_prologue(cfg, cu_seqlens, n_img, total_tokens, max_seqlen, b, &axis_code, s)) != VT_OK) return st;
   return run_attention(cfg, qkv, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen, axis_code, b,
                        out, out_dtype == VT_FP32, s);
+}
+
+// ---- vt_attention_varlen without a workspace argument
+// Its scratch is one file-scope device array, of which each GPU the library
+// runs on holds its own copy (from the first use of the library's code on
+// that GPU until the process ends).  In host code `scratch` names a host-side
+// stand-in, not device memory: the device address comes from
+// hipGetSymbolAddress, resolved once per device on the first call with that
+// device current, and only that address is passed to kernels.
+static __device__ __align__(256) char scratch[VT_NOALLOC_SCRATCH_BYTES];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[kMaxDevices] = {};
+
+static vt_status noalloc_scratch(void** out) {
+  int dev = 0;
+  VT_TRY_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(VT_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    VT_TRY_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p || (reinterpret_cast<uintptr_t>(p) & (kAlign - 1)))
+      return fail(VT_ERR_HIP, "device %d: the scratch array has no 256-byte aligned address", dev);
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return VT_OK;
+}
+
+VT_API vt_status vt_attention_varlen_noalloc(const vt_config* cfg, const uint16_t* qkv,
+                                             const int32_t* cu_seqlens, const int32_t* pos_thw,
+                                             int32_t n_img, int32_t total_tokens, int32_t max_seqlen,
+                                             void* out, vt_dtype out_dtype, void* stream) {
+  vt_status st = check_varlen(cfg, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen);
+  if (st != VT_OK) return st;
+  if ((st = check_ptr(qkv, "qkv")) != VT_OK) return st;
+  if ((st = check_ptr(out, "out")) != VT_OK) return st;
+  if (out_dtype != VT_BF16 && out_dtype != VT_FP32) return fail(VT_ERR_INVALID_ARG, "bad out_dtype");
+  const size_t need = attn_ws_bytes(cfg, total_tokens, n_img, max_seqlen);
+  if (need > size_t(VT_NOALLOC_SCRATCH_BYTES))
+    return fail(VT_ERR_WORKSPACE, "%d tokens in %d images need %zu bytes of attention scratch, more than "
+                "the %zu bytes of the fixed array", total_tokens, n_img, need,
+                size_t(VT_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if ((st = noalloc_scratch(&ws)) != VT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // Every buffer carved here is written in full by this call before it is
+  // read (schedule, packed Q, tile images with their padding and ones rows,
+  // RoPE table), so nothing left by an earlier call needs clearing.
+  Carver c(ws);
+  BlockBufs b;
+  carve_attention(c, dims_of(cfg, total_tokens, n_img), max_seqlen, &b);
+  int32_t axis_code = 0;
+  if ((st = attn_prologue(cfg, cu_seqlens, n_img, total_tokens, max_seqlen, b, &axis_code, s)) != VT_OK)
+    return st;
+  return run_attention(cfg, qkv, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen, axis_code, b, out,
+                       out_dtype == VT_FP32, s);
 }
 
 // Buffers of vt_attention_backward: the forward's attention buffers, its
