@@ -39,7 +39,14 @@
  * Errors.    Arguments are validated on the host before any launch, in every
  *            build; a failing call launches nothing and returns a status
  *            code, with details in vt_last_error() (thread-local).  Launch
- *            failures return VT_ERR_HIP.  Nothing is clamped silently.
+ *            failures return VT_ERR_HIP.  Nothing is clamped silently; the
+ *            one clamp, of RoPE coordinates, is stated at
+ *            vt_attention_varlen.
+ * Range.     Attention runs its matrix products on fp16 operands (fp32
+ *            accumulation): the rotated q times log2(e)/sqrt(head_dim), the
+ *            rotated k and v must stay below 65504 in magnitude, else the
+ *            result holds infinities or NaN.  Stated again at each entry
+ *            point that runs attention.
  * Threads.   Calls are reentrant; there is no global mutable state other
  *            than the thread-local error string, and the per-GPU scratch
  *            array of vt_attention_varlen_noalloc (with its device address,
@@ -176,10 +183,18 @@ vt_status vt_patch_embed(const vt_config* cfg, const uint16_t* pixels, const vt_
  *   cu_seqlens [n_img+1] int32 on the device; image i attends only to its own
  *              tokens cu[i] .. cu[i+1]-1 (block-diagonal, no padding tokens).
  *   pos_thw    [N, 3] int32 on the device: the RoPE positions of each token.
- *              Every coordinate must lie in [0, max_seqlen).
+ *              Coordinates lie in [0, max_seqlen); the device reads them
+ *              during the call, so they are not validated on the host: a
+ *              coordinate outside that range is clamped into it for the
+ *              angle-table lookup (the result is that of the clamped
+ *              position; no memory outside the table is read).
  *   out        [N, heads*head_dim], bf16 or fp32 by out_dtype:
  *              softmax(RoPE(q) RoPE(k)^T / sqrt(head_dim)) v per image and head.
  *   max_seqlen must be >= every image's token count; total_tokens = cu[n_img].
+ * Range: the products run on fp16 operands with fp32 accumulation, so
+ * |RoPE(q)| log2(e)/sqrt(head_dim), |RoPE(k)| and |v| must stay below 65504
+ * (larger values give infinities or NaN; they are not clamped).  bf16 q, k,
+ * v inside that range are represented exactly or to fp16 rounding (2^-11).
  * No [n, n] buffer is formed: memory is O(total_tokens). */
 vt_status vt_attention_varlen(const vt_config* cfg, const uint16_t* qkv, const int32_t* cu_seqlens,
                               const int32_t* pos_thw, int32_t n_img, int32_t total_tokens,
@@ -228,7 +243,9 @@ vt_status vt_attention_varlen_noalloc(const vt_config* cfg, const uint16_t* qkv,
  *   ws         device workspace of vt_attention_backward_workspace_size bytes
  *              (about 36 KB per token at 16 heads, affine in the token count).
  * Pointers are 16-byte aligned device memory owned by the caller; ws 256-byte
- * aligned.  Errors as for vt_attention_varlen; nothing is launched on error. */
+ * aligned.  Errors, the RoPE-coordinate clamp and the fp16 operand range
+ * (which here covers dO as well) as for vt_attention_varlen; nothing is
+ * launched on error. */
 vt_status vt_attention_backward(const vt_config* cfg, const uint16_t* qkv, const int32_t* cu_seqlens,
                                 const int32_t* pos_thw, int32_t n_img, int32_t total_tokens,
                                 int32_t max_seqlen, const uint16_t* dout, void* dqkv,
@@ -243,7 +260,9 @@ size_t vt_attention_backward_workspace_size(const vt_config* cfg, int32_t total_
  *   R += O(attention(RoPE(LN1(R) W_qkv^T + b_qkv)))  with O(a) = a W_o^T + b_o
  *   R += GELU_tanh(LN2(R) W_fc1^T + b_fc1) W_fc2^T + b_fc2
  * LayerNorm: biased variance over hidden, eps inside the square root.
- * Arguments as in vt_attention_varlen; resid is [total_tokens, hidden]. */
+ * Arguments as in vt_attention_varlen; resid is [total_tokens, hidden].  The
+ * attention inside keeps vt_attention_varlen's RoPE-coordinate clamp and fp16
+ * operand range (on the q, k, v this block computes). */
 vt_status vt_block_forward(const vt_config* cfg, float* resid, const vt_block_weights* w,
                            const int32_t* cu_seqlens, const int32_t* pos_thw, int32_t n_img,
                            int32_t total_tokens, int32_t max_seqlen, void* ws, size_t ws_bytes,
@@ -272,7 +291,8 @@ typedef struct vt_block_grads {
  *   dresid    fp32 [N, hidden]: in, dL/d(block output); out, dL/d(resid_in).
  *   grads     host struct of device pointers (members may be NULL); each
  *             formed gradient is overwritten, not accumulated.
- *   other arguments as in vt_block_forward; hidden <= 2048.
+ *   other arguments as in vt_block_forward (with its clamp and fp16 operand
+ *             range); hidden <= 2048.
  *   ws        vt_block_backward_workspace_size bytes (about 120 KB per token
  *             at the MiniMax-M3 shape, affine in the token count).
  * Errors as for vt_block_forward; nothing is launched on error. */
@@ -306,7 +326,8 @@ typedef struct vt_tower_grads {
  *   grads     host struct; every formed gradient is overwritten.
  *   ws        vt_tower_backward_workspace_size bytes (about 320 KB per token at
  *             32 layers: each block's fp32 input is kept).
- * Errors as for vt_tower_forward; hidden <= 2048; nothing is launched on error. */
+ * Errors, the clamp and the fp16 operand range as for vt_tower_forward;
+ * hidden <= 2048; nothing is launched on error. */
 vt_status vt_tower_backward(const vt_config* cfg, const uint16_t* pixels, const vt_grid_thw* grid,
                             int32_t n_img, const vt_tower_weights* w, const float* d_tower,
                             const vt_tower_grads* grads, void* ws, size_t ws_bytes, void* stream);
@@ -331,7 +352,11 @@ vt_status vt_merge_project(const vt_config* cfg, const uint16_t* tower, vt_order
  * not NULL) merge + projector.
  *   tower_out  bf16 [N, hidden] raster order, or NULL (last_hidden_state).
  *   merged_raw bf16 [N/4, 4*hidden] or NULL.
- *   out        bf16 [N/4, proj_out] or NULL.  At least one output is needed. */
+ *   out        bf16 [N/4, proj_out] or NULL.  At least one output is needed.
+ * Positions come from the grid list, so the RoPE clamp never applies; the
+ * attention of every block keeps vt_attention_varlen's fp16 operand range on
+ * the q, k, v the blocks compute (|RoPE(q)| below about 4.06e5 before its
+ * log2(e)/sqrt(head_dim) scale, |RoPE(k)| and |v| below 65504). */
 vt_status vt_tower_forward(const vt_config* cfg, const uint16_t* pixels, const vt_grid_thw* grid,
                            int32_t n_img, const vt_tower_weights* w, uint16_t* tower_out,
                            uint16_t* merged_raw, uint16_t* out, void* ws, size_t ws_bytes,
