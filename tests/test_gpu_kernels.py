@@ -481,6 +481,52 @@ def test_block_224(vt, affine):
     assert cosine_rows(got, ref["tower"]).min() >= 0.999
 
 
+@pytest.mark.parametrize("grids", [[(1, 32, 32)], [(1, 32, 32)] * 3, [(1, 144, 144)],
+                                   [(1, 30, 32), (1, 2, 2), (3, 6, 10), (1, 16, 18)]])
+def test_block_qkv_pack_epilogue_equals_separate_steps(vt, grids):
+    """vt_block_forward runs the QKV Linear with RoPE, the fp16 conversion and
+    the K/V tile-image writes in its epilogue (W_qkv rows read pair-major).
+    Composing the same block from the public steps -- vt_layer_norm,
+    vt_linear (bf16 QKV), vt_attention_varlen (its own pack kernel), the
+    residual vt_linear calls -- gives the same bits wherever vt_linear plans
+    the QKV GEMM without split-K (1,024 tokens and more; every tile shape
+    sums K in the same order): 128 x 128 tiles in one or several rounds,
+    256 x 256 tiles at 20,736 tokens, and 1,432 tokens over a clip and three
+    still images, where key tiles start inside the GEMM's row tiles."""
+    W = synth.make_weights(1, projector=False, affine="random")
+    d = {k: dev_bits(v, torch) for k, v in W.items()}
+    N = sum(t * h * w for t, h, w in grids)
+    n_img, max_seq = len(grids), max(t * h * w for t, h, w in grids)
+    log(f"block with the QKV pack epilogue vs separate steps: {n_img} items, {N} tokens")
+    cfg = vt.config(layers=1)
+    cu = torch.empty(n_img + 1, dtype=torch.int32, device="cuda")
+    pos = torch.empty((N, 3), dtype=torch.int32, device="cuda")
+    vt.vt_build_metadata(grids, cu, pos)
+    R0 = torch.from_numpy(rng(23).standard_normal((N, 1280), dtype=np.float32)).cuda()
+    R = R0.clone()
+    ws = vt.workspace(vt.vt_block_workspace_size(cfg, N, n_img, max_seq))
+    vt.vt_block_forward(cfg, R, vt.block_weights(d, "l0."), cu, pos, n_img, N, max_seq, ws)
+    # the same block from the public steps
+    g = lambda k: d["l0." + k]
+    x = torch.empty((N, 1280), dtype=torch.int16, device="cuda")
+    qkv = torch.empty((N, 3840), dtype=torch.int16, device="cuda")
+    att = torch.empty((N, 1280), dtype=torch.int16, device="cuda")
+    h = torch.empty((N, 5120), dtype=torch.int16, device="cuda")
+    S = R0.clone()
+    lin = lambda a, K, w, n, b, epi, o: vt.vt_linear(a, N, K, w, n, b, epi, o,
+                                                     vt.workspace(vt.vt_linear_workspace_size(N, n, K)))
+    vt.vt_layer_norm(S, N, 1280, g("ln1_g"), g("ln1_b"), 1e-6, x)
+    lin(x, 1280, g("w_qkv"), 3840, g("b_qkv"), vt.VT_EPI_BF16, qkv)
+    vt.vt_attention_varlen(cfg, qkv, cu, pos, n_img, N, max_seq, att, vt.VT_BF16, ws)
+    lin(att, 1280, g("w_o"), 1280, g("b_o"), vt.VT_EPI_RESID_F32, S)
+    vt.vt_layer_norm(S, N, 1280, g("ln2_g"), g("ln2_b"), 1e-6, x)
+    lin(x, 1280, g("w_fc1"), 5120, g("b_fc1"), vt.VT_EPI_GELU_TANH_BF16, h)
+    lin(h, 5120, g("w_fc2"), 1280, g("b_fc2"), vt.VT_EPI_RESID_F32, S)
+    torch.cuda.synchronize()
+    log(f"  max abs difference {(R - S).abs().max().item():.3e}")
+    assert torch.equal(R, S)
+
+
 # ---------------------------------------------------------------- mean pool
 @pytest.mark.parametrize("grids", [[(1, 32, 32)], [(1, 2, 2), (3, 4, 6), (1, 144, 144)]])
 def test_mean_pool(vt, grids):

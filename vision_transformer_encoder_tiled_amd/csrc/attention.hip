@@ -76,8 +76,8 @@ namespace vt {
 namespace {
 constexpr int HD = 80;              // head_dim
 constexpr int BKV = kAttnKTile;     // keys per tile
-constexpr int KROW = 88;            // fp16 per K row (176 B)
-constexpr int VROW = 72;            // fp16 per V^T row (144 B)
+constexpr int KROW = kAttnKRow;     // fp16 per K row (176 B)
+constexpr int VROW = kAttnVRow;     // fp16 per V^T row (144 B)
 constexpr int K_BYTES = BKV * KROW * 2;          // 11264
 constexpr int V_ROWS = HD + 1;                   // dims 0..79 and the ones row
 constexpr int IMG_BYTES = kAttnTileBytes;        // 24576: K + V^T rows 0..80 + pad
@@ -127,23 +127,15 @@ __global__ void __launch_bounds__(320) attn_pack_kernel(
     for (int which = 0; which < 2; ++which) {  // 0: q, 1: k
       const uint4 a = reinterpret_cast<const uint4*>(row + which * heads * HD)[c];
       const uint4 b = reinterpret_cast<const uint4*>(row + which * heads * HD)[c + 5];
-      const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
-      const float sc = which == 0 ? q_scale_log2 : 1.0f;
-      uint32_t r1[4], r2[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x1l = bflo(aw[j]), x1h = bfhi(aw[j]), x2l = bflo(bw[j]), x2h = bfhi(bw[j]);
-        const float cl = cs[4 * j], sl = cs[4 * j + 1], ch = cs[4 * j + 2], sh = cs[4 * j + 3];
-        r1[j] = pack_f16x2((x1l * cl - x2l * sl) * sc, (x1h * ch - x2h * sh) * sc);
-        r2[j] = pack_f16x2((x2l * cl + x1l * sl) * sc, (x2h * ch + x1h * sh) * sc);
-      }
+      uint4 o1, o2;
+      rope8_f16(a, b, cs, which == 0 ? q_scale_log2 : 1.0f, &o1, &o2);
       if (which == 0) {
         uint16_t* q = qpk + (int64_t(tok) * heads + head) * HD;
-        reinterpret_cast<uint4*>(q)[c] = make_uint4(r1[0], r1[1], r1[2], r1[3]);
-        reinterpret_cast<uint4*>(q)[c + 5] = make_uint4(r2[0], r2[1], r2[2], r2[3]);
+        reinterpret_cast<uint4*>(q)[c] = o1;
+        reinterpret_cast<uint4*>(q)[c + 5] = o2;
       } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { kr[j] = r1[j]; kr[4 + j] = r2[j]; }
+        kr[0] = o1.x; kr[1] = o1.y; kr[2] = o1.z; kr[3] = o1.w;
+        kr[4] = o2.x; kr[5] = o2.y; kr[6] = o2.z; kr[7] = o2.w;
       }
     }
     const uint4 a = reinterpret_cast<const uint4*>(row + 2 * heads * HD)[c];
@@ -182,6 +174,48 @@ __global__ void __launch_bounds__(320) attn_pack_kernel(
                            : make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
     *reinterpret_cast<uint4*>(vimg + d * VROW + 8 * sg) = v;
   }
+}
+
+// ---------------------------------------------------------------- image init
+// The parts of the K/V tile images that do not depend on the layer, for the
+// path where the QKV GEMM's epilogue writes the rotated Q and the images'
+// key rows itself (launch_gemm_qkv_pack): per (key tile, head), the V^T
+// ones row (row 80) and, past the image end in its last tile, zero K rows
+// and zero V^T slots; and, from the head-0 workgroups, kslot[tok] = 64 T + s,
+// the tile T and slot s that token tok's key occupies.  Block per (key tile,
+// head) like the pack kernel, 256 threads.
+__global__ void __launch_bounds__(256) attn_image_init_kernel(const int2* __restrict__ kdesc,
+                                                              int32_t heads, uint16_t* __restrict__ kv,
+                                                              int32_t* __restrict__ kslot) {
+  const int T = blockIdx.x / heads, head = blockIdx.x % heads;
+  const int2 desc = kdesc[T];
+  if (desc.x < 0) return;
+  const int valid = min(BKV, desc.y - desc.x);
+  const int t = threadIdx.x;
+  if (head == 0 && t < valid) kslot[desc.x + t] = T * BKV + t;
+  char* img = reinterpret_cast<char*>(kv) + (int64_t(T) * heads + head) * IMG_BYTES;
+  uint16_t* kimg = reinterpret_cast<uint16_t*>(img);
+  uint16_t* vimg = reinterpret_cast<uint16_t*>(img + K_BYTES);
+  if (t < BKV / 8) {  // the ones row: 8 slots per thread
+    *reinterpret_cast<uint4*>(vimg + HD * VROW + 8 * t) =
+        make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+  }
+  // padding keys: K rows (10 chunks of 16 bytes each) and V^T slots (80 dims)
+  for (int i = t; i < (BKV - valid) * 10; i += 256) {
+    const int k = valid + i / 10, c = i % 10;
+    *reinterpret_cast<uint4*>(kimg + k * KROW + 8 * c) = make_uint4(0u, 0u, 0u, 0u);
+  }
+  for (int i = t; i < (BKV - valid) * HD; i += 256) {
+    const int k = valid + i / HD, dim = i % HD;
+    vimg[dim * VROW + mfma_slot16(k)] = 0;
+  }
+}
+
+hipError_t launch_attn_image_init(const int2* kdesc, int32_t max_ktiles, int32_t heads, uint16_t* kv,
+                                  int32_t* kslot, hipStream_t s) {
+  hipLaunchKernelGGL(attn_image_init_kernel, dim3(unsigned(int64_t(max_ktiles) * heads)), dim3(256), 0, s,
+                     kdesc, heads, kv, kslot);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- attention
@@ -654,6 +688,12 @@ hipError_t launch_attention(const uint16_t* qkv, const int32_t* pos_thw, const i
                      qkv, pos_thw, kdesc, heads, n_pos, rope_cs, axis_code, q_scale_log2, qpk, kv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_attention_packed(qpk, kv, qdesc, max_qtiles, heads, variant, out, out_f32, lse, s);
+}
+
+hipError_t launch_attention_packed(const uint16_t* qpk, const uint16_t* kv, const int4* qdesc,
+                                   int32_t max_qtiles, int32_t heads, int32_t variant, void* out,
+                                   bool out_f32, float* lse, hipStream_t s) {
   switch (variant) {
     case kAttnSmall:
       return launch_attention_kernel<4, 2, 3>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, lse, s);

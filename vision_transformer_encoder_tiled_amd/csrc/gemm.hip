@@ -230,6 +230,89 @@ constexpr int pass_rows(int bm, int row_bytes, int ring) {
   return r;
 }
 
+// ---- the QKV Linear with the attention's pack step as its epilogue
+// Output tile columns -> W_qkv rows.  The q and k parts (features [0, 2d))
+// are read pair-major: tile column c of a BN-wide tile covers rotation pair
+// p = (tile start)/2 + c mod BN/2 of its part, its first half (x_j, j = p mod
+// 40 of head p / 40) for c < BN/2 and its partner x_{j+40} otherwise, so both
+// halves of every pair are in one tile.  v columns keep their order.
+template <int BN>
+__device__ __forceinline__ int qkv_feature(int n, int d) {
+  if (n >= 2 * d) return n;
+  const int part = n >= d;
+  const int local = n - part * d;
+  const int c = local % BN, p = (local - c) / 2 + c % (BN / 2);
+  return part * d + (p / 40) * 80 + p % 40 + 40 * (c / (BN / 2));
+}
+
+// Store phase of the pack epilogue: the tile (bias added, rounded to bf16,
+// staged row-major in LDS as for a bf16 output) leaves as rotated fp16 Q
+// rows, rotated fp16 K rows of the tile images, or fp16 V^T columns of the
+// tile images.  q/k: one item per (row, chunk of 8 pairs) -- the two halves
+// are chunks q and BN/16 + q of the row, rotated with the position of the
+// chunk's axis (rope8_f16, the pack kernel's arithmetic).  v: lane = token
+// row within a group of 64, so a store instruction writes one V^T row's
+// slots; two adjacent columns (dims of one head) per LDS read.
+template <int BN, int ROWS, int NT>
+__device__ __forceinline__ void qkv_pack_store(const char* cs, const QkvPack& pk, int r0, int M, int n0,
+                                               int tid) {
+  constexpr int ROWB = BN * 2, CHUNKS = ROWB / 16;
+  constexpr int IMG = kAttnTileBytes / 2, KOFF = kAttnKTile * kAttnKRow;  // in fp16 units
+  const int d = pk.d;
+  if (n0 < 2 * d) {
+    const int part = n0 >= d;
+    const int p0 = (n0 - part * d) / 2;
+    constexpr int QCH = BN / 16;
+    const float sc = part == 0 ? pk.q_scale : 1.0f;
+    for (int i = tid; i < ROWS * QCH; i += NT) {
+      const int r = i / QCH, q = i % QCH;
+      const int tok = r0 + r;
+      if (tok >= M) continue;
+      const uint4 a = *reinterpret_cast<const uint4*>(cs + r * ROWB + ((q + (r & 15)) % CHUNKS) * 16);
+      const uint4 b = *reinterpret_cast<const uint4*>(cs + r * ROWB + ((QCH + q + (r & 15)) % CHUNKS) * 16);
+      const int p = p0 + 8 * q, head = p / 40, j0 = p % 40;
+      const int ax = (pk.axis_code >> (2 * (j0 >> 3))) & 3;
+      const int ps = min(max(pk.pos[3 * tok + ax], 0), pk.n_pos - 1);
+      const float4* cs4 = reinterpret_cast<const float4*>(pk.rope + int64_t(ps) * 40 + j0);
+      float csv[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 v = cs4[j];
+        csv[4 * j] = v.x; csv[4 * j + 1] = v.y; csv[4 * j + 2] = v.z; csv[4 * j + 3] = v.w;
+      }
+      uint4 o1, o2;
+      rope8_f16(a, b, csv, sc, &o1, &o2);
+      uint16_t* dst;
+      if (part == 0) {
+        dst = pk.qpk + (int64_t(tok) * pk.heads + head) * 80 + j0;
+      } else {
+        const int ks = pk.kslot[tok];
+        dst = pk.kv + (int64_t(ks >> 6) * pk.heads + head) * IMG + (ks & 63) * kAttnKRow + j0;
+      }
+      *reinterpret_cast<uint4*>(dst) = o1;
+      *reinterpret_cast<uint4*>(dst + 40) = o2;
+    }
+  } else {
+    constexpr int RG = ROWS / 64, NWAVE = NT / 64, CSTEP = 2 * NWAVE / RG;
+    static_assert(ROWS % 64 == 0 && NWAVE % RG == 0, "V store groups");
+    const int wave = tid >> 6, lane = tid & 63;
+    const int r = (wave % RG) * 64 + lane, tok = r0 + r;
+    if (tok < M) {
+      const int ks = pk.kslot[tok];
+      uint16_t* vb = pk.kv + int64_t(ks >> 6) * pk.heads * IMG + KOFF + mfma_slot16(ks & 63);
+      const int f0 = n0 - 2 * d;
+      for (int c = 2 * (wave / RG); c < BN; c += CSTEP) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(
+            cs + r * ROWB + (((c >> 3) + (r & 15)) % CHUNKS) * 16 + (c & 7) * 2);
+        const int f = f0 + c, head = f / 80, dim = f % 80;  // dims dim, dim + 1 of one head
+        uint16_t* v = vb + int64_t(head) * IMG + dim * kAttnVRow;
+        v[0] = __builtin_bit_cast(uint16_t, (_Float16)bflo(w));
+        v[kAttnVRow] = __builtin_bit_cast(uint16_t, (_Float16)bfhi(w));
+      }
+    }
+  }
+}
+
 // GWM x GWN multiplying wavefronts, each owning a (BM/GWM) x (BN/GWN) block
 // of C, plus CW wavefronts that only copy (and help store the tile).
 // K is consumed in steps of BK (32 or 64) through a ring of NST LDS stages,
@@ -242,7 +325,8 @@ constexpr int pass_rows(int bm, int row_bytes, int ring) {
 template <int BM, int BN, int GWM, int GWN, int NST, int EPI, bool SPLIT, int BK = 32, int CW = 0>
 __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
     const uint16_t* __restrict__ A, int M, int K, const uint16_t* __restrict__ B, int N,
-    const uint16_t* __restrict__ bias, void* __restrict__ out, float* __restrict__ part, int kper) {
+    const uint16_t* __restrict__ bias, void* __restrict__ out, float* __restrict__ part, int kper,
+    QkvPack pk) {
   constexpr int NW = GWM * GWN;  // wavefronts that multiply
   constexpr int NWC = NW + CW;   // wavefronts that copy: all of them
   constexpr int WM = BM / GWM, WN = BN / GWN;
@@ -291,8 +375,10 @@ __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
   for (int j = 0; j < CP_HI; ++j) {
     const int g = min(wave + NWC * j, G - 1);
     const int lchunk = (lane % CH) ^ dl_swz<BK>(RPG * g + lq);
+    int brow = min(n0 + RPG * (g - GA) + lq, N - 1);
+    if constexpr (EPI == kEpiQkvPack) brow = qkv_feature<BN>(brow, pk.d);
     src[j] = g < GA ? A + int64_t(min(m0 + RPG * g + lq, M - 1)) * K + kbeg + 8 * lchunk
-                    : B + int64_t(min(n0 + RPG * (g - GA) + lq, N - 1)) * K + kbeg + 8 * lchunk;
+                    : B + int64_t(brow) * K + kbeg + 8 * lchunk;
   }
   const uint32_t lds0 = lds_offset(lds) + 1024 * wave;
 
@@ -331,6 +417,13 @@ __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
   // wider tiles have no registers to spare and load them in the epilogue).
   constexpr bool F32OUT = SPLIT || EPI == kEpiResid || EPI == kEpiF32;
   constexpr bool PRE = !F32OUT && BM == 128 && BN <= 160;
+  // Bias element of output column n (and the 3 after it): the W_qkv row read
+  // for it in the pack epilogue (4 consecutive columns are 4 consecutive
+  // features there too), else n itself.
+  auto bias_col = [&](int n) {
+    if constexpr (EPI == kEpiQkvPack) return qkv_feature<BN>(n, pk.d);
+    else return min(n, N - 4);
+  };
   uint2 bpre[PRE ? FB : 1][4];
   if constexpr (PRE) {
 #pragma unroll
@@ -338,7 +431,7 @@ __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
 #pragma unroll
       for (int g = 0; g < 4; ++g)
         bpre[f][g] = (bias && mw) ? *reinterpret_cast<const uint2*>(
-                                        bias + min(n0 + wn * WN + 32 * f + 8 * g + 4 * h, N - 4))
+                                        bias + bias_col(n0 + wn * WN + 32 * f + 8 * g + 4 * h))
                                   : make_uint2(0, 0);
   }
 
@@ -497,7 +590,7 @@ __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
               if (bias) {
                 uint2 bb;
                 if constexpr (PRE) bb = bpre[f][g];
-                else bb = *reinterpret_cast<const uint2*>(bias + min(n0 + wn * WN + 32 * f + 8 * g + 4 * h, N - 4));
+                else bb = *reinterpret_cast<const uint2*>(bias + bias_col(n0 + wn * WN + 32 * f + 8 * g + 4 * h));
                 v0 += bflo(bb.x); v1 += bfhi(bb.x); v2 += bflo(bb.y); v3 += bfhi(bb.y);
               }
               if constexpr (EPI == kEpiGeluTanh) {
@@ -516,6 +609,10 @@ __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
     __syncthreads();
     constexpr int TOTAL = PASS_ROWS * CHUNKS;
     constexpr int PER = (TOTAL + 64 * NWC - 1) / (64 * NWC);  // chunks per thread per pass
+    if constexpr (EPI == kEpiQkvPack) {
+      qkv_pack_store<BN, PASS_ROWS, 64 * NWC>(cs, pk, m0 + pass * PASS_ROWS, M, n0, tid);
+      continue;
+    }
     if constexpr (EPI == kEpiResid && !SPLIT) {
       // Residual update: every old value this thread needs is loaded first,
       // so the loads are in flight together rather than one store apart.
@@ -653,7 +750,7 @@ size_t gemm_workspace_bytes(int M, int N, int K) {
 template <int BM, int BN, int EPI, bool SPLIT, int BK>
 static hipError_t launch_dl(const uint16_t* A, int M, int K, const uint16_t* B, int N,
                             const uint16_t* bias, void* out, float* part, const GemmPlan& p,
-                            int tiles, hipStream_t s) {
+                            int tiles, hipStream_t s, const QkvPack& pk = QkvPack{}) {
   // 256 x 256: 8 wavefronts (2 per SIMD) of 128 x 64; 128 x 128: 8 of 32 x 64;
   // 128 x 160 and 128 x 192: 4 of 32 x BN plus 4 that only copy.  K steps of
   // 32 go through 4 stages, K steps of 64 through 3.
@@ -666,7 +763,7 @@ static hipError_t launch_dl(const uint16_t* A, int M, int K, const uint16_t* B, 
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3(tiles, SPLIT ? p.splits : 1), dim3(64 * (GWM * GWN + CW)), lds, s, A,
-                     M, K, B, N, bias, out, part, p.kper);
+                     M, K, B, N, bias, out, part, p.kper, pk);
   return hipGetLastError();
 }
 
@@ -735,6 +832,23 @@ hipError_t launch_gemm(const uint16_t* A, int M, int K, const uint16_t* B, int N
     case kEpiF32: return launch_epi<kEpiF32>(A, M, K, B, N, bias, out, ws, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_qkv_pack(const uint16_t* A, int M, int K, const uint16_t* B, const uint16_t* bias,
+                                const QkvPack& pk, hipStream_t s) {
+  // 256 x 256 tiles when they fill the chip (as plan_gemm), else 128 x 128;
+  // never split-K (the epilogue needs whole sums).  Both tile widths divide d.
+  const int N = 3 * pk.d;
+  if (K % 32 || pk.d % 256) return hipErrorInvalidValue;
+  auto cdiv = [](long a, long b) { return int((a + b - 1) / b); };
+  const GemmPlan p{128, 128, 1, K};
+  const int t256 = cdiv(M, 256) * cdiv(N, 256);
+  if (t256 >= 192) return launch_dl<256, 256, kEpiQkvPack, false, 32>(A, M, K, B, N, bias, nullptr, nullptr, p,
+                                                                      t256, s, pk);
+  const int t128 = cdiv(M, 128) * cdiv(N, 128);
+  if (t128 <= 256 && K % 64 == 0)
+    return launch_dl<128, 128, kEpiQkvPack, false, 64>(A, M, K, B, N, bias, nullptr, nullptr, p, t128, s, pk);
+  return launch_dl<128, 128, kEpiQkvPack, false, 32>(A, M, K, B, N, bias, nullptr, nullptr, p, t128, s, pk);
 }
 
 hipError_t launch_gemm_partials(const uint16_t* A, int M, int K, const uint16_t* B, int N, void* ws,

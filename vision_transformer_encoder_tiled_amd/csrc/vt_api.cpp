@@ -139,6 +139,7 @@ struct BlockBufs {
   int2* kdesc;     // per key-tile slot
   uint16_t* qpk;   // [N, heads, 80] fp16 rotated, scaled Q
   uint16_t* kv;    // max_ktiles x heads K/V tile images (fp16)
+  int32_t* kslot;  // [N] tile image and slot of each token's key
   float2* rope;
   uint16_t* xn;    // [N, d] LayerNorm output
   uint16_t* act;   // [N, max(4d, mlp)]: qkv [N,3d] then attn [N,d]; later the MLP hidden [N, mlp]
@@ -172,6 +173,7 @@ void carve_attention(Carver& c, const Dims& D, int32_t n_pos, BlockBufs* b) {
   b->qpk = c.take<uint16_t>(size_t(D.N) * D.d);
   b->kv = reinterpret_cast<uint16_t*>(
       c.take<char>(size_t(D.heads) * max_k_tiles(D.N, D.n_img) * vt::kAttnTileBytes));
+  b->kslot = c.take<int32_t>(D.N);
   b->rope = c.take<float2>(size_t(n_pos) * 40);
 }
 
@@ -285,15 +287,20 @@ int32_t attn_variant(int64_t N, int32_t n_img, int32_t heads) {
   return tiles256 * heads >= 1024 ? vt::kAttnLean8 : vt::kAttnLean4;
 }
 
-// The per-call attention prologue: LPT schedule and RoPE cos/sin table.
+// The per-call attention prologue: LPT schedule and RoPE cos/sin table; for
+// the blocks (whose QKV GEMM packs Q and the tile images itself) also the
+// layer-independent parts of the tile images and the token -> slot map.
 vt_status attn_prologue(const vt_config* cfg, const int32_t* cu, int32_t n_img, int64_t N,
-                        int32_t n_pos, const BlockBufs& b, int32_t* axis_code, hipStream_t s) {
+                        int32_t n_pos, const BlockBufs& b, int32_t* axis_code, hipStream_t s,
+                        bool for_blocks = false) {
   const int q_tile = vt::attn_q_tile(attn_variant(N, n_img, cfg->heads));
   VT_TRY_HIP(vt::launch_attn_schedule(cu, n_img, q_tile, vt::kAttnKTile,
                                       max_q_tiles(N, n_img, q_tile), max_k_tiles(N, n_img),
                                       b.order, b.tile_start, b.ktile_start, b.qdesc, b.kdesc, s));
   const vt::RopeFreq f = rope_freq(cfg, axis_code);
   VT_TRY_HIP(vt::launch_rope_table(f, n_pos, b.rope, s));
+  if (for_blocks)
+    VT_TRY_HIP(vt::launch_attn_image_init(b.kdesc, max_k_tiles(N, n_img), cfg->heads, b.kv, b.kslot, s));
   return VT_OK;
 }
 
@@ -325,9 +332,23 @@ vt_status run_block(const vt_config* cfg, float* R, const vt_block_weights* w, c
   uint16_t* att = b.act + size_t(N) * 3 * d;
   if (!*xn_ready)
     VT_TRY_HIP(vt::launch_layer_norm(R, M, d, w->ln1_g, w->ln1_b, cfg->ln_eps, b.xn, s));
-  VT_TRY_HIP(vt::launch_gemm(b.xn, M, d, w->w_qkv, 3 * d, w->b_qkv, vt::kEpiBf16, qkv, b.gemm_ws, s));
-  vt_status st = run_attention(cfg, qkv, cu, pos, n_img, N, n_pos, axis_code, b, att, false, s);
-  if (st != VT_OK) return st;
+  // QKV with RoPE, the fp16 conversion and the tile-image writes in its
+  // epilogue (the images' constant parts come from attn_prologue), then the
+  // attention kernel on what it packed.
+  const vt::QkvPack pk{b.qpk, b.kv, pos, b.kslot, b.rope, n_pos, axis_code, cfg->heads, d, q_scale_log2(cfg)};
+  const hipError_t e = vt::launch_gemm_qkv_pack(b.xn, M, d, w->w_qkv, w->b_qkv, pk, s);
+  if (e == hipSuccess) {
+    const int32_t var = attn_variant(N, n_img, cfg->heads);
+    VT_TRY_HIP(vt::launch_attention_packed(b.qpk, b.kv, b.qdesc, max_q_tiles(N, n_img, vt::attn_q_tile(var)),
+                                           cfg->heads, var, att, false, nullptr, s));
+  } else if (e == hipErrorInvalidValue) {  // a shape the pack epilogue does not take (nothing launched)
+    (void)hipGetLastError();
+    VT_TRY_HIP(vt::launch_gemm(b.xn, M, d, w->w_qkv, 3 * d, w->b_qkv, vt::kEpiBf16, qkv, b.gemm_ws, s));
+    vt_status st = run_attention(cfg, qkv, cu, pos, n_img, N, n_pos, axis_code, b, att, false, s);
+    if (st != VT_OK) return st;
+  } else {
+    return fail(VT_ERR_HIP, "QKV pack GEMM: %s", hipGetErrorString(e));
+  }
   const float* part = reinterpret_cast<const float*>(b.gemm_ws);
   if (vt::plan_gemm(M, d, d).splits > 1) {
     VT_TRY_HIP(vt::launch_gemm_partials(att, M, d, w->w_o, d, b.gemm_ws, s));
@@ -910,7 +931,8 @@ VT_API vt_status vt_block_forward(const vt_config* cfg, float* resid, const vt_b
   BlockBufs b;
   carve_block(c, dims_of(cfg, total_tokens, n_img), max_seqlen, &b);
   int32_t axis_code = 0;
-  if ((st = attn_prologue(cfg, cu_seqlens, n_img, total_tokens, max_seqlen, b, &axis_code, s)) != VT_OK) return st;
+  if ((st = attn_prologue(cfg, cu_seqlens, n_img, total_tokens, max_seqlen, b, &axis_code, s, true)) != VT_OK)
+    return st;
   bool xn_ready = false;
   return run_block(cfg, resid, w, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen, axis_code, b,
                    nullptr, nullptr, &xn_ready, s);
@@ -981,7 +1003,7 @@ VT_API vt_status vt_tower_forward(const vt_config* cfg, const uint16_t* pixels,
   carve_tower(c, dims_of(cfg, N, n_img), gi.max_hw, &t);
   if ((st = launch_meta(grid, n_img, N, t.cu, t.info, t.pos, t.ridx, t.tok_img, s)) != VT_OK) return st;
   int32_t axis_code = 0;
-  if ((st = attn_prologue(cfg, t.cu, n_img, N, gi.max_hw, t.blk, &axis_code, s)) != VT_OK) return st;
+  if ((st = attn_prologue(cfg, t.cu, n_img, N, gi.max_hw, t.blk, &axis_code, s, true)) != VT_OK) return st;
   VT_TRY_HIP(vt::launch_patchify(pixels, t.info, t.cu, t.tok_img, int32_t(N), t.X, s));
   VT_TRY_HIP(vt::launch_gemm(t.X, int(N), 1176, w->w_patch, cfg->hidden, w->b_patch, vt::kEpiF32, t.R,
                              t.blk.gemm_ws, s));
@@ -1089,7 +1111,7 @@ VT_API vt_status vt_tower_backward(const vt_config* cfg, const uint16_t* pixels,
   // forward, keeping each block's input
   if ((st = launch_meta(grid, n_img, N, t.cu, t.info, t.pos, t.ridx, t.tok_img, s)) != VT_OK) return st;
   int32_t axis_code = 0;
-  if ((st = attn_prologue(cfg, t.cu, n_img, N, gi.max_hw, t.blk, &axis_code, s)) != VT_OK) return st;
+  if ((st = attn_prologue(cfg, t.cu, n_img, N, gi.max_hw, t.blk, &axis_code, s, true)) != VT_OK) return st;
   VT_TRY_HIP(vt::launch_patchify(pixels, t.info, t.cu, t.tok_img, M, t.X, s));
   VT_TRY_HIP(vt::launch_gemm(t.X, M, 1176, w->w_patch, d, w->b_patch, vt::kEpiF32, t.R, t.blk.gemm_ws, s));
   bool xn_ready = false;

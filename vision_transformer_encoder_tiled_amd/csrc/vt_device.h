@@ -34,6 +34,30 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   v[1] = (_Float16)hi;
   return __builtin_bit_cast(uint32_t, v);
 }
+// 3D RoPE on 8 rotation pairs, rotate-half pairing (x_j, x_{j+40} of a head
+// of 80), then a scale and fp16 rounding.  a holds x_j .. x_{j+7} and b the
+// partners x_{j+40} .. x_{j+47} (bf16), cs[2i], cs[2i+1] = cos, sin of pair
+// j+i.  o1 = (a cos - b sin) sc, o2 = (b cos + a sin) sc, every product
+// rounded on its own (no contraction into fmas), so that the result does not
+// depend on what the compiler knows at the call site: the pack kernel and
+// the QKV GEMM epilogue produce the same bits.
+__device__ __forceinline__ void rope8_f16(uint4 a, uint4 b, const float (&cs)[16], float sc, uint4* o1,
+                                          uint4* o2) {
+#pragma clang fp contract(off)
+  const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+  uint32_t r1[4], r2[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float x1l = __uint_as_float(aw[j] << 16), x1h = __uint_as_float(aw[j] & 0xffff0000u);
+    const float x2l = __uint_as_float(bw[j] << 16), x2h = __uint_as_float(bw[j] & 0xffff0000u);
+    const float cl = cs[4 * j], sl = cs[4 * j + 1], ch = cs[4 * j + 2], sh = cs[4 * j + 3];
+    r1[j] = pack_f16x2((x1l * cl - x2l * sl) * sc, (x1h * ch - x2h * sh) * sc);
+    r2[j] = pack_f16x2((x2l * cl + x1l * sl) * sc, (x2h * ch + x1h * sh) * sc);
+  }
+  *o1 = make_uint4(r1[0], r1[1], r1[2], r1[3]);
+  *o2 = make_uint4(r2[0], r2[1], r2[2], r2[3]);
+}
+
 __device__ __forceinline__ uint16_t f2bf(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }

@@ -61,7 +61,8 @@ hipError_t launch_resid_ln(const float* part, int32_t splits, int32_t rows, int3
                            float eps, uint16_t* out, hipStream_t s);
 
 // ---- GEMM (gemm.hip)
-enum Epi : int { kEpiBf16 = 0, kEpiGeluTanh = 1, kEpiGeluErf = 2, kEpiResid = 3, kEpiF32 = 4 };
+enum Epi : int { kEpiBf16 = 0, kEpiGeluTanh = 1, kEpiGeluErf = 2, kEpiResid = 3, kEpiF32 = 4,
+                 kEpiQkvPack = 5 };
 struct GemmPlan {
   int bm, bn;        // tile
   int splits;        // split-K factor (1 = none)
@@ -75,10 +76,30 @@ hipError_t launch_gemm(const uint16_t* A, int M, int K, const uint16_t* B, int N
 // splits (> 1) to ws, no bias and no epilogue (launch_resid_ln finishes them).
 hipError_t launch_gemm_partials(const uint16_t* A, int M, int K, const uint16_t* B, int N, void* ws,
                                 hipStream_t s);
+// The QKV Linear of a block (N = 3 * d, head_dim 80) with the attention's
+// pack step as its epilogue: y = x W_qkv^T + b rounded to bf16 (the values
+// the pack kernel would read), then 3D RoPE on q and k (pairs (j, j+40) of
+// a head), q scaled by q_scale, both rounded to fp16: Q rows into qpk
+// [N, heads, 80], K rows and V^T columns into the tile images of kv at the
+// slots given by kslot (launch_attn_image_init).  W_qkv rows are read in an
+// order that puts both halves of every rotation pair in one output tile.
+struct QkvPack {
+  uint16_t* qpk;
+  uint16_t* kv;
+  const int32_t* pos;     // [N, 3] positions (t, row, col)
+  const int32_t* kslot;   // [N]
+  const float2* rope;     // [n_pos, 40] (cos, sin)
+  int32_t n_pos, axis_code, heads, d;
+  float q_scale;
+};
+hipError_t launch_gemm_qkv_pack(const uint16_t* A, int M, int K, const uint16_t* B, const uint16_t* bias,
+                                const QkvPack& pk, hipStream_t s);
 
 // ---- attention (attention.hip)
 constexpr int kAttnKTile = 64;         // keys per tile
 constexpr int kAttnTileBytes = 24576;  // one (head, key tile) image: K [64][88] + V^T [81][72] fp16 + pad
+constexpr int kAttnKRow = 88;          // fp16 per K row of an image (dims 0..79 + pad)
+constexpr int kAttnVRow = 72;          // fp16 per V^T row of an image (64 key slots + pad)
 // Attention kernel variants, chosen by the size of the call:
 //   kAttnSmall  attention_kernel, two key groups of 2 wavefronts, 64 queries
 //               per workgroup (few query tiles: every CU gets work);
@@ -100,6 +121,17 @@ hipError_t launch_attention(const uint16_t* qkv, const int32_t* pos_thw, const i
                             int32_t heads, int32_t n_pos, int32_t axis_code, const float2* rope_cs,
                             float q_scale_log2, int32_t variant, uint16_t* qpk, uint16_t* kv,
                             void* out, bool out_f32, float* lse, hipStream_t s);
+
+// The attention kernel alone, on Q and tile images already packed (by the
+// pack kernel inside launch_attention, or by the QKV GEMM epilogue).
+hipError_t launch_attention_packed(const uint16_t* qpk, const uint16_t* kv, const int4* qdesc,
+                                   int32_t max_qtiles, int32_t heads, int32_t variant, void* out,
+                                   bool out_f32, float* lse, hipStream_t s);
+// Layer-independent parts of the tile images (V^T ones rows, zero padding
+// keys) and kslot[tok] = 64 * key tile + slot of every token (int32 [N]),
+// from launch_attn_schedule's kdesc; run once before launch_gemm_qkv_pack.
+hipError_t launch_attn_image_init(const int2* kdesc, int32_t max_ktiles, int32_t heads, uint16_t* kv,
+                                  int32_t* kslot, hipStream_t s);
 
 // ---- block backward helpers (backward.hip)
 // 64 x 64-tiled transpose of in [M, C] (fp32 or bf16; C a multiple of 4, Mp
