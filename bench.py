@@ -6,15 +6,22 @@ raster-order tower output, the 2x2 merge and the projector -- over one batch
 of synthetic input that is already resident in device memory.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload tower_448]
-    python bench.py --kernel {fc1,attention,attention_bwd,block_bwd,copy} [--workload ...]   # one case
+    python bench.py --kernel {fc1,resid_gemm,attention,attention_bwd,block_bwd,copy} [--workload ...]   # one case
 
 Prints one JSON line.  Beside the headline workload it times, with HIP events
-on the stream the kernels run on, the dominant kernel of the headline
-workload (the bf16 GEMM at the FC1 shape) and one vt_attention_varlen call
-through their own entry points, one vt_attention_backward call (the
-backward pass of the attention step) and one vt_block_backward call (a
-whole block's backward pass), and the 2016x2016 single image as a
-secondary workload.  "traffic" (HBM-side bytes per launch) comes from the
+on the stream the kernels run on:
+  roofline           the dominant kernel of the headline workload at 1,024
+                     tokens: the split-K partial GEMM of the O and FC2
+                     residual Linears (vt_linear with the partials epilogue,
+                     the kernel the blocks launch), and the same Linears with
+                     their fused split-K reduce + LayerNorm
+                     (vt_linear_residual_ln);
+  fc1_roofline       the FC1 GEMM (bias + GELU epilogue);
+  attention_roofline one vt_attention_varlen call;
+one vt_attention_backward and one vt_block_backward call, the 2016x2016
+single image as a secondary workload, and further workloads (224x224 one
+block, clips, 16 x 448x448 with its own attention and GEMM rooflines, mixed
+grids, 4096x4096).  "traffic" (HBM-side bytes per launch) comes from the
 FETCH_SIZE / WRITE_SIZE counter summaries under profiles/, and is null when
 those were taken on other kernel sources.  The CPU oracle is timed on a
 bounded sample (one 448x448 image through the full tower) on the host.
@@ -61,13 +68,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="tower_448", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--secondary", default="tower_2016", help="second workload ('' to skip)")
-    ap.add_argument("--more", default="tower_clip16,tower_448x16,tower_mixed8,tower_4096",
+    ap.add_argument("--more", default="block_224,tower_clip16,tower_448x16,tower_mixed8,tower_4096",
                     help="comma-separated further workloads, throughput only ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-pass lines (forward-only kernel profiles)")
     ap.add_argument("--kernel-iters", type=int, default=20)
-    ap.add_argument("--kernel", choices=["fc1", "attention", "attention_bwd", "block_bwd", "copy"],
+    ap.add_argument("--kernel", choices=["fc1", "resid_gemm", "attention", "attention_bwd", "block_bwd", "copy"],
                     default=None,
                     help="run only this kernel case (counter runs) and exit")
     return ap.parse_args()
@@ -149,9 +156,31 @@ def at_clock(achieved_tflops, ghz):
     return {"clock_ghz": ghz, "peak_at_clock": peak, "frac_at_clock": achieved_tflops / peak}
 
 
+COLD_BYTES = 320 << 20   # more than the 256 MB memory-side cache
+
+
+def weight_copies(torch, w):
+    """Distinct copies of a weight tensor totalling more than the memory-side
+    cache, so that a loop that cycles through them reads every weight from
+    HBM, as the tower does (each layer's weights are used once per step); the
+    activations stay shared and cache-hot, as in the tower."""
+    n = max(2, -(-COLD_BYTES // (w.numel() * w.element_size())))
+    return [w.clone() for _ in range(n)]
+
+
+def cycled(fns):
+    """One call of the next function of the list per call (round robin)."""
+    state = [0]
+
+    def call():
+        fns[state[0] % len(fns)]()
+        state[0] += 1
+    return call
+
+
 def fc1_case(vt, torch, M):
     """The FC1 GEMM of one block (M x 5120 x 1280, bias + GELU epilogue) as a
-    vt_linear call on seeded bf16 operands."""
+    vt_linear call on seeded bf16 operands, cycling through cold weight copies."""
     N, K = 5120, 1280
     g = np.random.Generator(np.random.PCG64(0))
     x = torch.from_numpy(synth.bf16_bits(g.standard_normal((M, K), dtype=np.float32)).view(np.int16)).cuda()
@@ -159,7 +188,46 @@ def fc1_case(vt, torch, M):
     b = torch.zeros(N, dtype=torch.int16, device="cuda")
     out = torch.empty((M, N), dtype=torch.int16, device="cuda")
     ws = vt.workspace(vt.vt_linear_workspace_size(M, N, K))
-    return (lambda: vt.vt_linear(x, M, K, w, N, b, vt.VT_EPI_GELU_TANH_BF16, out, ws)), 2.0 * M * N * K
+    fns = [lambda wc=wc: vt.vt_linear(x, M, K, wc, N, b, vt.VT_EPI_GELU_TANH_BF16, out, ws)
+           for wc in weight_copies(torch, w)]
+    return cycled(fns), 2.0 * M * N * K
+
+
+def residual_cases(vt, torch, M):
+    """The O (M x 1280 x 1280) and FC2 (M x 1280 x 5120) residual Linears of a
+    block on seeded bf16 operands, each call on the next of its cold weight
+    copies (weight_copies): per shape, (the GEMM kernel alone -- the
+    split-K partial products when the shape splits K, else the GEMM with its
+    residual epilogue --, the whole residual step with its reduce +
+    LayerNorm, FLOPs, splits)."""
+    g = np.random.Generator(np.random.PCG64(4))
+    bits = lambda shape, sc=1.0: torch.from_numpy(
+        synth.bf16_bits(g.standard_normal(shape, dtype=np.float32) * np.float32(sc)).view(np.int16)).cuda()
+    N = 1280
+    R = torch.from_numpy(g.standard_normal((M, N), dtype=np.float32)).cuda()
+    gam = torch.from_numpy(synth.bf16_bits(np.ones(N, np.float32)).view(np.int16)).cuda()
+    bet = torch.zeros(N, dtype=torch.int16, device="cuda")
+    ln = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    out = []
+    for K in (1280, 5120):
+        x, w, b = bits((M, K)), bits((N, K), 0.02), torch.zeros(N, dtype=torch.int16, device="cuda")
+        ws_copies = weight_copies(torch, w)
+        nws = vt.vt_linear_workspace_size(M, N, K)
+        ws = vt.workspace(nws)
+        splits = nws // (M * N * 4) if nws else 1
+        if splits > 1:
+            part = torch.empty(nws // 4, dtype=torch.float32, device="cuda")
+            gemm = cycled([lambda x=x, w=wc, K=K, part=part:
+                           vt.vt_linear(x, M, K, w, N, None, vt.VT_EPI_SPLITK_PARTIALS_F32, part)
+                           for wc in ws_copies])
+        else:
+            gemm = cycled([lambda x=x, w=wc, K=K, b=b, ws=ws: vt.vt_linear(x, M, K, w, N, b, vt.VT_EPI_RESID_F32, R, ws)
+                           for wc in ws_copies])
+        step = cycled([lambda x=x, w=wc, K=K, b=b, ws=ws:
+                       vt.vt_linear_residual_ln(x, M, K, w, N, b, R, gam, bet, 1e-6, ln, ws)
+                       for wc in ws_copies])
+        out.append((gemm, step, 2.0 * M * N * K, splits))
+    return out
 
 
 def attention_case(vt, torch, grids):
@@ -282,6 +350,37 @@ def profile_traffic(name, source):
         return None
 
 
+def residual_gemm_roofline(vt, torch, M, iters):
+    """The split-K partial GEMM of the O and FC2 residual Linears at M tokens
+    (the kernel of the blocks with the largest share of the 448x448 step):
+    achieved = (2 M N K of O + of FC2) / (the average launch time at the O
+    shape + at the FC2 shape).  with_reduce_ln: the same FLOPs over the time
+    of the whole residual step as the blocks run it, partials + the fused
+    split-K reduce, residual update and LayerNorm."""
+    cases = residual_cases(vt, torch, M)
+    flops = sum(c[2] for c in cases)
+    t_gemm = [time_kernel(torch, c[0], iters) for c in cases]
+    t_step = [time_kernel(torch, c[1], iters) for c in cases]
+    both = lambda: (cases[0][0](), cases[1][0]())
+    ghz = clock_under(vt, torch, both, iters, sum(t_gemm))
+    ach = flops / sum(t_gemm) / 1e12
+    splits = [c[3] for c in cases]
+    name = ("gemm_dl_kernel<128, 128, 4, 2, 3, 3, true, 64, 0> (split-K partial products of the O %dx1280x1280 "
+            "and FC2 %dx1280x5120 residual Linears, %d and %d splits)" % (M, M, splits[0], splits[1])
+            if min(splits) > 1 else "gemm_dl_kernel (O and FC2 residual Linears at %d tokens, unsplit)" % M)
+    return {"kernel": name, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": ach / PEAK_BF16_TFLOPS,
+            "traffic": profile_traffic("gemm_residual_%d_traffic" % M,
+                                       "vision_transformer_encoder_tiled_amd/csrc/gemm.hip"),
+            **at_clock(ach, ghz), "flops_per_launch": flops / 2, "flops_O_FC2": [c[2] for c in cases],
+            "avg_launch_us": sum(t_gemm) / 2 * 1e6, "launch_us_O_FC2": [t * 1e6 for t in t_gemm],
+            "with_reduce_ln": {"kernels": "partials + resid_ln_row_kernel (split-K sum, bias, residual, LayerNorm)",
+                               "achieved": flops / sum(t_step) / 1e12,
+                               "frac": flops / sum(t_step) / 1e12 / PEAK_BF16_TFLOPS,
+                               "step_us_O_FC2": [t * 1e6 for t in t_step]},
+            "note": "traffic is per launch, averaged over one O and one FC2 launch"}
+
+
 def gemm_roofline(vt, torch, M, iters):
     fn, flops = fc1_case(vt, torch, M)
     t = time_kernel(torch, fn, iters)
@@ -370,6 +469,9 @@ def kernel_only(a):
     wl = synth.WORKLOADS[a.workload]
     if a.kernel == "fc1":
         fn, _ = fc1_case(vt, torch, wl.tokens)
+    elif a.kernel == "resid_gemm":  # one O and one FC2 partial GEMM per call
+        cases = residual_cases(vt, torch, wl.tokens)
+        fn = lambda: (cases[0][0](), cases[1][0]())
     elif a.kernel == "attention":
         fn, _ = attention_case(vt, torch, list(wl.grids))
     elif a.kernel == "attention_bwd":
@@ -446,7 +548,8 @@ def main():
         "tflops_total": (gemm_f + attn_f) / (secs / a.steps) / 1e12,
     }
     M = wl.tokens
-    res["roofline"] = gemm_roofline(vt, torch, M, a.kernel_iters)
+    res["roofline"] = residual_gemm_roofline(vt, torch, M, a.kernel_iters)
+    res["fc1_roofline"] = gemm_roofline(vt, torch, M, a.kernel_iters)
     res["attention_roofline"] = attention_roofline(vt, torch, list(wl.grids), a.kernel_iters)
     if not a.no_backward:
         res["attention_backward"] = attention_backward_line(vt, torch, list(wl.grids), a.kernel_iters)
@@ -485,12 +588,17 @@ def main():
         k3 = max(3, a.steps // 4)
         s3, _ = run3.time(k3, 1)
         g3, at3 = workload_flops(wl3)
-        more.append({"workload": wl3.name, "patches": wl3.tokens, "items": wl3.n_img,
-                     "grids": [list(g) for g in wl3.grids][:16],
-                     "patches_per_s": wl3.tokens * k3 / s3, "items_per_s": wl3.n_img * k3 / s3,
-                     "ms_per_step": s3 / k3 * 1e3, "steps": k3,
-                     "tflops_total": (g3 + at3) / (s3 / k3) / 1e12})
+        line = {"workload": wl3.name, "patches": wl3.tokens, "items": wl3.n_img,
+                "grids": [list(g) for g in wl3.grids][:16], "layers": wl3.layers, "projector": wl3.projector,
+                "patches_per_s": wl3.tokens * k3 / s3, "items_per_s": wl3.n_img * k3 / s3,
+                "ms_per_step": s3 / k3 * 1e3, "steps": k3,
+                "tflops_total": (g3 + at3) / (s3 / k3) / 1e12}
         del run3
+        if name == "tower_448x16":  # a 448x448 workload that fills the chip: its own rooflines
+            it3 = max(3, a.kernel_iters // 2)
+            line["attention_roofline"] = attention_roofline(vt, torch, list(wl3.grids), it3)
+            line["gemm_roofline"] = gemm_roofline(vt, torch, wl3.tokens, it3)
+        more.append(line)
     if more:
         res["more_workloads"] = more
 

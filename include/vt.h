@@ -81,7 +81,11 @@ typedef enum vt_epilogue {
   VT_EPI_GELU_TANH_BF16 = 1,/* out bf16 = gelu_tanh(y)                        */
   VT_EPI_GELU_ERF_BF16 = 2, /* out bf16 = gelu_erf(y)                         */
   VT_EPI_RESID_F32 = 3,     /* out fp32 += y   (residual update, in place)    */
-  VT_EPI_F32 = 4            /* out fp32 = y                                   */
+  VT_EPI_F32 = 4,           /* out fp32 = y                                   */
+  VT_EPI_SPLITK_PARTIALS_F32 = 5 /* out fp32 [splits, M, N]: the split-K partial
+                               products x[:, Kz] W[:, Kz]^T of the K ranges the
+                               library splits this shape into, no bias, not
+                               summed (kernel-level measurement and tests) */
 } vt_epilogue;
 
 /* One item: t temporal patches x h x w patches (README Architecture: temporal
@@ -405,11 +409,32 @@ vt_status vt_mean_pool(const uint16_t* tower, const int32_t* cu_seqlens, int32_t
  * vt_linear: y = x W^T + b with x bf16 [M, K], W bf16 [N, K], b bf16 [N] or
  * NULL, fp32 accumulation, then the epilogue (see vt_epilogue); out is bf16
  * or fp32 [M, N].  K must be a multiple of 8; N a multiple of 64.
- * ws: at least vt_linear_workspace_size(M, N, K) bytes (may be 0). */
+ * ws: at least vt_linear_workspace_size(M, N, K) bytes (may be 0).
+ * Shapes with few output tiles split K: the fp32 partial products go to ws,
+ * vt_linear_workspace_size(M, N, K) = splits * M * N * 4 bytes, and a second
+ * kernel sums them in split order.  VT_EPI_SPLITK_PARTIALS_F32 stops before
+ * that sum: out receives the partials themselves (it must hold
+ * vt_linear_workspace_size(M, N, K) bytes), bias must be NULL, ws is unused;
+ * a shape that is not split returns VT_ERR_UNSUPPORTED. */
 size_t vt_linear_workspace_size(int32_t M, int32_t N, int32_t K);
 vt_status vt_linear(const uint16_t* x, int32_t M, int32_t K, const uint16_t* w, int32_t N,
                     const uint16_t* bias, vt_epilogue epi, void* out, void* ws, size_t ws_bytes,
                     void* stream);
+
+/* The residual step of a pre-LN block (README Architecture: the attention
+ * output projection followed by LN2, and the second MLP Linear followed by
+ * the next block's LN1), as the blocks run it:
+ *   R   += x W^T + b          (R fp32 [M, N], in place; b bf16 [N] or NULL)
+ *   out  = LN(R) * g + beta   (bf16 [M, N]; biased variance, eps inside the
+ *                              square root)
+ * When the shape splits K, the partial products are summed in split order,
+ * the bias and the old R added and the LayerNorm taken in one kernel; else
+ * the GEMM updates R in its epilogue and a LayerNorm kernel follows.
+ *   x bf16 [M, K], W bf16 [N, K]; K a multiple of 8; N a multiple of 256, at
+ *   most 4096.  ws: vt_linear_workspace_size(M, N, K) bytes. */
+vt_status vt_linear_residual_ln(const uint16_t* x, int32_t M, int32_t K, const uint16_t* w, int32_t N,
+                                const uint16_t* bias, float* R, const uint16_t* g, const uint16_t* beta,
+                                float eps, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
 /* vt_layer_norm: out bf16 [rows, width] = LN(x) * g + b over fp32 x [rows, width];
  * width must be a multiple of 256 and at most 4096. */

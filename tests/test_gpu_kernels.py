@@ -230,6 +230,57 @@ def test_linear_epilogues(vt, epi, M, N, K):
     assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -8 + 2e-5)
 
 
+@pytest.mark.parametrize("M,N,K", [(1024, 1280, 1280), (1024, 1280, 5120), (100, 1280, 5120),
+                                   (4096, 1280, 1280)])
+def test_linear_residual_ln(vt, M, N, K):
+    """vt_linear_residual_ln (R += x W^T + b, then LayerNorm) equals
+    vt_linear with the residual epilogue followed by vt_layer_norm bit for
+    bit.  Where the shape splits K (the O and FC2 shapes at 1,024 tokens: 3
+    splits; 100 rows: 12), the partials of VT_EPI_SPLITK_PARTIALS_F32 summed
+    on the host in split order, then the bias and the old R added (fp32),
+    give the same R bit for bit; 4,096 rows run unsplit.  R and the LayerNorm
+    output also match the oracle (rel-L2 1e-5; half a bf16 ulp)."""
+    log(f"linear + residual + LayerNorm {M}x{N}x{K}")
+    x = random_bf16((M, K), 51)
+    w = random_bf16((N, K), 52, 0.02)
+    b = random_bf16(N, 53, 0.1)
+    gam = synth.bf16_bits(bf16_f32(random_bf16(N, 54, 0.2)) + 1)
+    bet = random_bf16(N, 55, 0.1)
+    R0 = rng(56).standard_normal((M, N), dtype=np.float32)
+    xd, wd, bd, gd, betd = (dev_bits(a, torch) for a in (x, w, b, gam, bet))
+    nws = vt.vt_linear_workspace_size(M, N, K)
+    ws = vt.workspace(nws)
+    R1 = torch.from_numpy(R0.copy()).cuda()
+    out1 = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    vt.vt_linear_residual_ln(xd, M, K, wd, N, bd, R1, gd, betd, 1e-6, out1, ws)
+    R2 = torch.from_numpy(R0.copy()).cuda()
+    out2 = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    vt.vt_linear(xd, M, K, wd, N, bd, vt.VT_EPI_RESID_F32, R2, ws)
+    vt.vt_layer_norm(R2, M, N, gd, betd, 1e-6, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(R1, R2) and torch.equal(out1, out2)
+    Rg = R1.cpu().numpy()
+    if nws:
+        splits = nws // (M * N * 4)
+        part = torch.empty(splits * M * N, dtype=torch.float32, device="cuda")
+        vt.vt_linear(xd, M, K, wd, N, None, vt.VT_EPI_SPLITK_PARTIALS_F32, part)
+        torch.cuda.synchronize()
+        P = part.cpu().numpy().reshape(splits, M, N)
+        acc = P[0].copy()
+        for z in range(1, splits):
+            acc = acc + P[z]
+        log(f"  {splits} splits")
+        assert np.array_equal(R0 + (acc + bf16_f32(b)), Rg)
+    else:
+        with pytest.raises(vt.VtError):
+            vt.vt_linear(xd, M, K, wd, N, None, vt.VT_EPI_SPLITK_PARTIALS_F32, R2)
+    want = R0 + oracle.linear(bf16_f32(x), bf16_f32(w), bf16_f32(b))
+    assert rel_l2(Rg, want) < 1e-5
+    ln = oracle.layer_norm(Rg, bf16_f32(gam), bf16_f32(bet), 1e-6)
+    got = bf16_f32(host_bits(out1))
+    assert np.all(np.abs(got - ln) <= np.abs(ln) * 2.0 ** -8 + 1e-5)
+
+
 # ---------------------------------------------------------------- attention
 def attention_case(vt, grids, seed, rows=None, qk_scale=1.0, qkv_bits=None):
     """Run vt_attention_varlen (fp32 output) on seeded bf16 qkv (or the given

@@ -19,6 +19,7 @@ VT_OK, VT_ERR_INVALID_ARG, VT_ERR_UNSUPPORTED, VT_ERR_WORKSPACE, VT_ERR_HIP = ra
 VT_BF16, VT_FP32 = 0, 1
 VT_ORDER_WINDOW, VT_ORDER_RASTER = 0, 1
 VT_EPI_BF16, VT_EPI_GELU_TANH_BF16, VT_EPI_GELU_ERF_BF16, VT_EPI_RESID_F32, VT_EPI_F32 = range(5)
+VT_EPI_SPLITK_PARTIALS_F32 = 5
 VT_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 EXPORTED = ("vt_config_default", "vt_status_string", "vt_last_error", "vt_version",
@@ -28,7 +29,8 @@ EXPORTED = ("vt_config_default", "vt_status_string", "vt_last_error", "vt_versio
             "vt_linear_workspace_size", "vt_linear", "vt_layer_norm", "vt_attention_backward",
             "vt_attention_backward_workspace_size", "vt_block_backward",
             "vt_block_backward_workspace_size", "vt_tower_backward",
-            "vt_tower_backward_workspace_size", "vt_clock_probe", "vt_attention_varlen_noalloc")
+            "vt_tower_backward_workspace_size", "vt_clock_probe", "vt_attention_varlen_noalloc",
+            "vt_linear_residual_ln")
 
 
 class VtError(RuntimeError):
@@ -114,6 +116,8 @@ def _load():
         "vt_linear_workspace_size": (SZ, [I32, I32, I32]),
         "vt_linear": (ctypes.c_int, [_P, I32, I32, _P, I32, _P, ctypes.c_int, _P, _P, SZ, _P]),
         "vt_layer_norm": (ctypes.c_int, [_P, I32, I32, _P, _P, ctypes.c_float, _P, _P]),
+        "vt_linear_residual_ln": (ctypes.c_int, [_P, I32, I32, _P, I32, _P, _P, _P, _P, ctypes.c_float, _P,
+                                                 _P, SZ, _P]),
         "vt_mean_pool": (ctypes.c_int, [_P, _P, I32, I32, _P, _P]),
         "vt_plan_patches": (ctypes.c_int, [_P, ctypes.c_size_t, I32, ctypes.c_int64, _P, _P]),
         "vt_pack_items": (ctypes.c_int, [_P, _P, I32, ctypes.c_size_t, _P, _P]),
@@ -360,6 +364,12 @@ def vt_tower_backward(cfg, pixels, grids, tw: TowerWeights, d_tower, tg: TowerGr
 def vt_linear(x, M, K, w, N, bias, epi, out, ws=None, stream=None):
     _check(LIB.vt_linear(_ptr(x), M, K, _ptr(w), N, _ptr(bias), epi, _ptr(out), _ptr(ws),
                          ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def vt_linear_residual_ln(x, M, K, w, N, bias, R, g, beta, eps, out, ws=None, stream=None):
+    _check(LIB.vt_linear_residual_ln(_ptr(x), M, K, _ptr(w), N, _ptr(bias), _ptr(R), _ptr(g), _ptr(beta),
+                                     ctypes.c_float(eps), _ptr(out), _ptr(ws),
+                                     ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def vt_plan_patches(cfg, budget_bytes, n_img=1, max_pixels=0):

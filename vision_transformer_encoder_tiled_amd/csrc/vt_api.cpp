@@ -1161,9 +1161,48 @@ VT_API vt_status vt_linear(const uint16_t* x, int32_t M, int32_t K, const uint16
   if (N % 64) return fail(VT_ERR_UNSUPPORTED, "N must be a multiple of 64 (got %d)", N);
   if (int64_t(M) * N > (int64_t(1) << 34) || int64_t(M) > kMaxTokens)
     return fail(VT_ERR_UNSUPPORTED, "M x N too large");
-  if (epi < VT_EPI_BF16 || epi > VT_EPI_F32) return fail(VT_ERR_INVALID_ARG, "bad epilogue %d", int(epi));
+  if (epi < VT_EPI_BF16 || epi > VT_EPI_SPLITK_PARTIALS_F32)
+    return fail(VT_ERR_INVALID_ARG, "bad epilogue %d", int(epi));
+  if (epi == VT_EPI_SPLITK_PARTIALS_F32) {
+    if (bias) return fail(VT_ERR_INVALID_ARG, "the split-K partials carry no bias (bias must be NULL)");
+    if (vt::plan_gemm(M, N, K).splits < 2)
+      return fail(VT_ERR_UNSUPPORTED, "%d x %d x %d runs without split-K: there are no partials", M, N, K);
+    VT_TRY_HIP(vt::launch_gemm_partials(x, M, K, w, N, out, static_cast<hipStream_t>(stream)));
+    return VT_OK;
+  }
   if ((st = check_ws(ws, ws_bytes, vt::gemm_workspace_bytes(M, N, K))) != VT_OK) return st;
   VT_TRY_HIP(vt::launch_gemm(x, M, K, w, N, bias, int(epi), out, ws, static_cast<hipStream_t>(stream)));
+  return VT_OK;
+}
+
+VT_API vt_status vt_linear_residual_ln(const uint16_t* x, int32_t M, int32_t K, const uint16_t* w,
+                                       int32_t N, const uint16_t* bias, float* R, const uint16_t* g,
+                                       const uint16_t* beta, float eps, uint16_t* out, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  vt_status st;
+  if ((st = check_ptr(x, "x")) != VT_OK) return st;
+  if ((st = check_ptr(w, "w")) != VT_OK) return st;
+  if ((st = check_ptr(R, "R")) != VT_OK) return st;
+  if ((st = check_ptr(g, "g")) != VT_OK) return st;
+  if ((st = check_ptr(beta, "beta")) != VT_OK) return st;
+  if ((st = check_ptr(out, "out")) != VT_OK) return st;
+  if (bias && !aligned16(bias)) return fail(VT_ERR_INVALID_ARG, "bias is not 16-byte aligned");
+  if (M <= 0 || N <= 0 || K <= 0) return fail(VT_ERR_INVALID_ARG, "M, N, K must be positive");
+  if (K % 8) return fail(VT_ERR_UNSUPPORTED, "K must be a multiple of 8 (got %d)", K);
+  if (N % 256 || N > 4096) return fail(VT_ERR_UNSUPPORTED, "N must be a multiple of 256, at most 4096 (got %d)", N);
+  if (int64_t(M) > kMaxTokens) return fail(VT_ERR_UNSUPPORTED, "M too large");
+  if (!(eps > 0.f)) return fail(VT_ERR_INVALID_ARG, "eps must be > 0");
+  if ((st = check_ws(ws, ws_bytes, vt::gemm_workspace_bytes(M, N, K))) != VT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int splits = vt::plan_gemm(M, N, K).splits;
+  if (splits > 1) {  // the blocks' fused path (run_block)
+    VT_TRY_HIP(vt::launch_gemm_partials(x, M, K, w, N, ws, s));
+    VT_TRY_HIP(vt::launch_resid_ln(reinterpret_cast<const float*>(ws), splits, M, N, bias, R, g, beta, eps,
+                                   out, s));
+  } else {
+    VT_TRY_HIP(vt::launch_gemm(x, M, K, w, N, bias, vt::kEpiResid, R, ws, s));
+    VT_TRY_HIP(vt::launch_layer_norm(R, M, N, g, beta, eps, out, s));
+  }
   return VT_OK;
 }
 
