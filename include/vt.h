@@ -151,7 +151,9 @@ const char* vt_last_error(void);
 const char* vt_version(void);
 
 /* Workspace bytes for vt_tower_forward / vt_patch_embed / vt_merge_project on
- * this grid list.  Affine in the token count (no term grows with seq^2).
+ * this grid list.  Affine in the token count (no term grows with seq^2), plus
+ * a fixed 86 MB of attention partial records once a call is large enough for
+ * the lean attention kernels.
  * Returns 0 and sets vt_last_error() if the arguments are invalid. */
 size_t vt_tower_workspace_size(const vt_config* cfg, const vt_grid_thw* grid, int32_t n_img);
 
@@ -199,7 +201,13 @@ vt_status vt_patch_embed(const vt_config* cfg, const uint16_t* pixels, const vt_
  * |RoPE(q)| log2(e)/sqrt(head_dim), |RoPE(k)| and |v| must stay below 65504
  * (larger values give infinities or NaN; they are not clamped).  bf16 q, k,
  * v inside that range are represented exactly or to fp16 rounding (2^-11).
- * No [n, n] buffer is formed: memory is O(total_tokens). */
+ * No [n, n] buffer is formed: memory is O(total_tokens).
+ * Rounding: a call's results are deterministic.  On large calls the work
+ * that would leave the GPU's workgroups partly idle in the last round is cut
+ * by key tiles across all of them and the pieces merged; where an image's
+ * rows are cut depends on the whole call (the other images packed into it,
+ * the GPU's CU count), so the same image in another batch can differ in its
+ * last bits. */
 vt_status vt_attention_varlen(const vt_config* cfg, const uint16_t* qkv, const int32_t* cu_seqlens,
                               const int32_t* pos_thw, int32_t n_img, int32_t total_tokens,
                               int32_t max_seqlen, void* out, vt_dtype out_dtype, void* ws,
@@ -208,8 +216,11 @@ vt_status vt_attention_varlen(const vt_config* cfg, const uint16_t* qkv, const i
 /* ---------------------------------------------------------------- no allocation
  * For callers that can neither allocate device memory nor pass a workspace:
  * code under HIP graph capture, tight serving loops, harnesses that forbid
- * hipMalloc.  vt_attention_varlen_noalloc computes exactly what
- * vt_attention_varlen computes (the same kernels, the same bits) with its
+ * hipMalloc.  vt_attention_varlen_noalloc computes what vt_attention_varlen
+ * computes, with the same kernels, except that it never cuts the last round
+ * across workgroups (the merge's partial records do not fit the array): its
+ * results equal vt_attention_varlen's bit for bit when that call does not
+ * cut (for example 7 images of 448x448), and to rounding otherwise.  Its
  * scratch -- the attention schedule, the rotated fp16 Q, the K/V tile images
  * and the RoPE table, about 8.5 KB per token plus 384 KB per image at 16
  * heads -- in one fixed device array of VT_NOALLOC_SCRATCH_BYTES inside the

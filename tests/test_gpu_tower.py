@@ -305,8 +305,11 @@ def test_2016_tower_end_to_end(vt, dev):
 
 def test_2016_tower_memory_and_invariance(vt, dev):
     """The full 2016x2016 tower: scratch is linear in tokens (no [n, n]
-    buffer), results are finite, deterministic, and unchanged when another
-    image is packed into the same call."""
+    buffer), results are finite, deterministic (bitwise, for the same
+    batch), and the same up to rounding when another image is packed into the
+    same call: the attention kernel spreads the last, partial round of its
+    work over all workgroups by key tiles, and where an image's rows are cut
+    depends on the whole batch, so their last bits may change."""
     wl = synth.WORKLOADS["tower_2016"]
     grids = list(wl.grids)
     px = synth.make_batch_pixels(wl)
@@ -329,8 +332,11 @@ def test_2016_tower_memory_and_invariance(vt, dev):
     # pack a 448x448 image after it: the 2016x2016 rows do not change
     px2 = np.concatenate([px, synth.make_pixels(32, 32, 2).reshape(-1)])
     c = gpu_tower(vt, dev[1], grids + [(1, 32, 32)], px2, merged=False)
-    assert np.array_equal(c["tower"][:20736], a["tower"])
-    assert np.array_equal(c["out"][:5184], a["out"])
+    e = rel_l2(bf16_f32(c["tower"][:20736]), bf16_f32(a["tower"]))
+    cos = cosine_rows(bf16_f32(c["out"][:5184]), bf16_f32(a["out"]))
+    log(f"  packed with a 448x448 image: tower rel-L2 {e:.2e}, projected cosine min {cos.min():.7f}")
+    assert e <= 1e-2      # the per-layer bound against the oracle (measured: 4.0e-3)
+    assert cos.min() >= 0.9999
 
 
 # ---------------------------------------------------------------- clips (t > 1)

@@ -158,3 +158,123 @@ def test_gemm_epilogue_staging_is_a_bijection(BM, BN, GWM, GWN, NST, BK, CW, f32
                     assert row_col not in done
                     done[row_col] = tid
     assert len(done) == BM * BN
+
+
+# ---------------------------------------------------------------- lean attention split tail
+def tail_pieces(n_items_keys, heads, S, min_tiles=8):
+    """attention.hip tail_plan, the piece walk of attention_lean_kernel and
+    the record lookup of attn_tail_merge_kernel.  n_items_keys[qt] = key
+    tiles of q-tile qt (the schedule's order).  Returns the (qt, head, j0, j1,
+    slot) pieces of every block and the merge's (item -> records) map."""
+    nq = len(n_items_keys)
+    qkpre = np.concatenate([[0], np.cumsum(n_items_keys)]).astype(np.int64)
+    n_items = nq * heads
+    nw = (n_items // S) * S // heads * heads
+    T = heads * (qkpre[nq] - qkpre[nw // heads]) if nw < n_items else 0
+    if T < S * min_tiles:
+        nw, T = n_items, 0
+    pieces = [(i // heads, i % heads, 0, n_items_keys[i // heads], -1) for i in range(nw)]
+    if T == 0:
+        return pieces, {}, nw, T
+    qt_tail = nw // heads
+    tbase = qkpre[qt_tail]
+    assert T < 2 ** 31
+    for k in range(S):
+        lo, hi = k * T // S, (k + 1) * T // S
+        pos = lo
+        a, z = qt_tail, nq - 1
+        while a < z:
+            mid = (a + z + 1) >> 1
+            if heads * (qkpre[mid] - tbase) <= lo:
+                a = mid
+            else:
+                z = mid - 1
+        qt = a
+        while pos < hi:
+            while heads * (qkpre[qt + 1] - tbase) <= pos:
+                qt += 1
+            n = qkpre[qt + 1] - qkpre[qt]
+            off = pos - heads * (qkpre[qt] - tbase)
+            head, j0 = off // n, off % n
+            j1 = min(n, j0 + (hi - pos))
+            slot = -1 if (j0 == 0 and j1 == n) else (2 * k if pos == lo else 2 * k + 1)
+            pieces.append((qt, head, j0, j1, slot))
+            pos += j1 - j0
+    merge = {}
+    for u in range(S + heads):                  # the merge kernel's grid
+        item = nw + u
+        if item >= n_items:
+            continue
+        qt, head = item // heads, item % heads
+        n = qkpre[qt + 1] - qkpre[qt]
+        P0 = heads * (qkpre[qt] - tbase) + head * n
+        wg_of = lambda p: ((p + 1) * S - 1) // T
+        kA, kB = wg_of(P0), wg_of(P0 + n - 1)
+        if kA == kB:
+            continue
+        merge[(qt, head)] = [2 * k if k * T // S >= P0 else 2 * k + 1 for k in range(kA, kB + 1)]
+    return pieces, merge, nw, T
+
+
+def q_tiles(grids, WQ):
+    """Key tiles per q-tile in the schedule's order (largest image first)."""
+    sizes = sorted((t * h * w for t, h, w in grids), reverse=True)
+    return [(-(-n // 64)) for n in sizes for _ in range(-(-n // WQ))]
+
+
+@pytest.mark.parametrize("grids,WQ,S", [
+    ([(1, 144, 144)], 256, 512),                 # 2016x2016: 1,296 items, 2.53 rounds
+    ([(1, 112, 112)], 256, 512),
+    ([(1, 128, 128)], 256, 512),                 # exactly two rounds: no tail
+    ([(1, 256, 256)], 256, 512),
+    ([(1, 32, 32)] * 16, 256, 512),
+    ([(1, 48, 48)], 128, 768),
+    ([(1, 96, 96), (1, 16, 18), (1, 40, 22), (1, 64, 64), (1, 2, 2), (1, 90, 60)], 256, 512),
+    ([(1, 96, 96), (1, 16, 18), (1, 40, 22), (1, 64, 64), (1, 2, 2), (1, 90, 60)], 128, 768),
+    ([(1, 60, 80), (1, 20, 24)], 128, 700),      # a resident count that is no multiple of the heads
+])
+def test_lean_split_tail_covers_every_key_tile_once(grids, WQ, S):
+    heads = 16
+    nk = q_tiles(grids, WQ)
+    pieces, merge, nw, T = tail_pieces(nk, heads, S)
+    seen = {}
+    slots = {}
+    for qt, head, j0, j1, slot in pieces:
+        assert 0 <= j0 < j1 <= nk[qt]
+        for j in range(j0, j1):
+            assert (qt, head, j) not in seen
+            seen[(qt, head, j)] = slot
+        if slot >= 0:
+            assert slot not in slots and slot < 2 * S
+            slots[slot] = (qt, head, j0, j1)
+    assert len(seen) == heads * sum(nk)
+    # each cut item's records are exactly the pieces written for it, and they
+    # partition its key tiles
+    cut = {(qt, head) for qt, head, j0, j1, slot in pieces if slot >= 0}
+    assert cut == set(merge)
+    for key, recs in merge.items():
+        assert len(recs) >= 2
+        spans = sorted(slots[r][2:] for r in recs)
+        assert all(slots[r][:2] == key for r in recs)
+        assert spans[0][0] == 0 and spans[-1][1] == nk[key[0]]
+        assert all(a[1] == b[0] for a, b in zip(spans, spans[1:]))
+    if T:
+        assert len(nk) * heads - nw < S + heads       # the merge grid covers the tail
+        assert min(j1 - j0 for *_, j0, j1, _s in pieces[nw:]) >= 1
+    # the launch: max_qtiles x heads + S blocks; those that are neither a whole
+    # item nor a tail range exit before reading a q-tile descriptor
+    N = sum(t * h * w for t, h, w in grids)
+    max_qtiles = -(-N // WQ) + len(grids)
+    assert len(nk) <= max_qtiles
+    n_run = 0
+    for b in range(max_qtiles * heads + S):
+        in_tail = T > 0 and b >= nw
+        if not in_tail and b >= nw:
+            continue
+        if in_tail:
+            assert b - nw >= 0
+            n_run += b - nw < S
+        else:
+            assert b // heads < len(nk)
+            n_run += 1
+    assert n_run == nw + (S if T else 0)

@@ -1,7 +1,9 @@
 """vt_attention_varlen_noalloc -- the attention step with its scratch in the
 library's fixed device array instead of a caller workspace -- against
 vt_attention_varlen on the same inputs, through the C ABI.  Both run the same
-kernels, so the outputs must be equal bit for bit: on two calls in a row, the
+kernels, and on these inputs vt_attention_varlen does not cut its last round
+of work across workgroups (which the no-allocation call never does), so the
+outputs must be equal bit for bit: on two calls in a row, the
 second smaller than the first (the array keeps the first call's contents),
 in fp32 and bf16 output, and when the call is captured into a HIP graph and
 replayed."""

@@ -68,6 +68,8 @@
 // largest images first (longest-processing-time order).  With 16 heads and
 // round-robin dispatch over the 8 XCDs, every q-tile of one (image, head)
 // lands on the same XCD, so its K/V stream is shared through one L2.
+#include <algorithm>
+
 #include "vt_device.h"
 #include "vt_kernels.h"
 
@@ -499,156 +501,346 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(
 // as attention_kernel with one key group (S^T onto -m, lazy rescale, P from
 // the score registers, the ones row for l), but register-lean so that more
 // wavefronts share each SIMD and hide one another's latencies: one set of
-// scores (no one-tile-ahead pipelining), K and V^T fragments read as they are
-// consumed, -m written into the score accumulators before each tile's first
-// MFMA (32 moves instead of a loop-carried 16-register C operand), and a
-// 2-stage ring (50 KB of LDS): 126 VGPRs.  4 wavefronts = 128 queries, three
-// workgroups per CU (LDS-bound), or 8 wavefronts = 256 queries sharing one
-// K/V stream, two workgroups per CU: four wavefronts per SIMD.  WPE is the
-// wavefronts per SIMD the register budget is set for.  A wavefront raises
-// its issue priority (s_setprio) over its two MFMA sections, so that of the
-// wavefronts sharing a SIMD, one with a matrix product ready goes ahead of
-// one in the softmax arithmetic and the matrix unit idles less (about 1% at
-// 20,736 tokens; scheduling only, the results are the same bits).
+// scores (no one-tile-ahead pipelining), K and V^T fragments read just ahead
+// of use (each K fragment one product ahead), -m written into the score
+// accumulators before each tile's first MFMA (16 moves instead of a
+// loop-carried 16-register C operand), and a 2-stage ring (50 KB of LDS):
+// 126 VGPRs.  4 wavefronts = 128 queries, three workgroups per CU
+// (LDS-bound), or 8 wavefronts = 256 queries sharing one K/V stream, two
+// workgroups per CU: four wavefronts per SIMD.  WPE is the wavefronts per
+// SIMD the register budget is set for.  A wavefront raises its issue
+// priority (s_setprio) over its two MFMA sections, so that of the wavefronts
+// sharing a SIMD, one with a matrix product ready goes ahead of one in the
+// softmax arithmetic and the matrix unit idles less (about 1% at 20,736
+// tokens; scheduling only, the results are the same bits).
+//
+// Work split (AttnTail in vt_kernels.h): block b < n_whole runs item b --
+// q-tile b / heads, head b % heads -- over all its key tiles; with a split
+// tail, block n_whole + k runs key tiles [k T / S, (k+1) T / S) of the tail,
+// one piece per item it touches, and an item it does not run whole goes to
+// partial record 2k (the range's first piece) or 2k + 1 (its last).
+namespace {
+struct TailPlan {
+  int32_t n_whole;  // items run whole, one per block
+  int32_t qt_tail;  // first q-tile of the split tail
+  int64_t T;        // key tiles of the tail over all heads (0: no split)
+};
+__device__ __forceinline__ TailPlan tail_plan(int nq, int heads, int S, const int32_t* qkpre) {
+  TailPlan p{nq * heads, nq, 0};
+  if (S <= 0) return p;
+  const int n_items = nq * heads;
+  const int nw = (n_items / S) * S / heads * heads;  // whole rounds, cut at a q-tile boundary
+  if (nw >= n_items) return p;
+  const int64_t T = int64_t(heads) * (qkpre[nq] - qkpre[nw / heads]);
+  if (T < int64_t(S) * kAttnTailMinTiles) return p;
+  p.n_whole = nw;
+  p.qt_tail = nw / heads;
+  p.T = T;
+  return p;
+}
+}  // namespace
+
 template <int NW, int NST, int WPE>
 __global__ void __launch_bounds__(64 * NW, WPE) attention_lean_kernel(
     const uint16_t* __restrict__ qpk, const uint16_t* __restrict__ kv,
     const int4* __restrict__ qdesc, int32_t heads, void* __restrict__ out, int32_t out_f32,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, const int32_t* __restrict__ qkpre, const int32_t* __restrict__ nq_ptr,
+    int32_t tail_wgs, float* __restrict__ part) {
   constexpr int COPIES = IMG_BYTES / (1024 * NW);
   constexpr int WQ = 32 * NW;
+  constexpr int REC = WQ * 82;  // partial record: O [WQ][80], m [WQ], l [WQ] (fp32)
   extern __shared__ __align__(16) char lds[];
-  const int head = blockIdx.x % heads;
-  const int4 desc = qdesc[blockIdx.x / heads];
-  if (desc.x < 0) return;
-  const int q0 = desc.x, kbeg = desc.y, kend = desc.z;
-  const int qend = min(q0 + WQ, kend);
-  const int ntiles = (kend - kbeg + BKV - 1) / BKV;
-  const char* src = reinterpret_cast<const char*>(kv) + (int64_t(desc.w) * heads + head) * IMG_BYTES;
   const int64_t tile_stride = int64_t(heads) * IMG_BYTES;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hf = lane >> 5, ln = lane & 31;
-  const uint32_t lds_wave = lds_offset(lds) + 1024 * wave;
-  auto issue = [&](int t) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_wave + (t % NST) * STAGE_BYTES);
-    const char* g = src + t * tile_stride + 1024 * wave + 16 * lane;
-#pragma unroll
-    for (int c = 0; c < COPIES; ++c) dma16(g + NW * 1024 * c, base + NW * 1024 * c);
-  };
-  const int qrow = q0 + wave * 32 + ln;
-  const bool qvalid = qrow < qend;
-  const int qr = qvalid ? qrow : qend - 1;
-  f16x8_t qfrag[5];
-  {
-    const uint4* q = reinterpret_cast<const uint4*>(qpk + (int64_t(qr) * heads + head) * HD);
-#pragma unroll
-    for (int s = 0; s < 5; ++s) qfrag[s] = __builtin_bit_cast(f16x8_t, q[2 * s + hf]);
+
+  // ---- this block's work: one whole item, or a range of the split tail.
+  // Every quantity here is uniform over the block; readfirstlane keeps it in
+  // scalar registers.
+  auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+  const int b = blockIdx.x;
+  TailPlan plan{0, 0, 0};
+  int nq = 0;
+  if (tail_wgs > 0) {
+    nq = uni(*nq_ptr);
+    plan = tail_plan(nq, heads, tail_wgs, qkpre);
   }
-  const int koff = ln * KROW * 2 + 16 * hf;
-  const int voff = K_BYTES + ln * VROW * 2 + 16 * hf;
-  f32x16_t acc[3];
-#pragma unroll
-  for (int d = 0; d < 3; ++d)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[d][e] = 0.f;
-  float m_use = 0.f;
-#pragma unroll
-  for (int r = 0; r < NST - 1; ++r)
-    if (r < ntiles) issue(r);
-  for (int t = 0; t < ntiles; ++t) {
-    wait_vmcnt<0>();
-    wait_lds_reads();
-    wg_barrier();
-    if (t + NST - 1 < ntiles) issue(t + NST - 1);
-    const char* st = lds + (t % NST) * STAGE_BYTES;
-    f32x16_t sc[2];
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sc[b][e] = -m_use;
-      sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-          *reinterpret_cast<const f16x8_t*>(st + koff + b * 32 * KROW * 2), qfrag[0], sc[b], 0, 0, 0);
+  const bool in_tail = plan.T > 0 && b >= plan.n_whole;
+  // With a tail allowance the grid runs past the schedule's q-tile slots:
+  // blocks past the last whole item that are not tail blocks have no work.
+  if (tail_wgs > 0 && !in_tail && b >= plan.n_whole) return;
+  // tail positions (key tiles over all heads) fit in 32 bits; only the
+  // products k T need 64
+  int lo = 0, hi = 0, pos = 0, tbase = 0, qt = b / heads, k = 0;
+  if (in_tail) {
+    k = b - plan.n_whole;
+    if (k >= tail_wgs) return;
+    lo = uni(int(int64_t(k) * plan.T / tail_wgs));
+    hi = uni(int(int64_t(k + 1) * plan.T / tail_wgs));
+    pos = lo;
+    tbase = uni(qkpre[plan.qt_tail]);
+    int a = plan.qt_tail, z = nq - 1;  // the q-tile holding position lo
+    while (a < z) {
+      const int mid = (a + z + 1) >> 1;
+      if (heads * (uni(qkpre[mid]) - tbase) <= lo) a = mid; else z = mid - 1;
     }
-#pragma unroll
-    for (int sl = 1; sl < 5; ++sl)
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-        sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-            *reinterpret_cast<const f16x8_t*>(st + koff + b * 32 * KROW * 2 + 32 * sl), qfrag[sl], sc[b], 0,
-            0, 0);
-    __builtin_amdgcn_s_setprio(0);
-    const int kt = kbeg + t * BKV;
-    if (kt + BKV > kend) {
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (kt + 32 * b + 8 * (e >> 2) + 4 * hf + (e & 3) >= kend) sc[b][e] = -INFINITY;
+    qt = uni(a);
+  }
+
+  for (bool first = true;; first = false) {
+    int head, j0, j1, slot;
+    if (in_tail) {
+      if (pos >= hi) break;
+      while (heads * (uni(qkpre[qt + 1]) - tbase) <= pos) ++qt;
+      const int kq = uni(qkpre[qt]);
+      const int n = uni(qkpre[qt + 1]) - kq;
+      const int off = pos - heads * (kq - tbase);
+      head = uni(off / n);
+      j0 = uni(off - head * n);
+      j1 = uni(min(n, j0 + (hi - pos)));
+      slot = (j0 == 0 && j1 == n) ? -1 : (pos == lo ? 2 * k : 2 * k + 1);
+      pos += j1 - j0;
+    } else {
+      if (!first) break;
+      head = b % heads;
+      j0 = 0;
+      j1 = -1;  // all key tiles
+      slot = -1;
     }
-    float mx = fmaxf(sc[0][0], sc[0][1]);
+    // Lane quantities are formed anew for each piece (tid passes through an
+    // empty asm statement): hoisted above the piece loop they would stay live
+    // across the whole kernel and push the tile loop past its register budget.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6;
+    const int hf = lane >> 5, ln = lane & 31;
+    const uint32_t lds_wave = lds_offset(lds) + 1024 * wave;
+    const int koff = ln * KROW * 2 + 16 * hf;
+    const int voff = K_BYTES + ln * VROW * 2 + 16 * hf;
+    const int4 desc = qdesc[qt];
+    if (desc.x < 0) return;
+    const int q0 = uni(desc.x), kbeg = uni(desc.y), kend = uni(desc.z);
+    const int qend = min(q0 + WQ, kend);
+    if (j1 < 0) j1 = (kend - kbeg + BKV - 1) / BKV;
+    const int ntiles = j1 - j0;
+    const char* src = reinterpret_cast<const char*>(kv) + (int64_t(uni(desc.w)) * heads + head) * IMG_BYTES +
+                      int64_t(j0) * tile_stride;
+    if (!first) {  // the previous piece's waves are done with the ring
+      wait_lds_reads();
+      wg_barrier();
+    }
+    auto issue = [&](int t) {
+      const uint32_t base = __builtin_amdgcn_readfirstlane(lds_wave + (t % NST) * STAGE_BYTES);
+      const char* g = src + t * tile_stride + 1024 * wave + 16 * lane;
 #pragma unroll
-    for (int e = 2; e < 16; ++e) mx = fmaxf(mx, sc[0][e]);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[1][e]);
+      for (int c = 0; c < COPIES; ++c) dma16(g + NW * 1024 * c, base + NW * 1024 * c);
+    };
+    const int qrow = q0 + wave * 32 + ln;
+    const bool qvalid = qrow < qend;
+    const int qr = qvalid ? qrow : qend - 1;
+    f16x8_t qfrag[5];
     {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const uint4* q = reinterpret_cast<const uint4*>(qpk + (int64_t(qr) * heads + head) * HD);
+#pragma unroll
+      for (int s = 0; s < 5; ++s) qfrag[s] = __builtin_bit_cast(f16x8_t, q[2 * s + hf]);
     }
-    if (t == 0 || __any(mx > kLazy)) {
-      const float delta = t == 0 ? mx : fmaxf(mx, 0.f);
-      m_use += delta;
-      if (t > 0) {
-        const float alpha = __builtin_amdgcn_exp2f(-delta);
+    f32x16_t acc[3];
 #pragma unroll
-        for (int d = 0; d < 3; ++d)
+    for (int d = 0; d < 3; ++d)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) acc[d][e] *= alpha;
+      for (int e = 0; e < 16; ++e) acc[d][e] = 0.f;
+    float m_use = 0.f;
+#pragma unroll
+    for (int r = 0; r < NST - 1; ++r)
+      if (r < ntiles) issue(r);
+    for (int t = 0; t < ntiles; ++t) {
+      wait_vmcnt<0>();
+      wait_lds_reads();
+      wg_barrier();
+      if (t + NST - 1 < ntiles) issue(t + NST - 1);
+      const char* st = lds + (t % NST) * STAGE_BYTES;
+      f32x16_t sc[2];
+      __builtin_amdgcn_s_setprio(1);
+      {
+        // K fragment i = (key block i & 1, dim slice i >> 1), read one
+        // product ahead of its use.
+        const char* kp = st + koff;
+        auto kfrag = [&](int i) {
+          return *reinterpret_cast<const f16x8_t*>(kp + (i & 1) * 32 * KROW * 2 + 32 * (i >> 1));
+        };
+        f16x8_t kf[2] = {kfrag(0), kfrag(1)};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[0][e] = sc[1][e] = -m_use;
+#pragma unroll
+        for (int i = 0; i < 10; ++i) {
+          sc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[i & 1], qfrag[i >> 1], sc[i & 1], 0, 0, 0);
+          if (i + 2 < 10) kf[i & 1] = kfrag(i + 2);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      const int kt = kbeg + (j0 + t) * BKV;
+      if (kt + BKV > kend) {
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (kt + 32 * bb + 8 * (e >> 2) + 4 * hf + (e & 3) >= kend) sc[bb][e] = -INFINITY;
+      }
+      float mx = fmaxf(sc[0][0], sc[0][1]);
+#pragma unroll
+      for (int e = 2; e < 16; ++e) mx = fmaxf(mx, sc[0][e]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[1][e]);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      if (t == 0 || __any(mx > kLazy)) {
+        const float delta = t == 0 ? mx : fmaxf(mx, 0.f);
+        m_use += delta;
+        if (t > 0) {
+          const float alpha = __builtin_amdgcn_exp2f(-delta);
+#pragma unroll
+          for (int d = 0; d < 3; ++d)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[d][e] *= alpha;
+        }
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sc[bb][e] -= delta;
+      }
+      const char* vst = st + voff;
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        f16x8_t pf[2];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) pf[e >> 3][e & 7] = (_Float16)__builtin_amdgcn_exp2f(sc[bb][e]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int d = 0; d < 3; ++d)
+            acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                *reinterpret_cast<const f16x8_t*>(vst + 32 * d * VROW * 2 + 32 * (2 * bb + h)), pf[h], acc[d],
+                0, 0, 0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+    }
+    // acc[d][4g + r] is dim 32d + 8g + 4hf + r of query ln; the row sum l
+    // (dim 80) is acc[2][8] in the lanes with hf == 0.
+    const float l_half0 = __shfl(acc[2][8], ln, 64);
+    if (slot >= 0) {
+      // A piece of an item: unnormalized O, the running max and the row sum.
+      float* rec = part + int64_t(slot) * REC;
+      const int ql = wave * 32 + ln;
+      if (hf == 0) {
+        rec[WQ * 80 + ql] = m_use;
+        rec[WQ * 81 + ql] = l_half0;
       }
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int d = 0; d < 3; ++d)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sc[b][e] -= delta;
+        for (int g = 0; g < 4; ++g) {
+          const int dim = 32 * d + 8 * g + 4 * hf;
+          if (dim < HD)
+            *reinterpret_cast<float4*>(rec + ql * HD + dim) =
+                make_float4(acc[d][4 * g], acc[d][4 * g + 1], acc[d][4 * g + 2], acc[d][4 * g + 3]);
+        }
+      continue;
     }
-    const char* vst = st + voff;
-    __builtin_amdgcn_s_setprio(1);
+    const float inv = 1.0f / l_half0;
+    if (qvalid) {
+      if (lse && hf == 0) lse[int64_t(qrow) * heads + head] = m_use + log2f(l_half0);
+      const int64_t orow = int64_t(qrow) * heads * HD + head * HD;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      f16x8_t pf[2];
+      for (int d = 0; d < 3; ++d) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) pf[e >> 3][e & 7] = (_Float16)__builtin_amdgcn_exp2f(sc[b][e]);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int d = 0; d < 3; ++d)
-          acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              *reinterpret_cast<const f16x8_t*>(vst + 32 * d * VROW * 2 + 32 * (2 * b + h)), pf[h], acc[d], 0,
-              0, 0);
-    }
-    __builtin_amdgcn_s_setprio(0);
-  }
-  const float l_half0 = __shfl(acc[2][8], ln, 64);
-  const float inv = 1.0f / l_half0;
-  if (!qvalid) return;
-  if (lse && hf == 0) lse[int64_t(qrow) * heads + head] = m_use + log2f(l_half0);
-  const int64_t orow = int64_t(qrow) * heads * HD + head * HD;
-#pragma unroll
-  for (int d = 0; d < 3; ++d) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int dim = 32 * d + 8 * g + 4 * hf;
-      if (dim >= HD) continue;
-      const float o0 = acc[d][4 * g] * inv, o1 = acc[d][4 * g + 1] * inv;
-      const float o2 = acc[d][4 * g + 2] * inv, o3 = acc[d][4 * g + 3] * inv;
-      if (out_f32) {
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + orow + dim) = make_float4(o0, o1, o2, o3);
-      } else {
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + orow + dim) =
-            make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+        for (int g = 0; g < 4; ++g) {
+          const int dim = 32 * d + 8 * g + 4 * hf;
+          if (dim >= HD) continue;
+          const float o0 = acc[d][4 * g] * inv, o1 = acc[d][4 * g + 1] * inv;
+          const float o2 = acc[d][4 * g + 2] * inv, o3 = acc[d][4 * g + 3] * inv;
+          if (out_f32) {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + orow + dim) = make_float4(o0, o1, o2, o3);
+          } else {
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + orow + dim) =
+                make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+          }
+        }
       }
     }
   }
 }
+
+// Combines the partial records of the split tail's cut items: block u takes
+// tail item n_whole + u, thread i its query q0 + i.  With the pieces' maxima
+// m_p, row sums l_p and unnormalized outputs O_p: m = max m_p,
+// l = sum l_p 2^(m_p - m), out = sum O_p 2^(m_p - m) / l, lse = m + log2 l.
+template <int WQ>
+__global__ void __launch_bounds__(WQ) attn_tail_merge_kernel(
+    const int4* __restrict__ qdesc, const int32_t* __restrict__ qkpre, const int32_t* __restrict__ nq_ptr,
+    int32_t heads, int32_t tail_wgs, const float* __restrict__ part, void* __restrict__ out, int32_t out_f32,
+    float* __restrict__ lse) {
+  constexpr int REC = WQ * 82;
+  const int nq = *nq_ptr;
+  const TailPlan plan = tail_plan(nq, heads, tail_wgs, qkpre);
+  if (plan.T == 0) return;
+  const int item = plan.n_whole + blockIdx.x;
+  if (item >= nq * heads) return;
+  const int qt = item / heads, head = item % heads;
+  const int n = qkpre[qt + 1] - qkpre[qt];
+  const int64_t P0 = int64_t(heads) * (qkpre[qt] - qkpre[plan.qt_tail]) + int64_t(head) * n;
+  // The tail workgroup whose range holds position p: the largest k with k T / S <= p.
+  auto wg_of = [&](int64_t p) { return int(((p + 1) * tail_wgs - 1) / plan.T); };
+  const int kA = wg_of(P0), kB = wg_of(P0 + n - 1);
+  if (kA == kB) return;  // run whole by one workgroup
+  const int4 desc = qdesc[qt];
+  const int ql = threadIdx.x, q = desc.x + ql;
+  if (q >= min(desc.x + WQ, desc.z)) return;
+  auto rec_of = [&](int k) {
+    const int64_t klo = int64_t(k) * plan.T / tail_wgs;
+    return part + int64_t(klo >= P0 ? 2 * k : 2 * k + 1) * REC;
+  };
+  float m = -INFINITY;
+  for (int k = kA; k <= kB; ++k) m = fmaxf(m, rec_of(k)[WQ * 80 + ql]);
+  float l = 0.f;
+  float4 o[HD / 4];
+#pragma unroll
+  for (int c = 0; c < HD / 4; ++c) o[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k = kA; k <= kB; ++k) {
+    const float* r = rec_of(k);
+    const float w = __builtin_amdgcn_exp2f(r[WQ * 80 + ql] - m);
+    l += r[WQ * 81 + ql] * w;
+    const float4* ro = reinterpret_cast<const float4*>(r + ql * HD);
+#pragma unroll
+    for (int c = 0; c < HD / 4; ++c) {
+      const float4 v = ro[c];
+      o[c].x += v.x * w;
+      o[c].y += v.y * w;
+      o[c].z += v.z * w;
+      o[c].w += v.w * w;
+    }
+  }
+  const float inv = 1.0f / l;
+  if (lse) lse[int64_t(q) * heads + head] = m + log2f(l);
+  const int64_t orow = int64_t(q) * heads * HD + head * HD;
+#pragma unroll
+  for (int c = 0; c < HD / 4; ++c) {
+    const float4 v = make_float4(o[c].x * inv, o[c].y * inv, o[c].z * inv, o[c].w * inv);
+    if (out_f32)
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + orow + 4 * c) = v;
+    else
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + orow + 4 * c) =
+          make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+  }
+}
+
 template <int NW, int KG, int NST>
 static hipError_t launch_attention_kernel(const uint16_t* qpk, const uint16_t* kv,
                                           const int4* qdesc, int32_t max_qtiles, int32_t heads,
@@ -664,18 +856,44 @@ static hipError_t launch_attention_kernel(const uint16_t* qpk, const uint16_t* k
   return hipGetLastError();
 }
 
-template <int NW, int WPE>
+// Workgroups of kern the GPU holds at once (blocks per CU x CUs), per device
+// (one cache per VARIANT: the lean kernels share a function type).
+template <int VARIANT, class K>
+static int resident_wgs(K kern, int threads, size_t lds) {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), threads,
+                                                     lds) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev] = std::max(per_cu * cus, 1);
+  }
+  return cached[dev];
+}
+
+template <int NW, int WPE, int VARIANT>
 static hipError_t launch_lean(const uint16_t* qpk, const uint16_t* kv, const int4* qdesc,
                               int32_t max_qtiles, int32_t heads, void* out, bool out_f32, float* lse,
-                              hipStream_t s) {
+                              hipStream_t s, const AttnTail& tail) {
   const size_t lds = size_t(2) * STAGE_BYTES;
   auto kern = attention_lean_kernel<NW, 2, WPE>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (attr != hipSuccess) return attr;
-  const int64_t blocks = int64_t(max_qtiles) * heads;
+  int S = 0;
+  if (tail.part && tail.qkpre && tail.nq)
+    S = std::min(resident_wgs<VARIANT>(kern, 64 * NW, lds), attn_tail_max_wgs(VARIANT));
+  const int64_t blocks = int64_t(max_qtiles) * heads + S;
   hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(64 * NW), lds, s, qpk, kv, qdesc, heads, out,
-                     out_f32 ? 1 : 0, lse);
+                     out_f32 ? 1 : 0, lse, tail.qkpre, tail.nq, S, tail.part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 0) return e;
+  // at most S + heads - 1 items are in a split tail
+  hipLaunchKernelGGL(attn_tail_merge_kernel<32 * NW>, dim3(unsigned(S + heads)), dim3(32 * NW), 0, s, qdesc,
+                     tail.qkpre, tail.nq, heads, S, tail.part, out, out_f32 ? 1 : 0, lse);
   return hipGetLastError();
 }
 
@@ -683,22 +901,24 @@ hipError_t launch_attention(const uint16_t* qkv, const int32_t* pos_thw, const i
                             const int2* kdesc, int32_t max_qtiles, int32_t max_ktiles,
                             int32_t heads, int32_t n_pos, int32_t axis_code, const float2* rope_cs,
                             float q_scale_log2, int32_t variant, uint16_t* qpk, uint16_t* kv,
-                            void* out, bool out_f32, float* lse, hipStream_t s) {
+                            void* out, bool out_f32, float* lse, hipStream_t s, const AttnTail& tail) {
   hipLaunchKernelGGL(attn_pack_kernel, dim3(unsigned(int64_t(max_ktiles) * heads)), dim3(320), 0, s,
                      qkv, pos_thw, kdesc, heads, n_pos, rope_cs, axis_code, q_scale_log2, qpk, kv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_attention_packed(qpk, kv, qdesc, max_qtiles, heads, variant, out, out_f32, lse, s);
+  return launch_attention_packed(qpk, kv, qdesc, max_qtiles, heads, variant, out, out_f32, lse, s, tail);
 }
 
 hipError_t launch_attention_packed(const uint16_t* qpk, const uint16_t* kv, const int4* qdesc,
                                    int32_t max_qtiles, int32_t heads, int32_t variant, void* out,
-                                   bool out_f32, float* lse, hipStream_t s) {
+                                   bool out_f32, float* lse, hipStream_t s, const AttnTail& tail) {
   switch (variant) {
     case kAttnSmall:
       return launch_attention_kernel<4, 2, 3>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, lse, s);
-    case kAttnLean4: return launch_lean<4, 3>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, lse, s);
-    case kAttnLean8: return launch_lean<8, 4>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, lse, s);
+    case kAttnLean4:
+      return launch_lean<4, 3, kAttnLean4>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, lse, s, tail);
+    case kAttnLean8:
+      return launch_lean<8, 4, kAttnLean8>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, lse, s, tail);
   }
   return hipErrorInvalidValue;
 }

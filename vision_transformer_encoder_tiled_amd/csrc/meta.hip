@@ -108,7 +108,7 @@ __global__ void __launch_bounds__(1024) attn_schedule_kernel(
     const int32_t* __restrict__ cu, int32_t n_img, int32_t q_tile, int32_t k_tile,
     int32_t max_qtiles, int32_t max_ktiles, int32_t* __restrict__ order,
     int32_t* __restrict__ tile_start, int32_t* __restrict__ ktile_start,
-    int4* __restrict__ qdesc, int2* __restrict__ kdesc) {
+    int4* __restrict__ qdesc, int2* __restrict__ kdesc, int32_t* __restrict__ qkpre) {
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x, nt = blockDim.x;
   for (int i = tid; i < n_img; i += nt) {
@@ -151,16 +151,30 @@ __global__ void __launch_bounds__(1024) attn_schedule_kernel(
     }
     kdesc[T] = d;
   }
+  if (qkpre) {
+    // Key tiles per q-tile slot (those of its image), recomputed from the
+    // scans above rather than read back from qdesc.
+    block_scan(max_qtiles, [&](int t) {
+      if (t >= nq) return 0;
+      int lo = 0, hi = n_img - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tile_start[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      const int i = order[lo];
+      return (cu[i + 1] - cu[i] + k_tile - 1) / k_tile;
+    }, qkpre, part);
+  }
 }
 
 hipError_t launch_attn_schedule(const int32_t* cu_seqlens, int32_t n_img, int32_t q_tile,
                                 int32_t k_tile, int32_t max_qtiles, int32_t max_ktiles,
                                 int32_t* order, int32_t* tile_start, int32_t* ktile_start,
-                                int4* qdesc, int2* kdesc, hipStream_t s) {
+                                int4* qdesc, int2* kdesc, hipStream_t s, int32_t* qkpre) {
   // block_scan's serial step runs over the thread count: keep it near n_img.
   const int threads = n_img >= 1024 ? 1024 : (n_img >= 256 ? 256 : 64);
   hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(threads), 0, s, cu_seqlens, n_img, q_tile,
-                     k_tile, max_qtiles, max_ktiles, order, tile_start, ktile_start, qdesc, kdesc);
+                     k_tile, max_qtiles, max_ktiles, order, tile_start, ktile_start, qdesc, kdesc, qkpre);
   return hipGetLastError();
 }
 

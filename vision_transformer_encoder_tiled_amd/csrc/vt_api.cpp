@@ -136,6 +136,8 @@ struct BlockBufs {
   int32_t* tile_start;
   int32_t* ktile_start;
   int4* qdesc;     // per q-tile slot (max_q_tiles at 64 queries)
+  int32_t* qkpre;  // key tiles before each q-tile slot (max_q_tiles at 64 queries, + 1)
+  float* part;     // partial records of the lean kernel's split tail (null: no split)
   int2* kdesc;     // per key-tile slot
   uint16_t* qpk;   // [N, heads, 80] fp16 rotated, scaled Q
   uint16_t* kv;    // max_ktiles x heads K/V tile images (fp16)
@@ -163,12 +165,20 @@ int32_t max_q_tiles(int64_t N, int32_t n_img, int32_t q_tile) {
   return int32_t((N + q_tile - 1) / q_tile + n_img);
 }
 
-// The attention step's buffers (schedule, packed Q, tile images, RoPE table).
-void carve_attention(Carver& c, const Dims& D, int32_t n_pos, BlockBufs* b) {
+int32_t attn_variant(int64_t N, int32_t n_img, int32_t heads);
+
+// The attention step's buffers (schedule, packed Q, tile images, RoPE table,
+// and with split_tail the lean kernel's partial records).
+void carve_attention(Carver& c, const Dims& D, int32_t n_pos, BlockBufs* b, bool split_tail = true) {
   b->order = c.take<int32_t>(D.n_img);
   b->tile_start = c.take<int32_t>(D.n_img + 1);
   b->ktile_start = c.take<int32_t>(D.n_img + 1);
   b->qdesc = c.take<int4>(max_q_tiles(D.N, D.n_img, vt::attn_q_tile(vt::kAttnSmall)));
+  b->qkpre = c.take<int32_t>(max_q_tiles(D.N, D.n_img, vt::attn_q_tile(vt::kAttnSmall)) + 1);
+  const int32_t var = attn_variant(D.N, D.n_img, D.heads);
+  // one size for both lean variants, so the workspace stays affine in the
+  // token count across the switch between them
+  b->part = split_tail && var != vt::kAttnSmall ? c.take<float>(size_t(vt::attn_tail_part_floats())) : nullptr;
   b->kdesc = c.take<int2>(max_k_tiles(D.N, D.n_img));
   b->qpk = c.take<uint16_t>(size_t(D.N) * D.d);
   b->kv = reinterpret_cast<uint16_t*>(
@@ -296,7 +306,8 @@ vt_status attn_prologue(const vt_config* cfg, const int32_t* cu, int32_t n_img, 
   const int q_tile = vt::attn_q_tile(attn_variant(N, n_img, cfg->heads));
   VT_TRY_HIP(vt::launch_attn_schedule(cu, n_img, q_tile, vt::kAttnKTile,
                                       max_q_tiles(N, n_img, q_tile), max_k_tiles(N, n_img),
-                                      b.order, b.tile_start, b.ktile_start, b.qdesc, b.kdesc, s));
+                                      b.order, b.tile_start, b.ktile_start, b.qdesc, b.kdesc, s,
+                                      b.qkpre));
   const vt::RopeFreq f = rope_freq(cfg, axis_code);
   VT_TRY_HIP(vt::launch_rope_table(f, n_pos, b.rope, s));
   if (for_blocks)
@@ -315,7 +326,8 @@ vt_status run_attention(const vt_config* cfg, const uint16_t* qkv, const int32_t
   const int32_t var = attn_variant(N, n_img, cfg->heads);
   VT_TRY_HIP(vt::launch_attention(qkv, pos, b.qdesc, b.kdesc, max_q_tiles(N, n_img, vt::attn_q_tile(var)),
                                   max_k_tiles(N, n_img), cfg->heads, n_pos, axis_code, b.rope,
-                                  q_scale_log2(cfg), var, b.qpk, b.kv, out, f32, lse, s));
+                                  q_scale_log2(cfg), var, b.qpk, b.kv, out, f32, lse, s,
+                                  vt::AttnTail{b.qkpre, b.tile_start + n_img, b.part}));
   return VT_OK;
 }
 
@@ -340,7 +352,8 @@ vt_status run_block(const vt_config* cfg, float* R, const vt_block_weights* w, c
   if (e == hipSuccess) {
     const int32_t var = attn_variant(N, n_img, cfg->heads);
     VT_TRY_HIP(vt::launch_attention_packed(b.qpk, b.kv, b.qdesc, max_q_tiles(N, n_img, vt::attn_q_tile(var)),
-                                           cfg->heads, var, att, false, nullptr, s));
+                                           cfg->heads, var, att, false, nullptr, s,
+                                           vt::AttnTail{b.qkpre, b.tile_start + n_img, b.part}));
   } else if (e == hipErrorInvalidValue) {  // a shape the pack epilogue does not take (nothing launched)
     (void)hipGetLastError();
     VT_TRY_HIP(vt::launch_gemm(b.xn, M, d, w->w_qkv, 3 * d, w->b_qkv, vt::kEpiBf16, qkv, b.gemm_ws, s));
@@ -423,11 +436,12 @@ size_t block_ws_bytes(const vt_config* cfg, int64_t N, int32_t n_img, int32_t n_
 }
 
 // The attention step's own buffers (schedule, packed Q, tile images, RoPE
-// table): what vt_attention_varlen_noalloc carves from its fixed array.
+// table; no split-tail records): what vt_attention_varlen_noalloc carves from
+// its fixed array.
 size_t attn_ws_bytes(const vt_config* cfg, int64_t N, int32_t n_img, int32_t n_pos) {
   Carver c(nullptr);
   BlockBufs b;
-  carve_attention(c, dims_of(cfg, N, n_img), n_pos, &b);
+  carve_attention(c, dims_of(cfg, N, n_img), n_pos, &b, false);
   return c.off;
 }
 
@@ -649,7 +663,7 @@ VT_API vt_status vt_attention_varlen_noalloc(const vt_config* cfg, const uint16_
   // RoPE table), so nothing left by an earlier call needs clearing.
   Carver c(ws);
   BlockBufs b;
-  carve_attention(c, dims_of(cfg, total_tokens, n_img), max_seqlen, &b);
+  carve_attention(c, dims_of(cfg, total_tokens, n_img), max_seqlen, &b, false);
   int32_t axis_code = 0;
   if ((st = attn_prologue(cfg, cu_seqlens, n_img, total_tokens, max_seqlen, b, &axis_code, s)) != VT_OK)
     return st;

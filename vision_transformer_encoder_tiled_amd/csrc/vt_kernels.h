@@ -29,11 +29,14 @@ hipError_t launch_cu_last(int32_t* cu_seqlens, int32_t n_img, int32_t total, hip
 // 64-key tile of image i (image order) in the packed K/V tile images.
 // qdesc[t] = (first query, image begin, image end, first key tile of the
 // image) of q-tile slot t < max_qtiles; kdesc[T] = (first token, image end)
-// of key-tile slot T < max_ktiles; unused slots have .x = -1.
+// of key-tile slot T < max_ktiles; unused slots have .x = -1.  qkpre, when
+// not null, receives max_qtiles + 1 entries: qkpre[t] = the key tiles of the
+// q-tile slots before t (a q-tile's key tiles are those of its image; unused
+// slots count 0).
 hipError_t launch_attn_schedule(const int32_t* cu_seqlens, int32_t n_img, int32_t q_tile,
                                 int32_t k_tile, int32_t max_qtiles, int32_t max_ktiles,
                                 int32_t* order, int32_t* tile_start, int32_t* ktile_start,
-                                int4* qdesc, int2* kdesc, hipStream_t s);
+                                int4* qdesc, int2* kdesc, hipStream_t s, int32_t* qkpre = nullptr);
 // RoPE table cs[pos][j] = (cos, sin)(pos * inv_freq[j]), pos < n_pos, j < 40.
 struct RopeFreq { double inv_freq[64]; int32_t pairs; };
 hipError_t launch_rope_table(const RopeFreq& f, int32_t n_pos, float2* cs, hipStream_t s);
@@ -111,6 +114,33 @@ enum AttnVariant : int { kAttnSmall = 0, kAttnLean4 = 1, kAttnLean8 = 2 };
 inline int attn_q_tile(int variant) {
   return variant == kAttnSmall ? 64 : variant == kAttnLean4 ? 128 : 256;
 }
+// The split tail of the lean kernels.  Work items are (q-tile, head) pairs,
+// q-tile major, in the schedule's order; one workgroup runs each.  When the
+// items do not fill a whole number of rounds of the workgroups the GPU holds
+// at once (S of them), the last, partial round is instead spread evenly over
+// S workgroups by key tiles: workgroup k of the tail takes key tiles
+// [k T / S, (k+1) T / S) of the tail's T (item after item, each item's
+// key tiles in order), and an item cut between workgroups leaves unnormalized
+// partial results (O, running max, row sum) that a merge kernel combines.
+// qkpre / nq: launch_attn_schedule's qkpre and q-tile count (tile_start[n_img]);
+// part: attn_tail_records(variant) records of attn_tail_record_floats(variant)
+// floats (attn_tail_part_floats() covers either lean variant), or null for no
+// split.
+struct AttnTail {
+  const int32_t* qkpre = nullptr;
+  const int32_t* nq = nullptr;
+  float* part = nullptr;
+};
+constexpr int kAttnTailMinTiles = 8;  // no split when a tail workgroup would get fewer key tiles
+inline int attn_tail_max_wgs(int variant) { return variant == kAttnLean4 ? 768 : 512; }
+inline int64_t attn_tail_records(int variant) { return variant == kAttnSmall ? 0 : 2 * attn_tail_max_wgs(variant); }
+inline int64_t attn_tail_record_floats(int variant) { return int64_t(attn_q_tile(variant)) * 82; }
+inline int64_t attn_tail_part_floats() {
+  const int64_t a = attn_tail_records(kAttnLean4) * attn_tail_record_floats(kAttnLean4);
+  const int64_t b = attn_tail_records(kAttnLean8) * attn_tail_record_floats(kAttnLean8);
+  return a > b ? a : b;
+}
+
 // qpk: [N, heads, 80] fp16 rotated+scaled Q; kv: max_ktiles x heads tile
 // images.  qdesc / kdesc come from launch_attn_schedule with
 // attn_q_tile(variant) and the same max_qtiles / max_ktiles.  lse, when
@@ -120,13 +150,14 @@ hipError_t launch_attention(const uint16_t* qkv, const int32_t* pos_thw, const i
                             const int2* kdesc, int32_t max_qtiles, int32_t max_ktiles,
                             int32_t heads, int32_t n_pos, int32_t axis_code, const float2* rope_cs,
                             float q_scale_log2, int32_t variant, uint16_t* qpk, uint16_t* kv,
-                            void* out, bool out_f32, float* lse, hipStream_t s);
+                            void* out, bool out_f32, float* lse, hipStream_t s,
+                            const AttnTail& tail = AttnTail());
 
 // The attention kernel alone, on Q and tile images already packed (by the
 // pack kernel inside launch_attention, or by the QKV GEMM epilogue).
 hipError_t launch_attention_packed(const uint16_t* qpk, const uint16_t* kv, const int4* qdesc,
                                    int32_t max_qtiles, int32_t heads, int32_t variant, void* out,
-                                   bool out_f32, float* lse, hipStream_t s);
+                                   bool out_f32, float* lse, hipStream_t s, const AttnTail& tail = AttnTail());
 // Layer-independent parts of the tile images (V^T ones rows, zero padding
 // keys) and kslot[tok] = 64 * key tile + slot of every token (int32 [N]),
 // from launch_attn_schedule's kdesc; run once before launch_gemm_qkv_pack.
