@@ -778,16 +778,21 @@ __global__ void __launch_bounds__(64 * NW, WPE) attention_lean_kernel(
   }
 }
 
-// Combines the partial records of the split tail's cut items: block u takes
-// tail item n_whole + u, thread i its query q0 + i.  With the pieces' maxima
-// m_p, row sums l_p and unnormalized outputs O_p: m = max m_p,
+// Combines the partial records of the split tail's cut items: block
+// (u, g) takes queries 32g .. 32g+31 of tail item n_whole + u, one thread per
+// (query, 16-byte chunk of its output row), so that consecutive threads read
+// consecutive chunks of a record row.  With the pieces' maxima m_p, row sums
+// l_p and unnormalized outputs O_p of a query: m = max m_p,
 // l = sum l_p 2^(m_p - m), out = sum O_p 2^(m_p - m) / l, lse = m + log2 l.
+constexpr int kMergeQ = 32;                 // queries per merge block
+constexpr int kMergeThreads = kMergeQ * HD / 4;  // 640
 template <int WQ>
-__global__ void __launch_bounds__(WQ) attn_tail_merge_kernel(
+__global__ void __launch_bounds__(kMergeThreads) attn_tail_merge_kernel(
     const int4* __restrict__ qdesc, const int32_t* __restrict__ qkpre, const int32_t* __restrict__ nq_ptr,
     int32_t heads, int32_t tail_wgs, const float* __restrict__ part, void* __restrict__ out, int32_t out_f32,
     float* __restrict__ lse) {
   constexpr int REC = WQ * 82;
+  constexpr int CH = HD / 4;  // 16-byte chunks per output row
   const int nq = *nq_ptr;
   const TailPlan plan = tail_plan(nq, heads, tail_wgs, qkpre);
   if (plan.T == 0) return;
@@ -801,8 +806,8 @@ __global__ void __launch_bounds__(WQ) attn_tail_merge_kernel(
   const int kA = wg_of(P0), kB = wg_of(P0 + n - 1);
   if (kA == kB) return;  // run whole by one workgroup
   const int4 desc = qdesc[qt];
-  const int ql = threadIdx.x, q = desc.x + ql;
-  if (q >= min(desc.x + WQ, desc.z)) return;
+  const int ql = blockIdx.y * kMergeQ + threadIdx.x / CH, c = threadIdx.x % CH;
+  if (ql >= min(WQ, desc.z - desc.x)) return;
   auto rec_of = [&](int k) {
     const int64_t klo = int64_t(k) * plan.T / tail_wgs;
     return part + int64_t(klo >= P0 ? 2 * k : 2 * k + 1) * REC;
@@ -810,35 +815,27 @@ __global__ void __launch_bounds__(WQ) attn_tail_merge_kernel(
   float m = -INFINITY;
   for (int k = kA; k <= kB; ++k) m = fmaxf(m, rec_of(k)[WQ * 80 + ql]);
   float l = 0.f;
-  float4 o[HD / 4];
-#pragma unroll
-  for (int c = 0; c < HD / 4; ++c) o[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int k = kA; k <= kB; ++k) {
     const float* r = rec_of(k);
     const float w = __builtin_amdgcn_exp2f(r[WQ * 80 + ql] - m);
     l += r[WQ * 81 + ql] * w;
-    const float4* ro = reinterpret_cast<const float4*>(r + ql * HD);
-#pragma unroll
-    for (int c = 0; c < HD / 4; ++c) {
-      const float4 v = ro[c];
-      o[c].x += v.x * w;
-      o[c].y += v.y * w;
-      o[c].z += v.z * w;
-      o[c].w += v.w * w;
-    }
+    const float4 v = reinterpret_cast<const float4*>(r + ql * HD)[c];
+    o.x += v.x * w;
+    o.y += v.y * w;
+    o.z += v.z * w;
+    o.w += v.w * w;
   }
   const float inv = 1.0f / l;
-  if (lse) lse[int64_t(q) * heads + head] = m + log2f(l);
-  const int64_t orow = int64_t(q) * heads * HD + head * HD;
-#pragma unroll
-  for (int c = 0; c < HD / 4; ++c) {
-    const float4 v = make_float4(o[c].x * inv, o[c].y * inv, o[c].z * inv, o[c].w * inv);
-    if (out_f32)
-      *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + orow + 4 * c) = v;
-    else
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + orow + 4 * c) =
-          make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
-  }
+  const int q = desc.x + ql;
+  if (lse && c == 0) lse[int64_t(q) * heads + head] = m + log2f(l);
+  const float4 v = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+  const int64_t at = int64_t(q) * heads * HD + head * HD + 4 * c;
+  if (out_f32)
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + at) = v;
+  else
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + at) =
+        make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
 }
 
 template <int NW, int KG, int NST>
@@ -892,7 +889,7 @@ static hipError_t launch_lean(const uint16_t* qpk, const uint16_t* kv, const int
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 0) return e;
   // at most S + heads - 1 items are in a split tail
-  hipLaunchKernelGGL(attn_tail_merge_kernel<32 * NW>, dim3(unsigned(S + heads)), dim3(32 * NW), 0, s, qdesc,
+  hipLaunchKernelGGL(attn_tail_merge_kernel<32 * NW>, dim3(unsigned(S + heads), NW), dim3(kMergeThreads), 0, s, qdesc,
                      tail.qkpre, tail.nq, heads, S, tail.part, out, out_f32 ? 1 : 0, lse);
   return hipGetLastError();
 }
