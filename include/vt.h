@@ -153,7 +153,8 @@ const char* vt_version(void);
 /* Workspace bytes for vt_tower_forward / vt_patch_embed / vt_merge_project on
  * this grid list.  Affine in the token count (no term grows with seq^2), plus
  * a fixed 86 MB of attention partial records once a call is large enough for
- * the lean attention kernels.
+ * the lean attention kernels, and up to 64 MB of GEMM partial sums whose
+ * presence depends on how a call's GEMM tiles fill the CUs.
  * Returns 0 and sets vt_last_error() if the arguments are invalid. */
 size_t vt_tower_workspace_size(const vt_config* cfg, const vt_grid_thw* grid, int32_t n_img);
 

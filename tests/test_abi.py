@@ -48,11 +48,16 @@ def test_default_config_is_the_minimax_m3_shape():
 
 def test_workspace_is_affine_in_tokens():
     cfg = vt.config()
-    # large square images: no split-K partial buffers, so the size is exactly affine
+    # large square images: affine in the tokens, up to the GEMM partial-sum
+    # area (at most 64 MiB: 256 tiles of 256 x 256 fp32), which a call has or
+    # has not depending on how its tiles fill the CUs' rounds
     sizes = [vt.vt_tower_workspace_size(cfg, [(1, 64, 64)] * k) for k in (8, 16, 24, 32)]
     d1 = sizes[1] - sizes[0]
-    assert abs((sizes[2] - sizes[1]) - d1) <= 4096 and abs((sizes[3] - sizes[2]) - d1) <= 4096
-    per_token = d1 / (8 * 64 * 64)
+    part = 256 * 256 * 256 * 4
+    # (a second difference can see the area appear in one step and go in the next)
+    assert abs((sizes[2] - sizes[1]) - d1) <= 2 * part + 4096
+    assert abs((sizes[3] - sizes[2]) - d1) <= 2 * part + 4096
+    per_token = (sizes[3] - sizes[0]) / (24 * 64 * 64)
     assert per_token < 64 * 1024          # tens of KB per token ...
     # ... so a 2016x2016 image (20,736 patches) needs well under a GB of scratch,
     # against ~13.8 GB for one layer's untiled fp16 [16, n, n] score tensor.
@@ -60,7 +65,7 @@ def test_workspace_is_affine_in_tokens():
     assert ws2016 < 1.5e9
     assert 16 * 20736 ** 2 * 2 > 13.7e9
     blk = [vt.vt_block_workspace_size(cfg, n, 1, n) for n in (4096, 8192, 16384)]
-    assert abs((blk[2] - blk[1]) - 2 * (blk[1] - blk[0])) <= 4096
+    assert abs((blk[2] - blk[1]) - 2 * (blk[1] - blk[0])) <= part + 4096
 
 
 def test_workspace_size_reports_invalid_grids():
@@ -222,7 +227,8 @@ def test_attention_backward_workspace_is_affine():
     assert abs((s[2] - s[1]) - 2 * (s[1] - s[0])) <= 4096
     assert (s[1] - s[0]) / 4096 < 40 * 1024       # about 36 KB per token at 16 heads
     b = [vt.vt_block_backward_workspace_size(cfg, n, 1, n) for n in (4096, 8192, 16384)]
-    assert abs((b[2] - b[1]) - 2 * (b[1] - b[0])) <= 4096
+    # up to the GEMMs' partial-sum area (at most 64 MiB), present or not by shape
+    assert abs((b[2] - b[1]) - 2 * (b[1] - b[0])) <= 256 * 256 * 256 * 4 + 4096
     assert (b[1] - b[0]) / 4096 < 128 * 1024      # about 115 KB per token
 
 

@@ -177,8 +177,9 @@ GEMM_SHAPES = [  # (M, N, K, what)
     (200, 6144, 24576, "ragged M, 256x256 split-K"),
     (1024, 1280, 1216, "split-K, K not a multiple of the split"),
     (20736, 5120, 1280, "FC1, 2016x2016 (256 tile)"),
-    (20736, 1280, 5120, "FC2, 2016x2016"),
-    (5184, 6144, 24576, "merged MLP 1, 2016x2016"),
+    (20736, 1280, 5120, "FC2, 2016x2016 (stream-K tail: 149 of 405 tiles over 256 workgroups)"),
+    (16384, 1280, 5120, "FC2, 16 x 448x448 (stream-K tail: 64 of 320 tiles)"),
+    (5184, 6144, 24576, "merged MLP 1, 2016x2016 (stream-K tail)"),
 ]
 
 
@@ -203,7 +204,8 @@ def test_linear_shapes(vt, M, N, K, what):
 
 @pytest.mark.parametrize("epi", ["bf16", "gelu_tanh", "gelu_erf", "resid"])
 @pytest.mark.parametrize("M,N,K", [(200, 512, 320), (1024, 1280, 5120), (1000, 5120, 1280),
-                                   (968, 6144, 640), (200, 6144, 6144)])
+                                   (968, 6144, 640), (200, 6144, 6144),
+                                   (4608, 4096, 2048)])  # stream-K tail: 32 of 288 tiles in eighths
 def test_linear_epilogues(vt, epi, M, N, K):
     log(f"linear epilogue {epi} {M}x{N}x{K}")
     x = random_bf16((M, K), 7)

@@ -278,3 +278,68 @@ def test_lean_split_tail_covers_every_key_tile_once(grids, WQ, S):
             assert b // heads < len(nk)
             n_run += 1
     assert n_run == nw + (S if T else 0)
+
+
+# ---------------------------------------------------------------- GEMM stream-K tail
+def gemm_streamk(M, N, K, CUs=256):
+    """gemm.hip plan_gemm (256 x 256 tiles), the piece walk of
+    gemm_dl_kernel<..., SK = true> and streamk_reduce_kernel's record lookup.
+    Returns (n_whole, sk_wgs, pieces, reduce map)."""
+    cdiv = lambda a, b: -(-a // b)
+    t256 = cdiv(M, 256) * cdiv(N, 256)
+    if not (t256 >= 192 and t256 > CUs and t256 % CUs and K >= 2048 and K % 32 == 0):
+        return None
+    nks = K // 32
+    n_whole = t256 // CUs * CUs
+    n_tail = t256 - n_whole
+    if CUs % n_tail or nks < 8 * (CUs // n_tail):
+        return None
+    S = CUs
+    T = n_tail * nks
+    assert T < 2 ** 31
+    pieces = []
+    for k in range(S):
+        lo, hi = k * T // S, (k + 1) * T // S
+        pos = lo
+        while pos < hi:
+            u, s0 = pos // nks, pos % nks
+            s1 = min(nks, s0 + (hi - pos))
+            pieces.append((u, s0, s1, k if pos == lo else S + k))
+            pos += s1 - s0
+    red = {}
+    for u in range(n_tail):
+        P0 = u * nks
+        wg_of = lambda p: ((p + 1) * S - 1) // T
+        kA, kB = wg_of(P0), wg_of(P0 + nks - 1)
+        red[u] = [k if k * T // S >= P0 else S + k for k in range(kA, kB + 1)]
+    return n_whole, S, pieces, red
+
+
+@pytest.mark.parametrize("M,N,K", [(16384, 1280, 5120), (4096, 6144, 24576), (4096, 6144, 6144),
+                                   (4608, 4096, 2048), (16384, 2560, 2048), (20736, 1280, 5120),
+                                   (5184, 6144, 24576)])
+def test_gemm_streamk_tail_covers_every_k_step_once(M, N, K):
+    plan = gemm_streamk(M, N, K)
+    if plan is None:
+        pytest.skip("no stream-K tail for this shape")
+    n_whole, S, pieces, red = plan
+    nks = K // 32
+    n_tail = -(-M // 256) * -(-N // 256) - n_whole
+    seen, slots = set(), {}
+    per_wg = {}
+    for u, s0, s1, slot in pieces:
+        assert 0 <= u < n_tail and 0 <= s0 < s1 <= nks
+        for j in range(s0, s1):
+            assert (u, j) not in seen
+            seen.add((u, j))
+        assert slot not in slots and 0 <= slot < S          # inside the S records of the workspace
+        slots[slot] = (u, s0, s1)
+        per_wg[slot % S] = per_wg.get(slot % S, 0) + 1
+    assert len(seen) == n_tail * nks
+    assert max(per_wg.values()) == 1 and len(per_wg) == S   # one aligned piece per workgroup
+    for u, recs in red.items():                             # the reduce reads exactly the pieces of its tile
+        spans = sorted(slots[r][1:] for r in recs)
+        assert all(slots[r][0] == u for r in recs)
+        assert spans[0][0] == 0 and spans[-1][1] == nks
+        assert all(a[1] == b[0] for a, b in zip(spans, spans[1:]))
+    assert sorted(r for rs in red.values() for r in rs) == sorted(slots)

@@ -188,11 +188,8 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
 // b is remapped so that each XCD runs a contiguous range of tiles, walked in
 // groups of 4 tile rows (GROUP_M): the ~32 tiles an XCD runs at once share
 // 4 activation panels and 8 weight panels through its L2.
-__device__ __forceinline__ void xcd_group_tile(int tiles_m, int tiles_n, int* tm, int* tn) {
-  const int G = tiles_m * tiles_n;
-  const int b = blockIdx.x;
-  const int q = G / 8, r = G % 8, x = b % 8, l = b / 8;
-  const int pid = (x < r) ? x * (q + 1) + l : r * (q + 1) + (x - r) * q + l;
+// Tile of linear index pid: groups of GM tile rows, walked column by column.
+__device__ __forceinline__ void group_tile(int pid, int tiles_m, int tiles_n, int* tm, int* tn) {
   constexpr int GM = 4;
   const int per_group = GM * tiles_n;
   const int gid = pid / per_group, first = gid * GM;
@@ -200,6 +197,12 @@ __device__ __forceinline__ void xcd_group_tile(int tiles_m, int tiles_n, int* tm
   const int in_g = pid - gid * per_group;
   *tm = first + in_g % gsz;
   *tn = in_g / gsz;
+}
+// Linear tile index of block b when npid tiles are spread over the 8 XCDs as
+// contiguous ranges (block b runs on XCD b mod 8).
+__device__ __forceinline__ int xcd_pid(int npid, int b) {
+  const int q = npid / 8, r = npid % 8, x = b % 8, l = b / 8;
+  return (x < r) ? x * (q + 1) + l : r * (q + 1) + (x - r) * q + l;
 }
 
 // 64-byte rows (K step 32 = 4 chunks of 16 B): logical chunk c of row r
@@ -322,11 +325,23 @@ __device__ __forceinline__ void qkv_pack_store(const char* cs, const QkvPack& pk
 // between them, NST - 1 steps in flight.  The finished tile is staged through
 // the (then idle) ring so that every global store writes whole 16-byte pieces
 // of contiguous rows.
-template <int BM, int BN, int GWM, int GWN, int NST, int EPI, bool SPLIT, int BK = 32, int CW = 0>
+//
+// SK (stream-K tail, with SPLIT): the grid is ts.sk_wgs workgroups that share
+// the K steps of the tiles past the first ts.n_whole evenly: workgroup k takes
+// positions [k T / S, (k+1) T / S) of the T = (tiles - n_whole) x (K / BK)
+// (tile, K step) pairs, tile after tile -- at most two pieces, since a range
+// is no longer than one tile's steps -- and writes each piece's raw fp32 sums
+// to record k (its first piece) or S + k (its second), BM x BN floats each;
+// streamk_reduce_kernel adds a tile's pieces in K order and applies the
+// epilogue.  (plan_gemm cuts only where every range is one aligned piece, so
+// records S.. are not used and the workspace holds S.)
+template <int BM, int BN, int GWM, int GWN, int NST, int EPI, bool SPLIT, int BK = 32, int CW = 0,
+          bool SK = false>
 __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
     const uint16_t* __restrict__ A, int M, int K, const uint16_t* __restrict__ B, int N,
     const uint16_t* __restrict__ bias, void* __restrict__ out, float* __restrict__ part, int kper,
-    QkvPack pk) {
+    QkvPack pk, TileSched ts) {
+  static_assert(!SK || (SPLIT && BK == 32 && CW == 0), "the stream-K tail writes partial sums");
   constexpr int NW = GWM * GWN;  // wavefronts that multiply
   constexpr int NWC = NW + CW;   // wavefronts that copy: all of them
   constexpr int WM = BM / GWM, WN = BN / GWN;
@@ -348,19 +363,47 @@ __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
   static_assert(NST >= 3, "ring depth");
   extern __shared__ __align__(16) uint16_t lds[];
   const char* smem = reinterpret_cast<const char*>(lds);
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Stream-K tail: this workgroup's range of (tail tile, K step) positions.
+  const int nks = K / BK;
+  int sk_lo = 0, sk_hi = 0, sk_pos = 0;
+  if constexpr (SK) {
+    const int64_t T = int64_t(tiles_m * tiles_n - ts.n_whole) * nks;
+    sk_lo = int(int64_t(blockIdx.x) * T / ts.sk_wgs);
+    sk_hi = int(int64_t(blockIdx.x + 1) * T / ts.sk_wgs);
+    sk_pos = sk_lo;
+  }
+  for (int piece = 0;; ++piece) {
+  int tm, tn, kbeg, kend, slot = 0;
+  if constexpr (SK) {
+    if (sk_pos >= sk_hi) break;
+    const int u = sk_pos / nks, s0 = sk_pos - u * nks, s1 = min(nks, s0 + (sk_hi - sk_pos));
+    group_tile(ts.n_whole + u, tiles_m, tiles_n, &tm, &tn);
+    kbeg = s0 * BK;
+    kend = s1 * BK;
+    slot = sk_pos == sk_lo ? int(blockIdx.x) : ts.sk_wgs + int(blockIdx.x);
+    sk_pos += s1 - s0;
+    if (piece > 0) __syncthreads();  // the previous piece's epilogue is done with the LDS
+  } else {
+    if (piece > 0) break;
+    group_tile(xcd_pid(ts.npid, blockIdx.x), tiles_m, tiles_n, &tm, &tn);
+    kbeg = SPLIT ? blockIdx.y * kper : 0;
+    kend = SPLIT ? min(K, kbeg + kper) : K;
+  }
+  // With pieces, lane quantities are formed anew for each (tid passes
+  // through an empty asm statement), so that nothing lane-dependent is
+  // hoisted above the piece loop and kept live across the whole kernel.
+  int tid = threadIdx.x;
+  if constexpr (SK) asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = tid >> 6;
   const bool mw = CW == 0 || wave < NW;  // a multiplying wavefront
   // Copy-only wavefronts issue at raised priority: the copies set the pace
   // of these tiles, and each shares its SIMD with one multiplying wavefront
   // (FC1 at 1,024 tokens: 22.3 -> 21.9 us; scheduling only, same bits).
   if (!mw) __builtin_amdgcn_s_setprio(1);
   const int wm = wave / GWN, wn = wave % GWN;
-  int tm, tn;
-  xcd_group_tile((M + BM - 1) / BM, (N + BN - 1) / BN, &tm, &tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int kbeg = SPLIT ? blockIdx.y * kper : 0;
-  const int kend = SPLIT ? min(K, kbeg + kper) : K;
   const int nk = (kend - kbeg) / BK;
 
   // Copy j of this lane: group g = wave + NWC j, i.e. row RPG g + lane / CH of
@@ -648,7 +691,9 @@ __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
       const int tok = m0 + pass * PASS_ROWS + r, col = n0 + c * EPC;
       if (tok >= M || col >= N) continue;
       const uint4 v = *reinterpret_cast<const uint4*>(cs + r * ROWB + ((c + (r & 15)) % CHUNKS) * 16);
-      if constexpr (SPLIT) {
+      if constexpr (SK) {
+        *reinterpret_cast<uint4*>(part + (int64_t(slot) * BM + (tok - m0)) * BN + (col - n0)) = v;
+      } else if constexpr (SPLIT) {
         *reinterpret_cast<uint4*>(part + (int64_t(blockIdx.y) * M + tok) * N + col) = v;
       } else if constexpr (EPI == kEpiResid || EPI == kEpiF32) {
         float4 a = __builtin_bit_cast(float4, v);
@@ -667,6 +712,7 @@ __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
       }
     }
   }
+  }  // pieces
 }
 
 // out = epilogue(sum_z part[z] + bias), summed in split order.  The loads of
@@ -700,11 +746,67 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
   }
 }
 
+// out = epilogue(sum of the pieces + bias) for the tiles of a stream-K tail:
+// block (i, u) takes float4 i of tail tile u (tile n_whole + u); the tile's
+// pieces are those of the tail workgroups whose ranges meet its K steps
+// [u nks, (u+1) nks), added in K order (deterministic).
+template <int EPI, int BM, int BN>
+__global__ void __launch_bounds__(256) streamk_reduce_kernel(const float* __restrict__ part, int M, int N,
+                                                             int nks, TileSched ts,
+                                                             const uint16_t* __restrict__ bias,
+                                                             void* __restrict__ out) {
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int u = blockIdx.y;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= BM * BN / 4) return;
+  const int r = idx / (BN / 4), c = 4 * (idx % (BN / 4));
+  int tm, tn;
+  group_tile(ts.n_whole + u, tiles_m, tiles_n, &tm, &tn);
+  const int tok = tm * BM + r, col = tn * BN + c;
+  if (tok >= M || col >= N) return;
+  const int64_t T = int64_t(tiles_m * tiles_n - ts.n_whole) * nks;
+  const int64_t P0 = int64_t(u) * nks;
+  // The tail workgroup whose range holds position p: the largest k with k T / S <= p.
+  auto wg_of = [&](int64_t p) { return int(((p + 1) * ts.sk_wgs - 1) / T); };
+  const int kA = wg_of(P0), kB = wg_of(P0 + nks - 1);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k = kA; k <= kB; ++k) {
+    const int64_t klo = int64_t(k) * T / ts.sk_wgs;
+    const int slot = klo >= P0 ? k : ts.sk_wgs + k;
+    const float4 v = *reinterpret_cast<const float4*>(part + (int64_t(slot) * BM + r) * BN + c);
+    if (k == kA) acc = v;
+    else { acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w; }
+  }
+  if (bias) {
+    const uint2 bb = *reinterpret_cast<const uint2*>(bias + col);
+    acc.x += bflo(bb.x); acc.y += bfhi(bb.x); acc.z += bflo(bb.y); acc.w += bfhi(bb.y);
+  }
+  epi_store4<EPI>(out, int64_t(tok) * N + col, acc.x, acc.y, acc.z, acc.w);
+}
+
 GemmPlan plan_gemm(int M, int N, int K) {
   auto cdiv = [](long a, long b) { return int((a + b - 1) / b); };
   GemmPlan p{256, 256, 1, K};
   const int t256 = cdiv(M, 256) * cdiv(N, 256);
-  if (t256 >= 192) return p;
+  if (t256 >= 192) {
+    // One 256 x 256 workgroup per CU.  Past whole rounds of the 256 CUs, a
+    // partial last round would leave CUs idle for a whole tile's time; with
+    // long K (the residual FC2 and the projector's wide Linears) its tiles'
+    // K steps are shared over the CUs instead.  Only when the tail tiles
+    // divide the CUs, so that every workgroup takes one aligned piece of one
+    // tile (16 x 448x448: 64 tiles in quarters): cut points that fall inside
+    // workgroup ranges (two pieces each, 2 x 256 KB of partial sums per
+    // workgroup) measured slower than the idle CUs at 2016x2016.
+    constexpr int kCUs = 256;
+    if (t256 > kCUs && t256 % kCUs != 0 && K >= 2048 && K % 32 == 0) {
+      const int n_whole = t256 / kCUs * kCUs, n_tail = t256 - n_whole, nks = K / 32;
+      if (kCUs % n_tail == 0 && nks >= 8 * (kCUs / n_tail)) {
+        p.n_whole = n_whole;
+        p.sk_wgs = kCUs;
+      }
+    }
+    return p;
+  }
   if (M <= 512 && K % 32 == 0) {
     // Few rows, large weights (the merged MLP of a small image): 256 x 256
     // tiles read each weight panel once; split K to fill the CUs.
@@ -744,10 +846,11 @@ GemmPlan plan_gemm(int M, int N, int K) {
 
 size_t gemm_workspace_bytes(int M, int N, int K) {
   const GemmPlan p = plan_gemm(M, N, K);
+  if (p.sk_wgs > 0) return size_t(p.sk_wgs) * p.bm * p.bn * sizeof(float);  // one piece per workgroup
   return p.splits > 1 ? size_t(p.splits) * M * N * sizeof(float) : 0;
 }
 
-template <int BM, int BN, int EPI, bool SPLIT, int BK>
+template <int BM, int BN, int EPI, bool SPLIT, int BK, bool SK = false>
 static hipError_t launch_dl(const uint16_t* A, int M, int K, const uint16_t* B, int N,
                             const uint16_t* bias, void* out, float* part, const GemmPlan& p,
                             int tiles, hipStream_t s, const QkvPack& pk = QkvPack{}) {
@@ -758,12 +861,14 @@ static hipError_t launch_dl(const uint16_t* A, int M, int K, const uint16_t* B, 
   constexpr int CW = (BK == 64 && GWM * GWN == 4) ? 4 : 0;
   constexpr int NST = BK == 64 ? 3 : 4;
   const size_t lds = size_t(NST) * dl_stage_bytes(BM, BN, BK);
-  auto kern = gemm_dl_kernel<BM, BN, GWM, GWN, NST, EPI, SPLIT, BK, CW>;
+  auto kern = gemm_dl_kernel<BM, BN, GWM, GWN, NST, EPI, SPLIT, BK, CW, SK>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(tiles, SPLIT ? p.splits : 1), dim3(64 * (GWM * GWN + CW)), lds, s, A,
-                     M, K, B, N, bias, out, part, p.kper, pk);
+  // tiles: the blocks of the launch (the stream-K tail: its sk_wgs workgroups)
+  const TileSched ts{tiles, p.n_whole, p.sk_wgs};
+  hipLaunchKernelGGL(kern, dim3(tiles, (SPLIT && !SK) ? p.splits : 1), dim3(64 * (GWM * GWN + CW)), lds, s,
+                     A, M, K, B, N, bias, out, part, p.kper, pk, ts);
   return hipGetLastError();
 }
 
@@ -814,6 +919,20 @@ static hipError_t launch_epi(const uint16_t* A, int M, int K, const uint16_t* B,
     if (blocks > 4096) blocks = 4096;
     hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3(unsigned(blocks)), dim3(256), 0, s, part,
                        p.splits, M, N, bias, out);
+    return hipGetLastError();
+  }
+  if (p.bm == 256 && p.sk_wgs > 0) {
+    // whole rounds, then the tail's K steps over sk_wgs workgroups, then the
+    // tail tiles' sums and epilogue
+    float* part = reinterpret_cast<float*>(ws);
+    hipError_t e = launch_dl<256, 256, EPI, false, 32>(A, M, K, B, N, bias, out, nullptr, p, p.n_whole, s);
+    if (e != hipSuccess) return e;
+    e = launch_dl<256, 256, kEpiF32, true, 32, true>(A, M, K, B, N, nullptr, nullptr, part, p, p.sk_wgs, s);
+    if (e != hipSuccess) return e;
+    const int n_tail = ((M + 255) / 256) * ((N + 255) / 256) - p.n_whole;
+    const TileSched ts{0, p.n_whole, p.sk_wgs};
+    hipLaunchKernelGGL((streamk_reduce_kernel<EPI, 256, 256>), dim3(256 * 256 / 4 / 256, n_tail), dim3(256), 0, s,
+                       part, M, N, K / 32, ts, bias, out);
     return hipGetLastError();
   }
   if (p.bm == 256) return launch_tile<256, 256, EPI, false>(A, M, K, B, N, bias, out, nullptr, p, s);

@@ -70,6 +70,19 @@ struct GemmPlan {
   int bm, bn;        // tile
   int splits;        // split-K factor (1 = none)
   int kper;          // K elements per split (multiple of 64)
+  // Stream-K tail (256 x 256 tiles only): the first n_whole tiles run whole,
+  // one workgroup each (whole rounds of the GPU's workgroups); the K steps of
+  // the rest are shared evenly by sk_wgs workgroups (0: no tail split).
+  int n_whole = 0;
+  int sk_wgs = 0;
+};
+// Which tiles a gemm_dl_kernel launch covers: its blocks map to the first npid
+// tiles (XCD-contiguous); with a stream-K tail, the tail kernel's sk_wgs blocks
+// share the K steps of the tiles from n_whole on.
+struct TileSched {
+  int npid;
+  int n_whole;
+  int sk_wgs;
 };
 GemmPlan plan_gemm(int M, int N, int K);
 size_t gemm_workspace_bytes(int M, int N, int K);
