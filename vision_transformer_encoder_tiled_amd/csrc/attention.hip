@@ -69,6 +69,7 @@
 // round-robin dispatch over the 8 XCDs, every q-tile of one (image, head)
 // lands on the same XCD, so its K/V stream is shared through one L2.
 #include <algorithm>
+#include <vector>
 
 #include "vt_device.h"
 #include "vt_kernels.h"
@@ -778,10 +779,11 @@ __global__ void __launch_bounds__(64 * NW, WPE) attention_lean_kernel(
   }
 }
 
-// Combines the partial records of the split tail's cut items: block
-// (u, g) takes queries 32g .. 32g+31 of tail item n_whole + u, one thread per
-// (query, 16-byte chunk of its output row), so that consecutive threads read
-// consecutive chunks of a record row.  With the pieces' maxima m_p, row sums
+// Combines the partial records of the split tail's cut items: block u takes
+// tail item n_whole + u, 32 queries at a time, one thread per (query, 16-byte
+// chunk of its output row), so that consecutive threads read consecutive
+// chunks of a record row.  (One block per item, so that a call without a
+// split tail costs only S + heads blocks that exit at once.)  With the pieces' maxima m_p, row sums
 // l_p and unnormalized outputs O_p of a query: m = max m_p,
 // l = sum l_p 2^(m_p - m), out = sum O_p 2^(m_p - m) / l, lse = m + log2 l.
 constexpr int kMergeQ = 32;                 // queries per merge block
@@ -806,12 +808,13 @@ __global__ void __launch_bounds__(kMergeThreads) attn_tail_merge_kernel(
   const int kA = wg_of(P0), kB = wg_of(P0 + n - 1);
   if (kA == kB) return;  // run whole by one workgroup
   const int4 desc = qdesc[qt];
-  const int ql = blockIdx.y * kMergeQ + threadIdx.x / CH, c = threadIdx.x % CH;
-  if (ql >= min(WQ, desc.z - desc.x)) return;
+  const int nvalid = min(WQ, desc.z - desc.x);
   auto rec_of = [&](int k) {
     const int64_t klo = int64_t(k) * plan.T / tail_wgs;
     return part + int64_t(klo >= P0 ? 2 * k : 2 * k + 1) * REC;
   };
+  for (int ql = threadIdx.x / CH; ql < nvalid; ql += kMergeQ) {
+  const int c = threadIdx.x % CH;
   float m = -INFINITY;
   for (int k = kA; k <= kB; ++k) m = fmaxf(m, rec_of(k)[WQ * 80 + ql]);
   float l = 0.f;
@@ -836,6 +839,7 @@ __global__ void __launch_bounds__(kMergeThreads) attn_tail_merge_kernel(
   else
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + at) =
         make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+  }
 }
 
 template <int NW, int KG, int NST>
@@ -851,6 +855,23 @@ static hipError_t launch_attention_kernel(const uint16_t* qpk, const uint16_t* k
   hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(64 * NW), lds, s, qpk, kv, qdesc, heads,
                      out, out_f32 ? 1 : 0, lse);
   return hipGetLastError();
+}
+
+// tail_plan on the host, from the images' token counts: the schedule's
+// q-tiles (images largest first, ties in image order) and their key tiles.
+static bool host_tail_splits(const int64_t* tokens, int n_img, int WQ, int heads, int S) {
+  std::vector<int> idx(n_img);
+  for (int i = 0; i < n_img; ++i) idx[i] = i;
+  std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return tokens[a] > tokens[b]; });
+  std::vector<int64_t> kt;  // key tiles of each q-tile, in schedule order
+  for (int i : idx)
+    for (int64_t q = 0; q < (tokens[i] + WQ - 1) / WQ; ++q) kt.push_back((tokens[i] + BKV - 1) / BKV);
+  const int64_t nq = int64_t(kt.size()), n_items = nq * heads;
+  const int64_t nw = (n_items / S) * S / heads * heads;
+  if (nw >= n_items) return false;
+  int64_t T = 0;
+  for (int64_t q = nw / heads; q < nq; ++q) T += heads * kt[q];
+  return T >= int64_t(S) * kAttnTailMinTiles;
 }
 
 // Workgroups of kern the GPU holds at once (blocks per CU x CUs), per device
@@ -883,13 +904,15 @@ static hipError_t launch_lean(const uint16_t* qpk, const uint16_t* kv, const int
   int S = 0;
   if (tail.part && tail.qkpre && tail.nq)
     S = std::min(resident_wgs<VARIANT>(kern, 64 * NW, lds), attn_tail_max_wgs(VARIANT));
+  if (S > 0 && tail.host_tokens && !host_tail_splits(tail.host_tokens, tail.host_n_img, 32 * NW, heads, S))
+    S = 0;
   const int64_t blocks = int64_t(max_qtiles) * heads + S;
   hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(64 * NW), lds, s, qpk, kv, qdesc, heads, out,
                      out_f32 ? 1 : 0, lse, tail.qkpre, tail.nq, S, tail.part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 0) return e;
   // at most S + heads - 1 items are in a split tail
-  hipLaunchKernelGGL(attn_tail_merge_kernel<32 * NW>, dim3(unsigned(S + heads), NW), dim3(kMergeThreads), 0, s, qdesc,
+  hipLaunchKernelGGL(attn_tail_merge_kernel<32 * NW>, dim3(unsigned(S + heads)), dim3(kMergeThreads), 0, s, qdesc,
                      tail.qkpre, tail.nq, heads, S, tail.part, out, out_f32 ? 1 : 0, lse);
   return hipGetLastError();
 }

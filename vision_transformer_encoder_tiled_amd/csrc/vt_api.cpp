@@ -79,6 +79,13 @@ struct GridInfo {
   int64_t pixels = 0;
 };
 
+// Token counts t*h*w of the items of a grid list.
+std::vector<int64_t> grid_tokens(const vt_grid_thw* grid, int32_t n_img) {
+  std::vector<int64_t> n(n_img);
+  for (int i = 0; i < n_img; ++i) n[i] = int64_t(grid[i].t) * grid[i].h * grid[i].w;
+  return n;
+}
+
 // Frames stored per item: one still frame for t = 1, 2t frames for a clip.
 int64_t frames_of(int32_t t) { return t == 1 ? 1 : 2 * int64_t(t); }
 
@@ -139,6 +146,8 @@ struct BlockBufs {
   int32_t* qkpre;  // key tiles before each q-tile slot (max_q_tiles at 64 queries, + 1)
   float* part;     // partial records of the lean kernel's split tail (null: no split)
   int2* kdesc;     // per key-tile slot
+  const int64_t* host_tokens = nullptr;  // the images' token counts when the host knows them
+  int32_t host_n_img = 0;
   uint16_t* qpk;   // [N, heads, 80] fp16 rotated, scaled Q
   uint16_t* kv;    // max_ktiles x heads K/V tile images (fp16)
   int32_t* kslot;  // [N] tile image and slot of each token's key
@@ -353,7 +362,8 @@ vt_status run_block(const vt_config* cfg, float* R, const vt_block_weights* w, c
     const int32_t var = attn_variant(N, n_img, cfg->heads);
     VT_TRY_HIP(vt::launch_attention_packed(b.qpk, b.kv, b.qdesc, max_q_tiles(N, n_img, vt::attn_q_tile(var)),
                                            cfg->heads, var, att, false, nullptr, s,
-                                           vt::AttnTail{b.qkpre, b.tile_start + n_img, b.part}));
+                                           vt::AttnTail{b.qkpre, b.tile_start + n_img, b.part, b.host_tokens,
+                                                        b.host_n_img}));
   } else if (e == hipErrorInvalidValue) {  // a shape the pack epilogue does not take (nothing launched)
     (void)hipGetLastError();
     VT_TRY_HIP(vt::launch_gemm(b.xn, M, d, w->w_qkv, 3 * d, w->b_qkv, vt::kEpiBf16, qkv, b.gemm_ws, s));
@@ -1021,6 +1031,9 @@ VT_API vt_status vt_tower_forward(const vt_config* cfg, const uint16_t* pixels,
   VT_TRY_HIP(vt::launch_patchify(pixels, t.info, t.cu, t.tok_img, int32_t(N), t.X, s));
   VT_TRY_HIP(vt::launch_gemm(t.X, int(N), 1176, w->w_patch, cfg->hidden, w->b_patch, vt::kEpiF32, t.R,
                              t.blk.gemm_ws, s));
+  const std::vector<int64_t> tokens = grid_tokens(grid, n_img);
+  t.blk.host_tokens = tokens.data();
+  t.blk.host_n_img = n_img;
   bool xn_ready = false;
   for (int l = 0; l < cfg->layers; ++l) {
     const vt_block_weights* nx = l + 1 < cfg->layers ? &w->blocks[l + 1] : nullptr;
@@ -1128,6 +1141,9 @@ VT_API vt_status vt_tower_backward(const vt_config* cfg, const uint16_t* pixels,
   if ((st = attn_prologue(cfg, t.cu, n_img, N, gi.max_hw, t.blk, &axis_code, s, true)) != VT_OK) return st;
   VT_TRY_HIP(vt::launch_patchify(pixels, t.info, t.cu, t.tok_img, M, t.X, s));
   VT_TRY_HIP(vt::launch_gemm(t.X, M, 1176, w->w_patch, d, w->b_patch, vt::kEpiF32, t.R, t.blk.gemm_ws, s));
+  const std::vector<int64_t> tokens = grid_tokens(grid, n_img);
+  t.blk.host_tokens = tokens.data();
+  t.blk.host_n_img = n_img;
   bool xn_ready = false;
   const size_t plane = size_t(N) * d;
   for (int l = 0; l < cfg->layers; ++l) {

@@ -143,6 +143,11 @@ struct AttnTail {
   const int32_t* qkpre = nullptr;
   const int32_t* nq = nullptr;
   float* part = nullptr;
+  // Optional, host memory: the images' token counts, when the caller knows
+  // them; a call whose plan (formed here on the host as on the device) has no
+  // split then launches neither the extra workgroups nor the merge.
+  const int64_t* host_tokens = nullptr;
+  int32_t host_n_img = 0;
 };
 constexpr int kAttnTailMinTiles = 8;  // no split when a tail workgroup would get fewer key tiles
 inline int attn_tail_max_wgs(int variant) { return variant == kAttnLean4 ? 768 : 512; }
