@@ -171,7 +171,7 @@ def tail_pieces(n_items_keys, heads, S, min_tiles=8):
     n_items = nq * heads
     nw = (n_items // S) * S // heads * heads
     T = heads * (qkpre[nq] - qkpre[nw // heads]) if nw < n_items else 0
-    if T < S * min_tiles:
+    if T < S * min_tiles or (nw < n_items and n_items_keys[nw // heads] < 64):
         nw, T = n_items, 0
     pieces = [(i // heads, i % heads, 0, n_items_keys[i // heads], -1) for i in range(nw)]
     if T == 0:

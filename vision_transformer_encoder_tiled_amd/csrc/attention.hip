@@ -532,7 +532,12 @@ __device__ __forceinline__ TailPlan tail_plan(int nq, int heads, int S, const in
   const int n_items = nq * heads;
   const int nw = (n_items / S) * S / heads * heads;  // whole rounds, cut at a q-tile boundary
   if (nw >= n_items) return p;
-  const int64_t T = int64_t(heads) * (qkpre[nq] - qkpre[nw / heads]);
+  const int qt = nw / heads;
+  // Short tail items (a mixed batch's smallest images, last in the schedule)
+  // leave little idle time under the hardware's dynamic dispatch; the split
+  // pays only for long ones.
+  if (qkpre[qt + 1] - qkpre[qt] < kAttnTailMinItemTiles) return p;
+  const int64_t T = int64_t(heads) * (qkpre[nq] - qkpre[qt]);
   if (T < int64_t(S) * kAttnTailMinTiles) return p;
   p.n_whole = nw;
   p.qt_tail = nw / heads;
@@ -779,11 +784,11 @@ __global__ void __launch_bounds__(64 * NW, WPE) attention_lean_kernel(
   }
 }
 
-// Combines the partial records of the split tail's cut items: block u takes
-// tail item n_whole + u, 32 queries at a time, one thread per (query, 16-byte
-// chunk of its output row), so that consecutive threads read consecutive
-// chunks of a record row.  (One block per item, so that a call without a
-// split tail costs only S + heads blocks that exit at once.)  With the pieces' maxima m_p, row sums
+// Combines the partial records of the split tail's cut items: block (u, g)
+// takes queries 32g .. 32g+31 of tail item n_whole + u, one thread per
+// (query, 16-byte chunk of its output row), so that consecutive threads read
+// consecutive chunks of a record row.  (Launched only when a split is
+// possible; callers that know their images' sizes skip it when none is cut.)  With the pieces' maxima m_p, row sums
 // l_p and unnormalized outputs O_p of a query: m = max m_p,
 // l = sum l_p 2^(m_p - m), out = sum O_p 2^(m_p - m) / l, lse = m + log2 l.
 constexpr int kMergeQ = 32;                 // queries per merge block
@@ -813,8 +818,8 @@ __global__ void __launch_bounds__(kMergeThreads) attn_tail_merge_kernel(
     const int64_t klo = int64_t(k) * plan.T / tail_wgs;
     return part + int64_t(klo >= P0 ? 2 * k : 2 * k + 1) * REC;
   };
-  for (int ql = threadIdx.x / CH; ql < nvalid; ql += kMergeQ) {
-  const int c = threadIdx.x % CH;
+  const int ql = blockIdx.y * kMergeQ + threadIdx.x / CH, c = threadIdx.x % CH;
+  if (ql < nvalid) {
   float m = -INFINITY;
   for (int k = kA; k <= kB; ++k) m = fmaxf(m, rec_of(k)[WQ * 80 + ql]);
   float l = 0.f;
@@ -869,6 +874,7 @@ static bool host_tail_splits(const int64_t* tokens, int n_img, int WQ, int heads
   const int64_t nq = int64_t(kt.size()), n_items = nq * heads;
   const int64_t nw = (n_items / S) * S / heads * heads;
   if (nw >= n_items) return false;
+  if (kt[nw / heads] < kAttnTailMinItemTiles) return false;
   int64_t T = 0;
   for (int64_t q = nw / heads; q < nq; ++q) T += heads * kt[q];
   return T >= int64_t(S) * kAttnTailMinTiles;
@@ -912,7 +918,7 @@ static hipError_t launch_lean(const uint16_t* qpk, const uint16_t* kv, const int
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 0) return e;
   // at most S + heads - 1 items are in a split tail
-  hipLaunchKernelGGL(attn_tail_merge_kernel<32 * NW>, dim3(unsigned(S + heads)), dim3(kMergeThreads), 0, s, qdesc,
+  hipLaunchKernelGGL(attn_tail_merge_kernel<32 * NW>, dim3(unsigned(S + heads), NW), dim3(kMergeThreads), 0, s, qdesc,
                      tail.qkpre, tail.nq, heads, S, tail.part, out, out_f32 ? 1 : 0, lse);
   return hipGetLastError();
 }

@@ -149,7 +149,8 @@ struct AttnTail {
   const int64_t* host_tokens = nullptr;
   int32_t host_n_img = 0;
 };
-constexpr int kAttnTailMinTiles = 8;  // no split when a tail workgroup would get fewer key tiles
+constexpr int kAttnTailMinTiles = 8;       // no split when a tail workgroup would get fewer key tiles
+constexpr int kAttnTailMinItemTiles = 64;  // ... or when the tail's longest item has fewer
 inline int attn_tail_max_wgs(int variant) { return variant == kAttnLean4 ? 768 : 512; }
 inline int64_t attn_tail_records(int variant) { return variant == kAttnSmall ? 0 : 2 * attn_tail_max_wgs(variant); }
 inline int64_t attn_tail_record_floats(int variant) { return int64_t(attn_q_tile(variant)) * 82; }
