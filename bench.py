@@ -246,6 +246,24 @@ def attention_case(vt, torch, grids):
     return (lambda: vt.vt_attention_varlen(cfg, qkv, cu, pos, len(grids), N, max_seq, out, vt.VT_BF16, ws)), flops
 
 
+def attention_packed_case(vt, torch, grids):
+    """The attention kernels alone, as the tower runs them after its QKV
+    Linear: vt_attention_pack once, then vt_attention_packed (timed) on what it
+    left in the workspace."""
+    N = sum(t * h * w for t, h, w in grids)
+    g = np.random.Generator(np.random.PCG64(1))
+    qkv = torch.from_numpy(synth.bf16_bits(g.standard_normal((N, 3840), dtype=np.float32) * 0.7).view(np.int16)).cuda()
+    cfg = vt.config()
+    cu = torch.empty(len(grids) + 1, dtype=torch.int32, device="cuda")
+    pos = torch.empty((N, 3), dtype=torch.int32, device="cuda")
+    vt.vt_build_metadata(grids, cu, pos)
+    max_seq = max(t * h * w for t, h, w in grids)
+    ws = vt.workspace(vt.vt_block_workspace_size(cfg, N, len(grids), max_seq))
+    out = torch.empty((N, 1280), dtype=torch.int16, device="cuda")
+    vt.vt_attention_pack(cfg, qkv, cu, pos, len(grids), N, max_seq, ws)
+    return lambda: vt.vt_attention_packed(cfg, len(grids), N, max_seq, out, vt.VT_BF16, ws)
+
+
 def attention_backward_case(vt, torch, grids):
     """vt_attention_backward on the workload's token layout (random bf16 q, k,
     v and dO).  FLOPs counted: the gradient's four n^2 products (dP = dO V^T,
@@ -394,21 +412,31 @@ def gemm_roofline(vt, torch, M, iters):
 
 
 def attention_roofline(vt, torch, grids, iters, traffic_profile=None):
-    fn, flops = attention_case(vt, torch, grids)
+    """The attention kernels as the tower runs them (vt_attention_packed: the
+    attention kernel and, when the last round is split, its merge), and the
+    whole vt_attention_varlen call beside them (with the RoPE/pack kernel and
+    the per-call schedule and RoPE-table kernels, which the tower's blocks do
+    in the QKV Linear's epilogue and once per call)."""
+    fn = attention_packed_case(vt, torch, grids)
+    call, flops = attention_case(vt, torch, grids)
     t = time_kernel(torch, fn, iters)
     ghz = clock_under(vt, torch, fn, iters, t)
+    tc = time_kernel(torch, call, iters)
     N = sum(t_ * h * w for t_, h, w in grids)
     traffic = (profile_traffic(traffic_profile, "vision_transformer_encoder_tiled_amd/csrc/attention.hip")
                if traffic_profile else None)
-    return {"kernel": "attention_kernel (%d tokens, %d images)" % (N, len(grids)), "bound": "mfma",
+    return {"kernel": "attention kernels (%d tokens, %d images)" % (N, len(grids)), "bound": "mfma",
             "achieved": flops / t / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": flops / t / 1e12 / PEAK_BF16_TFLOPS, "traffic": traffic,
             "traffic_note": "attention kernel only (not the pack kernel)" if traffic else None,
             **at_clock(flops / t / 1e12, ghz),
             "flops_per_launch": flops,
             "avg_launch_us": t * 1e6,
-            "note": "one vt_attention_varlen call: the RoPE/pack kernel and the attention kernel, "
-                    "plus the per-call schedule and RoPE-table kernels"}
+            "varlen_call_us": tc * 1e6,
+            "varlen_call_frac": flops / tc / 1e12 / PEAK_BF16_TFLOPS,
+            "note": "avg_launch_us: one vt_attention_packed call (the attention kernel, plus the tail "
+                    "merge when the last round is split), as in the tower; varlen_call_us: one whole "
+                    "vt_attention_varlen call (schedule, RoPE table, RoPE/pack kernel, attention)"}
 
 
 def layernorm_roofline(vt, torch, rows, iters):

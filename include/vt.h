@@ -214,6 +214,32 @@ vt_status vt_attention_varlen(const vt_config* cfg, const uint16_t* qkv, const i
                               int32_t max_seqlen, void* out, vt_dtype out_dtype, void* ws,
                               size_t ws_bytes, void* stream);
 
+/* vt_attention_varlen in its two parts, for callers that time them apart or
+ * run the attention on prepared operands more than once.  Same operation,
+ * same kernels: vt_attention_pack then vt_attention_packed on one workspace
+ * give vt_attention_varlen's output bit for bit.
+ * vt_attention_pack: the per-call schedule (which queries and key tiles each
+ *   workgroup takes), the RoPE angle table, q rotated, scaled by
+ *   log2(e)/sqrt(head_dim) and rounded to fp16, and k, v as fp16 key-tile
+ *   images, all written into ws (arguments, range and clamp as
+ *   vt_attention_varlen; ws sized by vt_block_workspace_size).
+ * vt_attention_packed: the attention kernels alone (the step the tower runs
+ *   after its QKV Linear, whose epilogue does the packing itself) on what the
+ *   last vt_attention_pack left in ws, writing out as vt_attention_varlen.
+ *   ws and the sizes (cfg, n_img, total_tokens, max_seqlen, ws_bytes) must be
+ *   those of that vt_attention_pack, ordered after it (same stream, or
+ *   otherwise synchronized); ws is read, not consumed, so the call may be
+ *   repeated.  The sizes are validated as for vt_attention_varlen; the
+ *   contents of ws are not (they are device data): a workspace not prepared
+ *   by vt_attention_pack with the same sizes gives undefined results,
+ *   including out-of-bounds device accesses. */
+vt_status vt_attention_pack(const vt_config* cfg, const uint16_t* qkv, const int32_t* cu_seqlens,
+                            const int32_t* pos_thw, int32_t n_img, int32_t total_tokens,
+                            int32_t max_seqlen, void* ws, size_t ws_bytes, void* stream);
+vt_status vt_attention_packed(const vt_config* cfg, int32_t n_img, int32_t total_tokens,
+                              int32_t max_seqlen, void* out, vt_dtype out_dtype, void* ws,
+                              size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- no allocation
  * For callers that can neither allocate device memory nor pass a workspace:
  * code under HIP graph capture, tight serving loops, harnesses that forbid

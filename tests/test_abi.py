@@ -30,7 +30,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     declared = header_functions()
-    assert len(declared) == 27
+    assert len(declared) == 29
     assert sorted(vt.EXPORTED) == declared
     lib = ctypes.CDLL(vt.LIB_PATH)
     for name in declared:
@@ -127,6 +127,39 @@ def test_attention_validation():
     assert _attn(vt.config(head_dim=64, hidden=1024, rope_pairs=(0, 16, 16))) == vt.VT_ERR_UNSUPPORTED
     assert _attn(vt.config(rope_pairs=(8, 12, 20))) == vt.VT_ERR_UNSUPPORTED
     assert _attn(vt.config(rope_pairs=(8, 16, 8))) == vt.VT_ERR_INVALID_ARG
+
+
+@needs_no_gpu
+def test_attention_two_part_validation():
+    """vt_attention_pack validates as vt_attention_varlen (less out and its
+    dtype); vt_attention_packed validates the sizes, out, dtype and ws (the
+    workspace's contents are device data and are not checked)."""
+    cfg = vt.config()
+    P = lambda v: None if v is None else ctypes.c_void_p(v)
+    need = vt.vt_block_workspace_size(cfg, 64, 1, 64)
+
+    def pack(cfg=cfg, qkv=FAKE, cu=FAKE, n_img=1, total=64, max_seq=64, ws=FAKE, ws_bytes=need):
+        return vt.LIB.vt_attention_pack(ctypes.byref(cfg), P(qkv), P(cu), P(FAKE), n_img, total, max_seq,
+                                        P(ws), ws_bytes, None)
+
+    def packed(cfg=cfg, n_img=1, total=64, max_seq=64, out=FAKE, dtype=vt.VT_BF16, ws=FAKE, ws_bytes=need):
+        return vt.LIB.vt_attention_packed(ctypes.byref(cfg), n_img, total, max_seq, P(out), dtype, P(ws),
+                                          ws_bytes, None)
+
+    assert pack(ws_bytes=need - 1) == vt.VT_ERR_WORKSPACE
+    assert pack(qkv=None) == vt.VT_ERR_INVALID_ARG
+    assert pack(cu=None) == vt.VT_ERR_INVALID_ARG
+    assert pack(max_seq=65) == vt.VT_ERR_INVALID_ARG
+    assert pack(ws=FAKE + 64) == vt.VT_ERR_INVALID_ARG
+    assert pack(vt.config(rope_pairs=(8, 12, 20))) == vt.VT_ERR_UNSUPPORTED
+    assert packed(ws_bytes=need - 1) == vt.VT_ERR_WORKSPACE
+    assert packed(ws=None) == vt.VT_ERR_WORKSPACE
+    assert packed(out=None) == vt.VT_ERR_INVALID_ARG
+    assert packed(out=FAKE + 8) == vt.VT_ERR_INVALID_ARG
+    assert packed(dtype=7) == vt.VT_ERR_INVALID_ARG
+    assert packed(n_img=0) == vt.VT_ERR_INVALID_ARG
+    assert packed(max_seq=65) == vt.VT_ERR_INVALID_ARG
+    assert packed(vt.config(head_dim=64, hidden=1024, rope_pairs=(0, 16, 16))) == vt.VT_ERR_UNSUPPORTED
 
 
 def _attn_bwd(cfg, qkv=FAKE, dout=FAKE, dqkv=FAKE, n_img=1, total=64, max_seq=64, ws=FAKE,

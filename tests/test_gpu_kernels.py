@@ -467,6 +467,37 @@ def test_attention_positions_are_clamped_to_the_table(vt):
     assert err <= 2e-3
 
 
+@pytest.mark.parametrize("grids", [[(1, 32, 32)], [(1, 20, 24), (1, 8, 14), (1, 2, 2)], [(1, 112, 112)],
+                                   [(1, 74, 92), (1, 88, 56), (1, 94, 22), (1, 38, 46)]])
+def test_attention_pack_then_packed_equals_varlen(vt, grids):
+    """vt_attention_pack + vt_attention_packed (the two halves of
+    vt_attention_varlen, the second one alone as the tower runs it) give
+    vt_attention_varlen's output bit for bit, bf16 and fp32, also when
+    vt_attention_packed is repeated on the same workspace: the two-key-group
+    kernel (448x448, small mixed items), the lean kernel with a split last
+    round (112x112) and without (mixed large grids)."""
+    N = sum(t * h * w for t, h, w in grids)
+    cfg = vt.config()
+    cu = torch.empty(len(grids) + 1, dtype=torch.int32, device="cuda")
+    pos = torch.empty((N, 3), dtype=torch.int32, device="cuda")
+    vt.vt_build_metadata(grids, cu, pos)
+    max_seq = max(t * h * w for t, h, w in grids)
+    qkv = dev_bits(synth.bf16_bits(rng(23).standard_normal((N, 3840), dtype=np.float32)), torch)
+    ws = vt.workspace(vt.vt_block_workspace_size(cfg, N, len(grids), max_seq))
+    for dtype, tdt in ((vt.VT_BF16, torch.int16), (vt.VT_FP32, torch.float32)):
+        want = torch.empty((N, 1280), dtype=tdt, device="cuda")
+        vt.vt_attention_varlen(cfg, qkv, cu, pos, len(grids), N, max_seq, want, dtype, ws)
+        ws.zero_()
+        vt.vt_attention_pack(cfg, qkv, cu, pos, len(grids), N, max_seq, ws)
+        for rep in range(2):
+            got = torch.full((N, 1280), 7, dtype=tdt, device="cuda")
+            vt.vt_attention_packed(cfg, len(grids), N, max_seq, got, dtype, ws)
+            torch.cuda.synchronize()
+            assert torch.equal(got.view(torch.int32) if tdt == torch.float32 else got,
+                               want.view(torch.int32) if tdt == torch.float32 else want), (dtype, rep)
+    log(f"pack + packed == varlen {grids[:2]}{'...' if len(grids) > 2 else ''} ({N} tokens)")
+
+
 def test_attention_mixed_grids_sampled(vt):
     grids = list(synth.WORKLOADS["tower_mixed8"].grids)
     N = sum(h * w for _, h, w in grids)

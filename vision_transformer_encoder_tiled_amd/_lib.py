@@ -30,7 +30,7 @@ EXPORTED = ("vt_config_default", "vt_status_string", "vt_last_error", "vt_versio
             "vt_attention_backward_workspace_size", "vt_block_backward",
             "vt_block_backward_workspace_size", "vt_tower_backward",
             "vt_tower_backward_workspace_size", "vt_clock_probe", "vt_attention_varlen_noalloc",
-            "vt_linear_residual_ln")
+            "vt_linear_residual_ln", "vt_attention_pack", "vt_attention_packed")
 
 
 class VtError(RuntimeError):
@@ -97,6 +97,8 @@ def _load():
                                                _P, SZ, _P]),
         "vt_attention_varlen_noalloc": (ctypes.c_int, [cfgp, _P, _P, _P, I32, I32, I32, _P, ctypes.c_int,
                                                        _P]),
+        "vt_attention_pack": (ctypes.c_int, [cfgp, _P, _P, _P, I32, I32, I32, _P, SZ, _P]),
+        "vt_attention_packed": (ctypes.c_int, [cfgp, I32, I32, I32, _P, ctypes.c_int, _P, SZ, _P]),
         "vt_attention_backward": (ctypes.c_int, [cfgp, _P, _P, _P, I32, I32, I32, _P, _P,
                                                  ctypes.c_int, _P, SZ, _P]),
         "vt_attention_backward_workspace_size": (SZ, [cfgp, I32, I32, I32]),
@@ -219,6 +221,17 @@ def vt_attention_varlen(cfg, qkv, cu_seqlens, pos_thw, n_img, total_tokens, max_
     _check(LIB.vt_attention_varlen(ctypes.byref(cfg), _ptr(qkv), _ptr(cu_seqlens), _ptr(pos_thw),
                                    n_img, total_tokens, max_seqlen, _ptr(out), out_dtype, _ptr(ws),
                                    ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def vt_attention_pack(cfg, qkv, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen, ws, stream=None):
+    _check(LIB.vt_attention_pack(ctypes.byref(cfg), _ptr(qkv), _ptr(cu_seqlens), _ptr(pos_thw), n_img,
+                                 total_tokens, max_seqlen, _ptr(ws), ws.numel() if ws is not None else 0,
+                                 _stream(stream)))
+
+
+def vt_attention_packed(cfg, n_img, total_tokens, max_seqlen, out, out_dtype, ws, stream=None):
+    _check(LIB.vt_attention_packed(ctypes.byref(cfg), n_img, total_tokens, max_seqlen, _ptr(out), out_dtype,
+                                   _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def vt_attention_varlen_noalloc(cfg, qkv, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen, out,

@@ -923,14 +923,21 @@ static hipError_t launch_lean(const uint16_t* qpk, const uint16_t* kv, const int
   return hipGetLastError();
 }
 
+hipError_t launch_attn_pack(const uint16_t* qkv, const int32_t* pos_thw, const int2* kdesc, int32_t max_ktiles,
+                            int32_t heads, int32_t n_pos, int32_t axis_code, const float2* rope_cs,
+                            float q_scale_log2, uint16_t* qpk, uint16_t* kv, hipStream_t s) {
+  hipLaunchKernelGGL(attn_pack_kernel, dim3(unsigned(int64_t(max_ktiles) * heads)), dim3(320), 0, s,
+                     qkv, pos_thw, kdesc, heads, n_pos, rope_cs, axis_code, q_scale_log2, qpk, kv);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(const uint16_t* qkv, const int32_t* pos_thw, const int4* qdesc,
                             const int2* kdesc, int32_t max_qtiles, int32_t max_ktiles,
                             int32_t heads, int32_t n_pos, int32_t axis_code, const float2* rope_cs,
                             float q_scale_log2, int32_t variant, uint16_t* qpk, uint16_t* kv,
                             void* out, bool out_f32, float* lse, hipStream_t s, const AttnTail& tail) {
-  hipLaunchKernelGGL(attn_pack_kernel, dim3(unsigned(int64_t(max_ktiles) * heads)), dim3(320), 0, s,
-                     qkv, pos_thw, kdesc, heads, n_pos, rope_cs, axis_code, q_scale_log2, qpk, kv);
-  hipError_t e = hipGetLastError();
+  const hipError_t e =
+      launch_attn_pack(qkv, pos_thw, kdesc, max_ktiles, heads, n_pos, axis_code, rope_cs, q_scale_log2, qpk, kv, s);
   if (e != hipSuccess) return e;
   return launch_attention_packed(qpk, kv, qdesc, max_qtiles, heads, variant, out, out_f32, lse, s, tail);
 }

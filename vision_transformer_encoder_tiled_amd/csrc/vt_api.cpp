@@ -599,6 +599,30 @@ static vt_status check_varlen(const vt_config* cfg, const int32_t* cu_seqlens, c
   return VT_OK;
 }
 
+// The two halves of vt_attention_varlen, on the workspace layout of
+// vt_block_forward (carve_block): the pack (schedule, RoPE table, rotated Q,
+// tile images) and the attention kernels on what it left there.
+static vt_status attention_pack_into(const vt_config* cfg, const uint16_t* qkv, const int32_t* cu_seqlens,
+                                     const int32_t* pos_thw, int32_t n_img, int32_t total_tokens,
+                                     int32_t max_seqlen, const BlockBufs& b, hipStream_t s) {
+  int32_t axis_code = 0;
+  vt_status st = attn_prologue(cfg, cu_seqlens, n_img, total_tokens, max_seqlen, b, &axis_code, s);
+  if (st != VT_OK) return st;
+  VT_TRY_HIP(vt::launch_attn_pack(qkv, pos_thw, b.kdesc, max_k_tiles(total_tokens, n_img), cfg->heads, max_seqlen,
+                                  axis_code, b.rope, q_scale_log2(cfg), b.qpk, b.kv, s));
+  return VT_OK;
+}
+
+static vt_status attention_on_packed(const vt_config* cfg, int32_t n_img, int32_t total_tokens, const BlockBufs& b,
+                                     void* out, bool f32, hipStream_t s) {
+  const int32_t var = attn_variant(total_tokens, n_img, cfg->heads);
+  VT_TRY_HIP(vt::launch_attention_packed(b.qpk, b.kv, b.qdesc,
+                                         max_q_tiles(total_tokens, n_img, vt::attn_q_tile(var)), cfg->heads,
+                                         var, out, f32, nullptr, s,
+                                         vt::AttnTail{b.qkpre, b.tile_start + n_img, b.part}));
+  return VT_OK;
+}
+
 VT_API vt_status vt_attention_varlen(const vt_config* cfg, const uint16_t* qkv,
                                      const int32_t* cu_seqlens, const int32_t* pos_thw,
                                      int32_t n_img, int32_t total_tokens, int32_t max_seqlen,
@@ -615,10 +639,44 @@ VT_API vt_status vt_attention_varlen(const vt_config* cfg, const uint16_t* qkv,
   Carver c(ws);
   BlockBufs b;
   carve_block(c, dims_of(cfg, total_tokens, n_img), max_seqlen, &b);
-  int32_t axis_code = 0;
-  if ((st = attn_prologue(cfg, cu_seqlens, n_img, total_tokens, max_seqlen, b, &axis_code, s)) != VT_OK) return st;
-  return run_attention(cfg, qkv, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen, axis_code, b,
-                       out, out_dtype == VT_FP32, s);
+  if ((st = attention_pack_into(cfg, qkv, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen, b, s)) != VT_OK)
+    return st;
+  return attention_on_packed(cfg, n_img, total_tokens, b, out, out_dtype == VT_FP32, s);
+}
+
+VT_API vt_status vt_attention_pack(const vt_config* cfg, const uint16_t* qkv, const int32_t* cu_seqlens,
+                                   const int32_t* pos_thw, int32_t n_img, int32_t total_tokens,
+                                   int32_t max_seqlen, void* ws, size_t ws_bytes, void* stream) {
+  vt_status st = check_varlen(cfg, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen);
+  if (st != VT_OK) return st;
+  if ((st = check_ptr(qkv, "qkv")) != VT_OK) return st;
+  const size_t need = block_ws_bytes(cfg, total_tokens, n_img, max_seqlen);
+  if ((st = check_ws(ws, ws_bytes, need)) != VT_OK) return st;
+  Carver c(ws);
+  BlockBufs b;
+  carve_block(c, dims_of(cfg, total_tokens, n_img), max_seqlen, &b);
+  return attention_pack_into(cfg, qkv, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen, b,
+                             static_cast<hipStream_t>(stream));
+}
+
+VT_API vt_status vt_attention_packed(const vt_config* cfg, int32_t n_img, int32_t total_tokens, int32_t max_seqlen,
+                                     void* out, vt_dtype out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  vt_status st = check_config(cfg);
+  if (st != VT_OK) return st;
+  if (n_img <= 0 || total_tokens <= 0 || max_seqlen <= 0)
+    return fail(VT_ERR_INVALID_ARG, "n_img, total_tokens and max_seqlen must be positive");
+  if (max_seqlen > total_tokens)
+    return fail(VT_ERR_INVALID_ARG, "max_seqlen %d exceeds total_tokens %d", max_seqlen, total_tokens);
+  if (total_tokens > kMaxTokens)
+    return fail(VT_ERR_UNSUPPORTED, "more than %lld tokens in one call", (long long)kMaxTokens);
+  if ((st = check_ptr(out, "out")) != VT_OK) return st;
+  if (out_dtype != VT_BF16 && out_dtype != VT_FP32) return fail(VT_ERR_INVALID_ARG, "bad out_dtype");
+  const size_t need = block_ws_bytes(cfg, total_tokens, n_img, max_seqlen);
+  if ((st = check_ws(ws, ws_bytes, need)) != VT_OK) return st;
+  Carver c(ws);
+  BlockBufs b;
+  carve_block(c, dims_of(cfg, total_tokens, n_img), max_seqlen, &b);
+  return attention_on_packed(cfg, n_img, total_tokens, b, out, out_dtype == VT_FP32, static_cast<hipStream_t>(stream));
 }
 
 // ---- vt_attention_varlen without a workspace argument

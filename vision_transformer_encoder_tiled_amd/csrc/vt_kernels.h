@@ -172,6 +172,13 @@ hipError_t launch_attention(const uint16_t* qkv, const int32_t* pos_thw, const i
                             void* out, bool out_f32, float* lse, hipStream_t s,
                             const AttnTail& tail = AttnTail());
 
+// The pack kernel alone: rotated, scaled fp16 Q into qpk and the K/V tile
+// images into kv, from bf16 qkv [N, 3, heads, 80] (the first step of
+// launch_attention).
+hipError_t launch_attn_pack(const uint16_t* qkv, const int32_t* pos_thw, const int2* kdesc, int32_t max_ktiles,
+                            int32_t heads, int32_t n_pos, int32_t axis_code, const float2* rope_cs,
+                            float q_scale_log2, uint16_t* qpk, uint16_t* kv, hipStream_t s);
+
 // The attention kernel alone, on Q and tile images already packed (by the
 // pack kernel inside launch_attention, or by the QKV GEMM epilogue).
 hipError_t launch_attention_packed(const uint16_t* qpk, const uint16_t* kv, const int4* qdesc,
