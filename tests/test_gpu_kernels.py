@@ -176,10 +176,12 @@ GEMM_SHAPES = [  # (M, N, K, what)
     (300, 960, 640, "ragged M and N, one round of 128x128 tiles, K steps of 64"),
     (200, 6144, 24576, "ragged M, 256x256 split-K"),
     (1024, 1280, 1216, "split-K, K not a multiple of the split"),
-    (20736, 5120, 1280, "FC1, 2016x2016 (256 tile)"),
+    (20736, 5120, 1280, "FC1, 2016x2016 (256 tile; quadrant tail: 84 of 1620 tiles)"),
     (20736, 1280, 5120, "FC2, 2016x2016 (stream-K tail: 149 of 405 tiles over 256 workgroups)"),
     (16384, 1280, 5120, "FC2, 16 x 448x448 (stream-K tail: 64 of 320 tiles)"),
     (5184, 6144, 24576, "merged MLP 1, 2016x2016 (stream-K tail)"),
+    (16384, 1280, 1280, "O, 16 x 448x448 (quadrant tail: 64 of 320 tiles as 128x128 quadrants)"),
+    (8192, 5120, 1280, "FC1, 16-frame clip (quadrant tail: 128 of 640 tiles, two rounds of quadrants)"),
 ]
 
 
@@ -205,7 +207,8 @@ def test_linear_shapes(vt, M, N, K, what):
 @pytest.mark.parametrize("epi", ["bf16", "gelu_tanh", "gelu_erf", "resid"])
 @pytest.mark.parametrize("M,N,K", [(200, 512, 320), (1024, 1280, 5120), (1000, 5120, 1280),
                                    (968, 6144, 640), (200, 6144, 6144),
-                                   (4608, 4096, 2048)])  # stream-K tail: 32 of 288 tiles in eighths
+                                   (4608, 4096, 2048),   # stream-K tail: 32 of 288 tiles in eighths
+                                   (2200, 7680, 320)])   # quadrant tail: 14 of 270 tiles, ragged M
 def test_linear_epilogues(vt, epi, M, N, K):
     log(f"linear epilogue {epi} {M}x{N}x{K}")
     x = random_bf16((M, K), 7)

@@ -343,3 +343,68 @@ def test_gemm_streamk_tail_covers_every_k_step_once(M, N, K):
         assert spans[0][0] == 0 and spans[-1][1] == nks
         assert all(a[1] == b[0] for a, b in zip(spans, spans[1:]))
     assert sorted(r for rs in red.values() for r in rs) == sorted(slots)
+
+
+def group_tile(pid, tiles_m, tiles_n, GM=4):
+    """gemm.hip group_tile: tile (tm, tn) of linear index pid, in groups of GM tile rows."""
+    per_group = GM * tiles_n
+    gid = pid // per_group
+    first = gid * GM
+    gsz = min(tiles_m - first, GM)
+    in_g = pid - gid * per_group
+    return first + in_g % gsz, in_g // gsz
+
+
+def xcd_pid(npid, b):
+    """gemm.hip xcd_pid: the tile index of block b when npid tiles are spread over 8 XCDs."""
+    q, r, x, l = npid // 8, npid % 8, b % 8, b // 8
+    return x * (q + 1) + l if x < r else r * (q + 1) + (x - r) * q + l
+
+
+def quadrant_tail(M, N, K, CUs=256, limit=128):
+    """gemm.hip tail_quadrant_tiles / plan_gemm: (n_whole, n_tail) when the
+    last partial round of a 256 x 256 tiling runs as 128 x 128 quadrants, else None."""
+    cdiv = lambda a, b: -(-a // b)
+    t256 = cdiv(M, 256) * cdiv(N, 256)
+    if t256 < 192 or t256 <= CUs or K % 32:
+        return None
+    n_tail = t256 % CUs
+    if n_tail == 0 or n_tail > limit:
+        return None
+    nks = K // 32
+    if K >= 2048 and CUs % n_tail == 0 and nks >= 8 * (CUs // n_tail):
+        return None                                   # the stream-K tail takes it
+    return t256 - n_tail, n_tail
+
+
+@pytest.mark.parametrize("M,N,K", [(16384, 1280, 1280), (34852, 3840, 1280), (20736, 5120, 1280),
+                                   (8192, 5120, 1280), (34852, 1280, 1280), (16500, 1280, 1280)])
+def test_gemm_quadrant_tail_covers_every_tile_once(M, N, K):
+    """The whole-tile launch (blocks 0 .. n_whole-1 through xcd_pid and
+    group_tile) and the quadrant launch (block b: quadrant b % 4 of 256-tile
+    n_whole + b / 4; quadrants past M or N exit) cover every 128 x 128 tile
+    of the output exactly once; no quadrant launch of more than two rounds."""
+    plan = quadrant_tail(M, N, K)
+    if plan is None:
+        pytest.skip("no quadrant tail for this shape")
+    n_whole, n_tail = plan
+    cdiv = lambda a, b: -(-a // b)
+    tm2, tn2 = cdiv(M, 256), cdiv(N, 256)
+    cover = {}
+    for b in range(n_whole):
+        tm, tn = group_tile(xcd_pid(n_whole, b), tm2, tn2)
+        assert 0 <= tm < tm2 and 0 <= tn < tn2
+        for q in range(4):
+            sub = (2 * tm + q // 2, 2 * tn + q % 2)
+            if sub[0] * 128 < M and sub[1] * 128 < N:
+                cover[sub] = cover.get(sub, 0) + 1
+    assert 4 * n_tail <= 512
+    for b in range(4 * n_tail):
+        tm, tn = group_tile(n_whole + b // 4, tm2, tn2)
+        sub = (2 * tm + (b >> 1 & 1), 2 * tn + (b & 1))
+        if sub[0] * 128 >= M or sub[1] * 128 >= N:
+            continue
+        cover[sub] = cover.get(sub, 0) + 1
+    want = {(i, j) for i in range(cdiv(M, 128)) for j in range(cdiv(N, 128))}
+    assert set(cover) == want
+    assert max(cover.values()) == 1

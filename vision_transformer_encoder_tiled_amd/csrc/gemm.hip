@@ -387,7 +387,17 @@ __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
     if (piece > 0) __syncthreads();  // the previous piece's epilogue is done with the LDS
   } else {
     if (piece > 0) break;
-    group_tile(xcd_pid(ts.npid, blockIdx.x), tiles_m, tiles_n, &tm, &tn);
+    if (BM == 128 && BN == 128 && ts.tail_of >= 0) {
+      // Quadrant blockIdx.x % 4 of 256 x 256 tile tail_of + blockIdx.x / 4
+      // (in that tiling's order); quadrants wholly past M or N have no work.
+      int t2m, t2n;
+      group_tile(ts.tail_of + int(blockIdx.x >> 2), (M + 255) / 256, (N + 255) / 256, &t2m, &t2n);
+      tm = 2 * t2m + int((blockIdx.x >> 1) & 1);
+      tn = 2 * t2n + int(blockIdx.x & 1);
+      if (tm * BM >= M || tn * BN >= N) return;
+    } else {
+      group_tile(xcd_pid(ts.npid, blockIdx.x), tiles_m, tiles_n, &tm, &tn);
+    }
     kbeg = SPLIT ? blockIdx.y * kper : 0;
     kend = SPLIT ? min(K, kbeg + kper) : K;
   }
@@ -784,6 +794,19 @@ __global__ void __launch_bounds__(256) streamk_reduce_kernel(const float* __rest
   epi_store4<EPI>(out, int64_t(tok) * N + col, acc.x, acc.y, acc.z, acc.w);
 }
 
+// Tiles of a 256 x 256 tiling's partial last round to run as 128 x 128
+// quadrants instead (0: none): a last round of at most half the CUs' tiles.
+// Its quadrants (up to 512 workgroups, two per CU) take well under a whole
+// tile's time: O at 16,384 tokens (64 tail tiles) 99.9 -> 81.3 us, QKV-shaped
+// 34,852 x 3840 x 1280 (7) 383 -> 361 us; fuller last rounds were slower
+// this way (173 of 256: 170 -> 189 us), so they keep whole tiles.
+static int tail_quadrant_tiles(int t256, int K) {
+  constexpr int kCUs = 256, kMaxTail = 128;
+  if (t256 <= kCUs || K % 32 != 0) return 0;
+  const int n_tail = t256 % kCUs;
+  return n_tail <= kMaxTail ? n_tail : 0;
+}
+
 GemmPlan plan_gemm(int M, int N, int K) {
   auto cdiv = [](long a, long b) { return int((a + b - 1) / b); };
   GemmPlan p{256, 256, 1, K};
@@ -804,6 +827,10 @@ GemmPlan plan_gemm(int M, int N, int K) {
         p.n_whole = n_whole;
         p.sk_wgs = kCUs;
       }
+    }
+    if (p.sk_wgs == 0) {
+      p.tail128 = tail_quadrant_tiles(t256, K);
+      if (p.tail128 > 0) p.n_whole = t256 - p.tail128;
     }
     return p;
   }
@@ -853,7 +880,7 @@ size_t gemm_workspace_bytes(int M, int N, int K) {
 template <int BM, int BN, int EPI, bool SPLIT, int BK, bool SK = false>
 static hipError_t launch_dl(const uint16_t* A, int M, int K, const uint16_t* B, int N,
                             const uint16_t* bias, void* out, float* part, const GemmPlan& p,
-                            int tiles, hipStream_t s, const QkvPack& pk = QkvPack{}) {
+                            int tiles, hipStream_t s, const QkvPack& pk = QkvPack{}, int tail_of = -1) {
   // 256 x 256: 8 wavefronts (2 per SIMD) of 128 x 64; 128 x 128: 8 of 32 x 64;
   // 128 x 160 and 128 x 192: 4 of 32 x BN plus 4 that only copy.  K steps of
   // 32 go through 4 stages, K steps of 64 through 3.
@@ -866,7 +893,7 @@ static hipError_t launch_dl(const uint16_t* A, int M, int K, const uint16_t* B, 
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (attr != hipSuccess) return attr;
   // tiles: the blocks of the launch (the stream-K tail: its sk_wgs workgroups)
-  const TileSched ts{tiles, p.n_whole, p.sk_wgs};
+  const TileSched ts{tiles, p.n_whole, p.sk_wgs, tail_of};
   hipLaunchKernelGGL(kern, dim3(tiles, (SPLIT && !SK) ? p.splits : 1), dim3(64 * (GWM * GWN + CW)), lds, s,
                      A, M, K, B, N, bias, out, part, p.kper, pk, ts);
   return hipGetLastError();
@@ -905,6 +932,21 @@ static hipError_t launch_tile(const uint16_t* A, int M, int K, const uint16_t* B
   }
 }
 
+// The first n_whole tiles of a 256 x 256 tiling whole, then its last
+// n_tail tiles as four 128 x 128 quadrants each: one round of one workgroup
+// per CU (K steps of 64) when the quadrants fit it, else two per CU.
+template <int EPI>
+static hipError_t launch_whole_then_quadrants(const uint16_t* A, int M, int K, const uint16_t* B, int N,
+                                              const uint16_t* bias, void* out, const GemmPlan& p, int n_whole,
+                                              int n_tail, hipStream_t s, const QkvPack& pk = QkvPack{}) {
+  hipError_t e = launch_dl<256, 256, EPI, false, 32>(A, M, K, B, N, bias, out, nullptr, p, n_whole, s, pk);
+  if (e != hipSuccess) return e;
+  const GemmPlan q{128, 128, 1, K};
+  if (4 * n_tail <= 256 && K % 64 == 0)
+    return launch_dl<128, 128, EPI, false, 64>(A, M, K, B, N, bias, out, nullptr, q, 4 * n_tail, s, pk, n_whole);
+  return launch_dl<128, 128, EPI, false, 32>(A, M, K, B, N, bias, out, nullptr, q, 4 * n_tail, s, pk, n_whole);
+}
+
 template <int EPI>
 static hipError_t launch_epi(const uint16_t* A, int M, int K, const uint16_t* B, int N,
                              const uint16_t* bias, void* out, void* ws, hipStream_t s) {
@@ -935,6 +977,8 @@ static hipError_t launch_epi(const uint16_t* A, int M, int K, const uint16_t* B,
                        part, M, N, K / 32, ts, bias, out);
     return hipGetLastError();
   }
+  if (p.bm == 256 && p.tail128 > 0)
+    return launch_whole_then_quadrants<EPI>(A, M, K, B, N, bias, out, p, p.n_whole, p.tail128, s);
   if (p.bm == 256) return launch_tile<256, 256, EPI, false>(A, M, K, B, N, bias, out, nullptr, p, s);
   if (p.bn == 160) return launch_tile<128, 160, EPI, false>(A, M, K, B, N, bias, out, nullptr, p, s);
   if (p.bn == 192) return launch_tile<128, 192, EPI, false>(A, M, K, B, N, bias, out, nullptr, p, s);
@@ -962,8 +1006,13 @@ hipError_t launch_gemm_qkv_pack(const uint16_t* A, int M, int K, const uint16_t*
   auto cdiv = [](long a, long b) { return int((a + b - 1) / b); };
   const GemmPlan p{128, 128, 1, K};
   const int t256 = cdiv(M, 256) * cdiv(N, 256);
-  if (t256 >= 192) return launch_dl<256, 256, kEpiQkvPack, false, 32>(A, M, K, B, N, bias, nullptr, nullptr, p,
-                                                                      t256, s, pk);
+  if (t256 >= 192) {
+    const int n_tail = tail_quadrant_tiles(t256, K);
+    if (n_tail > 0)
+      return launch_whole_then_quadrants<kEpiQkvPack>(A, M, K, B, N, bias, nullptr, p, t256 - n_tail, n_tail, s,
+                                                      pk);
+    return launch_dl<256, 256, kEpiQkvPack, false, 32>(A, M, K, B, N, bias, nullptr, nullptr, p, t256, s, pk);
+  }
   const int t128 = cdiv(M, 128) * cdiv(N, 128);
   if (t128 <= 256 && K % 64 == 0)
     return launch_dl<128, 128, kEpiQkvPack, false, 64>(A, M, K, B, N, bias, nullptr, nullptr, p, t128, s, pk);

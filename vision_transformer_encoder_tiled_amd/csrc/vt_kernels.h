@@ -75,6 +75,10 @@ struct GemmPlan {
   // the rest are shared evenly by sk_wgs workgroups (0: no tail split).
   int n_whole = 0;
   int sk_wgs = 0;
+  // Partial last round without a stream-K tail (256 x 256 tiles only): the
+  // first n_whole tiles run whole and the last tail128 tiles run as four
+  // 128 x 128 quadrants each (0: none).
+  int tail128 = 0;
 };
 // Which tiles a gemm_dl_kernel launch covers: its blocks map to the first npid
 // tiles (XCD-contiguous); with a stream-K tail, the tail kernel's sk_wgs blocks
@@ -83,6 +87,7 @@ struct TileSched {
   int npid;
   int n_whole;
   int sk_wgs;
+  int tail_of = -1;  // >= 0 (128 x 128 launches): the quadrants of 256 x 256 tiles tail_of, tail_of + 1, ...
 };
 GemmPlan plan_gemm(int M, int N, int K);
 size_t gemm_workspace_bytes(int M, int N, int K);
