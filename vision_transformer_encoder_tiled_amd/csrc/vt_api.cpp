@@ -328,6 +328,15 @@ float q_scale_log2(const vt_config* cfg) {
   return float(1.4426950408889634 / std::sqrt(double(cfg->head_dim)));
 }
 
+// The images' token counts on the host when the sizes alone fix them: n_img
+// images of at most max_seqlen tokens that add up to n_img * max_seqlen all
+// have max_seqlen.  Then the attention's split-tail plan is formed on the
+// host too and a call without a split launches no merge.  Else empty.
+std::vector<int64_t> uniform_tokens(int32_t n_img, int64_t total, int32_t max_seqlen) {
+  if (int64_t(n_img) * max_seqlen != total) return {};
+  return std::vector<int64_t>(size_t(n_img), int64_t(max_seqlen));
+}
+
 vt_status run_attention(const vt_config* cfg, const uint16_t* qkv, const int32_t* cu,
                         const int32_t* pos, int32_t n_img, int64_t N, int32_t n_pos,
                         int32_t axis_code, const BlockBufs& b, void* out, bool f32,
@@ -613,13 +622,15 @@ static vt_status attention_pack_into(const vt_config* cfg, const uint16_t* qkv, 
   return VT_OK;
 }
 
-static vt_status attention_on_packed(const vt_config* cfg, int32_t n_img, int32_t total_tokens, const BlockBufs& b,
-                                     void* out, bool f32, hipStream_t s) {
+static vt_status attention_on_packed(const vt_config* cfg, int32_t n_img, int32_t total_tokens, int32_t max_seqlen,
+                                     const BlockBufs& b, void* out, bool f32, hipStream_t s) {
   const int32_t var = attn_variant(total_tokens, n_img, cfg->heads);
+  const std::vector<int64_t> tok = uniform_tokens(n_img, total_tokens, max_seqlen);
   VT_TRY_HIP(vt::launch_attention_packed(b.qpk, b.kv, b.qdesc,
                                          max_q_tiles(total_tokens, n_img, vt::attn_q_tile(var)), cfg->heads,
                                          var, out, f32, nullptr, s,
-                                         vt::AttnTail{b.qkpre, b.tile_start + n_img, b.part}));
+                                         vt::AttnTail{b.qkpre, b.tile_start + n_img, b.part,
+                                                      tok.empty() ? nullptr : tok.data(), n_img}));
   return VT_OK;
 }
 
@@ -641,7 +652,7 @@ VT_API vt_status vt_attention_varlen(const vt_config* cfg, const uint16_t* qkv,
   carve_block(c, dims_of(cfg, total_tokens, n_img), max_seqlen, &b);
   if ((st = attention_pack_into(cfg, qkv, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen, b, s)) != VT_OK)
     return st;
-  return attention_on_packed(cfg, n_img, total_tokens, b, out, out_dtype == VT_FP32, s);
+  return attention_on_packed(cfg, n_img, total_tokens, max_seqlen, b, out, out_dtype == VT_FP32, s);
 }
 
 VT_API vt_status vt_attention_pack(const vt_config* cfg, const uint16_t* qkv, const int32_t* cu_seqlens,
@@ -676,7 +687,8 @@ VT_API vt_status vt_attention_packed(const vt_config* cfg, int32_t n_img, int32_
   Carver c(ws);
   BlockBufs b;
   carve_block(c, dims_of(cfg, total_tokens, n_img), max_seqlen, &b);
-  return attention_on_packed(cfg, n_img, total_tokens, b, out, out_dtype == VT_FP32, static_cast<hipStream_t>(stream));
+  return attention_on_packed(cfg, n_img, total_tokens, max_seqlen, b, out, out_dtype == VT_FP32,
+                             static_cast<hipStream_t>(stream));
 }
 
 // ---- vt_attention_varlen without a workspace argument
@@ -1016,6 +1028,11 @@ VT_API vt_status vt_block_forward(const vt_config* cfg, float* resid, const vt_b
   if ((st = attn_prologue(cfg, cu_seqlens, n_img, total_tokens, max_seqlen, b, &axis_code, s, true)) != VT_OK)
     return st;
   bool xn_ready = false;
+  const std::vector<int64_t> tok = uniform_tokens(n_img, total_tokens, max_seqlen);
+  if (!tok.empty()) {
+    b.host_tokens = tok.data();
+    b.host_n_img = n_img;
+  }
   return run_block(cfg, resid, w, cu_seqlens, pos_thw, n_img, total_tokens, max_seqlen, axis_code, b,
                    nullptr, nullptr, &xn_ready, s);
 }
