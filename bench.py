@@ -261,7 +261,8 @@ def attention_packed_case(vt, torch, grids):
     ws = vt.workspace(vt.vt_block_workspace_size(cfg, N, len(grids), max_seq))
     out = torch.empty((N, 1280), dtype=torch.int16, device="cuda")
     vt.vt_attention_pack(cfg, qkv, cu, pos, len(grids), N, max_seq, ws)
-    return lambda: vt.vt_attention_packed(cfg, len(grids), N, max_seq, out, vt.VT_BF16, ws)
+    lens = [t * h * w for t, h, w in grids]  # known to the caller, as to the tower
+    return lambda: vt.vt_attention_packed(cfg, len(grids), N, max_seq, out, vt.VT_BF16, ws, host_seqlens=lens)
 
 
 def attention_backward_case(vt, torch, grids):
@@ -622,7 +623,7 @@ def main():
                 "ms_per_step": s3 / k3 * 1e3, "steps": k3,
                 "tflops_total": (g3 + at3) / (s3 / k3) / 1e12}
         del run3
-        if name == "tower_448x16":  # a 448x448 workload that fills the chip: its own rooflines
+        if name in ("tower_448x16", "tower_mixed8"):  # workloads that fill the chip: their own rooflines
             it3 = max(3, a.kernel_iters // 2)
             line["attention_roofline"] = attention_roofline(vt, torch, list(wl3.grids), it3)
             line["gemm_roofline"] = gemm_roofline(vt, torch, wl3.tokens, it3)

@@ -232,13 +232,22 @@ vt_status vt_attention_varlen(const vt_config* cfg, const uint16_t* qkv, const i
  *   repeated.  The sizes are validated as for vt_attention_varlen; the
  *   contents of ws are not (they are device data): a workspace not prepared
  *   by vt_attention_pack with the same sizes gives undefined results,
- *   including out-of-bounds device accesses. */
+ *   including out-of-bounds device accesses.
+ *   host_seqlens: optional (NULL), host memory, n_img int32: the images'
+ *   token counts in cu_seqlens order, each in [1, max_seqlen], adding up to
+ *   total_tokens (else VT_ERR_INVALID_ARG).  Given them, the call forms on
+ *   the host the plan that decides whether the last round of workgroups is
+ *   split across key tiles, and launches neither the split's extra
+ *   workgroups nor its merge when nothing is split.  A performance hint
+ *   only: counts that pass these checks but do not match cu_seqlens can cost
+ *   time, never change the result (the device forms its own plan whenever a
+ *   split is launched). */
 vt_status vt_attention_pack(const vt_config* cfg, const uint16_t* qkv, const int32_t* cu_seqlens,
                             const int32_t* pos_thw, int32_t n_img, int32_t total_tokens,
                             int32_t max_seqlen, void* ws, size_t ws_bytes, void* stream);
 vt_status vt_attention_packed(const vt_config* cfg, int32_t n_img, int32_t total_tokens,
-                              int32_t max_seqlen, void* out, vt_dtype out_dtype, void* ws,
-                              size_t ws_bytes, void* stream);
+                              int32_t max_seqlen, const int32_t* host_seqlens, void* out,
+                              vt_dtype out_dtype, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- no allocation
  * For callers that can neither allocate device memory nor pass a workspace:

@@ -132,8 +132,9 @@ def test_attention_validation():
 @needs_no_gpu
 def test_attention_two_part_validation():
     """vt_attention_pack validates as vt_attention_varlen (less out and its
-    dtype); vt_attention_packed validates the sizes, out, dtype and ws (the
-    workspace's contents are device data and are not checked)."""
+    dtype); vt_attention_packed validates the sizes, out, dtype, ws and the
+    optional host-side lengths (the workspace's contents are device data and
+    are not checked)."""
     cfg = vt.config()
     P = lambda v: None if v is None else ctypes.c_void_p(v)
     need = vt.vt_block_workspace_size(cfg, 64, 1, 64)
@@ -142,8 +143,10 @@ def test_attention_two_part_validation():
         return vt.LIB.vt_attention_pack(ctypes.byref(cfg), P(qkv), P(cu), P(FAKE), n_img, total, max_seq,
                                         P(ws), ws_bytes, None)
 
-    def packed(cfg=cfg, n_img=1, total=64, max_seq=64, out=FAKE, dtype=vt.VT_BF16, ws=FAKE, ws_bytes=need):
-        return vt.LIB.vt_attention_packed(ctypes.byref(cfg), n_img, total, max_seq, P(out), dtype, P(ws),
+    def packed(cfg=cfg, n_img=1, total=64, max_seq=64, out=FAKE, dtype=vt.VT_BF16, ws=FAKE, ws_bytes=need,
+               lens=None):
+        hs = None if lens is None else (ctypes.c_int32 * len(lens))(*lens)
+        return vt.LIB.vt_attention_packed(ctypes.byref(cfg), n_img, total, max_seq, hs, P(out), dtype, P(ws),
                                           ws_bytes, None)
 
     assert pack(ws_bytes=need - 1) == vt.VT_ERR_WORKSPACE
@@ -160,6 +163,11 @@ def test_attention_two_part_validation():
     assert packed(n_img=0) == vt.VT_ERR_INVALID_ARG
     assert packed(max_seq=65) == vt.VT_ERR_INVALID_ARG
     assert packed(vt.config(head_dim=64, hidden=1024, rope_pairs=(0, 16, 16))) == vt.VT_ERR_UNSUPPORTED
+    assert packed(lens=[63]) == vt.VT_ERR_INVALID_ARG                 # does not add up to total_tokens
+    assert "add up" in vt.last_error()
+    assert packed(lens=[65]) == vt.VT_ERR_INVALID_ARG                 # beyond max_seqlen
+    assert packed(n_img=2, max_seq=40, lens=[0, 64]) == vt.VT_ERR_INVALID_ARG
+    assert packed(ws_bytes=need - 1, lens=[64]) == vt.VT_ERR_WORKSPACE
 
 
 def _attn_bwd(cfg, qkv=FAKE, dout=FAKE, dqkv=FAKE, n_img=1, total=64, max_seq=64, ws=FAKE,

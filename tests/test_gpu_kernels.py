@@ -476,7 +476,8 @@ def test_attention_pack_then_packed_equals_varlen(vt, grids):
     """vt_attention_pack + vt_attention_packed (the two halves of
     vt_attention_varlen, the second one alone as the tower runs it) give
     vt_attention_varlen's output bit for bit, bf16 and fp32, also when
-    vt_attention_packed is repeated on the same workspace: the two-key-group
+    vt_attention_packed is repeated on the same workspace, with or without
+    the host-side lengths (right or wrong: a hint only): the two-key-group
     kernel (448x448, small mixed items), the lean kernel with a split last
     round (112x112) and without (mixed large grids)."""
     N = sum(t * h * w for t, h, w in grids)
@@ -492,9 +493,11 @@ def test_attention_pack_then_packed_equals_varlen(vt, grids):
         vt.vt_attention_varlen(cfg, qkv, cu, pos, len(grids), N, max_seq, want, dtype, ws)
         ws.zero_()
         vt.vt_attention_pack(cfg, qkv, cu, pos, len(grids), N, max_seq, ws)
-        for rep in range(2):
+        # without, with, and with wrong host-side lengths (a hint: never a change of result)
+        lens = [t * h * w for t, h, w in grids]
+        for rep, hint in enumerate((None, lens, lens[::-1])):
             got = torch.full((N, 1280), 7, dtype=tdt, device="cuda")
-            vt.vt_attention_packed(cfg, len(grids), N, max_seq, got, dtype, ws)
+            vt.vt_attention_packed(cfg, len(grids), N, max_seq, got, dtype, ws, host_seqlens=hint)
             torch.cuda.synchronize()
             assert torch.equal(got.view(torch.int32) if tdt == torch.float32 else got,
                                want.view(torch.int32) if tdt == torch.float32 else want), (dtype, rep)

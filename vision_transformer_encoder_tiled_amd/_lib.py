@@ -98,7 +98,7 @@ def _load():
         "vt_attention_varlen_noalloc": (ctypes.c_int, [cfgp, _P, _P, _P, I32, I32, I32, _P, ctypes.c_int,
                                                        _P]),
         "vt_attention_pack": (ctypes.c_int, [cfgp, _P, _P, _P, I32, I32, I32, _P, SZ, _P]),
-        "vt_attention_packed": (ctypes.c_int, [cfgp, I32, I32, I32, _P, ctypes.c_int, _P, SZ, _P]),
+        "vt_attention_packed": (ctypes.c_int, [cfgp, I32, I32, I32, _P, _P, ctypes.c_int, _P, SZ, _P]),
         "vt_attention_backward": (ctypes.c_int, [cfgp, _P, _P, _P, I32, I32, I32, _P, _P,
                                                  ctypes.c_int, _P, SZ, _P]),
         "vt_attention_backward_workspace_size": (SZ, [cfgp, I32, I32, I32]),
@@ -229,8 +229,12 @@ def vt_attention_pack(cfg, qkv, cu_seqlens, pos_thw, n_img, total_tokens, max_se
                                  _stream(stream)))
 
 
-def vt_attention_packed(cfg, n_img, total_tokens, max_seqlen, out, out_dtype, ws, stream=None):
-    _check(LIB.vt_attention_packed(ctypes.byref(cfg), n_img, total_tokens, max_seqlen, _ptr(out), out_dtype,
+def vt_attention_packed(cfg, n_img, total_tokens, max_seqlen, out, out_dtype, ws, stream=None, host_seqlens=None):
+    """host_seqlens: optional list of the images' token counts (a host-side hint)."""
+    hs = None
+    if host_seqlens is not None:
+        hs = (ctypes.c_int32 * len(host_seqlens))(*[int(v) for v in host_seqlens])
+    _check(LIB.vt_attention_packed(ctypes.byref(cfg), n_img, total_tokens, max_seqlen, hs, _ptr(out), out_dtype,
                                    _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
 
 

@@ -623,9 +623,11 @@ static vt_status attention_pack_into(const vt_config* cfg, const uint16_t* qkv, 
 }
 
 static vt_status attention_on_packed(const vt_config* cfg, int32_t n_img, int32_t total_tokens, int32_t max_seqlen,
-                                     const BlockBufs& b, void* out, bool f32, hipStream_t s) {
+                                     const BlockBufs& b, void* out, bool f32, hipStream_t s,
+                                     const int32_t* host_seqlens = nullptr) {
   const int32_t var = attn_variant(total_tokens, n_img, cfg->heads);
-  const std::vector<int64_t> tok = uniform_tokens(n_img, total_tokens, max_seqlen);
+  std::vector<int64_t> tok = uniform_tokens(n_img, total_tokens, max_seqlen);
+  if (host_seqlens && tok.empty()) tok.assign(host_seqlens, host_seqlens + n_img);
   VT_TRY_HIP(vt::launch_attention_packed(b.qpk, b.kv, b.qdesc,
                                          max_q_tiles(total_tokens, n_img, vt::attn_q_tile(var)), cfg->heads,
                                          var, out, f32, nullptr, s,
@@ -671,7 +673,8 @@ VT_API vt_status vt_attention_pack(const vt_config* cfg, const uint16_t* qkv, co
 }
 
 VT_API vt_status vt_attention_packed(const vt_config* cfg, int32_t n_img, int32_t total_tokens, int32_t max_seqlen,
-                                     void* out, vt_dtype out_dtype, void* ws, size_t ws_bytes, void* stream) {
+                                     const int32_t* host_seqlens, void* out, vt_dtype out_dtype, void* ws,
+                                     size_t ws_bytes, void* stream) {
   vt_status st = check_config(cfg);
   if (st != VT_OK) return st;
   if (n_img <= 0 || total_tokens <= 0 || max_seqlen <= 0)
@@ -682,13 +685,23 @@ VT_API vt_status vt_attention_packed(const vt_config* cfg, int32_t n_img, int32_
     return fail(VT_ERR_UNSUPPORTED, "more than %lld tokens in one call", (long long)kMaxTokens);
   if ((st = check_ptr(out, "out")) != VT_OK) return st;
   if (out_dtype != VT_BF16 && out_dtype != VT_FP32) return fail(VT_ERR_INVALID_ARG, "bad out_dtype");
+  if (host_seqlens) {
+    int64_t sum = 0;
+    for (int32_t i = 0; i < n_img; ++i) {
+      if (host_seqlens[i] < 1 || host_seqlens[i] > max_seqlen)
+        return fail(VT_ERR_INVALID_ARG, "host_seqlens[%d] = %d is outside [1, max_seqlen]", i, host_seqlens[i]);
+      sum += host_seqlens[i];
+    }
+    if (sum != total_tokens)
+      return fail(VT_ERR_INVALID_ARG, "host_seqlens add up to %lld, not total_tokens %d", (long long)sum, total_tokens);
+  }
   const size_t need = block_ws_bytes(cfg, total_tokens, n_img, max_seqlen);
   if ((st = check_ws(ws, ws_bytes, need)) != VT_OK) return st;
   Carver c(ws);
   BlockBufs b;
   carve_block(c, dims_of(cfg, total_tokens, n_img), max_seqlen, &b);
   return attention_on_packed(cfg, n_img, total_tokens, max_seqlen, b, out, out_dtype == VT_FP32,
-                             static_cast<hipStream_t>(stream));
+                             static_cast<hipStream_t>(stream), host_seqlens);
 }
 
 // ---- vt_attention_varlen without a workspace argument
