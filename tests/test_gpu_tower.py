@@ -404,13 +404,18 @@ def test_tower_tiny_items(vt, weights, dev):
 @pytest.mark.parametrize("grids,seeds", [
     ([(1, 2, 2), (1, 2, 4), (1, 6, 10), (2, 4, 4), (1, 2, 2)], [81, 82, 83, 84, 85]),
     ([(1, 16, 16)], [86]),
+    ([(1, 112, 112)] * 2, [87, 88]),
 ])
 def test_tower_fused_equals_blockwise_small(vt, weights, dev, grids, seeds):
     """At 108 and 256 tokens the residual GEMMs run split-K (3 splits for O,
     12 or 13 for FC2, the latter summed by the any-count loop of the fused
     reduce + LayerNorm).  The tower entry point, which fuses each reduction
     with the next LayerNorm, gives the same tower output bits as patch embed
-    followed by the blocks one call at a time, whose LayerNorms run alone."""
+    followed by the blocks one call at a time, whose LayerNorms run alone.
+    At 2 x 112x112 (25,088 tokens) the attention's last round is split across
+    key tiles and the large GEMMs have whole-tile rounds and tails: the
+    tower (which plans the split from its grid list) and vt_block_forward
+    (from its sizes, two images of max_seqlen tokens) cut the same way."""
     px = item_pixels(grids, seeds)
     L = 3
     N = sum(t * h * w for t, h, w in grids)
