@@ -38,6 +38,31 @@ def test_library_exports_every_declared_function():
     assert vt.vt_version().startswith("vt ")
 
 
+def header_signatures():
+    """{name: (return type, parameter count)} of every declaration in vt.h."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for ret, name, params in re.findall(
+            r"\b(vt_status|size_t|void|const char\*|int32_t|int)\s+(vt_[a-z_0-9]+)\s*\(([^;]*?)\)\s*;", src, flags=re.S):
+        p = params.strip()
+        out[name] = (ret, 0 if p in ("", "void") else p.count(",") + 1)
+    return out
+
+
+def test_binding_signatures_match_the_header():
+    """Every ctypes prototype of the binding has the parameter count and
+    return type the header declares (a binding that passed one argument too
+    few or too many would shift every argument after it)."""
+    sigs = header_signatures()
+    assert sorted(sigs) == header_functions()
+    ret_types = {"vt_status": ctypes.c_int, "size_t": ctypes.c_size_t, "const char*": ctypes.c_char_p,
+                 "void": None, "int32_t": ctypes.c_int32, "int": ctypes.c_int}
+    for name, (ret, n) in sigs.items():
+        fn = getattr(vt.LIB, name)
+        assert fn.argtypes is not None and len(fn.argtypes) == n, (name, n, fn.argtypes)
+        assert fn.restype == ret_types[ret], (name, ret, fn.restype)
+
+
 def test_default_config_is_the_minimax_m3_shape():
     c = vt.vt_config_default()
     assert (c.layers, c.hidden, c.heads, c.head_dim, c.mlp) == (32, 1280, 16, 80, 5120)
