@@ -208,7 +208,9 @@ def test_linear_shapes(vt, M, N, K, what):
 @pytest.mark.parametrize("M,N,K", [(200, 512, 320), (1024, 1280, 5120), (1000, 5120, 1280),
                                    (968, 6144, 640), (200, 6144, 6144),
                                    (4608, 4096, 2048),   # stream-K tail: 32 of 288 tiles in eighths
-                                   (2200, 7680, 320)])   # quadrant tail: 14 of 270 tiles, ragged M
+                                   (2200, 7680, 320),    # quadrant tail: 14 of 270 tiles, ragged M
+                                   (4096, 4096, 64),     # 256 x 256, one K step of 64
+                                   (4000, 3328, 192)])   # 256 x 256, three K steps, ragged M
 def test_linear_epilogues(vt, epi, M, N, K):
     log(f"linear epilogue {epi} {M}x{N}x{K}")
     x = random_bf16((M, K), 7)

@@ -336,7 +336,7 @@ __device__ __forceinline__ void qkv_pack_store(const char* cs, const QkvPack& pk
 // epilogue.  (plan_gemm cuts only where every range is one aligned piece, so
 // records S.. are not used and the workspace holds S.)
 template <int BM, int BN, int GWM, int GWN, int NST, int EPI, bool SPLIT, int BK = 32, int CW = 0,
-          bool SK = false>
+          bool SK = false, bool SR = false>
 __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
     const uint16_t* __restrict__ A, int M, int K, const uint16_t* __restrict__ B, int N,
     const uint16_t* __restrict__ bias, void* __restrict__ out, float* __restrict__ part, int kper,
@@ -358,9 +358,16 @@ __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
   constexpr int GA = BM / RPG, G = (BM + BN) / RPG;
   constexpr int CP_HI = (G + NWC - 1) / NWC, CP_LO = G / NWC;
   constexpr int A_BYTES = BM * RB, STAGE = dl_stage_bytes(BM, BN, BK);
+  // SR (split ring, K steps of 64): the A and B parts of a step have slots of
+  // their own, 2 for A and 3 for B; step s's A lives in slot s mod 2 and its
+  // B in slot s mod 3, so B (the weights, which may come from HBM) is copied
+  // two steps ahead and A (activations, usually in L2) one step ahead.
+  constexpr int B_BYTES = BN * RB, RING = SR ? 2 * A_BYTES + 3 * B_BYTES : NST * STAGE;
+  constexpr int CPA = GA / NWC, CPB = (G - GA) / NWC;  // SR: A and B copies per wavefront per step
+  static_assert(!SR || (BK == 64 && CW == 0 && !SK && GA % NWC == 0 && (G - GA) % NWC == 0), "split ring");
   static_assert(WM % 32 == 0 && WN % 32 == 0 && BM % 16 == 0 && BN % 16 == 0, "tiling");
-  static_assert(NST * STAGE <= 160 * 1024, "LDS");
-  static_assert(NST >= 3, "ring depth");
+  static_assert(RING <= 160 * 1024, "LDS");
+  static_assert(SR || NST >= 3, "ring depth");
   extern __shared__ __align__(16) uint16_t lds[];
   const char* smem = reinterpret_cast<const char*>(lds);
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
@@ -442,6 +449,17 @@ __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
     if constexpr (CP_HI > CP_LO)
       if (hi) dma16(src[CP_LO] + it * BK, sa + 1024 * NWC * CP_LO);
   };
+  // Split ring: copy j < CPA of every wavefront is an A group, the rest B.
+  auto issue_a = [&](int it) {
+    const uint32_t sa = __builtin_amdgcn_readfirstlane(lds0 + (it % 2) * A_BYTES);
+#pragma unroll
+    for (int j = 0; j < CPA; ++j) dma16(src[j] + it * BK, sa + 1024 * NWC * j);
+  };
+  auto issue_b = [&](int it) {
+    const uint32_t sb = __builtin_amdgcn_readfirstlane(lds0 + 2 * A_BYTES + (it % 3) * B_BYTES - 1024 * GA);
+#pragma unroll
+    for (int j = CPA; j < CPA + CPB; ++j) dma16(src[j] + it * BK, sb + 1024 * NWC * j);
+  };
   // vmcnt <= the copies of the newest `steps` issued steps.
   auto wait_steps = [&](auto steps) {
     constexpr int n = decltype(steps)::value;
@@ -495,8 +513,8 @@ __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
   };
   auto load_frags = [&](Frags& F, int step, int u) {
     const char* st = smem + (step % NST) * STAGE;
-    const char* a_base = st + (wm * WM + fr) * RB;
-    const char* b_base = st + A_BYTES + (wn * WN + fr) * RB;
+    const char* a_base = (SR ? smem + (step % 2) * A_BYTES : st) + (wm * WM + fr) * RB;
+    const char* b_base = (SR ? smem + 2 * A_BYTES + (step % 3) * B_BYTES : st + A_BYTES) + (wn * WN + fr) * RB;
     const int choff0 = 16 * ((4 * u + h) ^ sw), choff1 = 16 * ((4 * u + 2 + h) ^ sw);
 #pragma unroll
     for (int f = 0; f < FB; ++f) F.w0[f] = *reinterpret_cast<const bf16x8_t*>(b_base + f * 32 * RB + choff0);
@@ -529,7 +547,38 @@ __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * FB * TB - 2 * (FB + TB), 0);
   };
 
-  if constexpr (BK == 32) {
+  if constexpr (SR) {
+    // As the BK = 64 ring below, with A_{it+1} and B_{it+2} issued at the
+    // start of step it (A first), into the slots of A_{it-1} and B_{it-1},
+    // whose reads were done at step it-1's barrier.  At step it's barrier
+    // everything but B_{it+2} must have landed: vmcnt <= CPB.
+    issue_a(0);
+    issue_b(0);
+    if (1 < nk) issue_b(1);
+    if (nk > 0) {
+      if (1 < nk) wait_vmcnt<CPB>();  // step 0 landed
+      else wait_vmcnt<0>();
+      wg_barrier();
+      Frags F0, F1;
+      load_frags(F0, 0, 0);
+      for (int it = 0; it < nk; ++it) {
+        if (it + 1 < nk) issue_a(it + 1);
+        if (it + 2 < nk) issue_b(it + 2);
+        load_frags(F1, it, 1);
+        mma(F0);
+        interleave();
+        if (it + 2 < nk) wait_vmcnt<CPB>();
+        else wait_vmcnt<0>();
+        wait_lds_reads();
+        wg_barrier();
+        load_frags(F0, it + 1, 0);  // on the last step a stale, never used slot
+        mma(F1);
+        interleave();
+      }
+      wait_lds_reads();
+      wg_barrier();
+    }
+  } else if constexpr (BK == 32) {
     using InFlight = std::integral_constant<int, NST - 3>;
     // One K step: copies for step it+NST-1 go out, step it+1's fragments are
     // read while step it's are multiplied; then step it+2's copies must have
@@ -617,7 +666,6 @@ __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
   // and, at its barrier, for every wave's fragment reads.
   constexpr int ESZ = F32OUT ? 4 : 2;
   constexpr int ROWB = BN * ESZ, CHUNKS = ROWB / 16, EPC = 16 / ESZ;
-  constexpr int RING = NST * STAGE;
   constexpr int PASS_ROWS = pass_rows(BM, ROWB, RING);
   static_assert(CHUNKS >= 16 && PASS_ROWS % WM == 0 && BM % PASS_ROWS == 0, "epilogue staging");
   char* cs = reinterpret_cast<char*>(lds);
@@ -887,8 +935,10 @@ static hipError_t launch_dl(const uint16_t* A, int M, int K, const uint16_t* B, 
   constexpr int GWM = (BM == 256) ? 2 : 4, GWN = (BM == 256) ? 4 : (BN == 128 ? 2 : 1);
   constexpr int CW = (BK == 64 && GWM * GWN == 4) ? 4 : 0;
   constexpr int NST = BK == 64 ? 3 : 4;
-  const size_t lds = size_t(NST) * dl_stage_bytes(BM, BN, BK);
-  auto kern = gemm_dl_kernel<BM, BN, GWM, GWN, NST, EPI, SPLIT, BK, CW, SK>;
+  // 256 x 256 with K steps of 64: the split ring (2 A + 3 B slots, 160 KB).
+  constexpr bool SR = BM == 256 && BN == 256 && BK == 64;
+  const size_t lds = SR ? size_t(2 * BM + 3 * BN) * 2 * BK : size_t(NST) * dl_stage_bytes(BM, BN, BK);
+  auto kern = gemm_dl_kernel<BM, BN, GWM, GWN, NST, EPI, SPLIT, BK, CW, SK, SR>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (attr != hipSuccess) return attr;
@@ -912,12 +962,13 @@ static hipError_t launch_tile(const uint16_t* A, int M, int K, const uint16_t* B
   } else {
     // 128 x 128 in one round of workgroups: K steps of 64 (96 KB of LDS, one
     // workgroup per CU).  More rounds: K steps of 32 (64 KB, two per CU).
-    // 256 x 256 keeps K steps of 32: with 64 only a 2-stage ring fits, whose
-    // single step of slack does not cover weights read from HBM inside the
-    // tower (measured slower there, though faster with cache-hot operands).
+    // 256 x 256: K steps of 64 through the split ring (whole 128-byte lines
+    // per copy, the weights two steps ahead).
     if constexpr (BM == 128)
       if (tiles * (SPLIT ? p.splits : 1) <= 256 && k_step_ok(64))
         return launch_dl<BM, BN, EPI, SPLIT, 64>(A, M, K, B, N, bias, out, part, p, tiles, s);
+    if constexpr (BM == 256)
+      if (k_step_ok(64)) return launch_dl<BM, BN, EPI, SPLIT, 64>(A, M, K, B, N, bias, out, part, p, tiles, s);
     if (k_step_ok(32))
       return launch_dl<BM, BN, EPI, SPLIT, 32>(A, M, K, B, N, bias, out, part, p, tiles, s);
     const size_t lds = size_t(2) * (BM + BN) * kLdsRow * sizeof(uint16_t);
@@ -932,6 +983,16 @@ static hipError_t launch_tile(const uint16_t* A, int M, int K, const uint16_t* B
   }
 }
 
+// The first `tiles` 256 x 256 tiles, no split: K steps of 64 (split ring)
+// when K allows, else 32.
+template <int EPI>
+static hipError_t launch_whole256(const uint16_t* A, int M, int K, const uint16_t* B, int N, const uint16_t* bias,
+                                  void* out, const GemmPlan& p, int tiles, hipStream_t s,
+                                  const QkvPack& pk = QkvPack{}) {
+  if (K % 64 == 0) return launch_dl<256, 256, EPI, false, 64>(A, M, K, B, N, bias, out, nullptr, p, tiles, s, pk);
+  return launch_dl<256, 256, EPI, false, 32>(A, M, K, B, N, bias, out, nullptr, p, tiles, s, pk);
+}
+
 // The first n_whole tiles of a 256 x 256 tiling whole, then its last
 // n_tail tiles as four 128 x 128 quadrants each: one round of one workgroup
 // per CU (K steps of 64) when the quadrants fit it, else two per CU.
@@ -939,7 +1000,7 @@ template <int EPI>
 static hipError_t launch_whole_then_quadrants(const uint16_t* A, int M, int K, const uint16_t* B, int N,
                                               const uint16_t* bias, void* out, const GemmPlan& p, int n_whole,
                                               int n_tail, hipStream_t s, const QkvPack& pk = QkvPack{}) {
-  hipError_t e = launch_dl<256, 256, EPI, false, 32>(A, M, K, B, N, bias, out, nullptr, p, n_whole, s, pk);
+  hipError_t e = launch_whole256<EPI>(A, M, K, B, N, bias, out, p, n_whole, s, pk);
   if (e != hipSuccess) return e;
   const GemmPlan q{128, 128, 1, K};
   if (4 * n_tail <= 256 && K % 64 == 0)
@@ -967,7 +1028,7 @@ static hipError_t launch_epi(const uint16_t* A, int M, int K, const uint16_t* B,
     // whole rounds, then the tail's K steps over sk_wgs workgroups, then the
     // tail tiles' sums and epilogue
     float* part = reinterpret_cast<float*>(ws);
-    hipError_t e = launch_dl<256, 256, EPI, false, 32>(A, M, K, B, N, bias, out, nullptr, p, p.n_whole, s);
+    hipError_t e = launch_whole256<EPI>(A, M, K, B, N, bias, out, p, p.n_whole, s);
     if (e != hipSuccess) return e;
     e = launch_dl<256, 256, kEpiF32, true, 32, true>(A, M, K, B, N, nullptr, nullptr, part, p, p.sk_wgs, s);
     if (e != hipSuccess) return e;
@@ -1011,7 +1072,7 @@ hipError_t launch_gemm_qkv_pack(const uint16_t* A, int M, int K, const uint16_t*
     if (n_tail > 0)
       return launch_whole_then_quadrants<kEpiQkvPack>(A, M, K, B, N, bias, nullptr, p, t256 - n_tail, n_tail, s,
                                                       pk);
-    return launch_dl<256, 256, kEpiQkvPack, false, 32>(A, M, K, B, N, bias, nullptr, nullptr, p, t256, s, pk);
+    return launch_whole256<kEpiQkvPack>(A, M, K, B, N, bias, nullptr, p, t256, s, pk);
   }
   const int t128 = cdiv(M, 128) * cdiv(N, 128);
   if (t128 <= 256 && K % 64 == 0)
