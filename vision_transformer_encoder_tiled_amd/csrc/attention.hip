@@ -227,15 +227,22 @@ hipError_t launch_attn_image_init(const int2* kdesc, int32_t max_ktiles, int32_t
 // image (tile r*KG + g in round r).  With KG = 2 a workgroup holds 64
 // queries, so small images give twice as many workgroups; the groups'
 // partial (max, O, l) are merged through LDS at the end.
-template <int NW, int KG, int NST>
-__global__ void __launch_bounds__(64 * NW) attention_kernel(
+//
+// CW > 0: CW more wavefronts that only copy the tile images (a wavefront
+// that issues copies stalls for ~100 cycles per 1 KB copy instruction, and
+// with one multiplying wavefront per SIMD nothing else runs meanwhile).  They
+// wait for their copies and meet every workgroup barrier of the others, in
+// the same order, then leave; the multiplying wavefronts issue no copies.
+template <int NW, int KG, int NST, int CW = 0>
+__global__ void __launch_bounds__(64 * (NW + CW)) attention_kernel(
     const uint16_t* __restrict__ qpk, const uint16_t* __restrict__ kv,
     const int4* __restrict__ qdesc, int32_t heads, void* __restrict__ out, int32_t out_f32,
     float* __restrict__ lse) {
   static_assert(NST == 3 || (NST == 4 && KG == 1), "stage ring");
   constexpr int QW = NW / KG;             // query wavefronts per group
-  constexpr int COPIES = IMG_BYTES / (1024 * NW);  // 1 KB DMA pieces per wave per tile
-  static_assert(COPIES * NW * 1024 == IMG_BYTES, "tile image must be whole rounds of copies");
+  constexpr int NCW = CW > 0 ? CW : NW;   // wavefronts that copy
+  constexpr int COPIES = IMG_BYTES / (1024 * NCW);  // 1 KB DMA pieces per copying wave per tile
+  static_assert(COPIES * NCW * 1024 == IMG_BYTES, "tile image must be whole rounds of copies");
   constexpr int WQ = 32 * QW;             // queries per workgroup
   constexpr int STAGE = KG * STAGE_BYTES; // one round: KG tiles
   extern __shared__ __align__(16) char lds[];
@@ -254,10 +261,11 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = wave / QW, qw = wave % QW;
   const int hf = lane >> 5, ln = lane & 31;
-  const uint32_t lds_wave = lds_offset(lds) + 1024 * wave;
+  const int cwave = CW > 0 ? wave - NW : wave;  // index among the copying wavefronts
+  const uint32_t lds_wave = lds_offset(lds) + 1024 * cwave;
 
   // Round r -> stage r % 3: tile r*KG + j at offset j * STAGE_BYTES; each
-  // wavefront copies COPIES 1 KB pieces of every tile that exists.
+  // copying wavefront copies COPIES 1 KB pieces of every tile that exists.
   auto issue = [&](int r) {
 #pragma unroll
     for (int j = 0; j < KG; ++j) {
@@ -265,12 +273,38 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(
       if (t < ntiles) {
         const uint32_t base =
             __builtin_amdgcn_readfirstlane(lds_wave + (r % NST) * STAGE + j * STAGE_BYTES);
-        const char* g = src + t * tile_stride + 1024 * wave + 16 * lane;
+        const char* g = src + t * tile_stride + 1024 * cwave + 16 * lane;
 #pragma unroll
-        for (int c = 0; c < COPIES; ++c) dma16(g + NW * 1024 * c, base + NW * 1024 * c);
+        for (int c = 0; c < COPIES; ++c) dma16(g + NCW * 1024 * c, base + NCW * 1024 * c);
       }
     }
   };
+
+  if constexpr (CW > 0) {
+    if (wave >= NW) {
+      // The copy-only wavefronts: the first NST - 1 rounds, the barrier after
+      // them, then per round the barrier of body() (everything issued so far,
+      // i.e. rounds <= r + 1, has landed) followed by the copy of round
+      // r + NST - 1 into the stage round r - 1 used; with KG = 2 the two
+      // barriers of the group merge.  The ring is idle once they leave.
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int r = 0; r < NST - 1; ++r)
+        if (r < rounds) issue(r);
+      wait_vmcnt<0>();
+      wg_barrier();
+      for (int r = 0; r < rounds; ++r) {
+        wait_vmcnt<0>();
+        wg_barrier();
+        if (r + NST - 1 < rounds) issue(r + NST - 1);
+      }
+      if constexpr (KG == 2) {
+        wg_barrier();
+        __syncthreads();
+      }
+      return;
+    }
+  }
 
   // Q fragments (B operand of S^T = K Q^T): dims 16s + 8hf .. +7 of this lane's query.
   const int qrow = q0 + qw * 32 + ln;
@@ -338,9 +372,11 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(
     return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
   };
 
+  if constexpr (CW == 0) {
 #pragma unroll
-  for (int r = 0; r < NST - 1; ++r)
-    if (r < rounds) issue(r);
+    for (int r = 0; r < NST - 1; ++r)
+      if (r < rounds) issue(r);
+  }
   wait_vmcnt<0>();
   wg_barrier();
 
@@ -374,7 +410,8 @@ __global__ void __launch_bounds__(64 * NW) attention_kernel(
     else wait_vmcnt<0>();
     wait_lds_reads();
     wg_barrier();
-    if (r + NST - 1 < rounds) issue(r + NST - 1);  // into the stage round r-1 used
+    if constexpr (CW == 0)
+      if (r + NST - 1 < rounds) issue(r + NST - 1);  // into the stage round r-1 used
     const int tc = r * KG + grp, tn = tc + KG;
     if (tn < ntiles) load_k(r + 1);
     if (tc >= ntiles) return;
@@ -847,17 +884,17 @@ __global__ void __launch_bounds__(kMergeThreads) attn_tail_merge_kernel(
   }
 }
 
-template <int NW, int KG, int NST>
+template <int NW, int KG, int NST, int CW>
 static hipError_t launch_attention_kernel(const uint16_t* qpk, const uint16_t* kv,
                                           const int4* qdesc, int32_t max_qtiles, int32_t heads,
                                           void* out, bool out_f32, float* lse, hipStream_t s) {
   const size_t lds = size_t(NST) * KG * STAGE_BYTES;
-  auto kern = attention_kernel<NW, KG, NST>;
+  auto kern = attention_kernel<NW, KG, NST, CW>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (attr != hipSuccess) return attr;
   const int64_t blocks = int64_t(max_qtiles) * heads;
-  hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(64 * NW), lds, s, qpk, kv, qdesc, heads,
+  hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(64 * (NW + CW)), lds, s, qpk, kv, qdesc, heads,
                      out, out_f32 ? 1 : 0, lse);
   return hipGetLastError();
 }
@@ -947,7 +984,7 @@ hipError_t launch_attention_packed(const uint16_t* qpk, const uint16_t* kv, cons
                                    bool out_f32, float* lse, hipStream_t s, const AttnTail& tail) {
   switch (variant) {
     case kAttnSmall:
-      return launch_attention_kernel<4, 2, 3>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, lse, s);
+      return launch_attention_kernel<4, 2, 3, 4>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, lse, s);
     case kAttnLean4:
       return launch_lean<4, 3, kAttnLean4>(qpk, kv, qdesc, max_qtiles, heads, out, out_f32, lse, s, tail);
     case kAttnLean8:
