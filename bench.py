@@ -9,7 +9,9 @@ of synthetic input that is already resident in device memory.
     python bench.py --kernel {fc1,resid_gemm,attention,attention_bwd,block_bwd,copy} [--workload ...]   # one case
 
 Prints one JSON line.  Beside the headline workload it times, with HIP events
-on the stream the kernels run on:
+on the stream the kernels run on (the kernel rooflines: a loop of launches
+captured into one HIP graph and replayed, so that no host time between
+launches enters a kernel's average duration):
   roofline           the dominant kernel of the headline workload at 1,024
                      tokens: the split-K partial GEMM of the O and FC2
                      residual Linears (vt_linear with the partials epilogue,
@@ -17,7 +19,9 @@ on the stream the kernels run on:
                      their fused split-K reduce + LayerNorm
                      (vt_linear_residual_ln);
   fc1_roofline       the FC1 GEMM (bias + GELU epilogue);
-  attention_roofline one vt_attention_varlen call;
+  attention_roofline the attention kernels as the tower runs them
+                     (vt_attention_packed), beside one whole
+                     vt_attention_varlen call;
 one vt_attention_backward and one vt_block_backward call, the 2016x2016
 single image as a secondary workload, and further workloads (224x224 one
 block, clips, 16 x 448x448 with its own attention and GEMM rooflines, mixed
@@ -128,6 +132,37 @@ def time_kernel(torch, fn, iters):
         fn()
     e.record()
     torch.cuda.synchronize()
+    return s.elapsed_time(e) / 1e3 / iters
+
+
+def time_graph(torch, fn, iters):
+    """Average duration of one launch sequence of ``fn``: ``iters`` calls
+    captured into one HIP graph (the library only enqueues kernels on the
+    caller's stream, so its calls capture), the graph replayed once untimed
+    and once between HIP events on the current stream.  Unlike the eager
+    loop of time_kernel, no host time between launches can leave the GPU
+    idle, which matters for kernels of ~10 us against ~8 us of host time per
+    call from Python."""
+    fn()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(iters):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    del g
     return s.elapsed_time(e) / 1e3 / iters
 
 
@@ -378,8 +413,8 @@ def residual_gemm_roofline(vt, torch, M, iters):
     split-K reduce, residual update and LayerNorm."""
     cases = residual_cases(vt, torch, M)
     flops = sum(c[2] for c in cases)
-    t_gemm = [time_kernel(torch, c[0], iters) for c in cases]
-    t_step = [time_kernel(torch, c[1], iters) for c in cases]
+    t_gemm = [time_graph(torch, c[0], iters) for c in cases]
+    t_step = [time_graph(torch, c[1], iters) for c in cases]
     both = lambda: (cases[0][0](), cases[1][0]())
     ghz = clock_under(vt, torch, both, iters, sum(t_gemm))
     ach = flops / sum(t_gemm) / 1e12
@@ -402,7 +437,7 @@ def residual_gemm_roofline(vt, torch, M, iters):
 
 def gemm_roofline(vt, torch, M, iters):
     fn, flops = fc1_case(vt, torch, M)
-    t = time_kernel(torch, fn, iters)
+    t = time_graph(torch, fn, iters)
     ghz = clock_under(vt, torch, fn, iters, t)
     return {"kernel": "gemm_dl_kernel (FC1: %d x 5120 x 1280, bias+GELU epilogue)" % M,
             "bound": "mfma", "achieved": flops / t / 1e12, "peak": PEAK_BF16_TFLOPS,
@@ -420,9 +455,9 @@ def attention_roofline(vt, torch, grids, iters, traffic_profile=None):
     in the QKV Linear's epilogue and once per call)."""
     fn = attention_packed_case(vt, torch, grids)
     call, flops = attention_case(vt, torch, grids)
-    t = time_kernel(torch, fn, iters)
+    t = time_graph(torch, fn, iters)
     ghz = clock_under(vt, torch, fn, iters, t)
-    tc = time_kernel(torch, call, iters)
+    tc = time_graph(torch, call, iters)
     N = sum(t_ * h * w for t_, h, w in grids)
     traffic = (profile_traffic(traffic_profile, "vision_transformer_encoder_tiled_amd/csrc/attention.hip")
                if traffic_profile else None)
@@ -449,7 +484,7 @@ def layernorm_roofline(vt, torch, rows, iters):
     bet = torch.zeros(1280, dtype=torch.int16, device="cuda")
     out = torch.empty((rows, 1280), dtype=torch.int16, device="cuda")
     fn = lambda: vt.vt_layer_norm(x, rows, 1280, gam, bet, 1e-6, out)
-    t = time_kernel(torch, fn, iters)
+    t = time_graph(torch, fn, iters)
     gbs = rows * 7680 / t / 1e9
     return {"kernel": "layer_norm_kernel (%d x 1280, fp32 in, bf16 out)" % rows, "bound": "hbm",
             "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
