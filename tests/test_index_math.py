@@ -160,6 +160,44 @@ def test_gemm_epilogue_staging_is_a_bijection(BM, BN, GWM, GWN, NST, BK, CW, f32
     assert len(done) == BM * BN
 
 
+@pytest.mark.parametrize("BM,BN,NW,CW,CO,BK", [
+    (128, 160, 4, 4, True, 64), (128, 192, 4, 4, True, 64), (128, 128, 8, 0, False, 64),
+    (128, 128, 8, 0, False, 32), (256, 256, 8, 0, False, 32)])
+def test_gemm_copy_groups_fill_each_stage_once(BM, BN, NW, CW, CO, BK):
+    """gemm.hip gemm_dl_kernel copy assignment: a K step is G = (BM + BN) / RPG
+    groups of RPG rows (1 KB, one copy instruction); copying wavefront cw
+    (with CO only the CW copy-only wavefronts, cw = wave - NW; else every
+    wavefront, cw = wave) copies groups cw + NCP j for j < CP_LO, and one more
+    (j = CP_LO) when cw < G % NCP, into LDS bytes 1024 cw + 1024 NCP j of the
+    stage.  Every group lands once, at 1024 g, and each of its lanes fetches
+    the row and chunk whose LDS bytes it writes (A rows first, then B rows)."""
+    NWC = NW + CW
+    NCP = CW if CO else NWC
+    RB = 2 * BK
+    CH, RPG = RB // 16, 1024 // RB
+    GA, G = BM // RPG, (BM + BN) // RPG
+    CP_HI, CP_LO = -(-G // NCP), G // NCP
+    seen = {}
+    for wave in range(NWC):
+        mw = CW == 0 or wave < NW
+        if CO and mw:
+            continue                                  # issue() returns at once
+        cw = max(wave - NW, 0) if CO else wave
+        hi = cw < G % NCP
+        for j in range(CP_HI):
+            if j == CP_LO and not (CP_HI > CP_LO and hi):
+                continue
+            g = min(cw + NCP * j, G - 1)
+            dst = 1024 * cw + 1024 * NCP * j
+            assert dst == 1024 * g and g not in seen
+            seen[g] = wave
+            for lane in range(64):
+                row = RPG * g + lane // CH            # stage row: A rows, then B rows
+                assert (row < BM) == (g < GA)
+                assert dst + 16 * lane == RB * row + 16 * (lane % CH)  # row r at byte RB r
+    assert sorted(seen) == list(range(G))
+
+
 # ---------------------------------------------------------------- lean attention split tail
 def tail_pieces(n_items_keys, heads, S, min_tiles=8):
     """attention.hip tail_plan, the piece walk of attention_lean_kernel and

@@ -336,35 +336,40 @@ __device__ __forceinline__ void qkv_pack_store(const char* cs, const QkvPack& pk
 // epilogue.  (plan_gemm cuts only where every range is one aligned piece, so
 // records S.. are not used and the workspace holds S.)
 template <int BM, int BN, int GWM, int GWN, int NST, int EPI, bool SPLIT, int BK = 32, int CW = 0,
-          bool SK = false, bool SR = false>
+          bool SK = false, bool SR = false, bool CO = false>
 __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
     const uint16_t* __restrict__ A, int M, int K, const uint16_t* __restrict__ B, int N,
     const uint16_t* __restrict__ bias, void* __restrict__ out, float* __restrict__ part, int kper,
     QkvPack pk, TileSched ts) {
   static_assert(!SK || (SPLIT && BK == 32 && CW == 0), "the stream-K tail writes partial sums");
   constexpr int NW = GWM * GWN;  // wavefronts that multiply
-  constexpr int NWC = NW + CW;   // wavefronts that copy: all of them
+  constexpr int NWC = NW + CW;   // all wavefronts (they all store the finished tile)
+  // CO: only the CW copy-only wavefronts issue the K loop's copies.  A
+  // wavefront stalls ~100 cycles per 1 KB copy instruction it issues; with one
+  // multiplying wavefront per SIMD, stalls of its own leave the matrix unit idle.
+  constexpr int NCP = CO ? CW : NWC;  // wavefronts that issue copies
+  static_assert(!CO || (CW > 0 && !SK && !SR), "copy-only issue");
   constexpr int WM = BM / GWM, WN = BN / GWN;
   constexpr int TB = WM / 32, FB = WN / 32;
   static_assert(BK == 32 || BK == 64, "K step");
   static_assert(CW == 0 || BK == 64, "copy-only wavefronts with K steps of 64 only");
   constexpr int RB = 2 * BK, CH = RB / 16, RPG = 1024 / RB;  // row bytes, chunks per row, rows per copy
   // Copy groups of one K step (RPG rows, 1 KB, one copy instruction): BM/RPG
-  // of A, then BN/RPG of B; group g is copied by wavefront g % NWC, so the
-  // first G % NWC wavefronts copy one group more (CP_HI against CP_LO) when G
-  // is not a multiple of NWC.  A wavefront issues copies at a limited rate
+  // of A, then BN/RPG of B; group g is copied by copying wavefront g % NCP, so
+  // the first G % NCP of them copy one group more (CP_HI against CP_LO) when G
+  // is not a multiple of NCP.  A wavefront issues copies at a limited rate
   // (~21 GB/s each, up to ~140 GB/s per CU from 8 wavefronts), so tiles with
   // 4 multiplying wavefronts add CW = 4 that only copy.
   constexpr int GA = BM / RPG, G = (BM + BN) / RPG;
-  constexpr int CP_HI = (G + NWC - 1) / NWC, CP_LO = G / NWC;
+  constexpr int CP_HI = (G + NCP - 1) / NCP, CP_LO = G / NCP;
   constexpr int A_BYTES = BM * RB, STAGE = dl_stage_bytes(BM, BN, BK);
   // SR (split ring, K steps of 64): the A and B parts of a step have slots of
   // their own, 2 for A and 3 for B; step s's A lives in slot s mod 2 and its
   // B in slot s mod 3, so B (the weights, which may come from HBM) is copied
   // two steps ahead and A (activations, usually in L2) one step ahead.
   constexpr int B_BYTES = BN * RB, RING = SR ? 2 * A_BYTES + 3 * B_BYTES : NST * STAGE;
-  constexpr int CPA = GA / NWC, CPB = (G - GA) / NWC;  // SR: A and B copies per wavefront per step
-  static_assert(!SR || (BK == 64 && CW == 0 && !SK && GA % NWC == 0 && (G - GA) % NWC == 0), "split ring");
+  constexpr int CPA = GA / NCP, CPB = (G - GA) / NCP;  // SR: A and B copies per wavefront per step
+  static_assert(!SR || (BK == 64 && CW == 0 && !SK && GA % NCP == 0 && (G - GA) % NCP == 0), "split ring");
   static_assert(WM % 32 == 0 && WN % 32 == 0 && BM % 16 == 0 && BN % 16 == 0, "tiling");
   static_assert(RING <= 160 * 1024, "LDS");
   static_assert(SR || NST >= 3, "ring depth");
@@ -423,42 +428,45 @@ __global__ void __launch_bounds__(64 * (GWM * GWN + CW)) gemm_dl_kernel(
   const int m0 = tm * BM, n0 = tn * BN;
   const int nk = (kend - kbeg) / BK;
 
-  // Copy j of this lane: group g = wave + NWC j, i.e. row RPG g + lane / CH of
+  // Copy j of this lane: group g = cw + NCP j (cw: the wavefront's index among
+  // the copying ones), i.e. row RPG g + lane / CH of
   // the stage (an A row while g < GA, else B row RPG (g - GA) + lane / CH),
   // logical chunk (lane % CH) ^ swz(row), landing in physical chunk lane % CH
   // of LDS bytes 1024 g + RB (lane / CH) of the stage.  Rows past M (N) read
   // the last valid row; their results are never stored.
   const int lq = lane / CH;
-  const bool hi = wave < G % NWC;  // copies CP_HI groups (else CP_LO)
+  const int cw = CO ? max(wave - NW, 0) : wave;  // index among the copying wavefronts
+  const bool hi = cw < G % NCP;  // copies CP_HI groups (else CP_LO)
   const uint16_t* src[CP_HI];
 #pragma unroll
   for (int j = 0; j < CP_HI; ++j) {
-    const int g = min(wave + NWC * j, G - 1);
+    const int g = min(cw + NCP * j, G - 1);
     const int lchunk = (lane % CH) ^ dl_swz<BK>(RPG * g + lq);
     int brow = min(n0 + RPG * (g - GA) + lq, N - 1);
     if constexpr (EPI == kEpiQkvPack) brow = qkv_feature<BN>(brow, pk.d);
     src[j] = g < GA ? A + int64_t(min(m0 + RPG * g + lq, M - 1)) * K + kbeg + 8 * lchunk
                     : B + int64_t(brow) * K + kbeg + 8 * lchunk;
   }
-  const uint32_t lds0 = lds_offset(lds) + 1024 * wave;
+  const uint32_t lds0 = lds_offset(lds) + 1024 * cw;
 
   auto issue = [&](int it) {
+    if (CO && mw) return;  // the multiplying wavefronts issue no copies
     const uint32_t sa = __builtin_amdgcn_readfirstlane(lds0 + (it % NST) * STAGE);
 #pragma unroll
-    for (int j = 0; j < CP_LO; ++j) dma16(src[j] + it * BK, sa + 1024 * NWC * j);
+    for (int j = 0; j < CP_LO; ++j) dma16(src[j] + it * BK, sa + 1024 * NCP * j);
     if constexpr (CP_HI > CP_LO)
-      if (hi) dma16(src[CP_LO] + it * BK, sa + 1024 * NWC * CP_LO);
+      if (hi) dma16(src[CP_LO] + it * BK, sa + 1024 * NCP * CP_LO);
   };
   // Split ring: copy j < CPA of every wavefront is an A group, the rest B.
   auto issue_a = [&](int it) {
     const uint32_t sa = __builtin_amdgcn_readfirstlane(lds0 + (it % 2) * A_BYTES);
 #pragma unroll
-    for (int j = 0; j < CPA; ++j) dma16(src[j] + it * BK, sa + 1024 * NWC * j);
+    for (int j = 0; j < CPA; ++j) dma16(src[j] + it * BK, sa + 1024 * NCP * j);
   };
   auto issue_b = [&](int it) {
     const uint32_t sb = __builtin_amdgcn_readfirstlane(lds0 + 2 * A_BYTES + (it % 3) * B_BYTES - 1024 * GA);
 #pragma unroll
-    for (int j = CPA; j < CPA + CPB; ++j) dma16(src[j] + it * BK, sb + 1024 * NWC * j);
+    for (int j = CPA; j < CPA + CPB; ++j) dma16(src[j] + it * BK, sb + 1024 * NCP * j);
   };
   // vmcnt <= the copies of the newest `steps` issued steps.
   auto wait_steps = [&](auto steps) {
@@ -930,15 +938,17 @@ static hipError_t launch_dl(const uint16_t* A, int M, int K, const uint16_t* B, 
                             const uint16_t* bias, void* out, float* part, const GemmPlan& p,
                             int tiles, hipStream_t s, const QkvPack& pk = QkvPack{}, int tail_of = -1) {
   // 256 x 256: 8 wavefronts (2 per SIMD) of 128 x 64; 128 x 128: 8 of 32 x 64;
-  // 128 x 160 and 128 x 192: 4 of 32 x BN plus 4 that only copy.  K steps of
-  // 32 go through 4 stages, K steps of 64 through 3.
+  // 128 x 160 and 128 x 192: 4 of 32 x BN (one per SIMD) plus 4 that issue
+  // every copy of the K loop (CO).  K steps of 32 go through 4 stages, K steps
+  // of 64 through 3.
   constexpr int GWM = (BM == 256) ? 2 : 4, GWN = (BM == 256) ? 4 : (BN == 128 ? 2 : 1);
   constexpr int CW = (BK == 64 && GWM * GWN == 4) ? 4 : 0;
+  constexpr bool CO = CW > 0;
   constexpr int NST = BK == 64 ? 3 : 4;
   // 256 x 256 with K steps of 64: the split ring (2 A + 3 B slots, 160 KB).
   constexpr bool SR = BM == 256 && BN == 256 && BK == 64;
   const size_t lds = SR ? size_t(2 * BM + 3 * BN) * 2 * BK : size_t(NST) * dl_stage_bytes(BM, BN, BK);
-  auto kern = gemm_dl_kernel<BM, BN, GWM, GWN, NST, EPI, SPLIT, BK, CW, SK, SR>;
+  auto kern = gemm_dl_kernel<BM, BN, GWM, GWN, NST, EPI, SPLIT, BK, CW, SK, SR, CO>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (attr != hipSuccess) return attr;
