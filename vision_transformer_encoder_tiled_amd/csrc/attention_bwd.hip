@@ -289,8 +289,12 @@ __device__ __forceinline__ f32x16_t splat(float v) {
 
 // ---------------------------------------------------------------- dQ
 // Lane (ln, hf) of wavefront w: query q0 + 32w + ln; accumulator rows are
-// keys (S^T, dP^T) or dims (dQ^T).
-__global__ void __launch_bounds__(64 * NW) bwd_dq_kernel(
+// keys (S^T, dP^T) or dims (dQ^T).  CW > 0: CW more wavefronts that only
+// copy the key-side images and meet the others' per-tile barriers (with one
+// multiplying wavefront per SIMD, its own copy-issue stalls would leave the
+// matrix unit idle); the multiplying wavefronts then issue no copies.
+template <int CW>
+__global__ void __launch_bounds__(64 * (NW + CW)) bwd_dq_kernel(
     const char* __restrict__ qimg, const char* __restrict__ kimg, const int4* __restrict__ bdesc,
     int32_t heads, const int32_t* __restrict__ pos, int32_t n_pos, const float2* __restrict__ rope_cs,
     int32_t axis_code, float scale, void* __restrict__ dqkv, int32_t out_f32) {
@@ -304,13 +308,28 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_kernel(
   const int64_t tile_stride = int64_t(heads) * KS_BYTES;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, ln = lane & 31;
-  const uint32_t lds_wave = lds_offset(lds) + 1024 * wave;
+  constexpr int NCP = CW > 0 ? CW : NW;           // wavefronts that copy
+  static_assert(KS_BYTES % (1024 * NCP) == 0, "whole rounds of copies");
+  const int cwave = CW > 0 ? wave - NW : wave;    // index among them
+  const uint32_t lds_wave = lds_offset(lds) + 1024 * cwave;
   auto issue = [&](int t) {
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_wave + (t & 1) * KS_BYTES);
-    const char* g = src + t * tile_stride + 1024 * wave + 16 * lane;
+    const char* g = src + t * tile_stride + 1024 * cwave + 16 * lane;
 #pragma unroll
-    for (int c = 0; c < KS_BYTES / (1024 * NW); ++c) dma16(g + NW * 1024 * c, base + NW * 1024 * c);
+    for (int c = 0; c < KS_BYTES / (1024 * NCP); ++c) dma16(g + NCP * 1024 * c, base + NCP * 1024 * c);
   };
+  if constexpr (CW > 0) {
+    if (wave >= NW) {  // copy-only: tile t + 1 after the barrier of tile t, as below
+      __builtin_amdgcn_s_setprio(1);
+      issue(0);
+      for (int t = 0; t < ntiles; ++t) {
+        wait_vmcnt<0>();
+        wg_barrier();
+        if (t + 1 < ntiles) issue(t + 1);
+      }
+      return;
+    }
+  }
 
   const int qrow = q0 + 32 * wave + ln;
   const bool qvalid = qrow < end;
@@ -330,12 +349,13 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_kernel(
 #pragma unroll
   for (int d = 0; d < 3; ++d) acc[d] = splat(0.f);
 
-  issue(0);
+  if constexpr (CW == 0) issue(0);
   for (int t = 0; t < ntiles; ++t) {
     wait_vmcnt<0>();      // tile t has landed
     wait_lds_reads();     // and every wave is done with tile t - 1
     wg_barrier();
-    if (t + 1 < ntiles) issue(t + 1);
+    if constexpr (CW == 0)
+      if (t + 1 < ntiles) issue(t + 1);
     const char* st = lds + (t & 1) * KS_BYTES;
     const int koff = ln * ROW * 2 + 16 * hf;
     f32x16_t sc[2], dp[2];
@@ -384,8 +404,9 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_kernel(
 // queries (S, dP) or dims (dK^T, dV^T).  KW wavefronts (4 or 8) share one
 // stream of query-side images: the 96 KB ring allows one workgroup per CU,
 // so 8 wavefronts (256 keys) put two on each SIMD when the image is large.
-template <int KW>
-__global__ void __launch_bounds__(64 * KW) bwd_dkv_kernel(
+// CW > 0: CW copy-only wavefronts, as in bwd_dq_kernel.
+template <int KW, int CW>
+__global__ void __launch_bounds__(64 * (KW + CW)) bwd_dkv_kernel(
     const char* __restrict__ qimg, const char* __restrict__ kimg, const int4* __restrict__ bdesc,
     int32_t heads, const int32_t* __restrict__ pos, int32_t n_pos, const float2* __restrict__ rope_cs,
     int32_t axis_code, float dk_scale, void* __restrict__ dqkv, int32_t out_f32) {
@@ -399,14 +420,28 @@ __global__ void __launch_bounds__(64 * KW) bwd_dkv_kernel(
   const int64_t tile_stride = int64_t(heads) * QS_BYTES;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, ln = lane & 31;
-  const uint32_t lds_wave = lds_offset(lds) + 1024 * wave;
-  static_assert(QS_BYTES % (1024 * KW) == 0, "whole rounds of copies");
+  constexpr int NCP = CW > 0 ? CW : KW;           // wavefronts that copy
+  static_assert(QS_BYTES % (1024 * NCP) == 0, "whole rounds of copies");
+  const int cwave = CW > 0 ? wave - KW : wave;    // index among them
+  const uint32_t lds_wave = lds_offset(lds) + 1024 * cwave;
   auto issue = [&](int t) {
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_wave + (t & 1) * QS_BYTES);
-    const char* g = src + t * tile_stride + 1024 * wave + 16 * lane;
+    const char* g = src + t * tile_stride + 1024 * cwave + 16 * lane;
 #pragma unroll
-    for (int c = 0; c < QS_BYTES / (1024 * KW); ++c) dma16(g + KW * 1024 * c, base + KW * 1024 * c);
+    for (int c = 0; c < QS_BYTES / (1024 * NCP); ++c) dma16(g + NCP * 1024 * c, base + NCP * 1024 * c);
   };
+  if constexpr (CW > 0) {
+    if (wave >= KW) {  // copy-only: tile t + 1 after the barrier of tile t, as below
+      __builtin_amdgcn_s_setprio(1);
+      issue(0);
+      for (int t = 0; t < ntiles; ++t) {
+        wait_vmcnt<0>();
+        wg_barrier();
+        if (t + 1 < ntiles) issue(t + 1);
+      }
+      return;
+    }
+  }
 
   const int krow = k0 + 32 * wave + ln;
   const bool kvalid = krow < end;
@@ -424,12 +459,13 @@ __global__ void __launch_bounds__(64 * KW) bwd_dkv_kernel(
 #pragma unroll
   for (int d = 0; d < 3; ++d) { dv[d] = splat(0.f); dk[d] = splat(0.f); }
 
-  issue(0);
+  if constexpr (CW == 0) issue(0);
   for (int t = 0; t < ntiles; ++t) {
     wait_vmcnt<0>();
     wait_lds_reads();
     wg_barrier();
-    if (t + 1 < ntiles) issue(t + 1);
+    if constexpr (CW == 0)
+      if (t + 1 < ntiles) issue(t + 1);
     const char* st = lds + (t & 1) * QS_BYTES;
     const int qoff = ln * ROW * 2 + 16 * hf;
     // Initial values: -L and -D of each accumulator row's query.
@@ -495,10 +531,12 @@ hipError_t launch_attention_backward(const uint16_t* qkv, const uint16_t* dout, 
                                      const float2* rope_cs, float q_scale_log2, char* qimg,
                                      char* kimg, void* dqkv, bool out_f32, const int4* kdesc256,
                                      int32_t max_ktiles256, hipStream_t s) {
-  static const hipError_t a1 = set_lds(bwd_dq_kernel, 2 * KS_BYTES);
-  static const hipError_t a2 = set_lds(bwd_dkv_kernel<4>, 2 * QS_BYTES);
-  static const hipError_t a3 = set_lds(bwd_dkv_kernel<8>, 2 * QS_BYTES);
+  static const hipError_t a1 = set_lds(bwd_dq_kernel<0>, 2 * KS_BYTES);
+  static const hipError_t a1c = set_lds(bwd_dq_kernel<4>, 2 * KS_BYTES);
+  static const hipError_t a2 = set_lds(bwd_dkv_kernel<4, 4>, 2 * QS_BYTES);
+  static const hipError_t a3 = set_lds(bwd_dkv_kernel<8, 0>, 2 * QS_BYTES);
   if (a1 != hipSuccess) return a1;
+  if (a1c != hipSuccess) return a1c;
   if (a2 != hipSuccess) return a2;
   if (a3 != hipSuccess) return a3;
   const dim3 pack_grid(unsigned(int64_t(max_ktiles) * heads));
@@ -509,14 +547,21 @@ hipError_t launch_attention_backward(const uint16_t* qkv, const uint16_t* dout, 
   const unsigned blocks = unsigned(int64_t(max_btiles) * heads);
   const float rsqrt_hd = 1.0f / sqrtf(float(HD));
   const float ln2 = 0.6931471805599453f;  // dK from the log2(e)/sqrt(80)-scaled Q: times sqrt(80)/log2(e)/sqrt(80)
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3(blocks), dim3(64 * NW), 2 * KS_BYTES, s, qimg, kimg, bdesc,
-                     heads, pos_thw, n_pos, rope_cs, axis_code, rsqrt_hd, dqkv, out_f32 ? 1 : 0);
+  // dQ: two 72 KB workgroups fit a CU, whose registers hold 4 wavefronts
+  // per SIMD of this kernel; so copy-only wavefronts (one workgroup per CU)
+  // only when the grid is a single round of the 256 CUs.
+  if (blocks <= 256)
+    hipLaunchKernelGGL(bwd_dq_kernel<4>, dim3(blocks), dim3(64 * (NW + 4)), 2 * KS_BYTES, s, qimg, kimg, bdesc,
+                       heads, pos_thw, n_pos, rope_cs, axis_code, rsqrt_hd, dqkv, out_f32 ? 1 : 0);
+  else
+    hipLaunchKernelGGL(bwd_dq_kernel<0>, dim3(blocks), dim3(64 * NW), 2 * KS_BYTES, s, qimg, kimg, bdesc,
+                       heads, pos_thw, n_pos, rope_cs, axis_code, rsqrt_hd, dqkv, out_f32 ? 1 : 0);
   if (kdesc256)
-    hipLaunchKernelGGL(bwd_dkv_kernel<8>, dim3(unsigned(int64_t(max_ktiles256) * heads)), dim3(512),
+    hipLaunchKernelGGL((bwd_dkv_kernel<8, 0>), dim3(unsigned(int64_t(max_ktiles256) * heads)), dim3(512),
                        2 * QS_BYTES, s, qimg, kimg, kdesc256, heads, pos_thw, n_pos, rope_cs, axis_code,
                        ln2, dqkv, out_f32 ? 1 : 0);
   else
-    hipLaunchKernelGGL(bwd_dkv_kernel<4>, dim3(blocks), dim3(256), 2 * QS_BYTES, s, qimg, kimg, bdesc,
+    hipLaunchKernelGGL((bwd_dkv_kernel<4, 4>), dim3(blocks), dim3(512), 2 * QS_BYTES, s, qimg, kimg, bdesc,
                        heads, pos_thw, n_pos, rope_cs, axis_code, ln2, dqkv, out_f32 ? 1 : 0);
   return hipGetLastError();
 }
