@@ -578,8 +578,8 @@ def cpu_baseline(weights):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus %d is not supported "
-                                   "(the multi-GPU sharding is a design note, not code)" % a.gpus}))
+        print(json.dumps({"error": "the library runs on one GPU only; --gpus %d is not supported "
+                                   "(how the path would shard is described, not implemented)" % a.gpus}))
         sys.exit(2)
     if a.kernel:
         return kernel_only(a)
